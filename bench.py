@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark: 16-layer hybrid backbone forward on one MI355X.
+
+Workload: 160 users of 1000..2000 tokens (70 % H, 20 % R, 10 % T), d_model
+512, 8 query / 2 KV heads, head_dim 64, bf16 storage with fp32 accumulation,
+4 blocks of (1 full-attention + 3 target-attention) layers; seeded synthetic
+inputs (the pages' production logs are private).  One step = building the
+mask metadata for the batch + the whole 16-layer forward, in place on X (each
+step consumes the previous step's output; every step does the full work).
+
+Prints ONE JSON line on stdout: user-samples/s, the full-attention kernel's
+achieved masked TFLOP/s against the bf16 MFMA peak (its duration measured with
+HIP events on its own launch stream inside the timed region), a per-kernel
+breakdown from a second, separately timed pass, and the CPU oracle timed on a
+bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(n_rows_meta, lens, split):
+    """Sum of n_i over full-layer rows and over T rows (from the device metadata)."""
+    import numpy as np
+    n = n_rows_meta
+    off = np.concatenate([[0], np.cumsum(lens[:, 0] + lens[:, 1] + split * lens[:, 2])])
+    lc = lens[:, 0] + lens[:, 1]
+    t_sum = sum(int(n[off[u] + lc[u]:off[u + 1]].sum()) for u in range(len(lens)))
+    return int(n.sum()), t_sum
+
+
+def cpu_baseline(wl, seconds: float):
+    """Oracle backbone (float64 numpy) on users of the batch until `seconds` pass."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import model as om
+    r = om.bf16_round
+    full = [{k: (v if k.startswith("ln") else r(v)) for k, v in w.items()} for w in wl.full]
+    tgt = [{k: (v if k.startswith("ln") else r(v)) for k, v in w.items()} for w in wl.target]
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        om.backbone(wl.batch, wl.x, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=r, users=[done])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= wl.batch.n_users:
+            break
+    threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = int(max(threads)) if threads else 1
+    return {"value": done / el, "unit": "user-samples/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {done} of {wl.batch.n_users} users, 16-layer backbone forward, float64 numpy, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    log("generating config-3 workload ...")
+    wl = synth.config3()
+    dw = DeviceWorkload(wl)
+    batch, dims = dw.batch, dw.dims
+    lay = B.meta_layout(batch)
+    meta = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
+    ws = B.workspace(batch, dims, B.OP_BACKBONE)
+    x = dw.x
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.mask_build(batch, meta)
+        B.backbone_fwd(batch, dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, x, ws)
+
+    log(f"rows={lay.n_rows} t_rows={lay.n_t_rows} full_tiles={lay.n_full_tiles} target_tiles={lay.n_target_tiles}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # counters for the FLOP / byte model (from the device metadata of this batch)
+    views = B.meta_views(meta, lay, wl.batch.n_users)
+    n_host = views["n"].cpu().numpy().astype(np.int64)
+    pairs_full, pairs_t = visible_pairs(n_host, wl.batch.lens.astype(np.int64), wl.batch.split)
+    d = wl.dims
+    H, G, dh, D = d.n_q_heads, d.n_kv_heads, d.head_dim, d.d_model
+    hd, gd = H * dh, G * dh
+    R, T, C = lay.n_rows, lay.n_t_rows, lay.n_ctx_rows
+    attn_full_flops = 4.0 * dh * H * pairs_full
+    attn_t_flops = 4.0 * dh * H * pairs_t
+    proj_full_flops = 2.0 * R * D * (2 * hd + 2 * gd) + 2.0 * R * hd * D
+    proj_t_flops = 2.0 * R * D * 2 * gd + 2.0 * T * D * 2 * hd + 2.0 * T * hd * D
+    layers_full, layers_t = wl.n_blocks, wl.n_blocks * wl.k_target
+    step_flops = layers_full * (attn_full_flops + proj_full_flops) + layers_t * (attn_t_flops + proj_t_flops)
+    # target attention algorithmic bytes: K and V of every row read once, Q and U of T rows in, Y out
+    attn_t_bytes = 2.0 * (R * 2 * gd + 3 * T * hd)
+
+    # ---- timed region: full-attention kernel bracketed by events on its stream
+    B.timing_enable([B.K_ATTN_FULL])
+    B.timing_read(B.K_ATTN_FULL)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.timing_enable([])
+    n_attn, ms_attn = B.timing_read(B.K_ATTN_FULL)
+    elapsed = t1 - t0
+    ms_step = 1000.0 * elapsed / args.steps
+    samples_s = wl.batch.n_users * args.steps / elapsed
+    attn_ms = ms_attn / max(1, n_attn)
+    attn_tflops = attn_full_flops / (attn_ms * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, {samples_s:.1f} user-samples/s; "
+        f"full attention {attn_ms:.3f} ms/launch -> {attn_tflops:.1f} TFLOP/s")
+
+    breakdown = None
+    if not args.no_breakdown:
+        classes = [B.K_MASK, B.K_GLN, B.K_GEMM_UQKV, B.K_ATTN_FULL, B.K_GEMM_OUT, B.K_GEMM_KV, B.K_GEMM_T,
+                   B.K_ATTN_TARGET]
+        names = ["mask", "gln", "gemm_uqkv", "attn_full", "gemm_out", "gemm_kv", "gemm_t", "attn_target"]
+        B.timing_enable(classes)
+        for k in classes:
+            B.timing_read(k)
+        kb = max(2, args.steps // 4)
+        for _ in range(kb):
+            step()
+        torch.cuda.synchronize()
+        B.timing_enable([])
+        breakdown = {}
+        for k, nm in zip(classes, names):
+            n, ms = B.timing_read(k)
+            breakdown[nm] = {"launches_per_step": n / kb, "ms_per_step": ms / kb,
+                             "ms_per_launch": ms / max(1, n)}
+        tat = breakdown["attn_target"]["ms_per_launch"]
+        breakdown["attn_target"]["achieved_GBs"] = attn_t_bytes / (tat * 1e-3) / 1e9 if tat > 0 else None
+        breakdown["attn_target"]["hbm_frac"] = (breakdown["attn_target"]["achieved_GBs"] or 0) / HBM_PEAK_GBS
+        breakdown["attn_target"]["achieved_TFLOPs"] = attn_t_flops / (tat * 1e-3) / 1e12 if tat > 0 else None
+        full_ms = (breakdown["attn_full"]["ms_per_step"] + breakdown["gemm_uqkv"]["ms_per_step"]
+                   + breakdown["gemm_out"]["ms_per_step"])
+        breakdown["full_layers_masked_TFLOPs"] = layers_full * (attn_full_flops + proj_full_flops) / (full_ms * 1e-3) / 1e12
+        breakdown["full_layers_mfma_frac"] = breakdown["full_layers_masked_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+        breakdown["sum_ms_per_step"] = sum(v["ms_per_step"] for v in breakdown.values() if isinstance(v, dict))
+        log("breakdown: " + json.dumps(breakdown))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": "user-samples/s, 16-layer hybrid attn fwd; masked TFLOP/s vs MFMA peak",
+        "value": samples_s,
+        "unit": "user-samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "config 3: 16-layer hybrid backbone fwd (4 x (1 full + 3 target)), 160 users, "
+                               "N~U[1000,2000] 70/20/10 H/R/T, d 512, 8Q/2KV, dh 64",
+                   "users": wl.batch.n_users, "rows": int(R), "t_rows": int(T), "parallelism": "single-gpu"},
+        "step_algorithmic_TFLOP": step_flops / 1e12,
+        "step_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
+        "roofline": {"kernel": "attn_bf16_kernel (full layer)", "bound": "mfma", "achieved": attn_tflops,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "flops_per_launch": attn_full_flops, "ms_per_launch": attn_ms},
+        "breakdown": breakdown,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,292 @@
+"""ctypes binding of libmtfm (argument marshalling only).
+
+Every function here turns torch tensors into the plain pointers and sizes of
+the C ABI declared in include/mtfm.h and calls it on the current torch
+stream.  All computation happens in the HIP library; if libmtfm.so is missing
+or fails to load, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p, c_char_p
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmtfm.so")
+
+OK, E_NULL, E_DIMS, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+OP_FULL, OP_TARGET, OP_BACKBONE, OP_FULL_BWD, OP_TARGET_BWD = 0, 1, 2, 3, 4
+TILE = 64
+UT_ROW, UT_ACT, UT_PARENT, UT_CTX, UT_FTILE, UT_TTILE, UT_TROW = range(7)
+
+# Names of the entry points declared in include/mtfm.h.
+ENTRY_POINTS = [
+    "mtfm_meta_bytes", "mtfm_meta_layout_of", "mtfm_mask_build", "mtfm_workspace_bytes",
+    "mtfm_workspace_probe", "mtfm_attn_full", "mtfm_attn_target", "mtfm_backbone_fwd",
+    "mtfm_attn_full_bwd", "mtfm_attn_target_bwd", "mtfm_timing_enable", "mtfm_timing_read",
+    "mtfm_status_str", "mtfm_last_error",
+]
+K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD = range(9)
+
+
+class MtfmError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status}) {detail}".rstrip())
+
+
+class CBatch(ctypes.Structure):
+    _fields_ = [("n_users", c_int32), ("split", c_int32), ("lens_h", c_void_p), ("lens_d", c_void_p),
+                ("ts_r_d", c_void_p), ("ts_t_d", c_void_p)]
+
+
+class CDims(ctypes.Structure):
+    _fields_ = [("d_model", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32), ("head_dim", c_int32),
+                ("ln_eps", c_float), ("dtype", c_int32)]
+
+
+class CFullW(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("ln1_g", "ln1_b", "w_uqkv", "ln2_g", "ln2_b", "w_o")]
+
+
+class CTargetW(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o")]
+
+
+class CFullGrad(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("ln1_g", "ln1_b", "w_uqkv", "ln2_g", "ln2_b", "w_o")]
+
+
+class CTargetGrad(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o")]
+
+
+class CMetaLayout(ctypes.Structure):
+    _fields_ = [(n, c_int64) for n in (
+        "n_rows", "n_t_rows", "n_parents", "n_ctx_rows", "n_full_tiles", "n_target_tiles", "off_user", "off_p",
+        "off_n", "off_type", "off_full_tiles", "off_target_tiles", "off_ctx_rows", "off_parent_row", "total_bytes")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmtfm (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmtfm.so is not built ({LIB_PATH}); run python -m hybrid_masked_attention_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.mtfm_meta_bytes.argtypes = [P(CBatch)]; L.mtfm_meta_bytes.restype = c_size_t
+    L.mtfm_meta_layout_of.argtypes = [P(CBatch), P(CMetaLayout)]; L.mtfm_meta_layout_of.restype = c_int32
+    L.mtfm_mask_build.argtypes = [P(CBatch), c_void_p, c_size_t, c_void_p]; L.mtfm_mask_build.restype = c_int32
+    L.mtfm_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]; L.mtfm_workspace_bytes.restype = c_size_t
+    L.mtfm_workspace_probe.argtypes = [P(CBatch), P(CDims), c_int32, P(c_int64), P(c_int64)]
+    L.mtfm_workspace_probe.restype = c_int32
+    L.mtfm_attn_full.argtypes = [P(CBatch), P(CDims), c_void_p, P(CFullW), c_void_p, c_void_p, c_void_p, c_size_t,
+                                 c_void_p]
+    L.mtfm_attn_full.restype = c_int32
+    L.mtfm_attn_target.argtypes = [P(CBatch), P(CDims), c_void_p, P(CTargetW), c_void_p, c_void_p, c_void_p,
+                                   c_size_t, c_void_p]
+    L.mtfm_attn_target.restype = c_int32
+    L.mtfm_backbone_fwd.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_void_p, P(CFullW), P(CTargetW),
+                                    c_void_p, c_void_p, c_size_t, c_void_p]
+    L.mtfm_backbone_fwd.restype = c_int32
+    L.mtfm_attn_full_bwd.argtypes = [P(CBatch), P(CDims), c_void_p, P(CFullW), c_void_p, c_void_p, c_void_p,
+                                     P(CFullGrad), c_void_p, c_size_t, c_void_p]
+    L.mtfm_attn_full_bwd.restype = c_int32
+    L.mtfm_attn_target_bwd.argtypes = [P(CBatch), P(CDims), c_void_p, P(CTargetW), c_void_p, c_void_p, c_void_p,
+                                       P(CTargetGrad), c_void_p, c_size_t, c_void_p]
+    L.mtfm_attn_target_bwd.restype = c_int32
+    L.mtfm_timing_enable.argtypes = [ctypes.c_uint32]; L.mtfm_timing_enable.restype = c_int32
+    L.mtfm_timing_read.argtypes = [c_int32, P(c_int64), P(ctypes.c_double)]; L.mtfm_timing_read.restype = c_int32
+    L.mtfm_status_str.argtypes = [c_int32]; L.mtfm_status_str.restype = c_char_p
+    L.mtfm_last_error.argtypes = []; L.mtfm_last_error.restype = c_char_p
+    _lib = L
+    return L
+
+
+def status_str(s: int) -> str:
+    try:
+        return lib().mtfm_status_str(int(s)).decode()
+    except Exception:  # noqa: BLE001 - used while formatting another error
+        return str(s)
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        detail = lib().mtfm_last_error().decode() if status == E_HIP else ""
+        raise MtfmError(status, where, detail)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+class DeviceBatch:
+    """A jagged batch on the device plus the host lengths, as the C struct wants it.
+
+    lens: int32 [B, 3] (L_H, L_R, L_T parents); ts_r / ts_t int32 (numpy or
+    torch).  `device` is a torch device string or None for a host-only batch
+    (enough for sizes and argument checks).
+    """
+
+    def __init__(self, lens, split: int, ts_r, ts_t, device: Optional[str] = "cuda"):
+        import torch
+        self.lens_h = torch.as_tensor(np.ascontiguousarray(np.asarray(lens, dtype=np.int32).reshape(-1, 3)))
+        self.split = int(split)
+        self.n_users = int(self.lens_h.shape[0])
+        ts_r = torch.as_tensor(np.ascontiguousarray(np.asarray(ts_r, dtype=np.int32)))
+        ts_t = torch.as_tensor(np.ascontiguousarray(np.asarray(ts_t, dtype=np.int32)))
+        if device is not None:
+            self.lens_d = self.lens_h.to(device)
+            self.ts_r_d = ts_r.to(device)
+            self.ts_t_d = ts_t.to(device)
+        else:
+            self.lens_d = self.ts_r_d = self.ts_t_d = None
+        self.c = CBatch(self.n_users, self.split, _ptr(self.lens_h), _ptr(self.lens_d),
+                        _ptr(self.ts_r_d) if (self.ts_r_d is not None and self.ts_r_d.numel()) else None,
+                        _ptr(self.ts_t_d) if (self.ts_t_d is not None and self.ts_t_d.numel()) else None)
+
+    @classmethod
+    def from_synth(cls, b, device="cuda"):
+        return cls(b.lens, b.split, b.ts_r, b.ts_t, device)
+
+
+def make_dims(d_model, n_q_heads, n_kv_heads, head_dim, ln_eps=1e-5, dtype=BF16) -> CDims:
+    return CDims(int(d_model), int(n_q_heads), int(n_kv_heads), int(head_dim), float(ln_eps), int(dtype))
+
+
+def meta_layout(batch: DeviceBatch) -> CMetaLayout:
+    out = CMetaLayout()
+    _check(lib().mtfm_meta_layout_of(ctypes.byref(batch.c), ctypes.byref(out)), "mtfm_meta_layout_of")
+    return out
+
+
+def meta_bytes(batch: DeviceBatch) -> int:
+    return int(lib().mtfm_meta_bytes(ctypes.byref(batch.c)))
+
+
+def mask_build(batch: DeviceBatch, meta=None, stream=None):
+    """Build the mask metadata into `meta` (a uint8 device tensor; allocated if None)."""
+    import torch
+    nb = meta_bytes(batch)
+    if meta is None:
+        meta = torch.empty(max(nb, 1), dtype=torch.uint8, device=batch.lens_d.device)
+    _check(lib().mtfm_mask_build(ctypes.byref(batch.c), _ptr(meta), meta.numel(), _stream(stream)), "mtfm_mask_build")
+    return meta
+
+
+def meta_views(meta, layout: CMetaLayout, n_users: int) -> Dict[str, "object"]:
+    """Typed views of the metadata arrays (torch tensors aliasing `meta`)."""
+    import torch
+
+    def view(off, count, dtype, shape=None):
+        itemsize = torch.empty(0, dtype=dtype).element_size()
+        t = meta[off:off + count * itemsize].view(dtype)
+        return t.view(*shape) if shape else t
+    L = layout
+    return {
+        "user": view(L.off_user, 7 * (n_users + 1), torch.int32, (7, n_users + 1)),
+        "p": view(L.off_p, L.n_rows, torch.int32),
+        "n": view(L.off_n, L.n_rows, torch.int32),
+        "row_type": view(L.off_type, L.n_rows, torch.uint8),
+        "full_tiles": view(L.off_full_tiles, L.n_full_tiles * 8, torch.int32, (L.n_full_tiles, 8)),
+        "target_tiles": view(L.off_target_tiles, L.n_target_tiles * 8, torch.int32, (L.n_target_tiles, 8)),
+        "ctx_rows": view(L.off_ctx_rows, L.n_ctx_rows, torch.int32),
+        "parent_row": view(L.off_parent_row, L.n_parents, torch.int32),
+    }
+
+
+def workspace_bytes(batch: DeviceBatch, dims: CDims, op: int) -> int:
+    return int(lib().mtfm_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(op)))
+
+
+def workspace(batch: DeviceBatch, dims: CDims, op: int, device="cuda"):
+    import torch
+    return torch.empty(max(workspace_bytes(batch, dims, op), 1), dtype=torch.uint8, device=device)
+
+
+def workspace_probe(batch: DeviceBatch, dims: CDims, op: int):
+    a, y = c_int64(), c_int64()
+    _check(lib().mtfm_workspace_probe(ctypes.byref(batch.c), ctypes.byref(dims), int(op), ctypes.byref(a),
+                                      ctypes.byref(y)), "mtfm_workspace_probe")
+    return int(a.value), int(y.value)
+
+
+def full_w(w: Dict[str, "object"]) -> CFullW:
+    return CFullW(*[_ptr(w[n]) for n in ("ln1_g", "ln1_b", "w_uqkv", "ln2_g", "ln2_b", "w_o")])
+
+
+def target_w(w: Dict[str, "object"]) -> CTargetW:
+    return CTargetW(*[_ptr(w[n]) for n in ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o")])
+
+
+def attn_full(batch, dims, meta, w, x_in, x_out, ws, stream=None):
+    cw = full_w(w)
+    _check(lib().mtfm_attn_full(ctypes.byref(batch.c), ctypes.byref(dims), _ptr(meta), ctypes.byref(cw),
+                                _ptr(x_in), _ptr(x_out), _ptr(ws), ws.numel(), _stream(stream)), "mtfm_attn_full")
+    return x_out
+
+
+def attn_target(batch, dims, meta, w, x_in, x_out, ws, stream=None):
+    cw = target_w(w)
+    _check(lib().mtfm_attn_target(ctypes.byref(batch.c), ctypes.byref(dims), _ptr(meta), ctypes.byref(cw),
+                                  _ptr(x_in), _ptr(x_out), _ptr(ws), ws.numel(), _stream(stream)), "mtfm_attn_target")
+    return x_out
+
+
+def backbone_fwd(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], tgt: Sequence[Dict], x_inout, ws,
+                 stream=None):
+    fa = (CFullW * max(1, len(full)))(*[full_w(w) for w in full])
+    ta = (CTargetW * max(1, len(tgt)))(*[target_w(w) for w in tgt])
+    _check(lib().mtfm_backbone_fwd(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks), int(k_target),
+                                   _ptr(meta), fa, ta, _ptr(x_inout), _ptr(ws), ws.numel(), _stream(stream)),
+           "mtfm_backbone_fwd")
+    return x_inout
+
+
+def attn_full_bwd(batch, dims, meta, w, x_in, dy, dx, grads: Dict, ws, stream=None):
+    cw = full_w(w)
+    cg = CFullGrad(*[_ptr(grads[n]) for n in ("ln1_g", "ln1_b", "w_uqkv", "ln2_g", "ln2_b", "w_o")])
+    _check(lib().mtfm_attn_full_bwd(ctypes.byref(batch.c), ctypes.byref(dims), _ptr(meta), ctypes.byref(cw),
+                                    _ptr(x_in), _ptr(dy), _ptr(dx), ctypes.byref(cg), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "mtfm_attn_full_bwd")
+    return dx
+
+
+def attn_target_bwd(batch, dims, meta, w, x_in, dy, dx, grads: Dict, ws, stream=None):
+    cw = target_w(w)
+    cg = CTargetGrad(*[_ptr(grads[n]) for n in ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o")])
+    _check(lib().mtfm_attn_target_bwd(ctypes.byref(batch.c), ctypes.byref(dims), _ptr(meta), ctypes.byref(cw),
+                                      _ptr(x_in), _ptr(dy), _ptr(dx), ctypes.byref(cg), _ptr(ws), ws.numel(),
+                                      _stream(stream)), "mtfm_attn_target_bwd")
+    return dx
+
+
+def timing_enable(classes: Sequence[int]):
+    """Bracket launches of the given kernel classes with HIP events (empty = off)."""
+    mask = 0
+    for k in classes:
+        mask |= 1 << int(k)
+    _check(lib().mtfm_timing_enable(mask), "mtfm_timing_enable")
+
+
+def timing_read(kclass: int):
+    """(launches, total ms) recorded for a kernel class since the last read."""
+    n, ms = c_int64(), ctypes.c_double()
+    _check(lib().mtfm_timing_read(int(kclass), ctypes.byref(n), ctypes.byref(ms)), "mtfm_timing_read")
+    return int(n.value), float(ms.value)

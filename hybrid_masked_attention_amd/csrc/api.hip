@@ -1,0 +1,434 @@
+// C ABI of libmtfm: argument validation, metadata and workspace layout, and
+// the launch sequences of the full-attention layer, the target-attention
+// layer and the hybrid backbone.  Host code only; kernels live in the other
+// translation units.  No entry point allocates, synchronises or reads device
+// memory back.
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "api_internal.h"
+
+thread_local std::string g_last_error;
+
+mtfm_status hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return MTFM_E_HIP;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// Metadata plan: totals from the host lengths, array offsets in the buffer.
+mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan) {
+  if (!b || !plan) return MTFM_E_NULL;
+  if (b->n_users < 0) return MTFM_E_DIMS;
+  if (b->split != 1 && b->split != 4) return MTFM_E_DIMS;
+  if (b->n_users > 0 && !b->lens_h) return MTFM_E_NULL;
+  MetaPlan p;
+  p.n_users = b->n_users;
+  p.split = b->split;
+  for (int u = 0; u < b->n_users; ++u) {
+    const int64_t lh = b->lens_h[3 * u], lr = b->lens_h[3 * u + 1], lt = b->lens_h[3 * u + 2];
+    if (lh < 0 || lr < 0 || lt < 0) return MTFM_E_DIMS;
+    const int64_t rows = lh + lr + b->split * lt;
+    p.n_rows += rows;
+    p.n_t_rows += b->split * lt;
+    p.n_parents += lt;
+    p.n_ctx_rows += lh + lr;
+    p.n_full_tiles += (rows + kTile - 1) / kTile;
+    p.n_target_tiles += (b->split * lt + kTile - 1) / kTile;
+    p.max_user_rows = (int32_t)std::min<int64_t>(std::max<int64_t>(p.max_user_rows, rows), INT32_MAX);
+    p.max_t_rows = (int32_t)std::min<int64_t>(std::max<int64_t>(p.max_t_rows, b->split * lt), INT32_MAX);
+    if (p.n_rows > INT32_MAX - 4096) return MTFM_E_DIMS;
+  }
+  mtfm_meta_layout& l = p.lay;
+  l.n_rows = p.n_rows; l.n_t_rows = p.n_t_rows; l.n_parents = p.n_parents; l.n_ctx_rows = p.n_ctx_rows;
+  l.n_full_tiles = p.n_full_tiles; l.n_target_tiles = p.n_target_tiles;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
+  l.off_user = take((int64_t)UT_COUNT * (p.n_users + 1) * 4);
+  l.off_p = take(p.n_rows * 4);
+  l.off_n = take(p.n_rows * 4);
+  l.off_type = take(p.n_rows);
+  l.off_full_tiles = take(p.n_full_tiles * 32);
+  l.off_target_tiles = take(p.n_target_tiles * 32);
+  l.off_ctx_rows = take(p.n_ctx_rows * 4);
+  l.off_parent_row = take(p.n_parents * 4);
+  l.total_bytes = off;
+  *plan = p;
+  return MTFM_OK;
+}
+
+MetaPtrs meta_ptrs(const MetaPlan& plan, const void* meta_d) {
+  const char* base = static_cast<const char*>(meta_d);
+  MetaPtrs m;
+  m.user = reinterpret_cast<const int32_t*>(base + plan.lay.off_user);
+  m.p = reinterpret_cast<const int32_t*>(base + plan.lay.off_p);
+  m.n = reinterpret_cast<const int32_t*>(base + plan.lay.off_n);
+  m.type = reinterpret_cast<const uint8_t*>(base + plan.lay.off_type);
+  m.full_tiles = reinterpret_cast<const int32_t*>(base + plan.lay.off_full_tiles);
+  m.target_tiles = reinterpret_cast<const int32_t*>(base + plan.lay.off_target_tiles);
+  m.ctx_rows = reinterpret_cast<const int32_t*>(base + plan.lay.off_ctx_rows);
+  m.parent_row = reinterpret_cast<const int32_t*>(base + plan.lay.off_parent_row);
+  return m;
+}
+
+mtfm_status check_dims(const mtfm_dims* d) {
+  if (!d) return MTFM_E_NULL;
+  if (d->d_model <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0) return MTFM_E_DIMS;
+  if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps)) return MTFM_E_DIMS;
+  if (d->dtype != MTFM_F32 && d->dtype != MTFM_BF16) return MTFM_E_UNSUPPORTED;
+  if (d->n_q_heads % d->n_kv_heads != 0) return MTFM_E_UNSUPPORTED;
+  const int hd = d->n_q_heads * d->head_dim;
+  if (d->dtype == MTFM_BF16) {
+    if (d->head_dim != 64) return MTFM_E_UNSUPPORTED;
+    const int r = d->n_q_heads / d->n_kv_heads;
+    if (r != 1 && r != 2 && r != 4 && r != 8) return MTFM_E_UNSUPPORTED;
+  } else {
+    if (d->head_dim != 32 && d->head_dim != 64) return MTFM_E_UNSUPPORTED;
+  }
+  if (d->d_model % 64 != 0 || hd % 64 != 0 || d->d_model > 1024 || hd > 1024) return MTFM_E_UNSUPPORTED;
+  return MTFM_OK;
+}
+
+// Workspace layout of one forward layer (byte offsets, 256-B aligned).
+LayerWs layer_ws(const MetaPlan& p, const mtfm_dims* d, int op) {
+  const int64_t es = elem_size(d->dtype);
+  const int64_t hd = (int64_t)d->n_q_heads * d->head_dim, gd = (int64_t)d->n_kv_heads * d->head_dim;
+  const int64_t zw = 2 * hd + 2 * gd;
+  LayerWs w;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
+  w.xt = take(p.n_rows * d->d_model * es);
+  if (op == MTFM_OP_FULL) {
+    w.z = take(p.n_rows * zw * es);
+    w.a = take(p.n_rows * hd * es);
+    w.y = take(p.n_rows * hd * es);
+  } else {
+    w.kv = take(p.n_rows * 2 * gd * es);
+    w.z = take(p.n_t_rows * zw * es);
+    w.a = take(p.n_t_rows * hd * es);
+    w.y = take(p.n_t_rows * hd * es);
+  }
+  w.total = off;
+  return w;
+}
+
+namespace {
+
+mtfm_status check_batch_device(const mtfm_batch* b, const MetaPlan& p) {
+  if (p.n_users > 0 && !b->lens_d) return MTFM_E_NULL;
+  int64_t n_act = 0;
+  for (int u = 0; u < p.n_users; ++u) n_act += b->lens_h[3 * u + 1];
+  if (n_act > 0 && !b->ts_r_d) return MTFM_E_NULL;
+  if (p.n_parents > 0 && !b->ts_t_d) return MTFM_E_NULL;
+  return MTFM_OK;
+}
+
+mtfm_status check_full_w(const mtfm_full_w* w) {
+  if (!w || !w->ln1_g || !w->ln1_b || !w->w_uqkv || !w->ln2_g || !w->ln2_b || !w->w_o) return MTFM_E_NULL;
+  return MTFM_OK;
+}
+
+mtfm_status check_target_w(const mtfm_target_w* w) {
+  if (!w || !w->ln1_g || !w->ln1_b || !w->w_u || !w->w_q || !w->w_kv || !w->ln2_g || !w->ln2_b || !w->w_o)
+    return MTFM_E_NULL;
+  return MTFM_OK;
+}
+
+}  // namespace
+
+mtfm_status prepare(const mtfm_batch* b, const mtfm_dims* d, const void* meta_d, const void* x0, const void* x1,
+                    void* ws, size_t ws_bytes, int op, Ctx* c, void* stream) {
+  TRY(plan_meta(b, &c->plan));
+  TRY(check_dims(d));
+  if (!meta_d || !x0 || !x1) return MTFM_E_NULL;
+  TRY(check_batch_device(b, c->plan));
+  const size_t need = mtfm_workspace_bytes(b, d, op);
+  if (need > 0 && !ws) return MTFM_E_NULL;
+  if (ws_bytes < need) return MTFM_E_WORKSPACE;
+  c->b = b;
+  c->meta = meta_ptrs(c->plan, meta_d);
+  c->s = (hipStream_t)stream;
+  return MTFM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Full-attention layer ([explainer] §4.1):
+//   X~ = GLN1(X); [U|Q|K|V] = SiLU(X~ W^T); A = masked SiLU attention / n;
+//   X' = (GLN2(A) (.) U) W_o^T + X
+mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out,
+                     char* ws) {
+  const MetaPlan& p = c.plan;
+  const int dt = d->dtype;
+  const int64_t es = elem_size(dt);
+  const int H = d->n_q_heads, G = d->n_kv_heads, dh = d->head_dim, D = d->d_model;
+  const int hd = H * dh, gd = G * dh, zw = 2 * hd + 2 * gd;
+  const LayerWs L = layer_ws(p, d, MTFM_OP_FULL);
+  char* xt = ws + L.xt;
+  char* z = ws + L.z;
+  char* a = ws + L.a;
+  char* y = ws + L.y;
+  if (p.n_rows == 0) return MTFM_OK;
+
+  GlnArgs g1{};
+  g1.rows = (int32_t)p.n_rows; g1.D = D; g1.x = x_in; g1.ldx = D; g1.y = xt; g1.ldy = D;
+  g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
+  TRY(timed_gln(g1, dt, c.s));
+
+  GemmArgs gp{};
+  gp.M = (int32_t)p.n_rows; gp.N = zw; gp.K = D; gp.groups = 1;
+  gp.A = xt; gp.lda = D; gp.amap = identity_map();
+  gp.B[0] = w->w_uqkv; gp.bn[0] = zw; gp.ldb = D;
+  gp.cmap = identity_map();
+  gp.epi = EPI_SILU_SPLIT;
+  gp.dst[0] = z; gp.ld[0] = zw; gp.cend[0] = hd; gp.scale[0] = 1.f;
+  gp.dst[1] = z + hd * es; gp.ld[1] = zw; gp.cend[1] = 2 * hd; gp.scale[1] = q_scale(dh);
+  gp.dst[2] = z + 2 * hd * es; gp.ld[2] = zw; gp.cend[2] = zw; gp.scale[2] = 1.f;
+  gp.cend[3] = zw;
+  TRY(timed_gemm(MTFM_K_GEMM_UQKV, gp, dt, c.s));
+
+  AttnArgs aa{};
+  aa.q = z + hd * es; aa.ldq = zw;
+  aa.k = z + 2 * hd * es; aa.ldk = zw;
+  aa.v = z + (2 * hd + gd) * es; aa.ldv = zw;
+  aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
+  aa.a = a; aa.lda = hd;
+  aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
+  aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
+  aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+  TRY(timed_attention(MTFM_K_ATTN_FULL, aa, dt, c.s));
+
+  GlnArgs g2{};
+  g2.rows = (int32_t)p.n_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
+  g2.gate = z; g2.ldg = zw;
+  g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = c.meta.type; g2.eps = d->ln_eps;
+  TRY(timed_gln(g2, dt, c.s));
+
+  GemmArgs go{};
+  go.M = (int32_t)p.n_rows; go.N = D; go.K = hd; go.groups = 1;
+  go.A = y; go.lda = hd; go.amap = identity_map();
+  go.B[0] = w->w_o; go.bn[0] = D; go.ldb = hd;
+  go.cmap = identity_map();
+  go.epi = EPI_RESID; go.resid = x_in; go.ldr = D; go.out = x_out; go.ldo = D;
+  TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
+  return MTFM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Target-attention layer ([explainer] §4.2; V2 per-sub-token Q, [blog] §3.3.2):
+//   X~ = GLN1(X) on all rows; [K|V] = SiLU(X~ W_kv^T) on H/R rows (a T row's
+//   own K/V comes from its row GEMM below, it is the only T key it sees);
+//   [U_T|Q_T|K_T|V_T] = SiLU(X~_T [W_u; W_q[k]; W_kv]^T) per sub-token k;
+//   A_T = masked attention; X'_T = (GLN2(A_T) (.) U_T) W_o^T + X_T.
+mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in, void* x_out,
+                       char* ws) {
+  const MetaPlan& p = c.plan;
+  const int dt = d->dtype;
+  const int64_t es = elem_size(dt);
+  const int H = d->n_q_heads, G = d->n_kv_heads, dh = d->head_dim, D = d->d_model;
+  const int hd = H * dh, gd = G * dh, zw = 2 * hd + 2 * gd;
+  const int S = p.split;
+  const LayerWs L = layer_ws(p, d, MTFM_OP_TARGET);
+  char* xt = ws + L.xt;
+  char* kv = ws + L.kv;
+  char* zt = ws + L.z;
+  char* a = ws + L.a;
+  char* y = ws + L.y;
+  if (x_out != x_in && p.n_rows > 0) {
+    hipError_t e = hipMemcpyAsync(x_out, x_in, (size_t)p.n_rows * D * es, hipMemcpyDeviceToDevice, c.s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  }
+  if (p.n_t_rows == 0) return MTFM_OK;
+
+  GlnArgs g1{};
+  g1.rows = (int32_t)p.n_rows; g1.D = D; g1.x = x_in; g1.ldx = D; g1.y = xt; g1.ldy = D;
+  g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
+  TRY(timed_gln(g1, dt, c.s));
+
+  if (p.n_ctx_rows > 0) {
+    GemmArgs gk{};
+    gk.M = (int32_t)p.n_ctx_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
+    gk.A = xt; gk.lda = D; gk.amap = RowMap{c.meta.ctx_rows, 0, 0};
+    gk.B[0] = w->w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
+    gk.cmap = RowMap{c.meta.ctx_rows, 0, 0};
+    gk.epi = EPI_SILU_SPLIT;
+    gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = 2 * gd; gk.scale[0] = 1.f;
+    gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd;
+    TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s));
+  }
+
+  GemmArgs gt{};
+  gt.M = (int32_t)p.n_parents; gt.N = zw; gt.K = D; gt.groups = S;
+  gt.A = xt; gt.lda = D; gt.amap = RowMap{c.meta.parent_row, 0, 0}; gt.amap_zadd = 1;
+  gt.B[0] = w->w_u; gt.bn[0] = hd;
+  gt.B[1] = w->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
+  gt.B[2] = w->w_kv; gt.bn[2] = 2 * gd;
+  gt.ldb = D;
+  gt.cmap = RowMap{nullptr, S, 0}; gt.cmap_zadd = 1;
+  gt.epi = EPI_SILU_SPLIT;
+  gt.dst[0] = zt; gt.ld[0] = zw; gt.cend[0] = hd; gt.scale[0] = 1.f;
+  gt.dst[1] = zt + hd * es; gt.ld[1] = zw; gt.cend[1] = 2 * hd; gt.scale[1] = q_scale(dh);
+  gt.dst[2] = zt + 2 * hd * es; gt.ld[2] = zw; gt.cend[2] = zw; gt.scale[2] = 1.f;
+  gt.cend[3] = zw;
+  TRY(timed_gemm(MTFM_K_GEMM_T, gt, dt, c.s));
+
+  AttnArgs aa{};
+  aa.q = zt + hd * es; aa.ldq = zw;
+  aa.k = kv; aa.ldk = 2 * gd;
+  aa.v = kv + gd * es; aa.ldv = 2 * gd;
+  aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
+  aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
+  aa.a = a; aa.lda = hd;
+  aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
+  aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
+  aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+  TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
+
+  GlnArgs g2{};
+  g2.rows = (int32_t)p.n_t_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
+  g2.gate = zt; g2.ldg = zw;
+  g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;
+  TRY(timed_gln(g2, dt, c.s));
+
+  GemmArgs go{};
+  go.M = (int32_t)p.n_parents; go.N = D; go.K = hd; go.groups = S;
+  go.A = y; go.lda = hd; go.amap = RowMap{nullptr, S, 0}; go.amap_zadd = 1;
+  go.B[0] = w->w_o; go.bn[0] = D; go.ldb = hd;
+  go.cmap = RowMap{c.meta.parent_row, 0, 0}; go.cmap_zadd = 1;
+  go.epi = EPI_RESID; go.resid = x_in; go.ldr = D; go.out = x_out; go.ldo = D;
+  TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
+  return MTFM_OK;
+}
+
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t mtfm_meta_bytes(const mtfm_batch* batch) {
+  MetaPlan p;
+  if (plan_meta(batch, &p) != MTFM_OK) return 0;
+  return (size_t)p.lay.total_bytes;
+}
+
+mtfm_status mtfm_meta_layout_of(const mtfm_batch* batch, mtfm_meta_layout* layout) {
+  if (!layout) return MTFM_E_NULL;
+  MetaPlan p;
+  TRY(plan_meta(batch, &p));
+  *layout = p.lay;
+  return MTFM_OK;
+}
+
+mtfm_status mtfm_mask_build(const mtfm_batch* batch, void* meta_d, size_t meta_bytes, void* stream) {
+  MetaPlan p;
+  TRY(plan_meta(batch, &p));
+  if (!meta_d) return MTFM_E_NULL;
+  TRY(check_batch_device(batch, p));
+  if (meta_bytes < (size_t)p.lay.total_bytes) return MTFM_E_WORKSPACE;
+  TimedLaunch t(MTFM_K_MASK, (hipStream_t)stream);
+  return launch_mask_build(batch, p, meta_d, (hipStream_t)stream);
+}
+
+size_t mtfm_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t op) {
+  MetaPlan p;
+  if (plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
+  switch (op) {
+    case MTFM_OP_FULL: return (size_t)layer_ws(p, dims, MTFM_OP_FULL).total;
+    case MTFM_OP_TARGET: return (size_t)layer_ws(p, dims, MTFM_OP_TARGET).total;
+    case MTFM_OP_BACKBONE:
+      return (size_t)std::max(layer_ws(p, dims, MTFM_OP_FULL).total, layer_ws(p, dims, MTFM_OP_TARGET).total);
+    case MTFM_OP_FULL_BWD: return (size_t)bwd_ws_bytes(p, dims, MTFM_OP_FULL_BWD);
+    case MTFM_OP_TARGET_BWD: return (size_t)bwd_ws_bytes(p, dims, MTFM_OP_TARGET_BWD);
+    default: return 0;
+  }
+}
+
+mtfm_status mtfm_workspace_probe(const mtfm_batch* batch, const mtfm_dims* dims, int32_t op, int64_t* off_a,
+                                 int64_t* off_y) {
+  if (!off_a || !off_y) return MTFM_E_NULL;
+  MetaPlan p;
+  TRY(plan_meta(batch, &p));
+  TRY(check_dims(dims));
+  if (op != MTFM_OP_FULL && op != MTFM_OP_TARGET) return MTFM_E_UNSUPPORTED;
+  const LayerWs L = layer_ws(p, dims, op);
+  *off_a = L.a;
+  *off_y = L.y;
+  return MTFM_OK;
+}
+
+mtfm_status mtfm_attn_full(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d, const mtfm_full_w* w,
+                           const void* x_in, void* x_out, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c;
+  TRY(prepare(batch, dims, meta_d, x_in, x_out, ws, ws_bytes, MTFM_OP_FULL, &c, stream));
+  TRY(check_full_w(w));
+  return run_full(c, dims, w, x_in, x_out, (char*)ws);
+}
+
+mtfm_status mtfm_attn_target(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d,
+                             const mtfm_target_w* w, const void* x_in, void* x_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  Ctx c;
+  TRY(prepare(batch, dims, meta_d, x_in, x_out, ws, ws_bytes, MTFM_OP_TARGET, &c, stream));
+  TRY(check_target_w(w));
+  return run_target(c, dims, w, x_in, x_out, (char*)ws);
+}
+
+mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                              const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                              void* x_inout, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c;
+  TRY(prepare(batch, dims, meta_d, x_inout, x_inout, ws, ws_bytes, MTFM_OP_BACKBONE, &c, stream));
+  if (n_blocks < 0 || k_target < 0) return MTFM_E_DIMS;
+  if (n_blocks > 0 && !full) return MTFM_E_NULL;
+  if (n_blocks > 0 && k_target > 0 && !tgt) return MTFM_E_NULL;
+  for (int b = 0; b < n_blocks; ++b) {
+    TRY(check_full_w(&full[b]));
+    for (int t = 0; t < k_target; ++t) TRY(check_target_w(&tgt[b * k_target + t]));
+  }
+  for (int b = 0; b < n_blocks; ++b) {
+    TRY(run_full(c, dims, &full[b], x_inout, x_inout, (char*)ws));
+    for (int t = 0; t < k_target; ++t) TRY(run_target(c, dims, &tgt[b * k_target + t], x_inout, x_inout, (char*)ws));
+  }
+  return MTFM_OK;
+}
+
+mtfm_status mtfm_attn_full_bwd(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d,
+                               const mtfm_full_w* w, const void* x_in, const void* dy, void* dx,
+                               const mtfm_full_grad* g, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c;
+  TRY(prepare(batch, dims, meta_d, x_in, dx, ws, ws_bytes, MTFM_OP_FULL_BWD, &c, stream));
+  TRY(check_full_w(w));
+  if (!dy || !g || !g->ln1_g || !g->ln1_b || !g->w_uqkv || !g->ln2_g || !g->ln2_b || !g->w_o) return MTFM_E_NULL;
+  if (dx == x_in || dx == dy) return MTFM_E_DIMS;
+  return run_full_bwd(c, dims, w, x_in, dy, dx, g, (char*)ws);
+}
+
+mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d,
+                                 const mtfm_target_w* w, const void* x_in, const void* dy, void* dx,
+                                 const mtfm_target_grad* g, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c;
+  TRY(prepare(batch, dims, meta_d, x_in, dx, ws, ws_bytes, MTFM_OP_TARGET_BWD, &c, stream));
+  TRY(check_target_w(w));
+  if (!dy || !g || !g->ln1_g || !g->ln1_b || !g->w_u || !g->w_q || !g->w_kv || !g->ln2_g || !g->ln2_b || !g->w_o)
+    return MTFM_E_NULL;
+  if (dx == x_in || dx == dy) return MTFM_E_DIMS;
+  return run_target_bwd(c, dims, w, x_in, dy, dx, g, (char*)ws);
+}
+
+const char* mtfm_status_str(int32_t status) {
+  switch (status) {
+    case MTFM_OK: return "MTFM_OK";
+    case MTFM_E_NULL: return "MTFM_E_NULL";
+    case MTFM_E_DIMS: return "MTFM_E_DIMS";
+    case MTFM_E_UNSUPPORTED: return "MTFM_E_UNSUPPORTED";
+    case MTFM_E_WORKSPACE: return "MTFM_E_WORKSPACE";
+    case MTFM_E_HIP: return "MTFM_E_HIP";
+    default: return "MTFM_E_UNKNOWN";
+  }
+}
+
+const char* mtfm_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

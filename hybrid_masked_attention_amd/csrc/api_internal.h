@@ -1,0 +1,79 @@
+// Host-side helpers shared by the C ABI and the backward orchestration (internal).
+#pragma once
+#include <cmath>
+
+#include "attn.h"
+#include "common.h"
+#include "gemm.h"
+#include "gln.h"
+
+#define TRY(x)                          \
+  do {                                  \
+    mtfm_status _s = (x);               \
+    if (_s != MTFM_OK) return _s;       \
+  } while (0)
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+inline int elem_size(int dtype) { return dtype == MTFM_BF16 ? 2 : 4; }
+inline RowMap identity_map() { return RowMap{nullptr, 1, 0}; }
+// Q is stored times log2(e) / sqrt(dh) so the attention kernels evaluate SiLU with exp2.
+inline float q_scale(int dh) { return kLog2e / std::sqrt((float)dh); }
+
+int64_t align_up(int64_t x, int64_t a);
+
+struct LayerWs {
+  int64_t xt = 0, z = 0, kv = 0, a = 0, y = 0, total = 0;
+};
+LayerWs layer_ws(const MetaPlan& p, const mtfm_dims* d, int op);
+
+struct Ctx {
+  const mtfm_batch* b = nullptr;
+  MetaPlan plan;
+  MetaPtrs meta{};
+  hipStream_t s = nullptr;
+};
+
+mtfm_status check_dims(const mtfm_dims* d);
+mtfm_status prepare(const mtfm_batch* b, const mtfm_dims* d, const void* meta_d, const void* x0, const void* x1,
+                    void* ws, size_t ws_bytes, int op, Ctx* c, void* stream);
+mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out, char* ws);
+mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in, void* x_out,
+                       char* ws);
+
+// backward (bwd.hip)
+int64_t bwd_ws_bytes(const MetaPlan& p, const mtfm_dims* d, int op);
+mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, const void* dy,
+                         void* dx, const mtfm_full_grad* g, char* ws);
+mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in,
+                           const void* dy, void* dx, const mtfm_target_grad* g, char* ws);
+
+// RAII bracket of one launch with HIP events when its kernel class is enabled
+// (see mtfm_timing_enable); a no-op otherwise.
+class TimedLaunch {
+ public:
+  TimedLaunch(int kclass, hipStream_t s);
+  ~TimedLaunch();
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  int cls_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
+// Launch helpers that time themselves under a kernel class.
+inline mtfm_status timed_gemm(int kclass, const GemmArgs& g, int dt, hipStream_t s) {
+  TimedLaunch t(kclass, s);
+  return launch_gemm(g, dt, s);
+}
+inline mtfm_status timed_attention(int kclass, const AttnArgs& a, int dt, hipStream_t s) {
+  TimedLaunch t(kclass, s);
+  return launch_attention(a, dt, s);
+}
+inline mtfm_status timed_gln(const GlnArgs& a, int dt, hipStream_t s) {
+  TimedLaunch t(MTFM_K_GLN, s);
+  return launch_gln(a, dt, s);
+}

@@ -1,0 +1,31 @@
+// Masked pointwise-SiLU attention interface (internal).
+//
+//   A_h[i] = (1 / n_i) * sum_{j visible to i} SiLU(q_ih . k_jg / sqrt(dh)) v_jg,  g = h / r
+//
+// ([explainer] §4.1 and §4.2 attention equations; [blog] §6.1: one FA2-style
+// interface for Full and Target attention with dynamic-mask reads and SiLU
+// fused.)  Queries come from a query space (all packed rows for the full
+// layer, the T rows for the target layer) tiled by the mask metadata; keys are
+// the user's context rows (H then R) plus, for T rows, the row itself.
+//
+// Q must be stored pre-multiplied by log2(e) / sqrt(dh): then with
+// s = q' . k, SiLU(x) = ln2 * s / (1 + 2^-s), so the kernels evaluate
+// s * rcp(1 + exp2(-s)) per visible pair and fold ln2 / n_i into the output.
+#pragma once
+#include "common.h"
+
+struct AttnArgs {
+  const void* q; int64_t ldq;    // query rows (query space); head h at column h*dh
+  const void* k; int64_t ldk;    // key rows (packed rows); group g at column g*dh
+  const void* v; int64_t ldv;
+  const void* kd; int64_t ldkd;  // the query rows' own keys / values (query space)
+  const void* vd; int64_t ldvd;
+  void* a; int64_t lda;          // output [query row][H*dh]
+  const int32_t* tiles; int32_t ntiles;
+  const int32_t* p; const int32_t* n;  // per packed row
+  const int32_t* lens;
+  int32_t H, G, dh;
+  float out_scale;               // ln 2
+};
+
+mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s);

@@ -1,0 +1,253 @@
+// Masked pointwise-SiLU attention kernels for gfx950.
+//
+// bf16 kernel: one workgroup per (64-row query tile, KV group g) with one wave
+// per query head of the group (r waves).  The group's K and V tiles (64 keys
+// x 64 dims) are staged once in LDS and shared by the r heads ([explainer]
+// §4.1 GQA: r query heads share a KV head).  Per key tile each wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulate), applies
+// SiLU pointwise in registers, rounds P to bf16 and accumulates O += P V on
+// MFMA.  The S^T accumulator layout (lane = query, registers = keys) is used
+// directly as the A operand of P V once V's key order is permuted to match,
+// so P never leaves registers.  V is transposed while being staged in LDS.
+//
+// Only key tiles the metadata marks visible are visited ([blog] §6.2: compute
+// only key blocks holding a valid key); the mask compare runs only on mixed
+// tiles and on a short last tile.  T columns are never tiled ([blog] §6.2:
+// the user-to-item direction is skipped): a T row's self term is one extra
+// "diagonal" tile built from the query tile's own K/V rows.
+//
+// fp32 kernel: one thread per (query row, head), plain loops; the fp32
+// correctness path.
+
+#include "attn.h"
+
+namespace {
+
+constexpr int DH = 64;
+constexpr int KS = DH + 8;  // K tile row stride in LDS (144 B)
+constexpr int VS = 64 + 4;  // V^T tile row stride in LDS (136 B)
+
+MTFM_DEV int xcd_remap(int bid, int nblocks) {
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int x = bid & 7, k = bid >> 3;
+  return x * q + min(x, r) + k;
+}
+
+MTFM_DEV float silu_scaled(float s) {
+  // s = x log2(e); returns SiLU(x) / ln2 = s / (1 + 2^-s)
+  return s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-s));
+}
+
+template <int R>
+__global__ __launch_bounds__(64 * R) void attn_bf16_kernel(AttnArgs g) {
+  constexpr int NT = 64 * R;
+  constexpr int KPT = (512 + NT - 1) / NT;  // 16-B K chunks per thread per tile
+  constexpr int VPT = (256 + NT - 1) / NT;  // V (key pair, 8 dims) items per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * KS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][DH * VS];
+  __shared__ float rinv[64];
+
+  const int nblocks = g.ntiles * g.G;
+  const int lb = xcd_remap(blockIdx.x, nblocks);
+  const int tile = lb / g.G, grp = lb % g.G;
+  const int32_t* td = g.tiles + 8 * tile;
+  const int u = td[TD_USER], row0 = td[TD_ROW0], nrows = td[TD_NROWS];
+  const int full_end = td[TD_FULL_END], key_end = td[TD_END];
+  const int grow0 = td[TD_GROW0], qrow0 = td[TD_QROW0], urow0 = td[TD_UROW0];
+  const int lctx = g.lens[3 * u] + g.lens[3 * u + 1];
+  const bool has_diag = row0 + nrows > lctx;
+  const int ntl = key_end + (has_diag ? 1 : 0);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = grp * R + wave;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  if (tid < 64) rinv[tid] = (tid < nrows) ? g.out_scale / (float)g.n[grow0 + tid] : 0.f;
+
+  // Q fragments (B operand of S^T = K Q^T): query row qb*32 + l32, dims kk*16 + 8*hi + [0, 8)
+  bf16x8 qf[2][4];
+  int plim[2], selfq[2];
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = qb * 32 + l32;
+    const bool ok = qi < nrows;
+    const bf16* src = (const bf16*)g.q + (int64_t)(qrow0 + (ok ? qi : 0)) * g.ldq + h * DH + 8 * hi;
+    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = ok ? *(const bf16x8*)(src + kk * 16) : bf16x8{};
+    const int pp = ok ? g.p[grow0 + qi] : 0;
+    plim[qb] = pp;
+    selfq[qb] = ok ? (g.n[grow0 + qi] - pp) : 0;
+  }
+
+  // tile staging: it < key_end -> context keys of the user; it == key_end -> the tile's own rows
+  bf16x8 rk[KPT], rv[VPT][2];
+  auto load_tile = [&](int it) {
+    const bool diag = it >= key_end;
+    const bf16* kb = diag ? (const bf16*)g.kd : (const bf16*)g.k;
+    const bf16* vb = diag ? (const bf16*)g.vd : (const bf16*)g.v;
+    const int64_t ldk = diag ? g.ldkd : g.ldk, ldv = diag ? g.ldvd : g.ldv;
+    const int base = diag ? qrow0 : urow0 + it * 64;
+    const int lim = diag ? nrows : min(64, lctx - it * 64);
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + NT * i;
+      const int j = c >> 3, kc = c & 7;
+      rk[i] = (c < 512 && j < lim) ? *(const bf16x8*)(kb + (int64_t)(base + j) * ldk + grp * DH + kc * 8) : bf16x8{};
+    }
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + NT * i;
+      const int jp = c & 31, vc = c >> 5;
+      const int j = 2 * jp;
+      const bool in = c < 256;
+      rv[i][0] = (in && j < lim) ? *(const bf16x8*)(vb + (int64_t)(base + j) * ldv + grp * DH + vc * 8) : bf16x8{};
+      rv[i][1] = (in && j + 1 < lim) ? *(const bf16x8*)(vb + (int64_t)(base + j + 1) * ldv + grp * DH + vc * 8) : bf16x8{};
+    }
+  };
+  auto store_tile = [&](int buf) {
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + NT * i;
+      if (c < 512) *(bf16x8*)(&Ks[buf][(c >> 3) * KS + (c & 7) * 8]) = rk[i];
+    }
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + NT * i;
+      if (c >= 256) continue;
+      const int jp = c & 31, vc = c >> 5;
+      for (int s = 0; s < 8; ++s) {
+        bf16x2 pr;
+        pr[0] = rv[i][0][s];
+        pr[1] = rv[i][1][s];
+        *(bf16x2*)(&Vs[buf][(vc * 8 + s) * VS + 2 * jp]) = pr;
+      }
+    }
+  };
+
+  f32x16 o[2][2];
+  for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b) o[a][b] = f32x16{};
+
+  if (ntl > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntl; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntl) load_tile(it + 1);
+    const bool diag = it >= key_end;
+    const bool masked = diag || it >= full_end || (it + 1) * 64 > lctx;
+    int lim[2], dsel[2];
+    for (int qb = 0; qb < 2; ++qb) {
+      lim[qb] = diag ? 0 : plim[qb] - it * 64;
+      dsel[qb] = (diag && selfq[qb]) ? qb * 32 + l32 : -1;
+    }
+    const bf16* K = Ks[buf];
+    const bf16* V = Vs[buf];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 st[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 af = *(const bf16x8*)(&K[(kb * 32 + l32) * KS + kk * 16 + 8 * hi]);
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[0][kk], st[0], 0, 0, 0);
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[1][kk], st[1], 0, 0, 0);
+      }
+      // P chunk c covers keys kb*32 + 16c + {4hi + t, 8 + 4hi + t : t < 4} in slot order
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const int i = 8 * c + s;
+            float pv = silu_scaled(st[qb][i]);
+            if (masked) {
+              const int key = kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+              const bool vis = key < lim[qb] || key == dsel[qb];
+              pv = vis ? pv : 0.f;
+            }
+            pf[qb][c][s] = (bf16)pv;
+          }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const bf16* vrow = &V[(nb * 32 + l32) * VS + kb * 32 + 16 * c + 4 * hi];
+          const bf16x4 lo4 = *(const bf16x4*)(vrow);
+          const bf16x4 hi4 = *(const bf16x4*)(vrow + 8);
+          bf16x8 vf;
+          for (int t = 0; t < 4; ++t) { vf[t] = lo4[t]; vf[4 + t] = hi4[t]; }
+          o[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[0][c], vf, o[0][nb], 0, 0, 0);
+          o[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[1][c], vf, o[1][nb], 0, 0, 0);
+        }
+    }
+    if (it + 1 < ntl) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // O layout: lane holds dim nb*32 + l32 of rows qb*32 + 8(i/4) + 4hi + i%4
+  bf16* out = (bf16*)g.a;
+  for (int qb = 0; qb < 2; ++qb)
+    for (int nb = 0; nb < 2; ++nb)
+      for (int i = 0; i < 16; ++i) {
+        const int qi = qb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        if (qi < nrows)
+          out[(int64_t)(qrow0 + qi) * g.lda + h * DH + nb * 32 + l32] = (bf16)(o[qb][nb][i] * rinv[qi]);
+      }
+}
+
+// fp32 path: thread = (query row of the tile, head).
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs g) {
+  const int tile = blockIdx.x, h = blockIdx.y;
+  const int32_t* td = g.tiles + 8 * tile;
+  const int u = td[TD_USER], nrows = td[TD_NROWS];
+  const int grow0 = td[TD_GROW0], qrow0 = td[TD_QROW0], urow0 = td[TD_UROW0];
+  const int qi = threadIdx.x;
+  if (qi >= nrows) return;
+  const int grp = h / (g.H / g.G);
+  const float* q = (const float*)g.q + (int64_t)(qrow0 + qi) * g.ldq + h * D;
+  float qv[D], acc[D];
+  for (int c = 0; c < D; ++c) { qv[c] = q[c]; acc[c] = 0.f; }
+  const int p = g.p[grow0 + qi];
+  const int self = g.n[grow0 + qi] - p;
+  auto visit = [&](const float* kr, const float* vr) {
+    float s = 0.f;
+    for (int c = 0; c < D; ++c) s = fmaf(qv[c], kr[c], s);
+    const float w = s / (1.0f + exp2f(-s));
+    for (int c = 0; c < D; ++c) acc[c] = fmaf(w, vr[c], acc[c]);
+  };
+  for (int j = 0; j < p; ++j)
+    visit((const float*)g.k + (int64_t)(urow0 + j) * g.ldk + grp * D,
+          (const float*)g.v + (int64_t)(urow0 + j) * g.ldv + grp * D);
+  if (self)
+    visit((const float*)g.kd + (int64_t)(qrow0 + qi) * g.ldkd + grp * D,
+          (const float*)g.vd + (int64_t)(qrow0 + qi) * g.ldvd + grp * D);
+  const float sc = g.out_scale / (float)g.n[grow0 + qi];
+  float* out = (float*)g.a + (int64_t)(qrow0 + qi) * g.lda + h * D;
+  for (int c = 0; c < D; ++c) out[c] = acc[c] * sc;
+  (void)u;
+}
+
+}  // namespace
+
+mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
+  if (a.ntiles <= 0) return MTFM_OK;
+  const int r = a.H / a.G;
+  if (dtype == MTFM_BF16) {
+    if (a.dh != 64) return MTFM_E_UNSUPPORTED;
+    const unsigned blocks = (unsigned)(a.ntiles * a.G);
+    switch (r) {
+      case 1: attn_bf16_kernel<1><<<blocks, 64, 0, s>>>(a); break;
+      case 2: attn_bf16_kernel<2><<<blocks, 128, 0, s>>>(a); break;
+      case 4: attn_bf16_kernel<4><<<blocks, 256, 0, s>>>(a); break;
+      case 8: attn_bf16_kernel<8><<<blocks, 512, 0, s>>>(a); break;
+      default: return MTFM_E_UNSUPPORTED;
+    }
+  } else {
+    dim3 grid((unsigned)a.ntiles, (unsigned)a.H);
+    if (a.dh == 32) attn_f32_kernel<32><<<grid, 64, 0, s>>>(a);
+    else if (a.dh == 64) attn_f32_kernel<64><<<grid, 64, 0, s>>>(a);
+    else return MTFM_E_UNSUPPORTED;
+  }
+  MTFM_LAUNCH_CHECK("attention");
+  return MTFM_OK;
+}

@@ -1,0 +1,22 @@
+// Group LayerNorm interface (internal).
+//
+// y[i] = ((x[i] - mean) / sqrt(var + eps)) * gamma[type_i] + beta[type_i]   (* gate[i])
+// over a row of width D, biased variance, fp32 statistics.  gamma / beta are
+// [3][D] (rows H, R, T), one parameter matrix indexed per token by its type
+// ([blog] §6.1: Group LayerNorm with a [G, D] parameter matrix and a per-token
+// group id; GLN-MUL fusion = the gate).
+#pragma once
+#include "common.h"
+
+struct GlnArgs {
+  int32_t rows, D;
+  const void* x; int64_t ldx;
+  void* y; int64_t ldy;
+  const void* gate; int64_t ldg;   // optional: y *= gate[i] (the U of the layer)
+  const float* gamma; const float* beta;
+  const uint8_t* type;             // per row; if null, every row has type `type_const`
+  int32_t type_const;
+  float eps;
+};
+
+mtfm_status launch_gln(const GlnArgs& a, int dtype, hipStream_t s);

@@ -1,0 +1,265 @@
+/*
+ * mtfm.h - C ABI of libmtfm, the MI355X (gfx950) hot path of the hybrid
+ * H/R/T masked-attention backbone.
+ *
+ * Pages cited (titles; sections as numbered on each page):
+ *   [explainer] "美团推荐大模型 MTFM (Meituan Foundation Model) 深度硬核解析：跨场景推荐的终极答案？"
+ *               (dingyadong.top)
+ *   [blog]      "MTFM：美团统一推荐基座大模型在外卖多业务场景的落地实践" (Meituan tech blog,
+ *               mirrored on dujian.net)
+ *   [digest]    "外卖几条业务线共用一套精排骨干：美团 MTFM 免掉跨业务特征对齐，推理成本降 24%"
+ *               (neodrop.ai)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named *_d are device pointers; *_h are host pointers.  The
+ *    caller owns every buffer; the library never allocates device memory.
+ *    Scratch space comes from a caller-provided workspace sized by
+ *    mtfm_workspace_bytes(); per-batch mask metadata lives in a caller
+ *    buffer sized by mtfm_meta_bytes().
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and is asynchronous: no entry point synchronises the host or
+ *    reads device memory back.  Grid sizes come from the host copy of the
+ *    per-user lengths.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    status other than MTFM_OK means nothing was enqueued, except
+ *    MTFM_E_HIP, which reports a failed launch (work enqueued before it may
+ *    have run).
+ *  - Data-level contracts are the caller's: action times ascending within
+ *    each user, device lengths equal to the host lengths.
+ *  - Rows of one user are packed H, R, T ([explainer] §2.1.3: X = (H; R; T));
+ *    users follow one another with no padding ("jagged": [blog] §6.1).  With
+ *    split S = 4 ([blog] §3.3.2, V2 target scale-up) each target parent
+ *    contributes 4 consecutive T rows (target-major), all carrying that
+ *    parent's exposure time.
+ *  - Activations and projection weights have the layer's dtype (fp32 or
+ *    bf16, row-major); group-LayerNorm parameters are always fp32.
+ *  - Re-entrant for distinct workspaces and streams.
+ */
+#ifndef MTFM_H
+#define MTFM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTFM_OK = 0,
+  MTFM_E_NULL = -1,        /* a required pointer is NULL */
+  MTFM_E_DIMS = -2,        /* a size is negative, inconsistent or too large */
+  MTFM_E_UNSUPPORTED = -3, /* valid, but not implemented (head_dim, H % G, split, dtype) */
+  MTFM_E_WORKSPACE = -4,   /* meta or workspace buffer smaller than required */
+  MTFM_E_HIP = -5          /* a HIP launch or runtime call failed */
+} mtfm_status;
+
+typedef enum { MTFM_F32 = 0, MTFM_BF16 = 1 } mtfm_dtype;
+
+/* Query/key tile edge used by the mask metadata and the attention kernels. */
+#define MTFM_TILE 64
+
+/* A jagged user-level batch ([explainer] §3; [blog] §4.1: one sample per user
+ * holding its history H, real-time actions R and exposed targets T). */
+typedef struct {
+  int32_t n_users;
+  int32_t split;          /* T rows per target parent: 1 (V1) or 4 (V2) */
+  const int32_t* lens_h;  /* host   [n_users][3] = {L_H, L_R, L_T parents}, all >= 0 */
+  const int32_t* lens_d;  /* device copy of lens_h */
+  const int32_t* ts_r_d;  /* device [sum L_R] action times, ascending within each user */
+  const int32_t* ts_t_d;  /* device [sum L_T] exposure time of each target parent */
+} mtfm_batch;
+
+/* Layer shape.  H query heads share G key/value heads, r = H / G
+ * ([explainer] §4.1, grouped-query attention). */
+typedef struct {
+  int32_t d_model;
+  int32_t n_q_heads;   /* H */
+  int32_t n_kv_heads;  /* G; H % G == 0 */
+  int32_t head_dim;    /* dh: 32 or 64 */
+  float ln_eps;        /* group-LayerNorm epsilon (the pages fix none; 1e-5 is used) */
+  int32_t dtype;       /* mtfm_dtype of activations and projection weights */
+} mtfm_dims;
+
+/* Full-attention layer weights ([explainer] §4.1):
+ *   X~ = GLN1(X);  [U|Q|K|V] = SiLU(X~ w_uqkv^T);  A_h = SiLU(Q_h K_g^T / sqrt(dh)) (.) M V_g / n
+ *   X' = (GLN2(A) (.) U) w_o^T + X
+ * GLN = LayerNorm over the row with affine parameters picked by the row's
+ * token type H/R/T ([blog] §6.1: a [G, D] parameter matrix indexed per token). */
+typedef struct {
+  const float* ln1_g; const float* ln1_b;  /* [3][d_model], rows H, R, T */
+  const void* w_uqkv;                      /* [2*H*dh + 2*G*dh][d_model], rows U|Q|K|V, heads contiguous */
+  const float* ln2_g; const float* ln2_b;  /* [3][H*dh] */
+  const void* w_o;                         /* [d_model][H*dh] */
+} mtfm_full_w;
+
+/* Target-attention layer weights ([explainer] §4.2; [blog] §3.3.2 per-sub-token Q):
+ *   X~ = GLN1(X);  [K|V] = SiLU(X~ w_kv^T) on all rows;
+ *   U_T = SiLU(X~_T w_u^T), Q_T = SiLU(X~_T w_q[k]^T) for sub-token k;
+ *   X'_T = (GLN2(A_T) (.) U_T) w_o^T + X_T;  X'_{H,R} = X_{H,R}. */
+typedef struct {
+  const float* ln1_g; const float* ln1_b;  /* [3][d_model] */
+  const void* w_u;                         /* [H*dh][d_model] */
+  const void* w_q;                         /* [split][H*dh][d_model] */
+  const void* w_kv;                        /* [2*G*dh][d_model], rows K|V */
+  const float* ln2_g; const float* ln2_b;  /* [3][H*dh] */
+  const void* w_o;                         /* [d_model][H*dh] */
+} mtfm_target_w;
+
+/* Gradients written by the backward entry points.  Weight and GLN-parameter
+ * gradients are fp32 and overwritten (not accumulated); shapes as in the
+ * matching weight struct. */
+typedef struct {
+  float* ln1_g; float* ln1_b; float* w_uqkv; float* ln2_g; float* ln2_b; float* w_o;
+} mtfm_full_grad;
+
+typedef struct {
+  float* ln1_g; float* ln1_b; float* w_u; float* w_q; float* w_kv; float* ln2_g; float* ln2_b; float* w_o;
+} mtfm_target_grad;
+
+/* Byte offsets of the arrays inside the mask-metadata buffer (host-side
+ * description; counts are element counts). */
+typedef struct {
+  int64_t n_rows;            /* total packed rows */
+  int64_t n_t_rows;          /* total T rows (split * sum L_T) */
+  int64_t n_parents;         /* sum L_T */
+  int64_t n_ctx_rows;        /* total H + R rows */
+  int64_t n_full_tiles;      /* query tiles of the full layer: sum ceil(N_u / 64) */
+  int64_t n_target_tiles;    /* query tiles of the target layer: sum ceil(split L_T / 64) */
+  int64_t off_user;          /* int32 [7][n_users + 1]: row, action, parent, ctx-row, full-tile,
+                                target-tile and T-row offsets of each user */
+  int64_t off_p;             /* int32 [n_rows] visible context prefix p_i */
+  int64_t off_n;             /* int32 [n_rows] visible key count n_i (p_i + self_i) */
+  int64_t off_type;          /* uint8 [n_rows] token type 0 = H, 1 = R, 2 = T */
+  int64_t off_full_tiles;    /* int32 [n_full_tiles][8] tile descriptors (below) */
+  int64_t off_target_tiles;  /* int32 [n_target_tiles][8] */
+  int64_t off_ctx_rows;      /* int32 [n_ctx_rows] packed row of each H/R row, users in order */
+  int64_t off_parent_row;    /* int32 [n_parents] packed row of each parent's first T row */
+  int64_t total_bytes;
+} mtfm_meta_layout;
+/* Tile descriptor, int32 x 8:
+ *   [0] user, [1] first query row within the user, [2] rows in the tile (<= 64),
+ *   [3] leading key tiles that are fully visible to every row of the tile,
+ *   [4] one past the last key tile with any visible key,
+ *   [5] packed row of the first query row, [6] row of the first query in the
+ *   layer's query space (= [5] for the full layer; the T-row index for the
+ *   target layer), [7] packed row of the user's first row.
+ * Key tiles cover the user's context columns (H then R) from its first row in
+ * steps of 64; tiles [0, [3]) are all visible, [[3], [4]) mixed, the rest
+ * invisible.  A T row's only T key is itself, carried by n_i - p_i = 1. */
+
+/* ---------------------------------------------------------------------------
+ * Mask metadata ([explainer] §4.1.1 and the worked matrix of §8.2; [blog]
+ * §3.2): H keys are visible to every query; H queries see only H; R queries
+ * see H and R up to themselves (causal, self included); T queries see H, the
+ * R actions strictly earlier than their exposure time, and themselves.
+ * [blog] §6.1 preprocesses the mask into a one-dimensional jagged form and
+ * §6.2 pre-scans it into an index of key blocks worth computing; here that is
+ * the per-row prefix p_i plus the tile descriptors above.
+ */
+
+/* Bytes of metadata for this batch (0 on invalid arguments). */
+size_t mtfm_meta_bytes(const mtfm_batch* batch);
+
+/* Fill *layout with the array offsets of the metadata buffer.  Host only. */
+mtfm_status mtfm_meta_layout_of(const mtfm_batch* batch, mtfm_meta_layout* layout);
+
+/* Build the metadata of `batch` into meta_d (device, meta_bytes >= mtfm_meta_bytes).
+ * Integer-only; the result is a pure function of lengths and timestamps and
+ * is shared by every layer of a backbone.  Errors: E_NULL, E_DIMS (negative
+ * lengths, split not 1 or 4, more than 2^31 - 1 rows), E_WORKSPACE, E_HIP. */
+mtfm_status mtfm_mask_build(const mtfm_batch* batch, void* meta_d, size_t meta_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Layers.  x_in / x_out: device [n_rows][d_model] of dims->dtype.  meta_d:
+ * the output of mtfm_mask_build for the same batch.  ws: device workspace of
+ * at least mtfm_workspace_bytes(batch, dims, op) bytes.
+ * Supported: head_dim 64 with bf16 (MFMA path), head_dim 32 or 64 with fp32;
+ * d_model a multiple of 64 (bf16) or 4 (fp32); H % G == 0.  Other shapes
+ * return MTFM_E_UNSUPPORTED.
+ */
+typedef enum {
+  MTFM_OP_FULL = 0, MTFM_OP_TARGET = 1, MTFM_OP_BACKBONE = 2,
+  MTFM_OP_FULL_BWD = 3, MTFM_OP_TARGET_BWD = 4
+} mtfm_op;
+
+size_t mtfm_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t op);
+
+/* Byte offsets, inside the workspace, of the attention output A (before
+ * GLN2, already divided by n) and of the gated Y = GLN2(A) (.) U left by the
+ * last forward call: [n_rows][H*dh] for the full layer, [n_t_rows][H*dh] in
+ * T-row order for the target layer, in dims->dtype.  Lets a caller check
+ * the attention and gating branches separately.  Host only. */
+mtfm_status mtfm_workspace_probe(const mtfm_batch* batch, const mtfm_dims* dims, int32_t op,
+                                 int64_t* off_a, int64_t* off_y);
+
+/* Full-attention layer ([explainer] §4.1).  x_out may equal x_in. */
+mtfm_status mtfm_attn_full(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d,
+                           const mtfm_full_w* w, const void* x_in, void* x_out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Target-attention layer ([explainer] §4.2): only T rows query; keys and
+ * values come from every row under the mask's T rows; H and R rows of x_out
+ * are copies of x_in (bit-exact).  x_out may equal x_in (then only T rows are
+ * written). */
+mtfm_status mtfm_attn_target(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d,
+                             const mtfm_target_w* w, const void* x_in, void* x_out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Hybrid backbone ([explainer] §4: B blocks of 1 full + K target layers;
+ * [blog] §3.3.1: 16 layers = 4 x (1 + 3)).  full: [n_blocks] weights,
+ * tgt: [n_blocks * k_target] weights in layer order.  In place on x_inout.
+ * The metadata is built once per batch by the caller and reused by all layers. */
+mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks,
+                              int32_t k_target, const void* meta_d, const mtfm_full_w* full,
+                              const mtfm_target_w* tgt, void* x_inout, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Backward of one full-attention layer: given x_in (the layer's input) and
+ * dy = dL/dX', writes dx = dL/dX ([n_rows][d_model], dims->dtype) and the
+ * fp32 weight/GLN gradients into *g.  Recomputes the forward internally.
+ * dx must not alias x_in or dy. */
+mtfm_status mtfm_attn_full_bwd(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d,
+                               const mtfm_full_w* w, const void* x_in, const void* dy, void* dx,
+                               const mtfm_full_grad* g, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of one target-attention layer, same conventions. */
+mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d,
+                                 const mtfm_target_w* w, const void* x_in, const void* dy, void* dx,
+                                 const mtfm_target_grad* g, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing (measurement aid).  While a kernel class is enabled, each of
+ * its launches is bracketed by two HIP events recorded on the stream the
+ * kernel is launched on; nothing else changes.  mtfm_timing_read waits for
+ * the recorded events of one class, returns the number of launches and their
+ * summed duration in milliseconds since the previous read, and resets that
+ * class.  Process-wide state, guarded by a mutex.
+ */
+typedef enum {
+  MTFM_K_MASK = 0,         /* mask-metadata builder */
+  MTFM_K_GLN = 1,          /* group LayerNorm (pre-norm and gated post-norm) */
+  MTFM_K_GEMM_UQKV = 2,    /* full layer: U|Q|K|V projection */
+  MTFM_K_ATTN_FULL = 3,    /* full layer: masked attention */
+  MTFM_K_GEMM_OUT = 4,     /* output projection + residual (both layer types) */
+  MTFM_K_GEMM_KV = 5,      /* target layer: K|V projection of the H/R rows */
+  MTFM_K_GEMM_T = 6,       /* target layer: U|Q|K|V projection of the T rows */
+  MTFM_K_ATTN_TARGET = 7,  /* target layer: masked attention */
+  MTFM_K_BWD = 8,          /* backward kernels */
+  MTFM_K_COUNT = 9
+} mtfm_kernel_class;
+
+mtfm_status mtfm_timing_enable(uint32_t class_mask);  /* bit k enables class k; 0 disables all */
+mtfm_status mtfm_timing_read(int32_t kernel_class, int64_t* launches, double* total_ms);
+
+/* Human-readable name of a status. */
+const char* mtfm_status_str(int32_t status);
+
+/* Last HIP error text recorded by this thread (empty if none). */
+const char* mtfm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MTFM_H */

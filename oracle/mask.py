@@ -67,6 +67,35 @@ def dense_mask(l_h: int, l_r: int, l_t: int, split: int, ts_r, ts_t) -> np.ndarr
     return m
 
 
+def dense_mask_fast(l_h, l_r, l_t, split, ts_r, ts_t):
+    """The same rules as dense_mask, written with numpy broadcasting.
+
+    Used for users too long for the pure-Python enumeration; the tests check
+    that both forms agree element for element.
+    """
+    n = l_h + l_r + split * l_t
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    lc = l_h + l_r
+    qh, qr, qt = i < l_h, (i >= l_h) & (i < lc), i >= lc
+    kh, kr, kt = j < l_h, (j >= l_h) & (j < lc), j >= lc
+    m = np.zeros((n, n), bool)
+    m |= qh & kh
+    m |= qr & kh
+    m |= qr & kr & (j <= i)
+    m |= qt & kh
+    if l_r > 0 and l_t > 0:
+        ts_r = np.asarray(ts_r, np.int64)
+        ts_t = np.asarray(ts_t, np.int64)
+        parent = np.clip((np.arange(n) - lc) // split, 0, l_t - 1)
+        e = ts_t[parent][:, None]
+        tr = ts_r[np.clip(np.arange(n) - l_h, 0, l_r - 1)][None, :]
+        m |= qt & kr & (tr < e)
+    m |= qt & kt & (i == j)
+    return m.astype(np.uint8)
+
+
+
 def row_types(l_h: int, l_r: int, l_t: int, split: int) -> np.ndarray:
     n = l_h + l_r + split * l_t
     return np.array([_kind(i, l_h, l_r) for i in range(n)], dtype=np.uint8)
@@ -139,9 +168,11 @@ def tile_desc_from_classes(cls: np.ndarray):
     return np.array(out, dtype=np.int32).reshape(-1, 2)
 
 
-def batch_meta(batch, bm: int = 64, bn: int = 64):
+def batch_meta(batch, bm: int = 64, bn: int = 64, fast: bool = False):
     """Mask metadata of a whole jagged batch, user by user.
 
+    ``fast`` builds each mask with the broadcast form (checked equal to the
+    enumeration by the tests) for users too long for Python loops.
     Returns a dict with per-row p, self, n, row_type (over all packed rows),
     and the full-layer and target-layer tile tables, each row
     (user, first row within the user, rows in tile, leading full key tiles,
@@ -154,7 +185,7 @@ def batch_meta(batch, bm: int = 64, bn: int = 64):
         l_h, l_r, l_t = (int(v) for v in batch.lens[u])
         ts_r = batch.ts_r[ro[u]:ro[u + 1]]
         ts_t = batch.ts_t[to[u]:to[u + 1]]
-        m = dense_mask(l_h, l_r, l_t, batch.split, ts_r, ts_t)
+        m = (dense_mask_fast if fast else dense_mask)(l_h, l_r, l_t, batch.split, ts_r, ts_t)
         p, selfv, n = row_meta(m, l_h, l_r)
         ps.append(p); ss.append(selfv); ns.append(n)
         ts.append(row_types(l_h, l_r, l_t, batch.split))

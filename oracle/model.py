@@ -33,6 +33,7 @@ from typing import Callable, Dict, List, Optional
 import numpy as np
 
 from . import mask as _mask
+from .mask import dense_mask_fast  # noqa: F401  (re-exported)
 
 
 def silu(x):
@@ -126,34 +127,6 @@ def user_mask(batch, u):
     l_h, l_r, l_t = (int(v) for v in batch.lens[u])
     ro, to = batch.r_off, batch.t_off
     return dense_mask_fast(l_h, l_r, l_t, batch.split, batch.ts_r[ro[u]:ro[u + 1]], batch.ts_t[to[u]:to[u + 1]])
-
-
-def dense_mask_fast(l_h, l_r, l_t, split, ts_r, ts_t):
-    """The same rules as mask.dense_mask, written with numpy broadcasting.
-
-    Used for users too long for the pure-Python enumeration; the tests check
-    that both forms agree element for element.
-    """
-    n = l_h + l_r + split * l_t
-    i = np.arange(n)[:, None]
-    j = np.arange(n)[None, :]
-    lc = l_h + l_r
-    qh, qr, qt = i < l_h, (i >= l_h) & (i < lc), i >= lc
-    kh, kr, kt = j < l_h, (j >= l_h) & (j < lc), j >= lc
-    m = np.zeros((n, n), bool)
-    m |= qh & kh
-    m |= qr & kh
-    m |= qr & kr & (j <= i)
-    m |= qt & kh
-    if l_r > 0 and l_t > 0:
-        ts_r = np.asarray(ts_r, np.int64)
-        ts_t = np.asarray(ts_t, np.int64)
-        parent = np.clip((np.arange(n) - lc) // split, 0, l_t - 1)
-        e = ts_t[parent][:, None]
-        tr = ts_r[np.clip(np.arange(n) - l_h, 0, l_r - 1)][None, :]
-        m |= qt & kr & (tr < e)
-    m |= qt & kt & (i == j)
-    return m.astype(np.uint8)
 
 
 def full_layer(batch, x, w, dims, return_parts=False):

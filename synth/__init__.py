@@ -218,11 +218,14 @@ def config3(seed: int = 3, n_users: int = 160, n_blocks: int = 4, k_target: int 
                     n_blocks=n_blocks, k_target=k_target)
 
 
-def config4(seed: int = 4, n_users: int = 64, lens=(4096, 512, 256)) -> Workload:
+def config4(seed: int = 4, n_users: int = 64, lens=(4096, 512, 256), arrays: bool = True) -> Workload:
     """Long-sequence fwd+bwd of one full and one target layer, V2 layout (split 4)."""
     rng = np.random.default_rng(seed)
     batch = make_batch(rng, np.tile(np.asarray(lens, np.int32), (n_users, 1)), 4)
     dims = Dims(1024, 16, 4, 64)
+    if not arrays:
+        return Workload("cfg4_long_fwd_bwd_bf16", batch, dims, "bf16", np.zeros((0, dims.d_model), np.float32),
+                        n_blocks=1, k_target=1)
     x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
     full = full_weights(rng, dims, 0.02, 0.02)
     tgt = target_weights(rng, dims, 4, 0.02, 0.02)

@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI (no GPU needed; nothing here launches a kernel).
+
+The library must load, export every entry point declared in include/mtfm.h,
+size its metadata from the host lengths, and reject bad arguments with the
+documented status before enqueuing anything.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtfm.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from hybrid_masked_attention_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from hybrid_masked_attention_amd import build
+        build.build()
+    binding.lib()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtfm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_entry_points(B):
+    assert declared_functions() == sorted(B.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(B):
+    L = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(B):
+    assert B.status_str(0) == "MTFM_OK"
+    assert B.status_str(-4) == "MTFM_E_WORKSPACE"
+
+
+def _host_batch(B, lens, split=1, ts_r=None, ts_t=None):
+    lens = np.asarray(lens, np.int32).reshape(-1, 3)
+    ts_r = np.zeros(max(0, int(lens[:, 1].sum())), np.int32) if ts_r is None else ts_r
+    ts_t = np.zeros(max(0, int(lens[:, 2].sum())), np.int32) if ts_t is None else ts_t
+    return B.DeviceBatch(lens, split, ts_r, ts_t, device=None)
+
+
+def test_meta_layout_counts_match_lengths(B):
+    for wl in (synth.config0(), synth.config1(), synth.config2(4)):
+        b = B.DeviceBatch.from_synth(wl.batch, device=None)
+        lay = B.meta_layout(b)
+        rows = wl.batch.user_rows
+        assert lay.n_rows == wl.batch.total_rows
+        assert lay.n_t_rows == wl.batch.total_t_rows
+        assert lay.n_full_tiles == int(np.sum((rows + 63) // 64))
+        assert lay.n_target_tiles == int(np.sum((wl.batch.split * wl.batch.lens[:, 2] + 63) // 64))
+        assert lay.n_ctx_rows == int(wl.batch.lens[:, :2].sum())
+        offs = [lay.off_user, lay.off_p, lay.off_n, lay.off_type, lay.off_full_tiles, lay.off_target_tiles,
+                lay.off_ctx_rows, lay.off_parent_row, lay.total_bytes]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        assert B.meta_bytes(b) == lay.total_bytes
+
+
+def test_empty_batch_is_valid(B):
+    b = _host_batch(B, np.zeros((0, 3), np.int32))
+    lay = B.meta_layout(b)
+    assert lay.n_rows == 0 and lay.n_full_tiles == 0
+
+
+def test_mask_build_rejects_bad_batches(B):
+    L = B.lib()
+    fake = ctypes.c_void_p(0x1000)
+    bad_split = _host_batch(B, [[2, 1, 1]], split=3)
+    assert L.mtfm_mask_build(ctypes.byref(bad_split.c), fake, 1 << 20, None) == B.E_DIMS
+    neg = _host_batch(B, [[2, -1, 1]])
+    assert L.mtfm_mask_build(ctypes.byref(neg.c), fake, 1 << 20, None) == B.E_DIMS
+    ok = _host_batch(B, [[2, 1, 1]])
+    assert L.mtfm_mask_build(ctypes.byref(ok.c), None, 1 << 20, None) == B.E_NULL
+    # device lengths missing (host-only batch)
+    assert L.mtfm_mask_build(ctypes.byref(ok.c), fake, 1 << 20, None) == B.E_NULL
+    assert L.mtfm_mask_build(None, fake, 1 << 20, None) == B.E_NULL
+
+
+def _with_fake_device(b):
+    b.c.lens_d = 0x2000
+    b.c.ts_r_d = 0x3000
+    b.c.ts_t_d = 0x4000
+    return b
+
+
+def test_mask_build_rejects_small_meta_buffer(B):
+    L = B.lib()
+    b = _with_fake_device(_host_batch(B, [[5, 3, 2]]))
+    need = B.meta_bytes(b)
+    assert L.mtfm_mask_build(ctypes.byref(b.c), ctypes.c_void_p(0x1000), need - 1, None) == B.E_WORKSPACE
+
+
+def test_layer_argument_checks(B):
+    L = B.lib()
+    b = _with_fake_device(_host_batch(B, [[5, 3, 2]]))
+    fake = ctypes.c_void_p(0x1000)
+    w = B.CFullW(*([0x5000] * 6))
+    good = B.make_dims(512, 8, 2, 64, dtype=B.BF16)
+    need = B.workspace_bytes(b, good, B.OP_FULL)
+    assert need > 0
+
+    def call(dims, ws_bytes=need, weights=w, meta=fake):
+        return L.mtfm_attn_full(ctypes.byref(b.c), ctypes.byref(dims), meta, ctypes.byref(weights), fake, fake,
+                                fake, ws_bytes, None)
+    assert call(good, need - 1) == B.E_WORKSPACE
+    assert call(B.make_dims(512, 8, 3, 64)) == B.E_UNSUPPORTED      # H % G != 0
+    assert call(B.make_dims(512, 8, 2, 48)) == B.E_UNSUPPORTED      # head_dim
+    assert call(B.make_dims(512, 8, 2, 32, dtype=B.BF16)) == B.E_UNSUPPORTED
+    assert call(B.make_dims(500, 8, 2, 64)) == B.E_UNSUPPORTED      # d_model % 64
+    assert call(B.make_dims(0, 8, 2, 64)) == B.E_DIMS
+    assert call(B.make_dims(512, 8, 2, 64, ln_eps=0.0)) == B.E_DIMS
+    assert call(B.make_dims(512, 8, 2, 64, dtype=7)) == B.E_UNSUPPORTED
+    assert call(good, meta=None) == B.E_NULL
+    w_missing = B.CFullW(0x5000, 0x5000, None, 0x5000, 0x5000, 0x5000)
+    assert call(good, weights=w_missing) == B.E_NULL
+    tw = B.CTargetW(*([0x5000] * 7 + [None]))
+    assert L.mtfm_attn_target(ctypes.byref(b.c), ctypes.byref(good), fake, ctypes.byref(tw), fake, fake, fake,
+                              1 << 30, None) == B.E_NULL
+    # backbone: negative block counts
+    fw = (B.CFullW * 1)(w)
+    tws = (B.CTargetW * 1)(B.CTargetW(*([0x5000] * 8)))
+    assert L.mtfm_backbone_fwd(ctypes.byref(b.c), ctypes.byref(good), -1, 3, fake, fw, tws, fake, fake, 1 << 30,
+                               None) == B.E_DIMS
+
+
+def test_workspace_sizes_grow_with_rows(B):
+    d = B.make_dims(512, 8, 2, 64)
+    small = _host_batch(B, [[10, 5, 2]])
+    big = _host_batch(B, [[1000, 500, 200]])
+    for op in (B.OP_FULL, B.OP_TARGET, B.OP_BACKBONE):
+        assert 0 < B.workspace_bytes(small, d, op) < B.workspace_bytes(big, d, op)
+    assert B.workspace_bytes(small, B.make_dims(500, 8, 2, 64), B.OP_FULL) == 0   # invalid dims -> 0

@@ -1,0 +1,191 @@
+"""GPU parity of the layers and the backbone against the oracle.
+
+Each case runs the HIP path through the C ABI and the float64 oracle on the
+same seeded inputs (bf16-rounded where the device stores bf16) and compares
+X', the residual branch dX = X' - X, the attention output A and the gated
+Y = GLN2(A) (.) U element by element:  max|gpu - ref| <= tol * max|ref| per
+tensor, tol = 1e-2 for bf16 storage / fp32 accumulation, 1e-4 for fp32.
+dX is read through the stored X', so the half-ulp rounding of X' itself is
+allowed for before its error is taken relative to max|dX_ref|.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import model as om
+from tests._parity import TOL_BF16, TOL_F32, Report, rounded_inputs, say, to_np, ws_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_layer(wl, kind, users_ref=None, inplace=False):
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    say(f"layer parity: {wl.name} {kind} rows={wl.batch.total_rows} users={wl.batch.n_users}")
+    dw = DeviceWorkload(wl)
+    meta = B.mask_build(dw.batch)
+    op = B.OP_FULL if kind == "full" else B.OP_TARGET
+    ws = B.workspace(dw.batch, dw.dims, op)
+    x_in = dw.x
+    x_out = x_in.clone() if inplace else torch.empty_like(x_in)
+    if kind == "full":
+        B.attn_full(dw.batch, dw.dims, meta, dw.full[0], x_out if inplace else x_in, x_out, ws)
+    else:
+        B.attn_target(dw.batch, dw.dims, meta, dw.target[0], x_out if inplace else x_in, x_out, ws)
+    torch.cuda.synchronize()
+    off_a, off_y = B.workspace_probe(dw.batch, dw.dims, op)
+    hd = wl.dims.n_q_heads * wl.dims.head_dim
+    rows = wl.batch.total_rows if kind == "full" else wl.batch.total_t_rows
+    a = to_np(ws_tensor(ws, off_a, rows, hd, wl.dtype))
+    y = to_np(ws_tensor(ws, off_y, rows, hd, wl.dtype))
+    return to_np(x_in), to_np(x_out), a, y
+
+
+def _ref_layer(wl, kind):
+    x, full, tgt = rounded_inputs(wl)
+    if kind == "full":
+        out, parts = om.full_layer(wl.batch, x, full[0], wl.dims, return_parts=True)
+    else:
+        out, parts = om.target_layer(wl.batch, x, tgt[0], wl.dims, return_parts=True)
+    return x, out, parts
+
+
+def _compare(wl, kind, got, tol):
+    x_dev, out_dev, a_dev, y_dev = got
+    x_ref, out_ref, parts = _ref_layer(wl, kind)
+    np.testing.assert_array_equal(x_dev, x_ref)        # the device saw the same inputs
+    r = Report(tol)
+    r.close("X'", out_dev, out_ref)
+    r.branch("dX", out_dev, out_ref, x_ref, wl.dtype)
+    r.close("A", a_dev, parts["a"])
+    r.close("Y", y_dev, parts["y"])
+    r.check()
+    return out_ref
+
+
+def test_config0_full_layer_fp32():
+    wl = synth.config0()
+    _compare(wl, "full", _run_layer(wl, "full"), TOL_F32)
+
+
+def test_config1_full_layer_bf16():
+    wl = synth.config1()
+    _compare(wl, "full", _run_layer(wl, "full"), TOL_BF16)
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_config2_target_layer_bf16(split):
+    wl = synth.config2(split)
+    got = _run_layer(wl, "target")
+    _compare(wl, "target", got, TOL_BF16)
+    x_dev, out_dev = got[0], got[1]
+    for u in range(wl.batch.n_users):      # H and R rows are copied bit-exactly
+        r0 = wl.batch.row_off[u]
+        lc = int(wl.batch.lens[u, 0] + wl.batch.lens[u, 1])
+        np.testing.assert_array_equal(out_dev[r0:r0 + lc], x_dev[r0:r0 + lc])
+
+
+def test_config2_target_layer_in_place():
+    wl = synth.config2(4)
+    a = _run_layer(wl, "target", inplace=False)
+    b = _run_layer(wl, "target", inplace=True)
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def _small_workload(lens, split, dtype, seed, dims=None, w_std=0.05):
+    rng = np.random.default_rng(seed)
+    batch = synth.make_batch(rng, np.asarray(lens, np.int32), split)
+    dims = dims or synth.Dims(512, 8, 2, 64)
+    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
+    wf = synth.full_weights(rng, dims, w_std, w_std)
+    wt = synth.target_weights(rng, dims, split, w_std, w_std)
+    return synth.Workload(f"edge_{seed}", batch, dims, dtype, x, full=[wf], target=[wt])
+
+
+EDGE_LENS = [[0, 0, 0], [64, 0, 0], [0, 64, 0], [0, 0, 3], [130, 64, 17], [1, 0, 1], [63, 1, 0], [0, 0, 0],
+             [65, 63, 33], [5, 200, 2]]
+
+
+@pytest.mark.parametrize("split", [1, 4])
+@pytest.mark.parametrize("kind", ["full", "target"])
+def test_edge_users_bf16(kind, split):
+    wl = _small_workload(EDGE_LENS, split, "bf16", 40 + split)
+    _compare(wl, kind, _run_layer(wl, kind), TOL_BF16)
+
+
+@pytest.mark.parametrize("kind", ["full", "target"])
+def test_edge_users_fp32(kind):
+    dims = synth.Dims(128, 4, 2, 32)
+    wl = _small_workload(EDGE_LENS, 4, "f32", 50, dims=dims, w_std=0.1)
+    _compare(wl, kind, _run_layer(wl, kind), TOL_F32)
+
+
+def test_fp32_head_dim_64_and_gqa_ratio_1():
+    dims = synth.Dims(128, 2, 2, 64)
+    wl = _small_workload([[20, 9, 4], [70, 3, 1]], 1, "f32", 51, dims=dims, w_std=0.1)
+    _compare(wl, "full", _run_layer(wl, "full"), TOL_F32)
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (8, 4), (8, 1)])
+def test_bf16_other_gqa_ratios(heads):
+    dims = synth.Dims(512, heads[0], heads[1], 64)
+    wl = _small_workload([[150, 40, 20], [70, 90, 5]], 1, "bf16", 52, dims=dims)
+    _compare(wl, "full", _run_layer(wl, "full"), TOL_BF16)
+    _compare(wl, "target", _run_layer(wl, "target"), TOL_BF16)
+
+
+def test_layers_are_deterministic():
+    wl = synth.config1()
+    a = _run_layer(wl, "full")
+    b = _run_layer(wl, "full")
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(a[2], b[2])
+
+
+def _backbone_gpu(wl, x_np=None):
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    dw = DeviceWorkload(wl)
+    meta = B.mask_build(dw.batch)
+    ws = B.workspace(dw.batch, dw.dims, B.OP_BACKBONE)
+    x = dw.x.clone()
+    B.backbone_fwd(dw.batch, dw.dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, x, ws)
+    torch.cuda.synchronize()
+    return to_np(dw.x), to_np(x)
+
+
+def test_config3_backbone_sampled_users():
+    """Full 160-user, 16-layer bf16 batch on the GPU (the benchmarked launch); oracle on sampled users."""
+    wl = synth.config3()
+    say(f"backbone parity: {wl.batch.n_users} users, {wl.batch.total_rows} rows, 16 layers")
+    x0, got = _backbone_gpu(wl)
+    xr, full, tgt = rounded_inputs(wl)
+    np.testing.assert_array_equal(x0, xr)
+    users = [0, 77, 159]
+    ref = om.backbone(wl.batch, xr, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=om.bf16_round,
+                      users=users)
+    rows = wl.batch.rows_of(users)
+    assert np.all(np.isfinite(got))
+    r = Report(TOL_BF16)
+    r.close("X' (3 users)", got[rows], ref)
+    r.branch("dX (3 users, 16 roundings allowed)", got[rows], ref, xr[rows], "bf16", roundings=16)
+    r.check()
+
+
+def test_config3_backbone_composition_fp32():
+    """The same 16-layer stack and weights for 3 of its users through the fp32 path (no bf16
+    boundary rounding): the residual branch is resolved to fp32 precision."""
+    wl = synth.config3()
+    users = [0, 77, 159]
+    xr, full, tgt = rounded_inputs(wl)
+    sub = synth.Workload("cfg3_3users_f32", wl.batch.subset(users), wl.dims, "f32",
+                         xr[wl.batch.rows_of(users)].astype(np.float32), full=full, target=tgt,
+                         n_blocks=wl.n_blocks, k_target=wl.k_target)
+    x0, got = _backbone_gpu(sub)
+    ref = om.backbone(sub.batch, x0, full, tgt, wl.dims, wl.n_blocks, wl.k_target)
+    r = Report(TOL_F32)
+    r.close("X'", got, ref)
+    r.branch("dX", got, ref, x0, "f32", roundings=16)
+    r.check()

@@ -1,0 +1,98 @@
+"""GPU parity of the mask-metadata builder: bit-exact against the oracle.
+
+The oracle builds every user's dense mask from the rules and reads the
+per-row prefixes, counts and tile classes off it by brute force; the device
+builder computes them from lengths and timestamps with binary searches and
+min/max reductions.  Integers only, so the bar is equality.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import mask as omask
+from tests._parity import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _device_meta(batch):
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    db = B.DeviceBatch.from_synth(batch)
+    meta = B.mask_build(db)
+    torch.cuda.synchronize()
+    lay = B.meta_layout(db)
+    v = {k: t.cpu().numpy() for k, t in B.meta_views(meta, lay, batch.n_users).items()}
+    return v
+
+
+def _check(batch, users=None, fast=True):
+    say(f"mask parity: {batch.n_users} users, split {batch.split}, {batch.total_rows} rows")
+    v = _device_meta(batch)
+    off = batch.row_off
+    sel = list(range(batch.n_users)) if users is None else list(users)
+    for u in sel:
+        ref = omask.batch_meta(batch.user(u), 64, 64, fast=fast)
+        r0, r1 = off[u], off[u + 1]
+        np.testing.assert_array_equal(v["p"][r0:r1], ref["p"])
+        np.testing.assert_array_equal(v["n"][r0:r1], ref["n"])
+        np.testing.assert_array_equal(v["row_type"][r0:r1], ref["row_type"])
+        for key in ("full_tiles", "target_tiles"):
+            got = v[key][v[key][:, 0] == u]
+            exp = ref[key]
+            np.testing.assert_array_equal(got[:, 1:5], exp[:, 1:5])
+            # packed-row fields
+            np.testing.assert_array_equal(got[:, 5], r0 + got[:, 1])
+            np.testing.assert_array_equal(got[:, 7], np.full(len(got), r0))
+    if users is None:
+        for key in ("full_tiles", "target_tiles"):
+            assert np.all(np.diff(v[key][:, 0]) >= 0)          # users in order
+        lc = batch.lens[:, 0] + batch.lens[:, 1]
+        ctx = np.concatenate([np.arange(off[u], off[u] + lc[u]) for u in range(batch.n_users)] or [[]])
+        np.testing.assert_array_equal(v["ctx_rows"], ctx.astype(np.int32))
+        par = np.concatenate([off[u] + lc[u] + batch.split * np.arange(batch.lens[u, 2])
+                              for u in range(batch.n_users)] or [[]])
+        np.testing.assert_array_equal(v["parent_row"], par.astype(np.int32))
+        # target tiles: query-space row = index of the T row among all T rows
+        tt = v["target_tiles"]
+        t_off = np.concatenate([[0], np.cumsum(batch.split * batch.lens[:, 2])])
+        np.testing.assert_array_equal(tt[:, 6], t_off[tt[:, 0]] + tt[:, 1] - lc[tt[:, 0]])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+@pytest.mark.parametrize("split", [1, 4])
+def test_mask_random_small_batches(seed, split):
+    rng = np.random.default_rng(100 + seed)
+    b = synth.random_small(rng, 40, split, None, max_h=90, max_r=70, max_t=20)
+    _check(b, fast=False)
+
+
+def test_mask_degenerate_users():
+    # empty users, no actions, no targets, no history, exact tile multiples
+    lens = np.array([[0, 0, 0], [64, 0, 0], [0, 64, 0], [0, 0, 16], [128, 64, 16], [1, 0, 1], [63, 1, 0],
+                     [0, 0, 0], [65, 63, 33]], np.int32)
+    rng = np.random.default_rng(9)
+    b = synth.make_batch(rng, lens, 4)
+    _check(b, fast=False)
+
+
+def test_mask_config0_to_config2():
+    _check(synth.config0().batch, fast=False)
+    _check(synth.config1().batch)
+    _check(synth.config2(4).batch)
+
+
+def test_mask_config3_full_batch():
+    _check(synth.config3(weights=False).batch)
+
+
+def test_mask_config4_sampled_users():
+    b = synth.config4(arrays=False).batch
+    _check(b, users=[0, 17, 63])
+
+
+def test_mask_build_is_deterministic():
+    b = synth.config1().batch
+    v1, v2 = _device_meta(b), _device_meta(b)
+    for k in v1:
+        np.testing.assert_array_equal(v1[k], v2[k])
