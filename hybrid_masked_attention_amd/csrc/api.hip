@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -156,6 +157,17 @@ mtfm_status prepare(const mtfm_batch* b, const mtfm_dims* d, const void* meta_d,
   return MTFM_OK;
 }
 
+// Workgroup shape of the full-layer attention kernel: 64 queries per wave by
+// default; MTFM_ATTN_FULL_QB=1 selects 32 queries per wave (twice the
+// workgroups, fewer registers).  A tuning knob: both shapes compute the same.
+static int full_attn_half_tiles() {
+  static const int v = [] {
+    const char* e = std::getenv("MTFM_ATTN_FULL_QB");
+    return (e && e[0] == '1') ? 1 : 0;
+  }();
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Full-attention layer ([explainer] §4.1):
 //   X~ = GLN1(X); [U|Q|K|V] = SiLU(X~ W^T); A = masked SiLU attention / n;
@@ -197,7 +209,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   aa.v = z + (2 * hd + gd) * es; aa.ldv = zw;
   aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
-  aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
+  aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles; aa.half_tiles = full_attn_half_tiles();
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   TRY(timed_attention(MTFM_K_ATTN_FULL, aa, dt, c.s));
@@ -283,7 +295,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
-  aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
+  aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));

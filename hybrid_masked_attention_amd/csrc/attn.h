@@ -12,6 +12,8 @@
 // s = q' . k, SiLU(x) = ln2 * s / (1 + 2^-s), so the kernels evaluate
 // s * rcp(1 + exp2(-s)) per visible pair and fold ln2 / n_i into the output.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 struct AttnArgs {
@@ -26,6 +28,7 @@ struct AttnArgs {
   const int32_t* lens;
   int32_t H, G, dh;
   float out_scale;               // ln 2
+  int32_t half_tiles;            // bf16: 1 = one workgroup per 32-row half tile (more workgroups)
 };
 
 mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s);

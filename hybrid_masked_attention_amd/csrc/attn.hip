@@ -1,20 +1,27 @@
 // Masked pointwise-SiLU attention kernels for gfx950.
 //
-// bf16 kernel: one workgroup per (64-row query tile, KV group g) with one wave
+// bf16 kernel: one workgroup per (query tile slice, KV group g) with one wave
 // per query head of the group (r waves).  The group's K and V tiles (64 keys
 // x 64 dims) are staged once in LDS and shared by the r heads ([explainer]
 // §4.1 GQA: r query heads share a KV head).  Per key tile each wave computes
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulate), applies
-// SiLU pointwise in registers, rounds P to bf16 and accumulates O += P V on
-// MFMA.  The S^T accumulator layout (lane = query, registers = keys) is used
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulate), applies SiLU
+// pointwise in registers, rounds P to bf16 and accumulates O += P V on MFMA.
+// The S^T accumulator layout (lane = query, registers = keys) is used
 // directly as the A operand of P V once V's key order is permuted to match,
 // so P never leaves registers.  V is transposed while being staged in LDS.
 //
 // Only key tiles the metadata marks visible are visited ([blog] §6.2: compute
 // only key blocks holding a valid key); the mask compare runs only on mixed
-// tiles and on a short last tile.  T columns are never tiled ([blog] §6.2:
+// tiles and on a short last tile (separate straight-line tile bodies, so the
+// unmasked body carries no compare).  T columns are never tiled ([blog] §6.2:
 // the user-to-item direction is skipped): a T row's self term is one extra
 // "diagonal" tile built from the query tile's own K/V rows.
+//
+// Throughput: every visible pair costs one exp and one reciprocal on the
+// VALU (about as many cycles as its share of MFMA work), so the kernel keeps
+// two waves per SIMD and issues the next key block's QK MFMAs next to the
+// current block's SiLU.  QB = 2 gives each wave 64 queries (full layer);
+// QB = 1 gives 32 (target layer: twice the workgroups for its few T rows).
 //
 // fp32 kernel: one thread per (query row, head), plain loops; the fp32
 // correctness path.
@@ -38,46 +45,53 @@ MTFM_DEV float silu_scaled(float s) {
   return s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-s));
 }
 
-template <int R>
-__global__ __launch_bounds__(64 * R) void attn_bf16_kernel(AttnArgs g) {
+template <int R, int QB, bool PIPE>
+__global__ __launch_bounds__(64 * R, 2) void attn_bf16_kernel(AttnArgs g) {
   constexpr int NT = 64 * R;
   constexpr int KPT = (512 + NT - 1) / NT;  // 16-B K chunks per thread per tile
   constexpr int VPT = (256 + NT - 1) / NT;  // V (key pair, 8 dims) items per thread per tile
+  constexpr int SLICES = 2 / QB;            // workgroups per 64-row query tile
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * KS];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][DH * VS];
-  __shared__ float rinv[64];
+  __shared__ float rinv[32 * QB];
 
-  const int nblocks = g.ntiles * g.G;
+  const int nblocks = g.ntiles * g.G * SLICES;
   const int lb = xcd_remap(blockIdx.x, nblocks);
-  const int tile = lb / g.G, grp = lb % g.G;
+  const int slice = lb % SLICES;
+  const int tile = (lb / SLICES) / g.G, grp = (lb / SLICES) % g.G;
   const int32_t* td = g.tiles + 8 * tile;
-  const int u = td[TD_USER], row0 = td[TD_ROW0], nrows = td[TD_NROWS];
+  const int u = td[TD_USER], row0 = td[TD_ROW0], tile_rows = td[TD_NROWS];
   const int full_end = td[TD_FULL_END], key_end = td[TD_END];
-  const int grow0 = td[TD_GROW0], qrow0 = td[TD_QROW0], urow0 = td[TD_UROW0];
+  const int qoff = slice * 32 * QB;
+  const int nrows = min(32 * QB, tile_rows - qoff);
+  if (nrows <= 0) return;                      // empty half of a short tile (whole workgroup)
+  const int grow0 = td[TD_GROW0] + qoff, qrow0 = td[TD_QROW0] + qoff, urow0 = td[TD_UROW0];
   const int lctx = g.lens[3 * u] + g.lens[3 * u + 1];
-  const bool has_diag = row0 + nrows > lctx;
+  const bool has_diag = row0 + qoff + nrows > lctx;
   const int ntl = key_end + (has_diag ? 1 : 0);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = grp * R + wave;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  if (tid < 64) rinv[tid] = (tid < nrows) ? g.out_scale / (float)g.n[grow0 + tid] : 0.f;
+  if (tid < 32 * QB) rinv[tid] = (tid < nrows) ? g.out_scale / (float)g.n[grow0 + tid] : 0.f;
 
   // Q fragments (B operand of S^T = K Q^T): query row qb*32 + l32, dims kk*16 + 8*hi + [0, 8)
-  bf16x8 qf[2][4];
-  int plim[2], selfq[2];
-  for (int qb = 0; qb < 2; ++qb) {
+  bf16x8 qf[QB][4];
+  int plim[QB], selfq[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
     const int qi = qb * 32 + l32;
     const bool ok = qi < nrows;
     const bf16* src = (const bf16*)g.q + (int64_t)(qrow0 + (ok ? qi : 0)) * g.ldq + h * DH + 8 * hi;
+#pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = ok ? *(const bf16x8*)(src + kk * 16) : bf16x8{};
     const int pp = ok ? g.p[grow0 + qi] : 0;
     plim[qb] = pp;
     selfq[qb] = ok ? (g.n[grow0 + qi] - pp) : 0;
   }
 
-  // tile staging: it < key_end -> context keys of the user; it == key_end -> the tile's own rows
+  // tile staging: it < key_end -> context keys of the user; it == key_end -> the slice's own rows
   bf16x8 rk[KPT], rv[VPT][2];
   auto load_tile = [&](int it) {
     const bool diag = it >= key_end;
@@ -86,11 +100,13 @@ __global__ __launch_bounds__(64 * R) void attn_bf16_kernel(AttnArgs g) {
     const int64_t ldk = diag ? g.ldkd : g.ldk, ldv = diag ? g.ldvd : g.ldv;
     const int base = diag ? qrow0 : urow0 + it * 64;
     const int lim = diag ? nrows : min(64, lctx - it * 64);
+#pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + NT * i;
       const int j = c >> 3, kc = c & 7;
       rk[i] = (c < 512 && j < lim) ? *(const bf16x8*)(kb + (int64_t)(base + j) * ldk + grp * DH + kc * 8) : bf16x8{};
     }
+#pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + NT * i;
       const int jp = c & 31, vc = c >> 5;
@@ -101,14 +117,17 @@ __global__ __launch_bounds__(64 * R) void attn_bf16_kernel(AttnArgs g) {
     }
   };
   auto store_tile = [&](int buf) {
+#pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + NT * i;
       if (c < 512) *(bf16x8*)(&Ks[buf][(c >> 3) * KS + (c & 7) * 8]) = rk[i];
     }
+#pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + NT * i;
       if (c >= 256) continue;
       const int jp = c & 31, vc = c >> 5;
+#pragma unroll
       for (int s = 0; s < 8; ++s) {
         bf16x2 pr;
         pr[0] = rv[i][0][s];
@@ -118,9 +137,75 @@ __global__ __launch_bounds__(64 * R) void attn_bf16_kernel(AttnArgs g) {
     }
   };
 
-  f32x16 o[2][2];
-  for (int a = 0; a < 2; ++a)
+  f32x16 o[QB][2];
+#pragma unroll
+  for (int a = 0; a < QB; ++a)
+#pragma unroll
     for (int b = 0; b < 2; ++b) o[a][b] = f32x16{};
+
+  // One key tile of two 32-key blocks.  With PIPE the QK MFMAs of both blocks
+  // are issued first (independent chains the scheduler can overlap with the
+  // SiLU of the first block); without it each block runs QK -> SiLU -> PV,
+  // which keeps fewer accumulators live.
+  auto silu_pv = [&](const bf16* V, int kb, const f32x16* stb, auto masked_tag, const int* lim, const int* dsel) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    // P chunk c covers keys kb*32 + 16c + {4hi + t, 8 + 4hi + t : t < 4} in slot order
+    bf16x8 pf[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int i = 8 * c + s;
+          float pv = silu_scaled(stb[qb][i]);
+          if constexpr (MASKED) {
+            const int key = kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const bool vis = key < lim[qb] || key == dsel[qb];
+            pv = vis ? pv : 0.f;
+          }
+          pf[qb][c][s] = (bf16)pv;
+        }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16* vrow = &V[(nb * 32 + l32) * VS + kb * 32 + 16 * c + 4 * hi];
+        const bf16x4 lo4 = *(const bf16x4*)(vrow);
+        const bf16x4 hi4 = *(const bf16x4*)(vrow + 8);
+        const bf16x8 vf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[qb][c], vf, o[qb][nb], 0, 0, 0);
+      }
+  };
+  auto qk = [&](const bf16* K, int kb, f32x16* stb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) stb[qb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 af = *(const bf16x8*)(&K[(kb * 32 + l32) * KS + kk * 16 + 8 * hi]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        stb[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][kk], stb[qb], 0, 0, 0);
+    }
+  };
+  auto tile_body = [&](const bf16* K, const bf16* V, auto masked_tag, const int* lim, const int* dsel) {
+    if constexpr (PIPE) {
+      f32x16 st[2][QB];
+      qk(K, 0, st[0]);
+      qk(K, 1, st[1]);
+      silu_pv(V, 0, st[0], masked_tag, lim, dsel);
+      silu_pv(V, 1, st[1], masked_tag, lim, dsel);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 st[QB];
+        qk(K, kb, st);
+        silu_pv(V, kb, st, masked_tag, lim, dsel);
+      }
+    }
+  };
 
   if (ntl > 0) {
     load_tile(0);
@@ -133,51 +218,16 @@ __global__ __launch_bounds__(64 * R) void attn_bf16_kernel(AttnArgs g) {
     if (it + 1 < ntl) load_tile(it + 1);
     const bool diag = it >= key_end;
     const bool masked = diag || it >= full_end || (it + 1) * 64 > lctx;
-    int lim[2], dsel[2];
-    for (int qb = 0; qb < 2; ++qb) {
-      lim[qb] = diag ? 0 : plim[qb] - it * 64;
-      dsel[qb] = (diag && selfq[qb]) ? qb * 32 + l32 : -1;
-    }
-    const bf16* K = Ks[buf];
-    const bf16* V = Vs[buf];
+    if (!masked) {
+      tile_body(Ks[buf], Vs[buf], std::false_type{}, nullptr, nullptr);
+    } else {
+      int lim[QB], dsel[QB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 st[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 af = *(const bf16x8*)(&K[(kb * 32 + l32) * KS + kk * 16 + 8 * hi]);
-        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[0][kk], st[0], 0, 0, 0);
-        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[1][kk], st[1], 0, 0, 0);
+      for (int qb = 0; qb < QB; ++qb) {
+        lim[qb] = diag ? 0 : plim[qb] - it * 64;
+        dsel[qb] = (diag && selfq[qb]) ? qb * 32 + l32 : -1;
       }
-      // P chunk c covers keys kb*32 + 16c + {4hi + t, 8 + 4hi + t : t < 4} in slot order
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const int i = 8 * c + s;
-            float pv = silu_scaled(st[qb][i]);
-            if (masked) {
-              const int key = kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-              const bool vis = key < lim[qb] || key == dsel[qb];
-              pv = vis ? pv : 0.f;
-            }
-            pf[qb][c][s] = (bf16)pv;
-          }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const bf16* vrow = &V[(nb * 32 + l32) * VS + kb * 32 + 16 * c + 4 * hi];
-          const bf16x4 lo4 = *(const bf16x4*)(vrow);
-          const bf16x4 hi4 = *(const bf16x4*)(vrow + 8);
-          bf16x8 vf;
-          for (int t = 0; t < 4; ++t) { vf[t] = lo4[t]; vf[4 + t] = hi4[t]; }
-          o[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[0][c], vf, o[0][nb], 0, 0, 0);
-          o[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[1][c], vf, o[1][nb], 0, 0, 0);
-        }
+      tile_body(Ks[buf], Vs[buf], std::true_type{}, lim, dsel);
     }
     if (it + 1 < ntl) store_tile(buf ^ 1);
     __syncthreads();
@@ -185,8 +235,11 @@ __global__ __launch_bounds__(64 * R) void attn_bf16_kernel(AttnArgs g) {
 
   // O layout: lane holds dim nb*32 + l32 of rows qb*32 + 8(i/4) + 4hi + i%4
   bf16* out = (bf16*)g.a;
-  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
     for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qi = qb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
         if (qi < nrows)
@@ -199,7 +252,7 @@ template <int D>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs g) {
   const int tile = blockIdx.x, h = blockIdx.y;
   const int32_t* td = g.tiles + 8 * tile;
-  const int u = td[TD_USER], nrows = td[TD_NROWS];
+  const int nrows = td[TD_NROWS];
   const int grow0 = td[TD_GROW0], qrow0 = td[TD_QROW0], urow0 = td[TD_UROW0];
   const int qi = threadIdx.x;
   if (qi >= nrows) return;
@@ -224,7 +277,20 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs g) {
   const float sc = g.out_scale / (float)g.n[grow0 + qi];
   float* out = (float*)g.a + (int64_t)(qrow0 + qi) * g.lda + h * D;
   for (int c = 0; c < D; ++c) out[c] = acc[c] * sc;
-  (void)u;
+}
+
+template <int QB>
+mtfm_status launch_bf16(const AttnArgs& a, int r, hipStream_t s) {
+  constexpr bool PIPE = QB == 1;
+  const unsigned blocks = (unsigned)(a.ntiles * a.G * (2 / QB));
+  switch (r) {
+    case 1: attn_bf16_kernel<1, QB, PIPE><<<blocks, 64, 0, s>>>(a); break;
+    case 2: attn_bf16_kernel<2, QB, PIPE><<<blocks, 128, 0, s>>>(a); break;
+    case 4: attn_bf16_kernel<4, QB, PIPE><<<blocks, 256, 0, s>>>(a); break;
+    case 8: attn_bf16_kernel<8, QB, PIPE><<<blocks, 512, 0, s>>>(a); break;
+    default: return MTFM_E_UNSUPPORTED;
+  }
+  return MTFM_OK;
 }
 
 }  // namespace
@@ -234,14 +300,8 @@ mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
   const int r = a.H / a.G;
   if (dtype == MTFM_BF16) {
     if (a.dh != 64) return MTFM_E_UNSUPPORTED;
-    const unsigned blocks = (unsigned)(a.ntiles * a.G);
-    switch (r) {
-      case 1: attn_bf16_kernel<1><<<blocks, 64, 0, s>>>(a); break;
-      case 2: attn_bf16_kernel<2><<<blocks, 128, 0, s>>>(a); break;
-      case 4: attn_bf16_kernel<4><<<blocks, 256, 0, s>>>(a); break;
-      case 8: attn_bf16_kernel<8><<<blocks, 512, 0, s>>>(a); break;
-      default: return MTFM_E_UNSUPPORTED;
-    }
+    mtfm_status st = a.half_tiles ? launch_bf16<1>(a, r, s) : launch_bf16<2>(a, r, s);
+    if (st != MTFM_OK) return st;
   } else {
     dim3 grid((unsigned)a.ntiles, (unsigned)a.H);
     if (a.dh == 32) attn_f32_kernel<32><<<grid, 64, 0, s>>>(a);

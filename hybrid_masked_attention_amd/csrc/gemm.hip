@@ -3,16 +3,20 @@
 // correctness path.
 //
 // bf16 kernel: 256 threads = 4 waves in a 2 x 2 grid, block tile 128 x 128,
-// each wave 64 x 64 = 2 x 2 MFMA tiles of 32 x 32; K steps of 32 staged in LDS,
-// double buffered with register prefetch of the next step.  Block ids are
-// remapped so that consecutive logical tiles (which share A rows) land on the
-// same XCD and hit its L2.
+// each wave 64 x 64 = 2 x 2 MFMA tiles of 32 x 32; K steps of 64 staged in LDS,
+// double buffered with register prefetch of the next step, two workgroups per
+// CU.  The MFMA computes C^T (weights as the A operand) so that each lane ends
+// up holding four consecutive output columns of one row: epilogue stores are
+// 8 bytes wide and the column segment (U / Q / K|V) is uniform per 32-column
+// block.  Block ids are remapped so that consecutive logical tiles (which share
+// A rows) land on the same XCD and hit its L2.
 
 #include "gemm.h"
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, LDS_STRIDE = BK + 8;  // +16 B per row against bank conflicts
+constexpr int BM = 128, BN = 128, BK = 64, LDS_STRIDE = BK + 8;  // +16 B per row against bank conflicts
+constexpr float kLog2eF = 1.44269504088896340736f;
 
 MTFM_DEV int64_t map_row(const RowMap& r, int m) {
   return (int64_t)(r.list ? r.list[m] : m * r.mul) + r.add;
@@ -35,8 +39,13 @@ MTFM_DEV const T* b_row_ptr(const GemmArgs& g, int z, int n) {
   return (const T*)g.B[2] + (int64_t)z * g.bz[2] + (int64_t)n * g.ldb;
 }
 
+MTFM_DEV float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2eF));
+}
+
+// Scalar epilogue (fp32 path).
 template <typename T>
-MTFM_DEV void epilogue_store(const GemmArgs& g, const RowMap& cmap, int m, int n, float acc) {
+MTFM_DEV void epilogue_one(const GemmArgs& g, const RowMap& cmap, int m, int n, float acc) {
   const int64_t crow = map_row(cmap, m);
   if (g.epi == EPI_SILU_SPLIT) {
     const float v = acc / (1.0f + __expf(-acc));
@@ -55,7 +64,8 @@ MTFM_DEV void epilogue_store(const GemmArgs& g, const RowMap& cmap, int m, int n
   }
 }
 
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDS_STRIDE];
 
@@ -69,69 +79,128 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
 
-  // each thread moves 2 x 16 B of A and 2 x 16 B of B per K step
-  const bf16* a_src[2];
-  const bf16* b_src[2];
-  int lds_off[2];
-  for (int i = 0; i < 2; ++i) {
+  // each thread moves 4 x 16 B of A and 4 x 16 B of B per K step
+  const bf16* a_src[4];
+  const bf16* b_src[4];
+  int lds_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
     const int c = tid + 256 * i;
-    const int row = c >> 2, kc = c & 3;
+    const int row = c >> 3, kc = c & 7;
     lds_off[i] = row * LDS_STRIDE + kc * 8;
     const int m = m0 + row, n = n0 + row;
     a_src[i] = (m < g.M) ? (const bf16*)g.A + map_row(amap, m) * g.lda + kc * 8 : nullptr;
     b_src[i] = (n < g.N) ? b_row_ptr<bf16>(g, z, n) + kc * 8 : nullptr;
   }
-  const bf16x8 zero8 = {};
-  bf16x8 ra[2], rb[2];
+  bf16x8 ra[4], rb[4];
   auto load_step = [&](int k0) {
-    for (int i = 0; i < 2; ++i) {
-      ra[i] = a_src[i] ? *(const bf16x8*)(a_src[i] + k0) : zero8;
-      rb[i] = b_src[i] ? *(const bf16x8*)(b_src[i] + k0) : zero8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = a_src[i] ? *(const bf16x8*)(a_src[i] + k0) : bf16x8{};
+      rb[i] = b_src[i] ? *(const bf16x8*)(b_src[i] + k0) : bf16x8{};
     }
   };
   auto store_step = [&](int buf) {
-    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       *(bf16x8*)(&As[buf][lds_off[i]]) = ra[i];
       *(bf16x8*)(&Bs[buf][lds_off[i]]) = rb[i];
     }
   };
 
+  // acc[nb][mb] holds C^T block: lane = row m (l32), registers = columns
   f32x16 acc[2][2];
+#pragma unroll
   for (int a = 0; a < 2; ++a)
+#pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
   const int nk = g.K / BK;
   load_step(0);
   store_step(0);
   __syncthreads();
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
   for (int ks = 0; ks < nk; ++ks) {
     const int buf = ks & 1;
     if (ks + 1 < nk) load_step((ks + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 xf[2], wf[2];
+#pragma unroll
       for (int mb = 0; mb < 2; ++mb)
-        af[mb] = *(const bf16x8*)(&As[buf][(wm * 64 + mb * 32 + fr) * LDS_STRIDE + kk * 16 + fk]);
+        xf[mb] = *(const bf16x8*)(&As[buf][(wm * 64 + mb * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * hi]);
+#pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        bfr[nb] = *(const bf16x8*)(&Bs[buf][(wn * 64 + nb * 32 + fr) * LDS_STRIDE + kk * 16 + fk]);
-      for (int mb = 0; mb < 2; ++mb)
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+        wf[nb] = *(const bf16x8*)(&Bs[buf][(wn * 64 + nb * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * hi]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[nb][mb], 0, 0, 0);
     }
     if (ks + 1 < nk) store_step(buf ^ 1);
     __syncthreads();
   }
 
-  // C layout of a 32x32 MFMA tile: lane l holds column l%32, rows 8(i/4) + 4(l/32) + i%4
-  for (int mb = 0; mb < 2; ++mb)
-    for (int nb = 0; nb < 2; ++nb)
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * 64 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const int n = n0 + wn * 64 + nb * 32 + (lane & 31);
-        if (m < g.M && n < g.N) epilogue_store<bf16>(g, cmap, m, n, acc[mb][nb][i]);
+  // C^T layout of a 32x32 tile: lane holds row m = l32 and columns
+  // 8(i/4) + 4hi + (i%4): registers 4j..4j+3 are four consecutive columns.
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = m0 + wm * 64 + mb * 32 + l32;
+    if (m >= g.M) continue;
+    const int64_t crow = map_row(cmap, m);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int nblk = n0 + wn * 64 + nb * 32;
+      if (nblk >= g.N) continue;
+      if constexpr (EPI == EPI_SILU_SPLIT) {
+        int r = 0;
+        while (r < 3 && nblk >= g.cend[r]) ++r;
+        const int c0 = r ? g.cend[r - 1] : 0;
+        const float sc = g.scale[r];
+        bf16* dst = (bf16*)g.dst[r] + crow * g.ld[r] + (nblk - c0) + 4 * hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = (bf16)(silu_fast(acc[nb][mb][4 * j + t]) * sc);
+          *(bf16x4*)(dst + 8 * j) = v;
+        }
+      } else if constexpr (EPI == EPI_RESID) {
+        const bf16* res = (const bf16*)g.resid + crow * g.ldr + nblk + 4 * hi;
+        bf16* dst = (bf16*)g.out + crow * g.ldo + nblk + 4 * hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x4 rr = *(const bf16x4*)(res + 8 * j);
+          bf16x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = (bf16)(acc[nb][mb][4 * j + t] + (float)rr[t]);
+          *(bf16x4*)(dst + 8 * j) = v;
+        }
+      } else if constexpr (EPI == EPI_STORE_F32) {
+        float* dst = (float*)g.out + crow * g.ldo + nblk + 4 * hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 v;
+          if (g.accumulate) v = *(const f32x4*)(dst + 8 * j);
+          else v = f32x4{};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] += acc[nb][mb][4 * j + t];
+          *(f32x4*)(dst + 8 * j) = v;
+        }
+      } else {
+        bf16* dst = (bf16*)g.out + crow * g.ldo + nblk + 4 * hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[nb][mb][4 * j + t];
+          *(bf16x4*)(dst + 8 * j) = v;
+        }
       }
+    }
+  }
 }
 
 // fp32 path: one thread per output element (tiny correctness configs).
@@ -146,7 +215,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   const float* b = b_row_ptr<float>(g, z, n);
   float acc = 0.f;
   for (int k = 0; k < g.K; ++k) acc = fmaf(a[k], b[k], acc);
-  epilogue_store<float>(g, cmap, m, n, acc);
+  epilogue_one<float>(g, cmap, m, n, acc);
 }
 
 }  // namespace
@@ -154,9 +223,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.groups <= 0) return MTFM_OK;
   if (dtype == MTFM_BF16) {
-    if (g.K % BK != 0) return MTFM_E_UNSUPPORTED;
-    const int blocks = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    gemm_bf16_kernel<<<dim3(blocks, 1, g.groups), 256, 0, s>>>(g);
+    // 32-column blocks must not straddle an output segment; K a multiple of the K step
+    if (g.K % BK != 0 || g.N % 32 != 0) return MTFM_E_UNSUPPORTED;
+    if (g.epi == EPI_SILU_SPLIT)
+      for (int r = 0; r < 4; ++r)
+        if (g.cend[r] % 32 != 0) return MTFM_E_UNSUPPORTED;
+    const dim3 grid(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN), 1, g.groups);
+    switch (g.epi) {
+      case EPI_SILU_SPLIT: gemm_bf16_kernel<EPI_SILU_SPLIT><<<grid, 256, 0, s>>>(g); break;
+      case EPI_RESID: gemm_bf16_kernel<EPI_RESID><<<grid, 256, 0, s>>>(g); break;
+      case EPI_STORE_F32: gemm_bf16_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(g); break;
+      default: gemm_bf16_kernel<EPI_STORE><<<grid, 256, 0, s>>>(g); break;
+    }
   } else {
     const int64_t total = (int64_t)g.M * g.N;
     gemm_f32_kernel<<<dim3((unsigned)((total + 255) / 256), 1, g.groups), 256, 0, s>>>(g);
