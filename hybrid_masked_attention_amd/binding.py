@@ -21,7 +21,8 @@ OK, E_NULL, E_DIMS, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 OP_FULL, OP_TARGET, OP_BACKBONE, OP_FULL_BWD, OP_TARGET_BWD = 0, 1, 2, 3, 4
 TILE = 64
-UT_ROW, UT_ACT, UT_PARENT, UT_CTX, UT_FTILE, UT_TTILE, UT_TROW = range(7)
+UT_ROW, UT_ACT, UT_PARENT, UT_CTX, UT_FTILE, UT_TTILE, UT_TROW, UT_KTILE = range(8)
+UT_COUNT = 8
 
 # Names of the entry points declared in include/mtfm.h.
 ENTRY_POINTS = [
@@ -67,7 +68,8 @@ class CTargetGrad(ctypes.Structure):
 
 class CMetaLayout(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in (
-        "n_rows", "n_t_rows", "n_parents", "n_ctx_rows", "n_full_tiles", "n_target_tiles", "off_user", "off_p",
+        "n_rows", "n_t_rows", "n_parents", "n_ctx_rows", "n_full_tiles", "n_target_tiles", "n_key_tiles",
+        "off_user", "off_p",
         "off_n", "off_type", "off_full_tiles", "off_target_tiles", "off_ctx_rows", "off_parent_row", "total_bytes")]
 
 
@@ -200,7 +202,7 @@ def meta_views(meta, layout: CMetaLayout, n_users: int) -> Dict[str, "object"]:
         return t.view(*shape) if shape else t
     L = layout
     return {
-        "user": view(L.off_user, 7 * (n_users + 1), torch.int32, (7, n_users + 1)),
+        "user": view(L.off_user, UT_COUNT * (n_users + 1), torch.int32, (UT_COUNT, n_users + 1)),
         "p": view(L.off_p, L.n_rows, torch.int32),
         "n": view(L.off_n, L.n_rows, torch.int32),
         "row_type": view(L.off_type, L.n_rows, torch.uint8),

@@ -41,13 +41,14 @@ mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan) {
     p.n_ctx_rows += lh + lr;
     p.n_full_tiles += (rows + kTile - 1) / kTile;
     p.n_target_tiles += (b->split * lt + kTile - 1) / kTile;
+    p.n_key_tiles += (lh + lr + kTile - 1) / kTile;
     p.max_user_rows = (int32_t)std::min<int64_t>(std::max<int64_t>(p.max_user_rows, rows), INT32_MAX);
     p.max_t_rows = (int32_t)std::min<int64_t>(std::max<int64_t>(p.max_t_rows, b->split * lt), INT32_MAX);
     if (p.n_rows > INT32_MAX - 4096) return MTFM_E_DIMS;
   }
   mtfm_meta_layout& l = p.lay;
   l.n_rows = p.n_rows; l.n_t_rows = p.n_t_rows; l.n_parents = p.n_parents; l.n_ctx_rows = p.n_ctx_rows;
-  l.n_full_tiles = p.n_full_tiles; l.n_target_tiles = p.n_target_tiles;
+  l.n_full_tiles = p.n_full_tiles; l.n_target_tiles = p.n_target_tiles; l.n_key_tiles = p.n_key_tiles;
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
   l.off_user = take((int64_t)UT_COUNT * (p.n_users + 1) * 4);

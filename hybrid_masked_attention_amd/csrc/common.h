@@ -19,7 +19,8 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 static constexpr int kTile = MTFM_TILE;
 
 // Rows of the user table inside the metadata buffer (each [n_users + 1]).
-enum UserTable { UT_ROW = 0, UT_ACT = 1, UT_PARENT = 2, UT_CTX = 3, UT_FTILE = 4, UT_TTILE = 5, UT_TROW = 6, UT_COUNT = 7 };
+enum UserTable { UT_ROW = 0, UT_ACT = 1, UT_PARENT = 2, UT_CTX = 3, UT_FTILE = 4, UT_TTILE = 5, UT_TROW = 6, UT_KTILE = 7,
+                 UT_COUNT = 8 };
 
 // Token types, also the row index into the [3][D] group-LayerNorm parameters.
 enum TokenType { TT_H = 0, TT_R = 1, TT_T = 2 };
@@ -66,7 +67,7 @@ MTFM_DEV int upper_index(const int32_t* off, int n, int x) {
 struct MetaPlan {
   int32_t n_users = 0, split = 1;
   int64_t n_rows = 0, n_t_rows = 0, n_parents = 0, n_ctx_rows = 0;
-  int64_t n_full_tiles = 0, n_target_tiles = 0;
+  int64_t n_full_tiles = 0, n_target_tiles = 0, n_key_tiles = 0;
   int32_t max_user_rows = 0, max_t_rows = 0;
   mtfm_meta_layout lay{};
 };

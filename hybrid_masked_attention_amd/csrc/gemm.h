@@ -12,9 +12,10 @@
 #include "common.h"
 
 struct RowMap {
-  const int32_t* list;  // if non-null: row = list[m] + add
+  const int32_t* list;  // if non-null: row = list[m / div] + m % div + add
   int32_t mul;          // else:        row = m * mul + add
   int32_t add;
+  int32_t div;          // 0 or 1: plain list lookup
 };
 
 enum GemmEpi {
@@ -36,6 +37,24 @@ struct GemmArgs {
   const void* resid; int64_t ldr;
   void* out; int64_t ldo;
   int32_t accumulate;
+  void* pre; int64_t ldpre;       // EPI_SILU_SPLIT: if set, also store the pre-activation acc here
 };
 
 mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s);
+
+// Weight-gradient GEMM: C[m][n] (fp32, overwritten or accumulated) =
+//   sum over r in [0, R) of A[arow(r)][m] * B[brow(r)][n]
+// (both operands row-major with the reduced index r as their row), for
+// dW = dZ^T X~ style products over all packed rows.  Split over r into
+// partial sums that are added in a fixed order (deterministic).
+struct GemmTNArgs {
+  int32_t M, N, R;
+  int32_t groups;                 // grid.z; group z shifts maps and pointers
+  const void* A; int64_t lda; RowMap amap; int32_t amap_zadd; int64_t a_zoff;  // element offset per group
+  const void* B; int64_t ldb; RowMap bmap; int32_t bmap_zadd;
+  float* C; int64_t ldc; int64_t c_zoff; int32_t accumulate;
+  float* partial; int64_t partial_elems;   // workspace for split partial sums
+};
+
+int64_t gemm_tn_partial_elems(int32_t M, int32_t N, int32_t R, int32_t groups);
+mtfm_status launch_gemm_tn(const GemmTNArgs& g, hipStream_t s);

@@ -11,6 +11,8 @@
 // block.  Block ids are remapped so that consecutive logical tiles (which share
 // A rows) land on the same XCD and hit its L2.
 
+#include <algorithm>
+
 #include "gemm.h"
 
 namespace {
@@ -19,7 +21,11 @@ constexpr int BM = 128, BN = 128, BK = 64, LDS_STRIDE = BK + 8;  // +16 B per ro
 constexpr float kLog2eF = 1.44269504088896340736f;
 
 MTFM_DEV int64_t map_row(const RowMap& r, int m) {
-  return (int64_t)(r.list ? r.list[m] : m * r.mul) + r.add;
+  if (r.list) {
+    if (r.div > 1) return (int64_t)r.list[m / r.div] + m % r.div + r.add;
+    return (int64_t)r.list[m] + r.add;
+  }
+  return (int64_t)m * r.mul + r.add;
 }
 
 // Logical block index such that blocks sharing an XCD (hardware dispatches
@@ -167,6 +173,16 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
           for (int t = 0; t < 4; ++t) v[t] = (bf16)(silu_fast(acc[nb][mb][4 * j + t]) * sc);
           *(bf16x4*)(dst + 8 * j) = v;
         }
+        if (g.pre) {
+          bf16* pd = (bf16*)g.pre + crow * g.ldpre + nblk + 4 * hi;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x4 v;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[nb][mb][4 * j + t];
+            *(bf16x4*)(pd + 8 * j) = v;
+          }
+        }
       } else if constexpr (EPI == EPI_RESID) {
         const bf16* res = (const bf16*)g.resid + crow * g.ldr + nblk + 4 * hi;
         bf16* dst = (bf16*)g.out + crow * g.ldo + nblk + 4 * hi;
@@ -203,6 +219,124 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Weight-gradient GEMM.  Block tile 128 (m) x 128 (n), 32 rows of r per step:
+// each thread loads a pair of rows r, r+1 at 8 consecutive m (or n) and
+// writes them transposed into LDS as [m][r] so the MFMA operands (8
+// consecutive r per lane) are 16-byte reads.  Grid: tiles x splits of r; a
+// split writes its partial tile, the reduction adds splits in order.
+constexpr int TBK = 32, T_STRIDE = TBK + 8;
+constexpr int TN_ROWS_PER_SPLIT = 2048;
+
+__global__ __launch_bounds__(256, 2) void gemm_tn_kernel(GemmTNArgs g, int n_split) {
+  __shared__ __attribute__((aligned(16))) bf16 As[BM * T_STRIDE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[BN * T_STRIDE];
+  const int z = blockIdx.z;
+  const int n_mt = (g.M + BM - 1) / BM, n_nt = (g.N + BN - 1) / BN;
+  const int tiles = n_mt * n_nt;
+  const int split = blockIdx.x / tiles, t = blockIdx.x % tiles;
+  const int mt = t / n_nt, nt = t % n_nt;
+  const int m0 = mt * BM, n0 = nt * BN;
+  RowMap amap = g.amap; amap.add += z * g.amap_zadd;
+  RowMap bmap = g.bmap; bmap.add += z * g.bmap_zadd;
+  const bf16* A = (const bf16*)g.A + (int64_t)z * g.a_zoff;
+  const bf16* B = (const bf16*)g.B;
+  const int r_begin = split * TN_ROWS_PER_SPLIT, r_end = min(g.R, r_begin + TN_ROWS_PER_SPLIT);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // staging item: row pair rp (16 pairs per step), 8-column chunk cc (16 chunks of 128)
+  const int rp = tid >> 4, cc = tid & 15;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  for (int r0 = r_begin; r0 < r_end; r0 += TBK) {
+    bf16x8 av[2], bv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = r0 + 2 * rp + e;
+      const bool ok = r < r_end;
+      const int m = m0 + cc * 8, n = n0 + cc * 8;
+      av[e] = (ok && m < g.M) ? *(const bf16x8*)(A + map_row(amap, r) * g.lda + m) : bf16x8{};
+      bv[e] = (ok && n < g.N) ? *(const bf16x8*)(B + map_row(bmap, r) * g.ldb + n) : bf16x8{};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x2 pa, pb;
+      pa[0] = av[0][s]; pa[1] = av[1][s];
+      pb[0] = bv[0][s]; pb[1] = bv[1][s];
+      *(bf16x2*)(&As[(cc * 8 + s) * T_STRIDE + 2 * rp]) = pa;
+      *(bf16x2*)(&Bs[(cc * 8 + s) * T_STRIDE + 2 * rp]) = pb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TBK / 16; ++kk) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        af[mb] = *(const bf16x8*)(&As[(wm * 64 + mb * 32 + l32) * T_STRIDE + kk * 16 + 8 * hi]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        bfr[nb] = *(const bf16x8*)(&Bs[(wn * 64 + nb * 32 + l32) * T_STRIDE + kk * 16 + 8 * hi]);
+      // C^T tiles: lane = m, registers = four consecutive n
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
+    }
+  }
+  float* P = g.partial + ((int64_t)z * n_split + split) * (int64_t)g.M * g.N;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = m0 + wm * 64 + mb * 32 + l32;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int nblk = n0 + wn * 64 + nb * 32;
+      if (nblk >= g.N) continue;
+      float* dst = P + (int64_t)m * g.N + nblk + 4 * hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[nb][mb][4 * j + q];
+        *(f32x4*)(dst + 8 * j) = v;
+      }
+    }
+  }
+}
+
+// C (+)= sum over splits of the partials, in split order.
+__global__ __launch_bounds__(256) void gemm_tn_reduce_kernel(GemmTNArgs g, int n_split) {
+  const int z = blockIdx.y;
+  const int64_t mn = (int64_t)g.M * g.N;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  const float* P = g.partial + (int64_t)z * n_split * mn + i;
+  f32x4 s = *(const f32x4*)P;
+  for (int k = 1; k < n_split; ++k) {
+    const f32x4 v = *(const f32x4*)(P + k * mn);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] += v[q];
+  }
+  const int m = (int)(i / g.N), n = (int)(i % g.N);
+  float* dst = g.C + (int64_t)z * g.c_zoff + (int64_t)m * g.ldc + n;
+  if (g.accumulate) {
+    const f32x4 o = *(const f32x4*)dst;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] += o[q];
+  }
+  *(f32x4*)dst = s;
+}
+
 // fp32 path: one thread per output element (tiny correctness configs).
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   const int z = blockIdx.z;
@@ -219,6 +353,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 }  // namespace
+
+int64_t gemm_tn_partial_elems(int32_t M, int32_t N, int32_t R, int32_t groups) {
+  const int64_t n_split = std::max<int64_t>(1, (R + TN_ROWS_PER_SPLIT - 1) / TN_ROWS_PER_SPLIT);
+  return n_split * (int64_t)M * N * groups;
+}
+
+mtfm_status launch_gemm_tn(const GemmTNArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.groups <= 0) return MTFM_OK;
+  if (g.M % 8 != 0 || g.N % 32 != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0 || g.ldc % 4 != 0)
+    return MTFM_E_UNSUPPORTED;
+  const int n_split = std::max(1, (g.R + TN_ROWS_PER_SPLIT - 1) / TN_ROWS_PER_SPLIT);
+  if (gemm_tn_partial_elems(g.M, g.N, g.R, g.groups) > g.partial_elems) return MTFM_E_WORKSPACE;
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  gemm_tn_kernel<<<dim3(tiles * n_split, 1, g.groups), 256, 0, s>>>(g, n_split);
+  MTFM_LAUNCH_CHECK("gemm_tn");
+  const int64_t mn4 = ((int64_t)g.M * g.N) / 4;
+  gemm_tn_reduce_kernel<<<dim3((unsigned)((mn4 + 255) / 256), g.groups), 256, 0, s>>>(g, n_split);
+  MTFM_LAUNCH_CHECK("gemm_tn_reduce");
+  return MTFM_OK;
+}
 
 mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.groups <= 0) return MTFM_OK;

@@ -31,6 +31,7 @@ MTFM_DEV void user_counts(const int32_t* lens, int u, int split, int32_t out[UT_
   out[UT_FTILE] = (rows + kTile - 1) / kTile;
   out[UT_TTILE] = (split * lt + kTile - 1) / kTile;
   out[UT_TROW] = split * lt;
+  out[UT_KTILE] = (lh + lr + kTile - 1) / kTile;
 }
 
 // One workgroup: exclusive prefix sums of the per-user counts.
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(kScanThreads) void user_scan_kernel(const int32_t* 
   const int t = threadIdx.x;
   const int chunk = (n_users + kScanThreads - 1) / kScanThreads;
   const int u0 = min(t * chunk, n_users), u1 = min(u0 + chunk, n_users);
-  int32_t sum[UT_COUNT] = {0, 0, 0, 0, 0, 0, 0};
+  int32_t sum[UT_COUNT] = {};
   for (int u = u0; u < u1; ++u) {
     int32_t c[UT_COUNT];
     user_counts(lens, u, split, c);

@@ -127,8 +127,9 @@ typedef struct {
   int64_t n_ctx_rows;        /* total H + R rows */
   int64_t n_full_tiles;      /* query tiles of the full layer: sum ceil(N_u / 64) */
   int64_t n_target_tiles;    /* query tiles of the target layer: sum ceil(split L_T / 64) */
-  int64_t off_user;          /* int32 [7][n_users + 1]: row, action, parent, ctx-row, full-tile,
-                                target-tile and T-row offsets of each user */
+  int64_t n_key_tiles;       /* 64-key tiles of the users' context (H + R) rows */
+  int64_t off_user;          /* int32 [8][n_users + 1]: row, action, parent, ctx-row, full-tile,
+                                target-tile, T-row and context key-tile offsets of each user */
   int64_t off_p;             /* int32 [n_rows] visible context prefix p_i */
   int64_t off_n;             /* int32 [n_rows] visible key count n_i (p_i + self_i) */
   int64_t off_type;          /* uint8 [n_rows] token type 0 = H, 1 = R, 2 = T */
