@@ -44,6 +44,24 @@ def visible_pairs(n_rows_meta, lens, split):
     return int(n.sum()), t_sum
 
 
+def recorded_traffic():
+    """HBM bytes per launch of the full-layer attention kernel from the committed PMC summary.
+
+    The summary records the hash of the kernel source it was measured on; a
+    different source means the figure no longer applies (None).
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_full_cfg3_hbm_traffic.md")
+    try:
+        fields = dict(l.split(": ", 1) for l in open(path).read().splitlines() if ": " in l and not l.startswith("|"))
+        src = open(os.path.join(ROOT, fields["kernel_source"].strip()), "rb").read()
+        if hashlib.sha256(src).hexdigest() != fields["kernel_source_sha256"].strip():
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, seconds: float):
     """Oracle backbone (float64 numpy) on users of the batch until `seconds` pass."""
     import numpy as np
@@ -75,6 +93,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB first (calibrates PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -106,6 +126,14 @@ def main():
         B.backbone_fwd(batch, dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, x, ws)
 
     log(f"rows={lay.n_rows} t_rows={lay.n_t_rows} full_tiles={lay.n_full_tiles} target_tiles={lay.n_target_tiles}")
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mb} MiB read + {args.copy_probe_mb} MiB written")
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -202,7 +230,7 @@ def main():
         "step_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
         "roofline": {"kernel": "attn_bf16_kernel (full layer)", "bound": "mfma", "achieved": attn_tflops,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "flops_per_launch": attn_full_flops, "ms_per_launch": attn_ms},
+                     "traffic": recorded_traffic(), "flops_per_launch": attn_full_flops, "ms_per_launch": attn_ms},
         "breakdown": breakdown,
         "cpu_baseline": cpu,
     }
