@@ -158,15 +158,13 @@ mtfm_status prepare(const mtfm_batch* b, const mtfm_dims* d, const void* meta_d,
   return MTFM_OK;
 }
 
-// Workgroup shape of the full-layer attention kernel: 64 queries per wave by
-// default; MTFM_ATTN_FULL_QB=1 selects 32 queries per wave (twice the
-// workgroups, fewer registers).  A tuning knob: both shapes compute the same.
+// Workgroup shape of the full-layer attention kernel: 32 queries per wave by
+// default (more workgroups, no register spills); MTFM_ATTN_FULL_QB=2 selects
+// 64 queries per wave.  A tuning knob: both shapes compute the same.
+// Read at every call, so one process can run both shapes.
 static int full_attn_half_tiles() {
-  static const int v = [] {
-    const char* e = std::getenv("MTFM_ATTN_FULL_QB");
-    return (e && e[0] == '1') ? 1 : 0;
-  }();
-  return v;
+  const char* e = std::getenv("MTFM_ATTN_FULL_QB");
+  return (e && e[0] == '2') ? 0 : 1;
 }
 
 // ---------------------------------------------------------------------------

@@ -40,6 +40,14 @@ MTFM_DEV int xcd_remap(int bid, int nblocks) {
   return x * q + min(x, r) + k;
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+// 16-byte buffer load; offsets at or past the resource's record count read as zero.
+MTFM_DEV bf16x8 buf_ld8(__amdgpu_buffer_rsrc_t r, int off) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 MTFM_DEV float silu_scaled(float s) {
   // s = x log2(e); returns SiLU(x) / ln2 = s / (1 + 2^-s)
   return s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-s));
@@ -91,29 +99,44 @@ __global__ __launch_bounds__(64 * R, 2) void attn_bf16_kernel(AttnArgs g) {
     selfq[qb] = ok ? (g.n[grow0 + qi] - pp) : 0;
   }
 
-  // tile staging: it < key_end -> context keys of the user; it == key_end -> the slice's own rows
-  bf16x8 rk[KPT], rv[VPT][2];
-  auto load_tile = [&](int it) {
-    const bool diag = it >= key_end;
-    const bf16* kb = diag ? (const bf16*)g.kd : (const bf16*)g.k;
-    const bf16* vb = diag ? (const bf16*)g.vd : (const bf16*)g.v;
-    const int64_t ldk = diag ? g.ldkd : g.ldk, ldv = diag ? g.ldvd : g.ldv;
-    const int base = diag ? qrow0 : urow0 + it * 64;
-    const int lim = diag ? nrows : min(64, lctx - it * 64);
+  // tile staging through buffer loads: the tile's first row and its number of
+  // valid rows go into the (scalar) resource, the per-thread byte offsets are
+  // loop-invariant, and rows past the valid count read as zero.
+  // it < key_end -> context keys of the user; it == key_end -> the slice's own rows
+  int koff[2][KPT], voff[2][VPT][2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int64_t ldk = d ? g.ldkd : g.ldk, ldv = d ? g.ldvd : g.ldv;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + NT * i;
-      const int j = c >> 3, kc = c & 7;
-      rk[i] = (c < 512 && j < lim) ? *(const bf16x8*)(kb + (int64_t)(base + j) * ldk + grp * DH + kc * 8) : bf16x8{};
+      koff[d][i] = c < 512 ? (int)(((c >> 3) * ldk + grp * DH + (c & 7) * 8) * 2) : 0x7ffffff0;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + NT * i;
-      const int jp = c & 31, vc = c >> 5;
-      const int j = 2 * jp;
-      const bool in = c < 256;
-      rv[i][0] = (in && j < lim) ? *(const bf16x8*)(vb + (int64_t)(base + j) * ldv + grp * DH + vc * 8) : bf16x8{};
-      rv[i][1] = (in && j + 1 < lim) ? *(const bf16x8*)(vb + (int64_t)(base + j + 1) * ldv + grp * DH + vc * 8) : bf16x8{};
+      const int j = 2 * (c & 31), vc = c >> 5;
+      voff[d][i][0] = c < 256 ? (int)((j * ldv + grp * DH + vc * 8) * 2) : 0x7ffffff0;
+      voff[d][i][1] = c < 256 ? (int)(((j + 1) * ldv + grp * DH + vc * 8) * 2) : 0x7ffffff0;
+    }
+  }
+  bf16x8 rk[KPT], rv[VPT][2];
+  auto load_tile = [&](int it) {
+    const bool diag = it >= key_end;
+    const int d = diag ? 1 : 0;
+    const int64_t ldk = diag ? g.ldkd : g.ldk, ldv = diag ? g.ldvd : g.ldv;
+    const int base = diag ? qrow0 : urow0 + it * 64;
+    const int lim = diag ? nrows : min(64, lctx - it * 64);
+    const bf16* kb = (diag ? (const bf16*)g.kd : (const bf16*)g.k) + (int64_t)base * ldk;
+    const bf16* vb = (diag ? (const bf16*)g.vd : (const bf16*)g.v) + (int64_t)base * ldv;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, (int)(lim * ldk * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, (int)(lim * ldv * 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) rk[i] = buf_ld8(kr, koff[d][i]);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      rv[i][0] = buf_ld8(vr, voff[d][i][0]);
+      rv[i][1] = buf_ld8(vr, voff[d][i][1]);
     }
   };
   auto store_tile = [&](int buf) {

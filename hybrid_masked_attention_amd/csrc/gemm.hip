@@ -71,84 +71,8 @@ MTFM_DEV void epilogue_one(const GemmArgs& g, const RowMap& cmap, int m, int n, 
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDS_STRIDE];
-
-  const int z = blockIdx.z;
-  const int n_mt = (g.M + BM - 1) / BM, n_nt = (g.N + BN - 1) / BN;
-  const int lb = xcd_remap(blockIdx.x, n_mt * n_nt);
-  const int mt = lb / n_nt, nt = lb % n_nt;
-  const int m0 = mt * BM, n0 = nt * BN;
-  RowMap amap = g.amap; amap.add += z * g.amap_zadd;
-  RowMap cmap = g.cmap; cmap.add += z * g.cmap_zadd;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, hi = lane >> 5;
-
-  // each thread moves 4 x 16 B of A and 4 x 16 B of B per K step
-  const bf16* a_src[4];
-  const bf16* b_src[4];
-  int lds_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int row = c >> 3, kc = c & 7;
-    lds_off[i] = row * LDS_STRIDE + kc * 8;
-    const int m = m0 + row, n = n0 + row;
-    a_src[i] = (m < g.M) ? (const bf16*)g.A + map_row(amap, m) * g.lda + kc * 8 : nullptr;
-    b_src[i] = (n < g.N) ? b_row_ptr<bf16>(g, z, n) + kc * 8 : nullptr;
-  }
-  bf16x8 ra[4], rb[4];
-  auto load_step = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = a_src[i] ? *(const bf16x8*)(a_src[i] + k0) : bf16x8{};
-      rb[i] = b_src[i] ? *(const bf16x8*)(b_src[i] + k0) : bf16x8{};
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(bf16x8*)(&As[buf][lds_off[i]]) = ra[i];
-      *(bf16x8*)(&Bs[buf][lds_off[i]]) = rb[i];
-    }
-  };
-
-  // acc[nb][mb] holds C^T block: lane = row m (l32), registers = columns
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-
-  const int nk = g.K / BK;
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) load_step((ks + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 xf[2], wf[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        xf[mb] = *(const bf16x8*)(&As[buf][(wm * 64 + mb * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * hi]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        wf[nb] = *(const bf16x8*)(&Bs[buf][(wn * 64 + nb * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * hi]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[nb][mb], 0, 0, 0);
-    }
-    if (ks + 1 < nk) store_step(buf ^ 1);
-    __syncthreads();
-  }
-
+MTFM_DEV void gemm_epilogue(const GemmArgs& g, const RowMap& cmap, const f32x16 (&acc)[2][2], int m0, int n0, int wm,
+                            int wn, int l32, int hi) {
   // C^T layout of a 32x32 tile: lane holds row m = l32 and columns
   // 8(i/4) + 4hi + (i%4): registers 4j..4j+3 are four consecutive columns.
 #pragma unroll
@@ -219,6 +143,111 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
+// Persistent: gridDim.x workgroups (two per CU) walk the tiles of all groups;
+// the (tile, K step) sequence of a workgroup is one software pipeline, so the
+// next tile's first operands are being fetched while the current tile's
+// epilogue runs.
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDS_STRIDE];
+
+  const int n_mt = (g.M + BM - 1) / BM, n_nt = (g.N + BN - 1) / BN;
+  const int tiles_per_group = n_mt * n_nt;
+  const int n_tiles = tiles_per_group * g.groups;
+  const int nk = g.K / BK;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int my_tiles = wg < n_tiles ? (n_tiles - 1 - wg) / gridDim.x + 1 : 0;
+  const int total = my_tiles * nk;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // per-thread staging slots: 4 x 16 B of A and of B per K step
+  int lds_off[4];
+  const int kc = tid & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lds_off[i] = ((tid + 256 * i) >> 3) * LDS_STRIDE + kc * 8;
+
+  const bf16* a_src[4];
+  const bf16* b_src[4];
+  int cur_tile = -1;
+  auto tile_setup = [&](int t) {   // operand row pointers of tile t (k = 0)
+    if (t == cur_tile) return;
+    cur_tile = t;
+    const int z = t / tiles_per_group, tt = t % tiles_per_group;
+    const int m0 = (tt / n_nt) * BM, n0 = (tt % n_nt) * BN;
+    RowMap amap = g.amap; amap.add += z * g.amap_zadd;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid + 256 * i) >> 3;
+      const int m = m0 + row, n = n0 + row;
+      a_src[i] = (m < g.M) ? (const bf16*)g.A + map_row(amap, m) * g.lda + kc * 8 : nullptr;
+      b_src[i] = (n < g.N) ? b_row_ptr<bf16>(g, z, n) + kc * 8 : nullptr;
+    }
+  };
+  bf16x8 ra[4], rb[4];
+  auto load_step = [&](int s) {
+    const int t = wg + (s / nk) * gridDim.x, k0 = (s % nk) * BK;
+    tile_setup(t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = a_src[i] ? *(const bf16x8*)(a_src[i] + k0) : bf16x8{};
+      rb[i] = b_src[i] ? *(const bf16x8*)(b_src[i] + k0) : bf16x8{};
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(bf16x8*)(&As[buf][lds_off[i]]) = ra[i];
+      *(bf16x8*)(&Bs[buf][lds_off[i]]) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  if (total > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < total; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < total) load_step(s + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 xf[2], wf[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        xf[mb] = *(const bf16x8*)(&As[buf][(wm * 64 + mb * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * hi]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        wf[nb] = *(const bf16x8*)(&Bs[buf][(wn * 64 + nb * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * hi]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[nb][mb], 0, 0, 0);
+    }
+    if (s % nk == nk - 1) {   // tile finished: write it, reset the accumulators
+      const int t = wg + (s / nk) * gridDim.x;
+      const int z = t / tiles_per_group, tt = t % tiles_per_group;
+      RowMap cmap = g.cmap; cmap.add += z * g.cmap_zadd;
+      gemm_epilogue<EPI>(g, cmap, acc, (tt / n_nt) * BM, (tt % n_nt) * BN, wm, wn, l32, hi);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    }
+    if (s + 1 < total) store_step(buf ^ 1);
+    __syncthreads();
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Weight-gradient GEMM.  Block tile 128 (m) x 128 (n), 32 rows of r per step:
@@ -354,6 +383,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
 }  // namespace
 
+// Compute units of the current device (cached per device id).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 int64_t gemm_tn_partial_elems(int32_t M, int32_t N, int32_t R, int32_t groups) {
   const int64_t n_split = std::max<int64_t>(1, (R + TN_ROWS_PER_SPLIT - 1) / TN_ROWS_PER_SPLIT);
   return n_split * (int64_t)M * N * groups;
@@ -382,7 +424,8 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
     if (g.epi == EPI_SILU_SPLIT)
       for (int r = 0; r < 4; ++r)
         if (g.cend[r] % 32 != 0) return MTFM_E_UNSUPPORTED;
-    const dim3 grid(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN), 1, g.groups);
+    const int64_t tiles = (int64_t)((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.groups;
+    const dim3 grid((unsigned)std::min<int64_t>(tiles, 2 * (int64_t)device_cu_count()), 1, 1);
     switch (g.epi) {
       case EPI_SILU_SPLIT: gemm_bf16_kernel<EPI_SILU_SPLIT><<<grid, 256, 0, s>>>(g); break;
       case EPI_RESID: gemm_bf16_kernel<EPI_RESID><<<grid, 256, 0, s>>>(g); break;

@@ -189,3 +189,12 @@ def test_config3_backbone_composition_fp32():
     r.close("X'", got, ref)
     r.branch("dX", got, ref, x0, "f32", roundings=16)
     r.check()
+
+
+@pytest.mark.parametrize("case", ["config1", "edge"])
+def test_full_layer_64_query_wave_shape(case, monkeypatch):
+    # The full-layer attention kernel has two workgroup shapes (32 or 64 query
+    # rows per wave, selected by MTFM_ATTN_FULL_QB); both must match the oracle.
+    monkeypatch.setenv("MTFM_ATTN_FULL_QB", "2")
+    wl = synth.config1() if case == "config1" else _small_workload(EDGE_LENS, 1, "bf16", 53)
+    _compare(wl, "full", _run_layer(wl, "full"), TOL_BF16)
