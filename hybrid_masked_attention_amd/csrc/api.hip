@@ -14,6 +14,8 @@
 
 thread_local std::string g_last_error;
 
+void set_last_error(const char* msg) { g_last_error = msg; }
+
 mtfm_status hip_fail(hipError_t e, const char* where) {
   g_last_error = std::string(where) + ": " + hipGetErrorString(e);
   return MTFM_E_HIP;
@@ -263,7 +265,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   if (p.n_ctx_rows > 0) {
     GemmArgs gk{};
     gk.M = (int32_t)p.n_ctx_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
-    gk.A = xt; gk.lda = D; gk.amap = RowMap{c.meta.ctx_rows, 0, 0};
+    gk.A = xt; gk.lda = D; gk.amap = RowMap{c.meta.ctx_rows, 0, 0}; gk.a_rows = c.plan.n_rows;
     gk.B[0] = w->w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
     gk.cmap = RowMap{c.meta.ctx_rows, 0, 0};
     gk.epi = EPI_SILU_SPLIT;
@@ -274,7 +276,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
 
   GemmArgs gt{};
   gt.M = (int32_t)p.n_parents; gt.N = zw; gt.K = D; gt.groups = S;
-  gt.A = xt; gt.lda = D; gt.amap = RowMap{c.meta.parent_row, 0, 0}; gt.amap_zadd = 1;
+  gt.A = xt; gt.lda = D; gt.amap = RowMap{c.meta.parent_row, 0, 0}; gt.amap_zadd = 1; gt.a_rows = c.plan.n_rows;
   gt.B[0] = w->w_u; gt.bn[0] = hd;
   gt.B[1] = w->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
   gt.B[2] = w->w_kv; gt.bn[2] = 2 * gd;

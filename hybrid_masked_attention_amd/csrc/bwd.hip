@@ -272,7 +272,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
   if (C > 0) {
     GemmArgs gk{};
     gk.M = C; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
-    gk.A = xt; gk.lda = D; gk.amap = ctx_rows;
+    gk.A = xt; gk.lda = D; gk.amap = ctx_rows; gk.a_rows = c.plan.n_rows;
     gk.B[0] = w->w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
     gk.cmap = ctx_rows; gk.epi = EPI_SILU_SPLIT;
     gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = 2 * gd; gk.scale[0] = 1.f;
@@ -283,7 +283,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
   if (T > 0) {
     GemmArgs gt{};
     gt.M = P; gt.N = zw; gt.K = D; gt.groups = S;
-    gt.A = xt; gt.lda = D; gt.amap = list_map(c.meta.parent_row); gt.amap_zadd = 1;
+    gt.A = xt; gt.lda = D; gt.amap = list_map(c.meta.parent_row); gt.amap_zadd = 1; gt.a_rows = c.plan.n_rows;
     gt.B[0] = w->w_u; gt.bn[0] = hd;
     gt.B[1] = w->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
     gt.B[2] = w->w_kv; gt.bn[2] = 2 * gd;
@@ -316,7 +316,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     TRY(transpose(s, w->w_o, D, nullptr, 0, nullptr, 0, hd, wot, D));
     GemmArgs gd_{};
     gd_.M = T; gd_.N = hd; gd_.K = D; gd_.groups = 1;
-    gd_.A = dy; gd_.lda = D; gd_.amap = t_rows;
+    gd_.A = dy; gd_.lda = D; gd_.amap = t_rows; gd_.a_rows = c.plan.n_rows;
     gd_.B[0] = wot; gd_.bn[0] = hd; gd_.ldb = D;
     gd_.cmap = identity_map(); gd_.epi = EPI_STORE_F32; gd_.out = dyv; gd_.ldo = hd;
     {
@@ -391,7 +391,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     TRY(transpose(s, w->w_kv, 2 * gd, nullptr, 0, nullptr, 0, D, wkvt, 2 * gd));
     GemmArgs gx{};
     gx.M = C; gx.N = D; gx.K = 2 * gd; gx.groups = 1;
-    gx.A = dhkv; gx.lda = 2 * gd; gx.amap = ctx_rows;
+    gx.A = dhkv; gx.lda = 2 * gd; gx.amap = ctx_rows; gx.a_rows = c.plan.n_rows;
     gx.B[0] = wkvt; gx.bn[0] = D; gx.ldb = 2 * gd;
     gx.cmap = ctx_rows; gx.epi = EPI_STORE_F32; gx.out = dxt; gx.ldo = D;
     TimedLaunch tl(MTFM_K_BWD, s);

@@ -88,6 +88,8 @@ MetaPtrs meta_ptrs(const MetaPlan& plan, const void* meta_d);
 
 // Records a HIP failure for mtfm_last_error and maps it to a status.
 mtfm_status hip_fail(hipError_t e, const char* where);
+// Records a message for mtfm_last_error (argument or size checks).
+void set_last_error(const char* msg);
 #define MTFM_LAUNCH_CHECK(where)                                  \
   do {                                                            \
     hipError_t _e = hipGetLastError();                            \

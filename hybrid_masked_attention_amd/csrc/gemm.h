@@ -29,6 +29,7 @@ struct GemmArgs {
   int32_t M, N, K;
   int32_t groups;                 // grid.z; group z shifts the maps and B pointers below
   const void* A; int64_t lda; RowMap amap; int32_t amap_zadd;
+  int64_t a_rows;                 // rows of the A buffer; required (bf16) when amap gathers through a list
   const void* B[3]; int32_t bn[3]; int64_t bz[3];   // segment rows; per-group element stride
   int64_t ldb;                    // row stride of B (elements), normally K
   RowMap cmap; int32_t cmap_zadd;
@@ -50,7 +51,8 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s);
 struct GemmTNArgs {
   int32_t M, N, R;
   int32_t groups;                 // grid.z; group z shifts maps and pointers
-  const void* A; int64_t lda; RowMap amap; int32_t amap_zadd; int64_t a_zoff;  // element offset per group
+  const void* A; int64_t lda; RowMap amap; int32_t amap_zadd;
+  int64_t a_zoff;                 // element offset per group
   const void* B; int64_t ldb; RowMap bmap; int32_t bmap_zadd;
   float* C; int64_t ldc; int64_t c_zoff; int32_t accumulate;
   float* partial; int64_t partial_elems;   // workspace for split partial sums

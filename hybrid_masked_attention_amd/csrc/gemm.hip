@@ -1,15 +1,12 @@
 // Projection GEMMs: bf16 MFMA (gfx950 v_mfma_f32_32x32x16_bf16, fp32
-// accumulation) with fused epilogues, and an fp32 FMA kernel for the fp32
-// correctness path.
+// accumulation) with fused epilogues, a weight-gradient (r-reduced) bf16
+// GEMM, and an fp32 FMA kernel for the fp32 correctness path.
 //
-// bf16 kernel: 256 threads = 4 waves in a 2 x 2 grid, block tile 128 x 128,
-// each wave 64 x 64 = 2 x 2 MFMA tiles of 32 x 32; K steps of 64 staged in LDS,
-// double buffered with register prefetch of the next step, two workgroups per
-// CU.  The MFMA computes C^T (weights as the A operand) so that each lane ends
-// up holding four consecutive output columns of one row: epilogue stores are
-// 8 bytes wide and the column segment (U / Q / K|V) is uniform per 32-column
-// block.  Block ids are remapped so that consecutive logical tiles (which share
-// A rows) land on the same XCD and hit its L2.
+// The MFMA computes C^T (weights as the A operand) so that each lane ends up
+// holding four consecutive output columns of one row; the column segment
+// (U / Q / K / V) is uniform per 64-column wave tile.  Block ids are remapped
+// so that consecutive logical tiles (which share A rows) land on the same XCD
+// and hit its L2.
 
 #include <algorithm>
 
@@ -17,7 +14,7 @@
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDS_STRIDE = BK + 8;  // +16 B per row against bank conflicts
+constexpr int BM = 128, BN = 128;   // weight-gradient GEMM tile
 constexpr float kLog2eF = 1.44269504088896340736f;
 
 MTFM_DEV int64_t map_row(const RowMap& r, int m) {
@@ -70,182 +67,316 @@ MTFM_DEV void epilogue_one(const GemmArgs& g, const RowMap& cmap, int m, int n, 
   }
 }
 
-template <int EPI>
-MTFM_DEV void gemm_epilogue(const GemmArgs& g, const RowMap& cmap, const f32x16 (&acc)[2][2], int m0, int n0, int wm,
-                            int wn, int l32, int hi) {
-  // C^T layout of a 32x32 tile: lane holds row m = l32 and columns
-  // 8(i/4) + 4hi + (i%4): registers 4j..4j+3 are four consecutive columns.
+// ---------------------------------------------------------------------------
+// bf16 kernel.  Tile 256 (m) x 128 (n), four waves in a 2 x 2 grid (wave tile
+// 128 x 64 = 4 x 2 MFMA tiles), K steps of 32 in a three-stage LDS ring that
+// is filled by buffer loads straight into LDS (no VGPR staging; rows past the
+// end of a matrix read as zero).  Each 64-byte LDS row keeps its four 16-byte
+// chunks XOR-swizzled by row so that both the DMA writes and the MFMA
+// fragment reads are free of bank conflicts.  Fragments are double buffered
+// in registers: the next K slice is read while the current one multiplies.
+// The epilogue stages the wave's output tile in the (then idle) LDS ring and
+// writes whole 128-byte row segments with 16-byte stores.
+constexpr int GBM = 256, GBN = 128, GBK = 32, GS = 3, GWN = 2, GNW = 4;
+constexpr int G_RPC = 16;                         // rows per 1 KB DMA chunk (4 x 16 B per row)
+constexpr int G_LA = GBM / G_RPC / GNW;           // DMA instructions per wave per K step: A
+constexpr int G_LB = GBN / G_RPC / GNW;           //                                        B
+constexpr int G_TM = 4, G_TN = 2, G_KK = GBK / 16;
+constexpr int G_WR = 128, G_WC = 64;              // wave tile
+constexpr int G_STAGE = (GBM + GBN) * GBK * 2;    // bytes per stage
+constexpr int G_VMC = (GS - 2) * (G_LA + G_LB);   // DMA instructions allowed in flight at a stage wait
+constexpr int G_VMC0 = (GS - 1) * (G_LA + G_LB);
+constexpr int G_EP_BYTES = 17408;                 // per-wave epilogue staging (128 x 136 B, or 64 x 272 B)
+static_assert(GNW * G_EP_BYTES <= GS * G_STAGE, "epilogue staging fits in the ring");
+constexpr uint32_t kOobOffset = 0x80000000u;      // voffset of a row past the end (reads zero)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+MTFM_DEV int g_swz(int r) { return (r >> 2) & 3; }
+
+MTFM_DEV void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+#endif
+}
+
+// Buffer resource of a wave-uniform base and size (readfirstlane keeps it in
+// scalar registers even where the compiler cannot prove uniformity).
+MTFM_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// s_waitcnt immediates: vmcnt(n) alone, and vmcnt(n) with lgkmcnt(0)
+template <int N> MTFM_DEV void wait_vm() { __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70); }
+template <int N> MTFM_DEV void wait_vm_lgkm() { __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070); }
+MTFM_DEV void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+// Workgroup barrier without the memory-model waits that __syncthreads adds
+// (those would also wait for the DMA loads still in flight).
+MTFM_DEV void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((__vector_size__(2 * sizeof(int64_t)))) int64_t i64x2;
+
+// One pass of the staged epilogue: the wave's fp32 accumulators of MFMA row
+// blocks [a0, a0 + NA) go through LDS as bf16 (OUTF32 = false; 136-byte rows)
+// or fp32 (272-byte rows), then each lane handles one row and 8 consecutive
+// columns, calling f(row_local, col_local, v[8]) with the values in fp32.
+template <bool OUTF32, int NA, typename F>
+MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][G_TM], int a0, int l32, int hi, int lane, F&& f) {
+  constexpr int RS = OUTF32 ? G_WC * 4 + 16 : G_WC * 2 + 8;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = m0 + wm * 64 + mb * 32 + l32;
-    if (m >= g.M) continue;
-    const int64_t crow = map_row(cmap, m);
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int nblk = n0 + wn * 64 + nb * 32;
-      if (nblk >= g.N) continue;
-      if constexpr (EPI == EPI_SILU_SPLIT) {
-        int r = 0;
-        while (r < 3 && nblk >= g.cend[r]) ++r;
-        const int c0 = r ? g.cend[r - 1] : 0;
-        const float sc = g.scale[r];
-        bf16* dst = (bf16*)g.dst[r] + crow * g.ld[r] + (nblk - c0) + 4 * hi;
+    for (int b = 0; b < G_TN; ++b)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 v;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = (bf16)(silu_fast(acc[nb][mb][4 * j + t]) * sc);
-          *(bf16x4*)(dst + 8 * j) = v;
-        }
-        if (g.pre) {
-          bf16* pd = (bf16*)g.pre + crow * g.ldpre + nblk + 4 * hi;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            bf16x4 v;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[nb][mb][4 * j + t];
-            *(bf16x4*)(pd + 8 * j) = v;
-          }
-        }
-      } else if constexpr (EPI == EPI_RESID) {
-        const bf16* res = (const bf16*)g.resid + crow * g.ldr + nblk + 4 * hi;
-        bf16* dst = (bf16*)g.out + crow * g.ldo + nblk + 4 * hi;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x4 rr = *(const bf16x4*)(res + 8 * j);
-          bf16x4 v;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = (bf16)(acc[nb][mb][4 * j + t] + (float)rr[t]);
-          *(bf16x4*)(dst + 8 * j) = v;
-        }
-      } else if constexpr (EPI == EPI_STORE_F32) {
-        float* dst = (float*)g.out + crow * g.ldo + nblk + 4 * hi;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) {
+        char* d = ep + (a * 32 + l32) * RS + (b * 32 + 8 * j + 4 * hi) * (OUTF32 ? 4 : 2);
+        if constexpr (OUTF32) {
           f32x4 v;
-          if (g.accumulate) v = *(const f32x4*)(dst + 8 * j);
-          else v = f32x4{};
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] += acc[nb][mb][4 * j + t];
-          *(f32x4*)(dst + 8 * j) = v;
-        }
-      } else {
-        bf16* dst = (bf16*)g.out + crow * g.ldo + nblk + 4 * hi;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+          for (int q = 0; q < 4; ++q) v[q] = acc[b][a0 + a][4 * j + q];
+          *(f32x4*)d = v;
+        } else {
           bf16x4 v;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[nb][mb][4 * j + t];
-          *(bf16x4*)(dst + 8 * j) = v;
+          for (int q = 0; q < 4; ++q) v[q] = (bf16)acc[b][a0 + a][4 * j + q];
+          *(bf16x4*)d = v;
         }
       }
+  // read back: 8 lanes per row (8 columns each), 8 rows per round
+#pragma unroll
+  for (int i = 0; i < NA * 32 / 8; ++i) {
+    const int r = i * 8 + (lane >> 3), c = (lane & 7) * 8;
+    float v[8];
+    if constexpr (OUTF32) {
+      const f32x4 x0 = *(const f32x4*)(ep + r * RS + c * 4);
+      const f32x4 x1 = *(const f32x4*)(ep + r * RS + c * 4 + 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { v[q] = x0[q]; v[4 + q] = x1[q]; }
+    } else {
+      const int64_t* src = (const int64_t*)(ep + r * RS + c * 2);
+      i64x2 raw; raw[0] = src[0]; raw[1] = src[1];
+      const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = (float)x[q];
     }
+    f(a0 * 32 + r, c, v);
   }
 }
 
-// Persistent: gridDim.x workgroups (two per CU) walk the tiles of all groups;
-// the (tile, K step) sequence of a workgroup is one software pipeline, so the
-// next tile's first operands are being fetched while the current tile's
-// epilogue runs.
+MTFM_DEV bf16x8 pack8(const float (&v)[8]) {
+  bf16x8 o;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] = (bf16)v[q];
+  return o;
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDS_STRIDE];
+  __shared__ __attribute__((aligned(1024))) char lds[GS * G_STAGE];
 
-  const int n_mt = (g.M + BM - 1) / BM, n_nt = (g.N + BN - 1) / BN;
+  const int n_mt = (g.M + GBM - 1) / GBM, n_nt = (g.N + GBN - 1) / GBN;
   const int tiles_per_group = n_mt * n_nt;
-  const int n_tiles = tiles_per_group * g.groups;
-  const int nk = g.K / BK;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int my_tiles = wg < n_tiles ? (n_tiles - 1 - wg) / gridDim.x + 1 : 0;
-  const int total = my_tiles * nk;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int z = t / tiles_per_group, tt = t % tiles_per_group;
+  const int m0 = (tt / n_nt) * GBM, n0 = (tt % n_nt) * GBN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / GWN, wn = wave % GWN, l32 = lane & 31, hi = lane >> 5;
+  const int rin = lane >> 2, slot = lane & 3;       // DMA lane: row within the chunk, 16-byte slot
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, hi = lane >> 5;
+  RowMap amap = g.amap; amap.add += z * g.amap_zadd;
+  RowMap cmap = g.cmap; cmap.add += z * g.cmap_zadd;
 
-  // per-thread staging slots: 4 x 16 B of A and of B per K step
-  int lds_off[4];
-  const int kc = tid & 7;
+  // A: one buffer resource per DMA instruction.  Contiguous row maps rebase
+  // the resource on the chunk's first row (no 4 GiB limit); gathered rows
+  // address the whole matrix (bounded on the host).
+  __amdgpu_buffer_rsrc_t ra[G_LA];
+  uint32_t aoff[G_LA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lds_off[i] = ((tid + 256 * i) >> 3) * LDS_STRIDE + kc * 8;
-
-  const bf16* a_src[4];
-  const bf16* b_src[4];
-  int cur_tile = -1;
-  auto tile_setup = [&](int t) {   // operand row pointers of tile t (k = 0)
-    if (t == cur_tile) return;
-    cur_tile = t;
-    const int z = t / tiles_per_group, tt = t % tiles_per_group;
-    const int m0 = (tt / n_nt) * BM, n0 = (tt % n_nt) * BN;
-    RowMap amap = g.amap; amap.add += z * g.amap_zadd;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid + 256 * i) >> 3;
-      const int m = m0 + row, n = n0 + row;
-      a_src[i] = (m < g.M) ? (const bf16*)g.A + map_row(amap, m) * g.lda + kc * 8 : nullptr;
-      b_src[i] = (n < g.N) ? b_row_ptr<bf16>(g, z, n) + kc * 8 : nullptr;
+  for (int i = 0; i < G_LA; ++i) {
+    const int rs = (i * GNW + wave) * G_RPC;               // first tile row of the chunk
+    const int r = rs + rin, m = m0 + r;
+    const uint32_t cb = (uint32_t)((slot ^ g_swz(r)) * 16);
+    if (amap.list) {
+      ra[i] = make_rsrc(g.A, (uint32_t)(g.a_rows * g.lda * 2));
+      aoff[i] = m < g.M ? (uint32_t)(map_row(amap, m) * g.lda * 2) + cb : kOobOffset;
+    } else {
+      const int valid = min(max(g.M - (m0 + rs), 0), G_RPC);
+      const int64_t row0 = (int64_t)(m0 + rs) * amap.mul + amap.add;
+      const uint32_t bytes = valid ? (uint32_t)(((int64_t)(valid - 1) * amap.mul * g.lda + g.K) * 2) : 0u;
+      ra[i] = make_rsrc((const bf16*)g.A + (valid ? row0 * g.lda : 0), bytes);
+      aoff[i] = (uint32_t)(rin * amap.mul * g.lda * 2) + cb;
     }
-  };
-  bf16x8 ra[4], rb[4];
-  auto load_step = [&](int s) {
-    const int t = wg + (s / nk) * gridDim.x, k0 = (s % nk) * BK;
-    tile_setup(t);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = a_src[i] ? *(const bf16x8*)(a_src[i] + k0) : bf16x8{};
-      rb[i] = b_src[i] ? *(const bf16x8*)(b_src[i] + k0) : bf16x8{};
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(bf16x8*)(&As[buf][lds_off[i]]) = ra[i];
-      *(bf16x8*)(&Bs[buf][lds_off[i]]) = rb[i];
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-
-  if (total > 0) {
-    load_step(0);
-    store_step(0);
   }
-  __syncthreads();
-  for (int s = 0; s < total; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < total) load_step(s + 1);
+  // B: the weight rows of a chunk lie in one segment (segment sizes are multiples of 16)
+  __amdgpu_buffer_rsrc_t rb[G_LB];
+  uint32_t boff[G_LB];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 xf[2], wf[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        xf[mb] = *(const bf16x8*)(&As[buf][(wm * 64 + mb * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * hi]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        wf[nb] = *(const bf16x8*)(&Bs[buf][(wn * 64 + nb * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * hi]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[nb][mb], 0, 0, 0);
+  for (int i = 0; i < G_LB; ++i) {
+    const int rs = (i * GNW + wave) * G_RPC;
+    const int r = rs + rin, n = n0 + rs;
+    const int valid = min(max(g.N - n, 0), G_RPC);
+    // (explicit selects keep the segment pointer in scalar registers)
+    const void* bseg = g.B[0];
+    int64_t bz = g.bz[0];
+    int nn = n;
+    if (nn >= g.bn[0]) {
+      nn -= g.bn[0]; bseg = g.B[1]; bz = g.bz[1];
+      if (nn >= g.bn[1]) { nn -= g.bn[1]; bseg = g.B[2]; bz = g.bz[2]; }
     }
-    if (s % nk == nk - 1) {   // tile finished: write it, reset the accumulators
-      const int t = wg + (s / nk) * gridDim.x;
-      const int z = t / tiles_per_group, tt = t % tiles_per_group;
-      RowMap cmap = g.cmap; cmap.add += z * g.cmap_zadd;
-      gemm_epilogue<EPI>(g, cmap, acc, (tt / n_nt) * BM, (tt % n_nt) * BN, wm, wn, l32, hi);
+    const bf16* base = (const bf16*)bseg + (int64_t)z * bz + (int64_t)nn * g.ldb;
+    rb[i] = make_rsrc(valid ? base : (const bf16*)g.B[0], valid ? (uint32_t)(((int64_t)(valid - 1) * g.ldb + g.K) * 2) : 0u);
+    boff[i] = (uint32_t)(rin * g.ldb * 2 + (slot ^ g_swz(r)) * 16);
+  }
+  auto issue = [&](int step, int stage) {
+    char* base = lds + stage * G_STAGE;
+    const uint32_t so = (uint32_t)step * GBK * 2;
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < G_LA; ++i) lds_dma16(ra[i], (lds_void*)(base + (i * GNW + wave) * 1024), aoff[i], so);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    for (int i = 0; i < G_LB; ++i)
+      lds_dma16(rb[i], (lds_void*)(base + GBM * GBK * 2 + (i * GNW + wave) * 1024), boff[i], so);
+  };
+
+  // fragment offsets within a stage: chunk (2 kk + hi) of row r sits at slot chunk ^ f(r)
+  int arow[G_TM], af[G_TM], brow[G_TN], bfo[G_TN];
+#pragma unroll
+  for (int i = 0; i < G_TM; ++i) {
+    const int r = wm * G_WR + i * 32 + l32;
+    arow[i] = r * GBK * 2; af[i] = hi ^ g_swz(r);
+  }
+#pragma unroll
+  for (int i = 0; i < G_TN; ++i) {
+    const int r = wn * G_WC + i * 32 + l32;
+    brow[i] = GBM * GBK * 2 + r * GBK * 2; bfo[i] = hi ^ g_swz(r);
+  }
+  bf16x8 fa[2][G_TM], fb[2][G_TN];
+  auto read = [&](int stage, int kk, int buf) {
+    const char* st = lds + stage * G_STAGE;
+#pragma unroll
+    for (int i = 0; i < G_TM; ++i) fa[buf][i] = *(const bf16x8*)(st + arow[i] + (((2 * kk) ^ af[i]) << 4));
+#pragma unroll
+    for (int i = 0; i < G_TN; ++i) fb[buf][i] = *(const bf16x8*)(st + brow[i] + (((2 * kk) ^ bfo[i]) << 4));
+  };
+  f32x16 acc[G_TN][G_TM];
+#pragma unroll
+  for (int b = 0; b < G_TN; ++b)
+#pragma unroll
+    for (int a = 0; a < G_TM; ++a) acc[b][a] = f32x16{};
+  auto mma = [&](int buf) {   // C^T tiles: weights as the A operand, so a lane holds 4 consecutive columns
+#pragma unroll
+    for (int b = 0; b < G_TN; ++b)
+#pragma unroll
+      for (int a = 0; a < G_TM; ++a)
+        acc[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][b], fa[buf][a], acc[b][a], 0, 0, 0);
+  };
+
+  const int nk = g.K / GBK;
+#pragma unroll
+  for (int s = 0; s < GS; ++s)
+    if (s < nk) issue(s, s);
+  if (GS - 1 < nk) wait_vm<G_VMC0>();
+  else wait_vm<0>();
+  barrier_only();
+  read(0, 0, 0);
+  int stage = 0;
+  for (int s = 0; s < nk - 1; ++s) {
+#pragma unroll
+    for (int kk = 0; kk < G_KK; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < G_KK) {
+        read(stage, kk + 1, cur ^ 1);
+      } else {
+        // step s + 1 has landed once at most G_VMC newer DMA instructions are
+        // outstanding; the barrier also tells every wave that this stage has
+        // been read (lgkmcnt(0)) so it can be refilled with step s + GS
+        if (s + GS - 1 < nk) wait_vm_lgkm<G_VMC>();
+        else wait_vm_lgkm<0>();
+        barrier_only();
+        if (s + GS < nk) issue(s + GS, stage);
+        stage = (stage + 1 == GS) ? 0 : stage + 1;
+        read(stage, 0, cur ^ 1);
+      }
+      mma(cur);
     }
-    if (s + 1 < total) store_step(buf ^ 1);
-    __syncthreads();
+  }
+#pragma unroll
+  for (int kk = 0; kk < G_KK; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < G_KK) read(stage, kk + 1, cur ^ 1);
+    mma(cur);
+  }
+
+  // ---- epilogue: the ring is free once every wave has finished its reads
+  wait_lgkm();
+  barrier_only();
+  char* ep = lds + wave * G_EP_BYTES;
+  const int mw = m0 + wm * G_WR, nw = n0 + wn * G_WC;
+  if (nw >= g.N) return;   // wave tile entirely past the last column (after the barrier)
+  if constexpr (EPI == EPI_SILU_SPLIT) {
+    // output segment of this wave's columns (selects, not a dynamic index into the arguments)
+    void* dseg = g.dst[0];
+    int64_t ldseg = g.ld[0];
+    float sc = g.scale[0];
+    int c0 = 0;
+    if (nw >= g.cend[0]) {
+      c0 = g.cend[0]; dseg = g.dst[1]; ldseg = g.ld[1]; sc = g.scale[1];
+      if (nw >= g.cend[1]) {
+        c0 = g.cend[1]; dseg = g.dst[2]; ldseg = g.ld[2]; sc = g.scale[2];
+        if (nw >= g.cend[2]) { c0 = g.cend[2]; dseg = g.dst[3]; ldseg = g.ld[3]; sc = g.scale[3]; }
+      }
+    }
+    if (g.pre) {
+      staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+        const int m = mw + rl;
+        if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.pre + map_row(cmap, m) * g.ldpre + nw + cl) = pack8(v);
+      });
+    }
+#pragma unroll
+    for (int b = 0; b < G_TN; ++b)
+#pragma unroll
+      for (int a = 0; a < G_TM; ++a)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[b][a][e] = silu_fast(acc[b][a][e]) * sc;
+    staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+      const int m = mw + rl;
+      if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)dseg + map_row(cmap, m) * ldseg + (nw - c0) + cl) = pack8(v);
+    });
+  } else if constexpr (EPI == EPI_STORE) {
+    staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+      const int m = mw + rl;
+      if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.out + map_row(cmap, m) * g.ldo + nw + cl) = pack8(v);
+    });
+  } else {
+    // fp32 staging in two halves of 64 rows
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      staged_pass<true, G_TM / 2>(ep, acc, h * (G_TM / 2), l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+        const int m = mw + rl;
+        if (m >= g.M || nw + cl >= g.N) return;
+        const int64_t crow = map_row(cmap, m);
+        if constexpr (EPI == EPI_RESID) {
+          const bf16x8 res = *(const bf16x8*)((const bf16*)g.resid + crow * g.ldr + nw + cl);
+          float o[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) o[q] = v[q] + (float)res[q];
+          *(bf16x8*)((bf16*)g.out + crow * g.ldo + nw + cl) = pack8(o);
+        } else {
+          float* d = (float*)g.out + crow * g.ldo + nw + cl;
+          f32x4 o0, o1;
+          if (g.accumulate) { o0 = *(const f32x4*)d; o1 = *(const f32x4*)(d + 4); }
+          else { o0 = f32x4{}; o1 = f32x4{}; }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { o0[q] += v[q]; o1[q] += v[4 + q]; }
+          *(f32x4*)d = o0;
+          *(f32x4*)(d + 4) = o1;
+        }
+      });
+    }
   }
 }
 
@@ -416,16 +547,37 @@ mtfm_status launch_gemm_tn(const GemmTNArgs& g, hipStream_t s) {
   return MTFM_OK;
 }
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.groups <= 0) return MTFM_OK;
   if (dtype == MTFM_BF16) {
-    // 32-column blocks must not straddle an output segment; K a multiple of the K step
-    if (g.K % BK != 0 || g.N % 32 != 0) return MTFM_E_UNSUPPORTED;
-    if (g.epi == EPI_SILU_SPLIT)
-      for (int r = 0; r < 4; ++r)
-        if (g.cend[r] % 32 != 0) return MTFM_E_UNSUPPORTED;
-    const int64_t tiles = (int64_t)((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.groups;
-    const dim3 grid((unsigned)std::min<int64_t>(tiles, 2 * (int64_t)device_cu_count()), 1, 1);
+    // K in whole steps; 16-byte rows and stores; weight segments in whole DMA
+    // chunks; output segments aligned to the 64-column wave tile
+    if (g.K % GBK != 0 || g.N % 8 != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0) return MTFM_E_UNSUPPORTED;
+    if (!aligned16(g.A) || !aligned16(g.B[0])) return MTFM_E_UNSUPPORTED;
+    if (g.N > g.bn[0] && (g.bn[0] % G_RPC != 0 || !aligned16(g.B[1]))) return MTFM_E_UNSUPPORTED;
+    if (g.N > g.bn[0] + g.bn[1] && (g.bn[1] % G_RPC != 0 || !aligned16(g.B[2]))) return MTFM_E_UNSUPPORTED;
+    if (g.amap.list) {
+      // gathered rows address the whole A buffer through one 31-bit offset
+      if (g.a_rows <= 0 || g.a_rows * g.lda * 2 + (int64_t)g.K * 2 >= (int64_t)kOobOffset) {
+        set_last_error("gemm: gathered activation matrix exceeds 2 GiB");
+        return MTFM_E_UNSUPPORTED;
+      }
+    }
+    if (g.epi == EPI_SILU_SPLIT) {
+      for (int r = 0; r < 4; ++r) {
+        if (g.cend[r] % G_WC != 0 && g.cend[r] < g.N) return MTFM_E_UNSUPPORTED;
+        if (g.dst[r] && (!aligned16(g.dst[r]) || g.ld[r] % 8 != 0)) return MTFM_E_UNSUPPORTED;
+      }
+      if (g.pre && (!aligned16(g.pre) || g.ldpre % 8 != 0)) return MTFM_E_UNSUPPORTED;
+    } else {
+      if (!aligned16(g.out) || g.ldo % 8 != 0) return MTFM_E_UNSUPPORTED;
+      if (g.epi == EPI_RESID && (!aligned16(g.resid) || g.ldr % 8 != 0)) return MTFM_E_UNSUPPORTED;
+    }
+    const int64_t tiles = (int64_t)((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN) * g.groups;
+    if (tiles > 0x7fffffff) return MTFM_E_UNSUPPORTED;
+    const dim3 grid((unsigned)tiles, 1, 1);
     switch (g.epi) {
       case EPI_SILU_SPLIT: gemm_bf16_kernel<EPI_SILU_SPLIT><<<grid, 256, 0, s>>>(g); break;
       case EPI_RESID: gemm_bf16_kernel<EPI_RESID><<<grid, 256, 0, s>>>(g); break;
