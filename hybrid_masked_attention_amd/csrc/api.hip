@@ -107,6 +107,10 @@ LayerWs layer_ws(const MetaPlan& p, const mtfm_dims* d, int op) {
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
   w.xt = take(p.n_rows * d->d_model * es);
+  if (d->dtype == MTFM_BF16) {
+    w.ldvt = vt_ld(p.n_rows);
+    w.vt = take(gd * w.ldvt * es);
+  }
   if (op == MTFM_OP_FULL) {
     w.z = take(p.n_rows * zw * es);
     w.a = take(p.n_rows * hd * es);
@@ -161,8 +165,8 @@ mtfm_status prepare(const mtfm_batch* b, const mtfm_dims* d, const void* meta_d,
 }
 
 // Workgroup shape of the full-layer attention kernel: 32 queries per wave by
-// default (more workgroups, no register spills); MTFM_ATTN_FULL_QB=2 selects
-// 64 queries per wave.  A tuning knob: both shapes compute the same.
+// default; MTFM_ATTN_FULL_QB=2 selects 64 queries per wave (half the
+// workgroups, more registers).  A tuning knob: both shapes compute the same.
 // Read at every call, so one process can run both shapes.
 static int full_attn_half_tiles() {
   const char* e = std::getenv("MTFM_ATTN_FULL_QB");
@@ -202,12 +206,14 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   gp.dst[1] = z + hd * es; gp.ld[1] = zw; gp.cend[1] = 2 * hd; gp.scale[1] = q_scale(dh);
   gp.dst[2] = z + 2 * hd * es; gp.ld[2] = zw; gp.cend[2] = zw; gp.scale[2] = 1.f;
   gp.cend[3] = zw;
+  if (dt == MTFM_BF16) { gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd; }
   TRY(timed_gemm(MTFM_K_GEMM_UQKV, gp, dt, c.s));
 
   AttnArgs aa{};
   aa.q = z + hd * es; aa.ldq = zw;
   aa.k = z + 2 * hd * es; aa.ldk = zw;
   aa.v = z + (2 * hd + gd) * es; aa.ldv = zw;
+  aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows;
   aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
   aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles; aa.half_tiles = full_attn_half_tiles();
@@ -263,14 +269,19 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   TRY(timed_gln(g1, dt, c.s));
 
   if (p.n_ctx_rows > 0) {
+    // K (row-major) and V of every packed row (the T rows' are unused): the
+    // attention reads the context keys as whole 64-row tiles of packed rows,
+    // V through its transposed copy (bf16)
     GemmArgs gk{};
-    gk.M = (int32_t)p.n_ctx_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
-    gk.A = xt; gk.lda = D; gk.amap = RowMap{c.meta.ctx_rows, 0, 0}; gk.a_rows = c.plan.n_rows;
+    gk.M = (int32_t)p.n_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
+    gk.A = xt; gk.lda = D; gk.amap = identity_map();
     gk.B[0] = w->w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
-    gk.cmap = RowMap{c.meta.ctx_rows, 0, 0};
+    gk.cmap = identity_map();
     gk.epi = EPI_SILU_SPLIT;
-    gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = 2 * gd; gk.scale[0] = 1.f;
-    gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd;
+    gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
+    gk.dst[1] = dt == MTFM_BF16 ? nullptr : kv + gd * es; gk.ld[1] = 2 * gd; gk.cend[1] = 2 * gd; gk.scale[1] = 1.f;
+    gk.cend[2] = gk.cend[3] = 2 * gd;
+    if (dt == MTFM_BF16) { gk.vt = ws + L.vt; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd; }
     TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s));
   }
 
@@ -293,6 +304,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   aa.q = zt + hd * es; aa.ldq = zw;
   aa.k = kv; aa.ldk = 2 * gd;
   aa.v = kv + gd * es; aa.ldv = 2 * gd;
+  aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows;
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;

@@ -24,8 +24,11 @@ inline float q_scale(int dh) { return kLog2e / std::sqrt((float)dh); }
 int64_t align_up(int64_t x, int64_t a);
 
 struct LayerWs {
-  int64_t xt = 0, z = 0, kv = 0, a = 0, y = 0, total = 0;
+  int64_t xt = 0, z = 0, kv = 0, vt = 0, a = 0, y = 0, total = 0;
+  int64_t ldvt = 0;   // row length of the transposed values (bf16 path)
 };
+// Row length of the transposed value copy: every packed row, rounded up to 64.
+inline int64_t vt_ld(int64_t n_rows) { return (n_rows + 63) / 64 * 64; }
 LayerWs layer_ws(const MetaPlan& p, const mtfm_dims* d, int op);
 
 struct Ctx {

@@ -19,7 +19,12 @@
 struct AttnArgs {
   const void* q; int64_t ldq;    // query rows (query space); head h at column h*dh
   const void* k; int64_t ldk;    // key rows (packed rows); group g at column g*dh
-  const void* v; int64_t ldv;
+  const void* v; int64_t ldv;    // value rows (fp32 path)
+  // bf16 path: values transposed, vt[(g*dh + d) * ldvt + perm16(packed row)]
+  // (rows permuted within aligned groups of 16 as {0-3, 8-11, 4-7, 12-15});
+  // ldvt a multiple of 64 covering every packed row, slots past the last row zero
+  const void* vt; int64_t ldvt;
+  int32_t n_key_rows;            // packed rows in k (rows past it read as zero)
   const void* kd; int64_t ldkd;  // the query rows' own keys / values (query space)
   const void* vd; int64_t ldvd;
   void* a; int64_t lda;          // output [query row][H*dh]

@@ -22,7 +22,7 @@
 namespace {
 
 struct BwdWs {
-  int64_t xt, z, hpre, kv, kvpre, a, y, wot, w1t, wkvt, dyv, dan, dan_lo, dq, dh, dhkv, dxt, pg, part;
+  int64_t xt, z, hpre, kv, kvpre, vt, ldvt, a, y, wot, w1t, wkvt, dyv, dan, dan_lo, dq, dh, dhkv, dxt, pg, part;
   int64_t part_elems, pg_blocks, total;
 };
 
@@ -41,6 +41,8 @@ BwdWs bwd_layout(const MetaPlan& p, const mtfm_dims* d, int op) {
   w.hpre = take(Q * zw * 2);
   w.kv = full ? 0 : take(R * 2 * gd * 2);
   w.kvpre = full ? 0 : take(R * 2 * gd * 2);
+  w.ldvt = vt_ld(R);
+  w.vt = take(gd * w.ldvt * 2);
   w.a = take(Q * hd * 2);
   w.y = take(Q * hd * 2);
   w.wot = take(hd * D * 2);
@@ -148,9 +150,11 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
   gp.dst[2] = z + 2 * hd; gp.ld[2] = zw; gp.cend[2] = zw; gp.scale[2] = 1.f;
   gp.cend[3] = zw;
   gp.pre = hpre; gp.ldpre = zw;
+  gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd;
   TRY(timed_gemm(MTFM_K_GEMM_UQKV, gp, MTFM_BF16, s));
   AttnArgs aa{};
   aa.q = z + hd; aa.ldq = zw; aa.k = z + 2 * hd; aa.ldk = zw; aa.v = z + 2 * hd + gd; aa.ldv = zw;
+  aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
   aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
   aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
@@ -270,14 +274,16 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
   g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
   TRY(timed_gln(g1, MTFM_BF16, s));
   if (C > 0) {
+    // K, V (and their pre-activations) of every packed row, V also transposed
     GemmArgs gk{};
-    gk.M = C; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
-    gk.A = xt; gk.lda = D; gk.amap = ctx_rows; gk.a_rows = c.plan.n_rows;
+    gk.M = R; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
+    gk.A = xt; gk.lda = D; gk.amap = identity_map();
     gk.B[0] = w->w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
-    gk.cmap = ctx_rows; gk.epi = EPI_SILU_SPLIT;
+    gk.cmap = identity_map(); gk.epi = EPI_SILU_SPLIT;
     gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = 2 * gd; gk.scale[0] = 1.f;
     gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd;
     gk.pre = kvpre; gk.ldpre = 2 * gd;
+    gk.vt = ws + L.vt; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
     TRY(timed_gemm(MTFM_K_GEMM_KV, gk, MTFM_BF16, s));
   }
   if (T > 0) {
@@ -298,6 +304,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     TRY(timed_gemm(MTFM_K_GEMM_T, gt, MTFM_BF16, s));
     AttnArgs aa{};
     aa.q = zt + hd; aa.ldq = zw; aa.k = kv; aa.ldk = 2 * gd; aa.v = kv + gd; aa.ldv = 2 * gd;
+    aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
     aa.kd = zt + 2 * hd; aa.ldkd = zw; aa.vd = zt + 2 * hd + gd; aa.ldvd = zw;
     aa.a = a; aa.lda = hd;
     aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;

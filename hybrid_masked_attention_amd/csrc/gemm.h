@@ -39,6 +39,12 @@ struct GemmArgs {
   void* out; int64_t ldo;
   int32_t accumulate;
   void* pre; int64_t ldpre;       // EPI_SILU_SPLIT: if set, also store the pre-activation acc here
+  // EPI_SILU_SPLIT (bf16, identity row maps): if set, output columns
+  // [vt_col0, vt_col0 + vt_cols) are also written transposed,
+  //   vt[(n - vt_col0) * ldvt + perm16(m)]  for every m < ldvt,
+  // rows past M as zeros; perm16 permutes rows within aligned groups of 16 as
+  // {0-3, 8-11, 4-7, 12-15} (the key order of the attention's P V operand).
+  void* vt; int64_t ldvt; int32_t vt_col0, vt_cols;
 };
 
 mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s);

@@ -342,10 +342,40 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
       for (int a = 0; a < G_TM; ++a)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[b][a][e] = silu_fast(acc[b][a][e]) * sc;
-    staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
-      const int m = mw + rl;
-      if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)dseg + map_row(cmap, m) * ldseg + (nw - c0) + cl) = pack8(v);
-    });
+    if (dseg) {
+      staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+        const int m = mw + rl;
+        if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)dseg + map_row(cmap, m) * ldseg + (nw - c0) + cl) = pack8(v);
+      });
+    }
+    if (g.vt && nw >= g.vt_col0 && nw < g.vt_col0 + g.vt_cols) {
+      // transposed copy: LDS [64 columns][128 rows] (272-byte rows), then each
+      // lane writes 8 consecutive slots of one column: slots 16G + 8h + [0, 8)
+      // hold rows 16G + 4h + [0, 4) and 16G + 8 + 4h + [0, 4)
+      constexpr int RT = G_WR * 2 + 16;
+#pragma unroll
+      for (int a = 0; a < G_TM; ++a)
+#pragma unroll
+        for (int b = 0; b < G_TN; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int col = b * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+            *(bf16*)(ep + col * RT + (a * 32 + l32) * 2) = (bf16)acc[b][a][e];
+          }
+      const int64_t col0 = nw - g.vt_col0;
+#pragma unroll
+      for (int i = 0; i < G_WC / 4; ++i) {
+        const int col = i * 4 + (lane >> 4), sc = lane & 15;     // 16 lanes per column, 8 slots each
+        const int grp16 = sc >> 1, h = sc & 1;
+        const int r0 = grp16 * 16 + 4 * h;
+        const int64_t* s0 = (const int64_t*)(ep + col * RT + r0 * 2);
+        const int64_t* s1 = (const int64_t*)(ep + col * RT + (r0 + 8) * 2);
+        i64x2 v; v[0] = *s0; v[1] = *s1;
+        const int64_t slot0 = (int64_t)mw + sc * 8;
+        if (slot0 < g.ldvt && nw + col < g.N)
+          *(i64x2*)((bf16*)g.vt + (col0 + col) * g.ldvt + slot0) = v;
+      }
+    }
   } else if constexpr (EPI == EPI_STORE) {
     staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
       const int m = mw + rl;
@@ -571,6 +601,12 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
         if (g.dst[r] && (!aligned16(g.dst[r]) || g.ld[r] % 8 != 0)) return MTFM_E_UNSUPPORTED;
       }
       if (g.pre && (!aligned16(g.pre) || g.ldpre % 8 != 0)) return MTFM_E_UNSUPPORTED;
+      if (g.vt) {
+        // rows map to themselves; whole 64-column wave tiles; slots up to ldvt covered by the grid
+        if (g.amap.list || g.cmap.list || g.cmap.mul != 1 || g.cmap.add != 0 || g.groups != 1) return MTFM_E_UNSUPPORTED;
+        if (g.vt_col0 % G_WC != 0 || g.vt_cols % G_WC != 0 || !aligned16(g.vt) || g.ldvt % 64 != 0) return MTFM_E_UNSUPPORTED;
+        if (g.ldvt < g.M || g.ldvt > (int64_t)((g.M + GBM - 1) / GBM) * GBM) return MTFM_E_UNSUPPORTED;
+      }
     } else {
       if (!aligned16(g.out) || g.ldo % 8 != 0) return MTFM_E_UNSUPPORTED;
       if (g.epi == EPI_RESID && (!aligned16(g.resid) || g.ldr % 8 != 0)) return MTFM_E_UNSUPPORTED;
