@@ -69,15 +69,15 @@ MTFM_DEV void epilogue_one(const GemmArgs& g, const RowMap& cmap, int m, int n, 
 
 // ---------------------------------------------------------------------------
 // bf16 kernel.  Tile 256 (m) x 128 (n), four waves in a 2 x 2 grid (wave tile
-// 128 x 64 = 4 x 2 MFMA tiles), K steps of 32 in a three-stage LDS ring that
-// is filled by buffer loads straight into LDS (no VGPR staging; rows past the
-// end of a matrix read as zero).  Each 64-byte LDS row keeps its four 16-byte
+// 128 x 64 = 4 x 2 MFMA tiles), K steps of 32 in a two-stage LDS ring that is
+// filled by buffer loads straight into LDS (no VGPR staging; rows past the end
+// of a matrix read as zero); 48 KB of LDS lets three workgroups share a CU.  Each 64-byte LDS row keeps its four 16-byte
 // chunks XOR-swizzled by row so that both the DMA writes and the MFMA
 // fragment reads are free of bank conflicts.  Fragments are double buffered
 // in registers: the next K slice is read while the current one multiplies.
 // The epilogue stages the wave's output tile in the (then idle) LDS ring and
 // writes whole 128-byte row segments with 16-byte stores.
-constexpr int GBM = 256, GBN = 128, GBK = 32, GS = 3, GWN = 2, GNW = 4;
+constexpr int GBM = 256, GBN = 128, GBK = 32, GS = 2, GWN = 2, GNW = 4;
 constexpr int G_RPC = 16;                         // rows per 1 KB DMA chunk (4 x 16 B per row)
 constexpr int G_LA = GBM / G_RPC / GNW;           // DMA instructions per wave per K step: A
 constexpr int G_LB = GBN / G_RPC / GNW;           //                                        B
@@ -86,7 +86,7 @@ constexpr int G_WR = 128, G_WC = 64;              // wave tile
 constexpr int G_STAGE = (GBM + GBN) * GBK * 2;    // bytes per stage
 constexpr int G_VMC = (GS - 2) * (G_LA + G_LB);   // DMA instructions allowed in flight at a stage wait
 constexpr int G_VMC0 = (GS - 1) * (G_LA + G_LB);
-constexpr int G_EP_BYTES = 17408;                 // per-wave epilogue staging (128 x 136 B, or 64 x 272 B)
+constexpr int G_EP_BYTES = 9216;                  // per-wave epilogue staging: 64 x 136 B, 32 x 272 B or 64 x 144 B
 static_assert(GNW * G_EP_BYTES <= GS * G_STAGE, "epilogue staging fits in the ring");
 constexpr uint32_t kOobOffset = 0x80000000u;      // voffset of a row past the end (reads zero)
 
@@ -175,7 +175,7 @@ MTFM_DEV bf16x8 pack8(const float (&v)[8]) {
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char lds[GS * G_STAGE];
 
   const int n_mt = (g.M + GBM - 1) / GBM, n_nt = (g.N + GBN - 1) / GBN;
@@ -331,10 +331,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
       }
     }
     if (g.pre) {
-      staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
-        const int m = mw + rl;
-        if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.pre + map_row(cmap, m) * g.ldpre + nw + cl) = pack8(v);
-      });
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        staged_pass<false, 2>(ep, acc, 2 * h, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+          const int m = mw + rl;
+          if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.pre + map_row(cmap, m) * g.ldpre + nw + cl) = pack8(v);
+        });
     }
 #pragma unroll
     for (int b = 0; b < G_TN; ++b)
@@ -343,49 +345,56 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[b][a][e] = silu_fast(acc[b][a][e]) * sc;
     if (dseg) {
-      staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
-        const int m = mw + rl;
-        if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)dseg + map_row(cmap, m) * ldseg + (nw - c0) + cl) = pack8(v);
-      });
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        staged_pass<false, 2>(ep, acc, 2 * h, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+          const int m = mw + rl;
+          if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)dseg + map_row(cmap, m) * ldseg + (nw - c0) + cl) = pack8(v);
+        });
     }
     if (g.vt && nw >= g.vt_col0 && nw < g.vt_col0 + g.vt_cols) {
-      // transposed copy: LDS [64 columns][128 rows] (272-byte rows), then each
-      // lane writes 8 consecutive slots of one column: slots 16G + 8h + [0, 8)
-      // hold rows 16G + 4h + [0, 4) and 16G + 8 + 4h + [0, 4)
-      constexpr int RT = G_WR * 2 + 16;
-#pragma unroll
-      for (int a = 0; a < G_TM; ++a)
-#pragma unroll
-        for (int b = 0; b < G_TN; ++b)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int col = b * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-            *(bf16*)(ep + col * RT + (a * 32 + l32) * 2) = (bf16)acc[b][a][e];
-          }
+      // transposed copy, in two passes of 64 rows: LDS [64 columns][64 rows]
+      // (144-byte rows), then each lane writes 8 consecutive slots of one
+      // column: slots 16G + 8h + [0, 8) hold rows 16G + 4h + [0, 4) and
+      // 16G + 8 + 4h + [0, 4)
+      constexpr int RT = 64 * 2 + 16;
       const int64_t col0 = nw - g.vt_col0;
 #pragma unroll
-      for (int i = 0; i < G_WC / 4; ++i) {
-        const int col = i * 4 + (lane >> 4), sc = lane & 15;     // 16 lanes per column, 8 slots each
-        const int grp16 = sc >> 1, h = sc & 1;
-        const int r0 = grp16 * 16 + 4 * h;
-        const int64_t* s0 = (const int64_t*)(ep + col * RT + r0 * 2);
-        const int64_t* s1 = (const int64_t*)(ep + col * RT + (r0 + 8) * 2);
-        i64x2 v; v[0] = *s0; v[1] = *s1;
-        const int64_t slot0 = (int64_t)mw + sc * 8;
-        if (slot0 < g.ldvt && nw + col < g.N)
-          *(i64x2*)((bf16*)g.vt + (col0 + col) * g.ldvt + slot0) = v;
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < G_TN; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int col = b * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+              *(bf16*)(ep + col * RT + (a * 32 + l32) * 2) = (bf16)acc[b][2 * pass + a][e];
+            }
+#pragma unroll
+        for (int i = 0; i < G_WC / 8; ++i) {
+          const int col = i * 8 + (lane >> 3), sc = lane & 7;      // 8 lanes per column, 8 slots each
+          const int r0 = (sc >> 1) * 16 + 4 * (sc & 1);
+          const int64_t* s0 = (const int64_t*)(ep + col * RT + r0 * 2);
+          const int64_t* s1 = (const int64_t*)(ep + col * RT + (r0 + 8) * 2);
+          i64x2 v; v[0] = *s0; v[1] = *s1;
+          const int64_t slot0 = (int64_t)mw + pass * 64 + sc * 8;
+          if (slot0 < g.ldvt && nw + col < g.N)
+            *(i64x2*)((bf16*)g.vt + (col0 + col) * g.ldvt + slot0) = v;
+        }
       }
     }
   } else if constexpr (EPI == EPI_STORE) {
-    staged_pass<false, G_TM>(ep, acc, 0, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
-      const int m = mw + rl;
-      if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.out + map_row(cmap, m) * g.ldo + nw + cl) = pack8(v);
-    });
-  } else {
-    // fp32 staging in two halves of 64 rows
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      staged_pass<true, G_TM / 2>(ep, acc, h * (G_TM / 2), l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+    for (int h = 0; h < 2; ++h)
+      staged_pass<false, 2>(ep, acc, 2 * h, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
+        const int m = mw + rl;
+        if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.out + map_row(cmap, m) * g.ldo + nw + cl) = pack8(v);
+      });
+  } else {
+    // fp32 staging in four passes of 32 rows
+#pragma unroll
+    for (int h = 0; h < G_TM; ++h) {
+      staged_pass<true, 1>(ep, acc, h, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
         const int m = mw + rl;
         if (m >= g.M || nw + cl >= g.N) return;
         const int64_t crow = map_row(cmap, m);
