@@ -77,17 +77,24 @@ MTFM_DEV void epilogue_one(const GemmArgs& g, const RowMap& cmap, int m, int n, 
 // in registers: the next K slice is read while the current one multiplies.
 // The epilogue stages the wave's output tile in the (then idle) LDS ring and
 // writes whole 128-byte row segments with 16-byte stores.
-constexpr int GBM = 256, GBN = 128, GBK = 32, GS = 2, GWN = 2, GNW = 4;
+constexpr int GBN = 128, GBK = 32, GS = 2, GWN = 2, GNW = 4;
 constexpr int G_RPC = 16;                         // rows per 1 KB DMA chunk (4 x 16 B per row)
-constexpr int G_LA = GBM / G_RPC / GNW;           // DMA instructions per wave per K step: A
-constexpr int G_LB = GBN / G_RPC / GNW;           //                                        B
-constexpr int G_TM = 4, G_TN = 2, G_KK = GBK / 16;
-constexpr int G_WR = 128, G_WC = 64;              // wave tile
-constexpr int G_STAGE = (GBM + GBN) * GBK * 2;    // bytes per stage
-constexpr int G_VMC = (GS - 2) * (G_LA + G_LB);   // DMA instructions allowed in flight at a stage wait
-constexpr int G_VMC0 = (GS - 1) * (G_LA + G_LB);
+constexpr int G_LB = GBN / G_RPC / GNW;           // DMA instructions per wave per K step: B
+constexpr int G_TN = 2, G_KK = GBK / 16;
+constexpr int G_WC = 64;                          // wave tile columns
 constexpr int G_EP_BYTES = 9216;                  // per-wave epilogue staging: 64 x 136 B, 32 x 272 B or 64 x 144 B
-static_assert(GNW * G_EP_BYTES <= GS * G_STAGE, "epilogue staging fits in the ring");
+
+// Tile rows: 256 (wave tile 128 x 64, three workgroups per CU) for large M,
+// 128 (wave tile 64 x 64, four per CU) when 256-row tiles would leave CUs idle.
+template <int BM> struct GShape {
+  static constexpr int LA = BM / G_RPC / GNW;     // DMA instructions per wave per K step: A
+  static constexpr int TM = BM / 64;              // MFMA row blocks per wave
+  static constexpr int WR = BM / 2;               // wave tile rows
+  static constexpr int STAGE = (BM + GBN) * GBK * 2;
+  static constexpr int VMC0 = (GS - 1) * (LA + G_LB);
+  static constexpr int WG_PER_CU = BM == 256 ? 3 : 4;
+  static constexpr int LDS = GS * STAGE > GNW * G_EP_BYTES ? GS * STAGE : GNW * G_EP_BYTES;  // ring, then staging
+};
 constexpr uint32_t kOobOffset = 0x80000000u;      // voffset of a row past the end (reads zero)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -124,8 +131,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(int64_t)))) int64_t i64x2;
 // blocks [a0, a0 + NA) go through LDS as bf16 (OUTF32 = false; 136-byte rows)
 // or fp32 (272-byte rows), then each lane handles one row and 8 consecutive
 // columns, calling f(row_local, col_local, v[8]) with the values in fp32.
-template <bool OUTF32, int NA, typename F>
-MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][G_TM], int a0, int l32, int hi, int lane, F&& f) {
+template <bool OUTF32, int NA, int TM, typename F>
+MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][TM], int a0, int l32, int hi, int lane, F&& f) {
   constexpr int RS = OUTF32 ? G_WC * 4 + 16 : G_WC * 2 + 8;
 #pragma unroll
   for (int a = 0; a < NA; ++a)
@@ -174,9 +181,12 @@ MTFM_DEV bf16x8 pack8(const float (&v)[8]) {
   return o;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) char lds[GS * G_STAGE];
+template <int EPI, int GBM>
+__global__ __launch_bounds__(256, GShape<GBM>::WG_PER_CU) void gemm_bf16_kernel(GemmArgs g) {
+  using SH = GShape<GBM>;
+  constexpr int G_LA = SH::LA, G_TM = SH::TM, G_WR = SH::WR, G_STAGE = SH::STAGE, G_VMC0 = SH::VMC0;
+  constexpr int G_VMC = (GS - 2) * (G_LA + G_LB);
+  __shared__ __attribute__((aligned(1024))) char lds[SH::LDS];
 
   const int n_mt = (g.M + GBM - 1) / GBM, n_nt = (g.N + GBN - 1) / GBN;
   const int tiles_per_group = n_mt * n_nt;
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
     }
     if (g.pre) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < G_WR / 64; ++h)
         staged_pass<false, 2>(ep, acc, 2 * h, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
           const int m = mw + rl;
           if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.pre + map_row(cmap, m) * g.ldpre + nw + cl) = pack8(v);
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
         for (int e = 0; e < 16; ++e) acc[b][a][e] = silu_fast(acc[b][a][e]) * sc;
     if (dseg) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < G_WR / 64; ++h)
         staged_pass<false, 2>(ep, acc, 2 * h, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
           const int m = mw + rl;
           if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)dseg + map_row(cmap, m) * ldseg + (nw - c0) + cl) = pack8(v);
@@ -360,7 +370,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
       constexpr int RT = 64 * 2 + 16;
       const int64_t col0 = nw - g.vt_col0;
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
+      for (int pass = 0; pass < G_WR / 64; ++pass) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -385,7 +395,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
     }
   } else if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < G_WR / 64; ++h)
       staged_pass<false, 2>(ep, acc, 2 * h, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
         const int m = mw + rl;
         if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.out + map_row(cmap, m) * g.ldo + nw + cl) = pack8(v);
@@ -614,20 +624,30 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
         // rows map to themselves; whole 64-column wave tiles; slots up to ldvt covered by the grid
         if (g.amap.list || g.cmap.list || g.cmap.mul != 1 || g.cmap.add != 0 || g.groups != 1) return MTFM_E_UNSUPPORTED;
         if (g.vt_col0 % G_WC != 0 || g.vt_cols % G_WC != 0 || !aligned16(g.vt) || g.ldvt % 64 != 0) return MTFM_E_UNSUPPORTED;
-        if (g.ldvt < g.M || g.ldvt > (int64_t)((g.M + GBM - 1) / GBM) * GBM) return MTFM_E_UNSUPPORTED;
+        if (g.ldvt < g.M) return MTFM_E_UNSUPPORTED;
       }
     } else {
       if (!aligned16(g.out) || g.ldo % 8 != 0) return MTFM_E_UNSUPPORTED;
       if (g.epi == EPI_RESID && (!aligned16(g.resid) || g.ldr % 8 != 0)) return MTFM_E_UNSUPPORTED;
     }
-    const int64_t tiles = (int64_t)((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN) * g.groups;
+    // 256-row tiles unless they would not give every workgroup slot a tile
+    const int64_t n_nt = (g.N + GBN - 1) / GBN;
+    const int64_t tiles256 = (int64_t)((g.M + 255) / 256) * n_nt * g.groups;
+    const bool small = tiles256 < 2 * (int64_t)GShape<256>::WG_PER_CU * device_cu_count();
+    const int bm = small ? 128 : 256;
+    if (g.vt && g.ldvt > (int64_t)((g.M + bm - 1) / bm) * bm) return MTFM_E_UNSUPPORTED;
+    const int64_t tiles = (int64_t)((g.M + bm - 1) / bm) * n_nt * g.groups;
     if (tiles > 0x7fffffff) return MTFM_E_UNSUPPORTED;
     const dim3 grid((unsigned)tiles, 1, 1);
-    switch (g.epi) {
-      case EPI_SILU_SPLIT: gemm_bf16_kernel<EPI_SILU_SPLIT><<<grid, 256, 0, s>>>(g); break;
-      case EPI_RESID: gemm_bf16_kernel<EPI_RESID><<<grid, 256, 0, s>>>(g); break;
-      case EPI_STORE_F32: gemm_bf16_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(g); break;
-      default: gemm_bf16_kernel<EPI_STORE><<<grid, 256, 0, s>>>(g); break;
+    switch (g.epi * 2 + (small ? 1 : 0)) {
+      case 2 * EPI_SILU_SPLIT: gemm_bf16_kernel<EPI_SILU_SPLIT, 256><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_SILU_SPLIT + 1: gemm_bf16_kernel<EPI_SILU_SPLIT, 128><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_RESID: gemm_bf16_kernel<EPI_RESID, 256><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_RESID + 1: gemm_bf16_kernel<EPI_RESID, 128><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_STORE_F32: gemm_bf16_kernel<EPI_STORE_F32, 256><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_STORE_F32 + 1: gemm_bf16_kernel<EPI_STORE_F32, 128><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_STORE: gemm_bf16_kernel<EPI_STORE, 256><<<grid, 256, 0, s>>>(g); break;
+      default: gemm_bf16_kernel<EPI_STORE, 128><<<grid, 256, 0, s>>>(g); break;
     }
   } else {
     const int64_t total = (int64_t)g.M * g.N;
