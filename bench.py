@@ -117,7 +117,7 @@ def main():
     batch, dims = dw.batch, dw.dims
     lay = B.meta_layout(batch)
     meta = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
-    ws = B.workspace(batch, dims, B.OP_BACKBONE)
+    ws = B.workspace(batch, dims, B.OP_BACKBONE, k_target=wl.k_target)
     x = dw.x
     stream = torch.cuda.current_stream()
 

@@ -29,7 +29,7 @@ ENTRY_POINTS = [
     "mtfm_meta_bytes", "mtfm_meta_layout_of", "mtfm_mask_build", "mtfm_workspace_bytes",
     "mtfm_workspace_probe", "mtfm_attn_full", "mtfm_attn_target", "mtfm_backbone_fwd",
     "mtfm_attn_full_bwd", "mtfm_attn_target_bwd", "mtfm_timing_enable", "mtfm_timing_read",
-    "mtfm_status_str", "mtfm_last_error",
+    "mtfm_status_str", "mtfm_last_error", "mtfm_backbone_workspace_bytes",
 ]
 K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD = range(9)
 
@@ -89,6 +89,8 @@ def lib():
     L.mtfm_meta_layout_of.argtypes = [P(CBatch), P(CMetaLayout)]; L.mtfm_meta_layout_of.restype = c_int32
     L.mtfm_mask_build.argtypes = [P(CBatch), c_void_p, c_size_t, c_void_p]; L.mtfm_mask_build.restype = c_int32
     L.mtfm_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]; L.mtfm_workspace_bytes.restype = c_size_t
+    L.mtfm_backbone_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]
+    L.mtfm_backbone_workspace_bytes.restype = c_size_t
     L.mtfm_workspace_probe.argtypes = [P(CBatch), P(CDims), c_int32, P(c_int64), P(c_int64)]
     L.mtfm_workspace_probe.restype = c_int32
     L.mtfm_attn_full.argtypes = [P(CBatch), P(CDims), c_void_p, P(CFullW), c_void_p, c_void_p, c_void_p, c_size_t,
@@ -217,9 +219,17 @@ def workspace_bytes(batch: DeviceBatch, dims: CDims, op: int) -> int:
     return int(lib().mtfm_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(op)))
 
 
-def workspace(batch: DeviceBatch, dims: CDims, op: int, device="cuda"):
+def backbone_workspace_bytes(batch: DeviceBatch, dims: CDims, k_target: int) -> int:
+    return int(lib().mtfm_backbone_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(k_target)))
+
+
+def workspace(batch: DeviceBatch, dims: CDims, op: int, device="cuda", k_target: int = 0):
+    """Workspace for `op`; for the backbone, pass k_target to size the bf16
+    path that computes a block's target-layer context stage once."""
     import torch
-    return torch.empty(max(workspace_bytes(batch, dims, op), 1), dtype=torch.uint8, device=device)
+    n = backbone_workspace_bytes(batch, dims, k_target) if (op == OP_BACKBONE and k_target) else \
+        workspace_bytes(batch, dims, op)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def workspace_probe(batch: DeviceBatch, dims: CDims, op: int):

@@ -125,6 +125,39 @@ LayerWs layer_ws(const MetaPlan& p, const mtfm_dims* d, int op) {
   return w;
 }
 
+// Workspace of the backbone with the target layers' context stage hoisted
+// (bf16): the full layer's workspace, then per target layer of a block its
+// normalised rows X~ [R][d], K [R][G*dh] and V^T [G*dh][ldvt], then the T-row
+// buffers shared by the target layers.
+struct BackboneWs {
+  int64_t full = 0;
+  int64_t xt[4] = {}, k[4] = {}, vt[4] = {};
+  int64_t xtt = 0, zt = 0, a = 0, y = 0;
+  int64_t ldvt = 0, total = 0;
+};
+
+BackboneWs backbone_ws(const MetaPlan& p, const mtfm_dims* d, int k_target) {
+  const int64_t es = elem_size(d->dtype);
+  const int64_t hd = (int64_t)d->n_q_heads * d->head_dim, gd = (int64_t)d->n_kv_heads * d->head_dim;
+  const int64_t zw = 2 * hd + 2 * gd;
+  BackboneWs w;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
+  w.full = take(layer_ws(p, d, MTFM_OP_FULL).total);
+  w.ldvt = vt_ld(p.n_rows);
+  for (int l = 0; l < k_target; ++l) {
+    w.xt[l] = take(p.n_rows * d->d_model * es);
+    w.k[l] = take(p.n_rows * gd * es);
+    w.vt[l] = take(gd * w.ldvt * es);
+  }
+  w.xtt = take(p.n_t_rows * d->d_model * es);
+  w.zt = take(p.n_t_rows * zw * es);
+  w.a = take(p.n_t_rows * hd * es);
+  w.y = take(p.n_t_rows * hd * es);
+  w.total = off;
+  return w;
+}
+
 namespace {
 
 mtfm_status check_batch_device(const mtfm_batch* b, const MetaPlan& p) {
@@ -330,6 +363,109 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
 }
 
 // ---------------------------------------------------------------------------
+// Context stage of the target layers l = 0..k-1 of one block, right after its
+// full layer: one normalisation pass over all rows writes every layer's X~
+// (T rows as zeros: their K/V are never read as keys), then each layer's K
+// and V^T over all packed rows.
+mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, int k, const void* x,
+                               char* ws, const BackboneWs& L) {
+  const MetaPlan& p = c.plan;
+  const int dt = d->dtype;
+  const int64_t es = elem_size(dt);
+  const int G = d->n_kv_heads, dh = d->head_dim, D = d->d_model, gd = G * dh;
+  GlnArgs g1{};
+  g1.rows = (int32_t)p.n_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = ws + L.xt[0]; g1.ldy = D;
+  g1.gamma = w[0].ln1_g; g1.beta = w[0].ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
+  g1.n_more = k - 1; g1.zero_t = 1;
+  for (int l = 1; l < k; ++l) {
+    g1.y_more[l - 1] = ws + L.xt[l]; g1.gamma_more[l - 1] = w[l].ln1_g; g1.beta_more[l - 1] = w[l].ln1_b;
+  }
+  TRY(timed_gln(g1, dt, c.s));
+  for (int l = 0; l < k; ++l) {
+    GemmArgs gk{};
+    gk.M = (int32_t)p.n_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
+    gk.A = ws + L.xt[l]; gk.lda = D; gk.amap = identity_map();
+    gk.B[0] = w[l].w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
+    gk.cmap = identity_map();
+    gk.epi = EPI_SILU_SPLIT;
+    gk.dst[0] = ws + L.k[l]; gk.ld[0] = gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
+    gk.dst[1] = nullptr; gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd; gk.scale[1] = 1.f;
+    gk.vt = ws + L.vt[l]; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
+    TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s));
+    (void)es;
+  }
+  return MTFM_OK;
+}
+
+// T-row part of target layer l after run_target_context: normalise the T rows
+// of the current X, project them, attend over the precomputed K / V^T, gate,
+// project out and add the residual in place.
+mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, void* x, char* ws,
+                            const BackboneWs& L, int l) {
+  const MetaPlan& p = c.plan;
+  const int dt = d->dtype;
+  const int64_t es = elem_size(dt);
+  const int H = d->n_q_heads, G = d->n_kv_heads, dh = d->head_dim, D = d->d_model;
+  const int hd = H * dh, gd = G * dh, zw = 2 * hd + 2 * gd;
+  const int S = p.split;
+  char* xtt = ws + L.xtt;
+  char* zt = ws + L.zt;
+  char* a = ws + L.a;
+  char* y = ws + L.y;
+  if (p.n_t_rows == 0) return MTFM_OK;
+
+  // T row t = parent m * S + sub-token z sits at packed row parent_row[m] + z
+  GlnArgs g1{};
+  g1.rows = (int32_t)p.n_t_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = xtt; g1.ldy = D;
+  g1.xlist = c.meta.parent_row; g1.xdiv = S;
+  g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = nullptr; g1.type_const = TT_T; g1.eps = d->ln_eps;
+  TRY(timed_gln(g1, dt, c.s));
+
+  GemmArgs gt{};
+  gt.M = (int32_t)p.n_parents; gt.N = zw; gt.K = D; gt.groups = S;
+  gt.A = xtt; gt.lda = D; gt.amap = RowMap{nullptr, S, 0}; gt.amap_zadd = 1;
+  gt.B[0] = w->w_u; gt.bn[0] = hd;
+  gt.B[1] = w->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
+  gt.B[2] = w->w_kv; gt.bn[2] = 2 * gd;
+  gt.ldb = D;
+  gt.cmap = RowMap{nullptr, S, 0}; gt.cmap_zadd = 1;
+  gt.epi = EPI_SILU_SPLIT;
+  gt.dst[0] = zt; gt.ld[0] = zw; gt.cend[0] = hd; gt.scale[0] = 1.f;
+  gt.dst[1] = zt + hd * es; gt.ld[1] = zw; gt.cend[1] = 2 * hd; gt.scale[1] = q_scale(dh);
+  gt.dst[2] = zt + 2 * hd * es; gt.ld[2] = zw; gt.cend[2] = zw; gt.scale[2] = 1.f;
+  gt.cend[3] = zw;
+  TRY(timed_gemm(MTFM_K_GEMM_T, gt, dt, c.s));
+
+  AttnArgs aa{};
+  aa.q = zt + hd * es; aa.ldq = zw;
+  aa.k = ws + L.k[l]; aa.ldk = gd;
+  aa.v = nullptr; aa.ldv = 0;
+  aa.vt = ws + L.vt[l]; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows;
+  aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
+  aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
+  aa.a = a; aa.lda = hd;
+  aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
+  aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
+  aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+  TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
+
+  GlnArgs g2{};
+  g2.rows = (int32_t)p.n_t_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
+  g2.gate = zt; g2.ldg = zw;
+  g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;
+  TRY(timed_gln(g2, dt, c.s));
+
+  GemmArgs go{};
+  go.M = (int32_t)p.n_parents; go.N = D; go.K = hd; go.groups = S;
+  go.A = y; go.lda = hd; go.amap = RowMap{nullptr, S, 0}; go.amap_zadd = 1;
+  go.B[0] = w->w_o; go.bn[0] = D; go.ldb = hd;
+  go.cmap = RowMap{c.meta.parent_row, 0, 0}; go.cmap_zadd = 1;
+  go.epi = EPI_RESID; go.resid = x; go.ldr = D; go.out = x; go.ldo = D;
+  TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
+  return MTFM_OK;
+}
+
+// ---------------------------------------------------------------------------
 extern "C" {
 
 size_t mtfm_meta_bytes(const mtfm_batch* batch) {
@@ -412,11 +548,33 @@ mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, in
     TRY(check_full_w(&full[b]));
     for (int t = 0; t < k_target; ++t) TRY(check_target_w(&tgt[b * k_target + t]));
   }
+  const bool hoist = dims->dtype == MTFM_BF16 && k_target >= 1 && k_target <= 4 &&
+                     ws_bytes >= (size_t)backbone_ws(c.plan, dims, k_target).total;
+  if (hoist) {
+    const BackboneWs L = backbone_ws(c.plan, dims, k_target);
+    char* w = (char*)ws;
+    for (int b = 0; b < n_blocks; ++b) {
+      TRY(run_full(c, dims, &full[b], x_inout, x_inout, w + L.full));
+      const mtfm_target_w* tw = &tgt[b * k_target];
+      if (c.plan.n_t_rows == 0) continue;   // target layers change T rows only
+      TRY(run_target_context(c, dims, tw, k_target, x_inout, w, L));
+      for (int t = 0; t < k_target; ++t) TRY(run_target_rows(c, dims, &tw[t], x_inout, w, L, t));
+    }
+    return MTFM_OK;
+  }
   for (int b = 0; b < n_blocks; ++b) {
     TRY(run_full(c, dims, &full[b], x_inout, x_inout, (char*)ws));
     for (int t = 0; t < k_target; ++t) TRY(run_target(c, dims, &tgt[b * k_target + t], x_inout, x_inout, (char*)ws));
   }
   return MTFM_OK;
+}
+
+size_t mtfm_backbone_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t k_target) {
+  MetaPlan p;
+  if (k_target < 0 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
+  const size_t base = mtfm_workspace_bytes(batch, dims, MTFM_OP_BACKBONE);
+  if (dims->dtype != MTFM_BF16 || k_target < 1 || k_target > 4) return base;
+  return std::max(base, (size_t)backbone_ws(p, dims, k_target).total);
 }
 
 mtfm_status mtfm_attn_full_bwd(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d,

@@ -17,6 +17,15 @@ struct GlnArgs {
   const uint8_t* type;             // per row; if null, every row has type `type_const`
   int32_t type_const;
   float eps;
+  // optional: input row of output row i is xlist[i / xdiv] + i % xdiv (type from that row)
+  const int32_t* xlist; int32_t xdiv;
+  // optional: up to three more outputs of the same statistics with their own
+  // parameters (same stride ldy); rows of type T written as zeros in every
+  // output when zero_t is set (context-only normalisation)
+  int32_t n_more;
+  void* y_more[3];
+  const float* gamma_more[3]; const float* beta_more[3];
+  int32_t zero_t;
 };
 
 mtfm_status launch_gln(const GlnArgs& a, int dtype, hipStream_t s);

@@ -217,6 +217,17 @@ mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, in
                               const mtfm_target_w* tgt, void* x_inout, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Workspace for mtfm_backbone_fwd with k_target target layers per block.
+ * On the bf16 path with 1 <= k_target <= 4, the normalised context (H and R)
+ * rows and the K/V of all target layers of a block are computed right after
+ * the block's full layer, from one read of its output (a target layer never
+ * changes H or R rows); each target layer then normalises only its T rows.
+ * That needs this much workspace; with less (but at least
+ * mtfm_workspace_bytes(batch, dims, MTFM_OP_BACKBONE)) the layers run one by
+ * one.  Both orders compute the same values.  Returns 0 on invalid arguments.
+ * Host only. */
+size_t mtfm_backbone_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t k_target);
+
 /* Backward of one full-attention layer: given x_in (the layer's input) and
  * dy = dL/dX', writes dx = dL/dX ([n_rows][d_model], dims->dtype) and the
  * fp32 weight/GLN gradients into *g.  Recomputes the forward internally.

@@ -143,13 +143,14 @@ def test_layers_are_deterministic():
     np.testing.assert_array_equal(a[2], b[2])
 
 
-def _backbone_gpu(wl, x_np=None):
+def _backbone_gpu(wl, hoist=True):
+    """Run the backbone; hoist=False gives it only the layer-by-layer workspace."""
     import torch
     from hybrid_masked_attention_amd import binding as B
     from hybrid_masked_attention_amd.tensors import DeviceWorkload
     dw = DeviceWorkload(wl)
     meta = B.mask_build(dw.batch)
-    ws = B.workspace(dw.batch, dw.dims, B.OP_BACKBONE)
+    ws = B.workspace(dw.batch, dw.dims, B.OP_BACKBONE, k_target=wl.k_target if hoist else 0)
     x = dw.x.clone()
     B.backbone_fwd(dw.batch, dw.dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, x, ws)
     torch.cuda.synchronize()
@@ -188,6 +189,44 @@ def test_config3_backbone_composition_fp32():
     r = Report(TOL_F32)
     r.close("X'", got, ref)
     r.branch("dX", got, ref, x0, "f32", roundings=16)
+    r.check()
+
+
+def _small_backbone(split, seed, n_blocks=2, k_target=3):
+    rng = np.random.default_rng(seed)
+    lens = np.stack([rng.integers(40, 200, 6), rng.integers(0, 90, 6), rng.integers(0, 20, 6)], 1).astype(np.int32)
+    lens[2] = (70, 0, 5)      # no R rows
+    lens[4] = (30, 50, 0)     # no T rows
+    batch = synth.make_batch(rng, lens, split)
+    dims = synth.Dims(512, 8, 2, 64)
+    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
+    full = [synth.full_weights(rng, dims, 0.02, 0.02) for _ in range(n_blocks)]
+    tgt = [synth.target_weights(rng, dims, split, 0.02, 0.02) for _ in range(n_blocks * k_target)]
+    return synth.Workload(f"small_backbone_s{split}", batch, dims, "bf16", x, full=full, target=tgt,
+                          n_blocks=n_blocks, k_target=k_target)
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_backbone_context_stage_matches_layer_by_layer(split):
+    """The block-level context stage (one normalisation pass and the K/V of all target layers
+    right after the full layer) computes bit-identical outputs to running the layers one by one."""
+    wl = _small_backbone(split, 60 + split)
+    _, a = _backbone_gpu(wl, hoist=True)
+    _, b = _backbone_gpu(wl, hoist=False)
+    assert np.all(np.isfinite(a))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_small_v2_backbone_against_oracle():
+    """2 blocks x (1 full + 3 target), V2 sub-tokens, all users checked against the oracle."""
+    wl = _small_backbone(4, 70)
+    x0, got = _backbone_gpu(wl)
+    xr, full, tgt = rounded_inputs(wl)
+    np.testing.assert_array_equal(x0, xr)
+    ref = om.backbone(wl.batch, xr, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=om.bf16_round)
+    r = Report(TOL_BF16)
+    r.close("X'", got, ref)
+    r.branch("dX (8 roundings allowed)", got, ref, xr, "bf16", roundings=8)
     r.check()
 
 
