@@ -209,3 +209,43 @@ def target_layer_bwd(batch, x, w, dims, dy):
     """Batch gradients of sum(target_layer(x) * dy); weight gradients summed over users."""
     return _batch_bwd(batch, x, dy,
                       lambda xu, m, t, lc, dyu: target_layer_user_bwd(xu, m, t, lc, batch.split, w, dims, dyu))
+
+
+def backbone_bwd(batch, x, full_ws, tgt_ws, dims, n_blocks, k_target, dy, boundary=None):
+    """Gradients of sum(backbone(x) * dy) through the whole hybrid stack.
+
+    The stack is n_blocks x (1 full layer + k_target target layers) ([explainer]
+    §4: B blocks of 1 full + K target layers; [blog] §3.3.1).  One forward pass
+    keeps every layer's input; then the layers' backward run in reverse order,
+    the upstream gradient of layer l being the input gradient of layer l + 1
+    (chain rule through the stack).  ``boundary`` (e.g. bf16 rounding) is
+    applied to the activations between layers, as in oracle.model.backbone, and
+    to the gradients handed from one layer to the next, mirroring a run that
+    stores both in reduced precision.  Returns {"x": dL/dX, "full": [grads of
+    each full layer], "target": [grads of each target layer]} in the layers'
+    order.
+    """
+    from .model import full_layer, target_layer
+    b = boundary or (lambda a: a)
+    layers = []
+    for blk in range(n_blocks):
+        layers.append(("full", full_ws[blk]))
+        for t in range(k_target):
+            layers.append(("target", tgt_ws[blk * k_target + t]))
+    inputs = []
+    cur = b(np.asarray(x, np.float64))
+    for l, (kind, w) in enumerate(layers):
+        inputs.append(cur)
+        if l + 1 < len(layers):
+            cur = b(full_layer(batch, cur, w, dims) if kind == "full" else target_layer(batch, cur, w, dims))
+    g = np.asarray(dy, np.float64)
+    out_full, out_tgt = [], []
+    for l in reversed(range(len(layers))):
+        kind, w = layers[l]
+        fn = full_layer_bwd if kind == "full" else target_layer_bwd
+        r = fn(batch, inputs[l], w, dims, g)
+        g = r.pop("x")
+        if l > 0:
+            g = b(g)
+        (out_full if kind == "full" else out_tgt).insert(0, r)
+    return {"x": g, "full": out_full, "target": out_tgt}
