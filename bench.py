@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--train-steps", type=int, default=3,
+                    help="also time this many training gradient passes (mtfm_backbone_bwd: forward keeping the "
+                         "layer inputs, then every layer's backward); 0 skips")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (calibrates PMC byte counters)")
     args = ap.parse_args()
@@ -204,6 +207,39 @@ def main():
         breakdown["sum_ms_per_step"] = sum(v["ms_per_step"] for v in breakdown.values() if isinstance(v, dict))
         log("breakdown: " + json.dumps(breakdown))
 
+    train = None
+    if args.train_steps > 0:
+        # training gradient pass of the same batch: dL/dX and every layer's weight / GLN gradients
+        nb = B.backbone_bwd_workspace_bytes(batch, dims, wl.n_blocks, wl.k_target)
+        ws_b = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(33)
+        dy = torch.randn(x.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        dx = torch.empty_like(x)
+        fg = [{k: torch.empty(tuple(w[k].shape), dtype=torch.float32, device="cuda") for k in B.FULL_GRAD_KEYS}
+              for w in dw.full]
+        tg = [{k: torch.empty(tuple(w[k].shape), dtype=torch.float32, device="cuda") for k in B.TARGET_GRAD_KEYS}
+              for w in dw.target]
+
+        def train_step():
+            B.mask_build(batch, meta)
+            B.backbone_bwd(batch, dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, x, dy, dx, fg, tg, ws_b)
+
+        train_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.train_steps):
+            train_step()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        train = {"what": "mtfm_backbone_bwd: forward keeping 15 layer inputs + backward of all 16 layers "
+                         "(dX and every weight / GLN gradient), incl. mask build",
+                 "steps": args.train_steps, "ms_per_step": 1000.0 * el / args.train_steps,
+                 "user_samples_per_s": wl.batch.n_users * args.train_steps / el,
+                 "workspace_GiB": nb / 2 ** 30}
+        log(f"training gradient pass: {train['ms_per_step']:.2f} ms/step, {train['user_samples_per_s']:.1f} "
+            f"user-samples/s")
+        del ws_b, dy, dx, fg, tg
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
@@ -232,6 +268,7 @@ def main():
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": recorded_traffic(), "flops_per_launch": attn_full_flops, "ms_per_launch": attn_ms},
         "breakdown": breakdown,
+        "train": train,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -30,6 +30,7 @@ ENTRY_POINTS = [
     "mtfm_workspace_probe", "mtfm_attn_full", "mtfm_attn_target", "mtfm_backbone_fwd",
     "mtfm_attn_full_bwd", "mtfm_attn_target_bwd", "mtfm_timing_enable", "mtfm_timing_read",
     "mtfm_status_str", "mtfm_last_error", "mtfm_backbone_workspace_bytes",
+    "mtfm_backbone_bwd_workspace_bytes", "mtfm_backbone_bwd",
 ]
 K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD = range(9)
 
@@ -108,6 +109,12 @@ def lib():
     L.mtfm_attn_target_bwd.argtypes = [P(CBatch), P(CDims), c_void_p, P(CTargetW), c_void_p, c_void_p, c_void_p,
                                        P(CTargetGrad), c_void_p, c_size_t, c_void_p]
     L.mtfm_attn_target_bwd.restype = c_int32
+    L.mtfm_backbone_bwd_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32, c_int32]
+    L.mtfm_backbone_bwd_workspace_bytes.restype = c_size_t
+    L.mtfm_backbone_bwd.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_void_p, P(CFullW), P(CTargetW),
+                                    c_void_p, c_void_p, c_void_p, P(CFullGrad), P(CTargetGrad), c_void_p, c_size_t,
+                                    c_void_p]
+    L.mtfm_backbone_bwd.restype = c_int32
     L.mtfm_timing_enable.argtypes = [ctypes.c_uint32]; L.mtfm_timing_enable.restype = c_int32
     L.mtfm_timing_read.argtypes = [c_int32, P(c_int64), P(ctypes.c_double)]; L.mtfm_timing_read.restype = c_int32
     L.mtfm_status_str.argtypes = [c_int32]; L.mtfm_status_str.restype = c_char_p
@@ -286,6 +293,30 @@ def attn_target_bwd(batch, dims, meta, w, x_in, dy, dx, grads: Dict, ws, stream=
     _check(lib().mtfm_attn_target_bwd(ctypes.byref(batch.c), ctypes.byref(dims), _ptr(meta), ctypes.byref(cw),
                                       _ptr(x_in), _ptr(dy), _ptr(dx), ctypes.byref(cg), _ptr(ws), ws.numel(),
                                       _stream(stream)), "mtfm_attn_target_bwd")
+    return dx
+
+
+FULL_GRAD_KEYS = ("ln1_g", "ln1_b", "w_uqkv", "ln2_g", "ln2_b", "w_o")
+TARGET_GRAD_KEYS = ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o")
+
+
+def backbone_bwd_workspace_bytes(batch: DeviceBatch, dims: CDims, n_blocks: int, k_target: int) -> int:
+    return int(lib().mtfm_backbone_bwd_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks),
+                                                       int(k_target)))
+
+
+def backbone_bwd(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], tgt: Sequence[Dict], x_in, dy, dx,
+                 full_grads: Sequence[Dict], tgt_grads: Sequence[Dict], ws, stream=None):
+    """dL/dX_in into dx and every layer's gradients (dicts of fp32 tensors shaped like the weights)."""
+    fa = (CFullW * max(1, len(full)))(*[full_w(w) for w in full])
+    ta = (CTargetW * max(1, len(tgt)))(*[target_w(w) for w in tgt])
+    fg = (CFullGrad * max(1, len(full_grads)))(*[CFullGrad(*[_ptr(g[n]) for n in FULL_GRAD_KEYS])
+                                                 for g in full_grads])
+    tg = (CTargetGrad * max(1, len(tgt_grads)))(*[CTargetGrad(*[_ptr(g[n]) for n in TARGET_GRAD_KEYS])
+                                                  for g in tgt_grads])
+    _check(lib().mtfm_backbone_bwd(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks), int(k_target),
+                                   _ptr(meta), fa, ta, _ptr(x_in), _ptr(dy), _ptr(dx), fg, tg, _ptr(ws), ws.numel(),
+                                   _stream(stream)), "mtfm_backbone_bwd")
     return dx
 
 

@@ -600,6 +600,102 @@ mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims,
   return run_target_bwd(c, dims, w, x_in, dy, dx, g, (char*)ws);
 }
 
+// ---------------------------------------------------------------------------
+// Backward through the whole stack: one forward pass keeps every layer's input
+// (bf16, as the forward hands it on), then the layers' backward run from the
+// last to the first, each taking the next layer's input gradient as its
+// upstream gradient.  Workspace: the largest single-layer workspace, the
+// inputs of layers 1 .. L-1, and one gradient buffer (the caller's dx is the
+// other one of the pair).
+namespace {
+
+struct BackboneBwdWs {
+  int64_t layer = 0, stash = 0, xbytes = 0, gbuf = 0, total = 0;
+};
+
+BackboneBwdWs backbone_bwd_ws(const MetaPlan& p, const mtfm_dims* d, int n_layers) {
+  BackboneBwdWs w;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
+  const int64_t lw = std::max(std::max(layer_ws(p, d, MTFM_OP_FULL).total, layer_ws(p, d, MTFM_OP_TARGET).total),
+                              std::max(bwd_ws_bytes(p, d, MTFM_OP_FULL_BWD), bwd_ws_bytes(p, d, MTFM_OP_TARGET_BWD)));
+  w.layer = take(lw);
+  w.xbytes = align_up(p.n_rows * d->d_model * elem_size(d->dtype), 256);
+  w.stash = take(std::max(n_layers - 1, 0) * w.xbytes);
+  w.gbuf = take(w.xbytes);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t mtfm_backbone_bwd_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks,
+                                         int32_t k_target) {
+  MetaPlan p;
+  if (n_blocks < 0 || k_target < 0 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
+  if (bwd_ws_bytes(p, dims, MTFM_OP_FULL_BWD) == 0) return 0;   // shapes the backward does not support
+  return (size_t)backbone_bwd_ws(p, dims, n_blocks * (1 + k_target)).total;
+}
+
+mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                              const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                              const void* x_in, const void* dy, void* dx, const mtfm_full_grad* full_g,
+                              const mtfm_target_grad* tgt_g, void* ws, size_t ws_bytes, void* stream) {
+  if (n_blocks < 0 || k_target < 0) return MTFM_E_DIMS;
+  Ctx c;
+  TRY(plan_meta(batch, &c.plan));
+  TRY(check_dims(dims));
+  if (!meta_d || !x_in || !dy || !dx) return MTFM_E_NULL;
+  if (dx == x_in || dx == dy) return MTFM_E_DIMS;
+  TRY(check_batch_device(batch, c.plan));
+  if (bwd_ws_bytes(c.plan, dims, MTFM_OP_FULL_BWD) == 0) return MTFM_E_UNSUPPORTED;
+  if (n_blocks > 0 && (!full || !full_g)) return MTFM_E_NULL;
+  if (n_blocks > 0 && k_target > 0 && (!tgt || !tgt_g)) return MTFM_E_NULL;
+  for (int b = 0; b < n_blocks; ++b) {
+    TRY(check_full_w(&full[b]));
+    const mtfm_full_grad& g = full_g[b];
+    if (!g.ln1_g || !g.ln1_b || !g.w_uqkv || !g.ln2_g || !g.ln2_b || !g.w_o) return MTFM_E_NULL;
+    for (int t = 0; t < k_target; ++t) {
+      TRY(check_target_w(&tgt[b * k_target + t]));
+      const mtfm_target_grad& h = tgt_g[b * k_target + t];
+      if (!h.ln1_g || !h.ln1_b || !h.w_u || !h.w_q || !h.w_kv || !h.ln2_g || !h.ln2_b || !h.w_o) return MTFM_E_NULL;
+    }
+  }
+  const int L = n_blocks * (1 + k_target);
+  const BackboneBwdWs W = backbone_bwd_ws(c.plan, dims, L);
+  if (W.total > 0 && !ws) return MTFM_E_NULL;
+  if (ws_bytes < (size_t)W.total) return MTFM_E_WORKSPACE;
+  c.b = batch;
+  c.meta = meta_ptrs(c.plan, meta_d);
+  c.s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const size_t xb = (size_t)c.plan.n_rows * dims->d_model * elem_size(dims->dtype);
+  if (L == 0) {   // the empty stack is the identity
+    if (xb == 0) return MTFM_OK;
+    const hipError_t e = hipMemcpyAsync(dx, dy, xb, hipMemcpyDeviceToDevice, c.s);
+    return e == hipSuccess ? MTFM_OK : hip_fail(e, "hipMemcpyAsync");
+  }
+  const int per = 1 + k_target;
+  auto input_of = [&](int l) -> const void* { return l == 0 ? x_in : (const void*)(w + W.stash + (l - 1) * W.xbytes); };
+  // gradient buffers alternate so that layer 0 writes dx
+  auto grad_buf = [&](int l) -> void* { return (l % 2 == 0) ? dx : (void*)(w + W.gbuf); };
+  for (int l = 0; l + 1 < L; ++l) {
+    void* out = w + W.stash + l * W.xbytes;
+    const int b = l / per, t = l % per;
+    if (t == 0) TRY(run_full(c, dims, &full[b], input_of(l), out, w + W.layer));
+    else TRY(run_target(c, dims, &tgt[b * k_target + t - 1], input_of(l), out, w + W.layer));
+  }
+  for (int l = L - 1; l >= 0; --l) {
+    const void* g_in = l == L - 1 ? dy : grad_buf(l + 1);
+    void* g_out = grad_buf(l);
+    const int b = l / per, t = l % per;
+    if (t == 0) TRY(run_full_bwd(c, dims, &full[b], input_of(l), g_in, g_out, &full_g[b], w + W.layer));
+    else TRY(run_target_bwd(c, dims, &tgt[b * k_target + t - 1], input_of(l), g_in, g_out,
+                            &tgt_g[b * k_target + t - 1], w + W.layer));
+  }
+  return MTFM_OK;
+}
+
 const char* mtfm_status_str(int32_t status) {
   switch (status) {
     case MTFM_OK: return "MTFM_OK";

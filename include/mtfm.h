@@ -241,6 +241,27 @@ mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims,
                                  const mtfm_target_w* w, const void* x_in, const void* dy, void* dx,
                                  const mtfm_target_grad* g, void* ws, size_t ws_bytes, void* stream);
 
+/* Backward of the whole backbone (the training step's gradient pass): the
+ * stack of mtfm_backbone_fwd, n_blocks x (1 full + k_target target layers)
+ * ([explainer] §4; [blog] §3.3.1), differentiated layer by layer with the
+ * chain rule.  Given x_in (the backbone's input) and dy = dL/dX_out, writes
+ * dx = dL/dX_in and every layer's fp32 weight/GLN gradients (overwritten):
+ * full_g[b] for the full layer of block b, tgt_g[b * k_target + t] for its
+ * target layer t.  One forward pass keeps the inputs of layers 1 .. L-1 in
+ * the workspace (bf16, as the forward passes them on); then each layer's
+ * backward runs from the last to the first, the gradient handed between
+ * layers stored in dims->dtype.  dx also serves as one of the two
+ * intermediate gradient buffers, so it must not alias x_in or dy.
+ * bf16 only (MTFM_E_UNSUPPORTED otherwise).  ws: at least
+ * mtfm_backbone_bwd_workspace_bytes(batch, dims, n_blocks, k_target) bytes.
+ * Stream-ordered, no host synchronisation. */
+size_t mtfm_backbone_bwd_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks,
+                                         int32_t k_target);
+mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                              const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                              const void* x_in, const void* dy, void* dx, const mtfm_full_grad* full_g,
+                              const mtfm_target_grad* tgt_g, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel timing (measurement aid).  While a kernel class is enabled, each of
  * its launches is bracketed by two HIP events recorded on the stream the

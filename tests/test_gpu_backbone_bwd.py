@@ -1,0 +1,202 @@
+"""GPU parity of the whole-backbone backward (the training step's gradient pass).
+
+mtfm_backbone_bwd keeps every layer's input from one forward pass and runs
+the layers' backward from the last to the first.  The device stores those
+activations and the gradient handed from layer to layer in bf16; the oracle
+(float64, same bf16-rounded inputs) mirrors both roundings at the layer
+boundaries.  Every gradient tensor -- dX and each layer's weights and GLN
+parameters -- must satisfy max|gpu - ref| <= 1e-2 * max|ref|.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import grad as og
+from oracle import model as om
+from tests._parity import TOL_BF16, Report, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+SMALL_LENS = [[130, 64, 17], [1, 0, 1], [63, 1, 0], [0, 0, 3], [65, 63, 33], [5, 70, 2], [0, 0, 0], [90, 30, 9]]
+
+
+def _workload(split, seed, n_blocks, k_target, lens, name):
+    rng = np.random.default_rng(seed)
+    batch = synth.make_batch(rng, np.asarray(lens, np.int32), split)
+    dims = synth.Dims(512, 8, 2, 64)
+    x = rng.standard_normal((batch.total_rows, 512)).astype(np.float32)
+    full = [synth.full_weights(rng, dims, 0.05, 0.05) for _ in range(n_blocks)]
+    tgt = [synth.target_weights(rng, dims, split, 0.05, 0.05) for _ in range(n_blocks * k_target)]
+    dy = rng.standard_normal((batch.total_rows, 512)).astype(np.float32)
+    return synth.Workload(name, batch, dims, "bf16", x, full=full, target=tgt, n_blocks=n_blocks,
+                          k_target=k_target, dy=dy)
+
+
+def _grad_like(w, keys):
+    import torch
+    return {k: torch.full(tuple(w[k].shape), float("nan"), dtype=torch.float32, device="cuda") for k in keys}
+
+
+def _device(wl):
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload, to_device
+    dw = DeviceWorkload(wl)
+    meta = B.mask_build(dw.batch)
+    n = B.backbone_bwd_workspace_bytes(dw.batch, dw.dims, wl.n_blocks, wl.k_target)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dy = to_device(wl.dy, "bf16")
+    dx = torch.empty_like(dw.x)
+    fg = [_grad_like(w, B.FULL_GRAD_KEYS) for w in dw.full]
+    tg = [_grad_like(w, B.TARGET_GRAD_KEYS) for w in dw.target]
+    B.backbone_bwd(dw.batch, dw.dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, dw.x, dy, dx, fg, tg, ws)
+    torch.cuda.synchronize()
+    npg = lambda gs: [{k: v.cpu().numpy().astype(np.float64) for k, v in g.items()} for g in gs]
+    return to_np(dx), npg(fg), npg(tg), to_np(dy), to_np(dw.x)
+
+
+def _rounded_weights(ws):
+    r = om.bf16_round
+    return [{k: (v.astype(np.float64) if k.startswith("ln") else r(v)) for k, v in w.items()} for w in ws]
+
+
+def _chained_layer_calls(wl):
+    """Per-layer forward and backward entry points called by hand: every layer's input
+    (as the device computes it) and every gradient handed between layers."""
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload, to_device
+    dw = DeviceWorkload(wl)
+    meta = B.mask_build(dw.batch)
+    ws_f = B.workspace(dw.batch, dw.dims, B.OP_FULL)
+    ws_t = B.workspace(dw.batch, dw.dims, B.OP_TARGET)
+    ws_fb = B.workspace(dw.batch, dw.dims, B.OP_FULL_BWD)
+    ws_tb = B.workspace(dw.batch, dw.dims, B.OP_TARGET_BWD)
+    per = 1 + wl.k_target
+    n_layers = wl.n_blocks * per
+    layer = lambda l: ("full", dw.full[l // per]) if l % per == 0 else \
+        ("target", dw.target[(l // per) * wl.k_target + l % per - 1])
+    xs = [dw.x]
+    for l in range(n_layers - 1):
+        kind, w = layer(l)
+        out = torch.empty_like(dw.x)
+        if kind == "full":
+            B.attn_full(dw.batch, dw.dims, meta, w, xs[-1], out, ws_f)
+        else:
+            B.attn_target(dw.batch, dw.dims, meta, w, xs[-1], out, ws_t)
+        xs.append(out)
+    gs = [None] * (n_layers + 1)
+    gs[n_layers] = to_device(wl.dy, "bf16")
+    grads = [None] * n_layers
+    for l in reversed(range(n_layers)):
+        kind, w = layer(l)
+        d = torch.empty_like(dw.x)
+        if kind == "full":
+            gr = _grad_like(w, B.FULL_GRAD_KEYS)
+            B.attn_full_bwd(dw.batch, dw.dims, meta, w, xs[l], gs[l + 1], d, gr, ws_fb)
+        else:
+            gr = _grad_like(w, B.TARGET_GRAD_KEYS)
+            B.attn_target_bwd(dw.batch, dw.dims, meta, w, xs[l], gs[l + 1], d, gr, ws_tb)
+        grads[l] = gr
+        gs[l] = d
+    torch.cuda.synchronize()
+    npg = lambda g: {k: v.cpu().numpy().astype(np.float64) for k, v in g.items()}
+    return [to_np(x) for x in xs], [to_np(g) for g in gs], [npg(g) for g in grads]
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_backbone_backward_layer_by_layer(split):
+    """2 blocks x (1 full + 2 target layers) over ragged users (empty R, empty T, empty users).
+
+    mtfm_backbone_bwd gives bit for bit the gradients of the per-layer entry points chained by
+    hand, and each layer of that chain, given the device's own layer input and upstream gradient,
+    matches the oracle's layer backward at the activation bar."""
+    wl = _workload(split, 80 + split, 2, 2, SMALL_LENS, f"bb_bwd_small_s{split}")
+    say(f"backbone backward: {wl.name} rows={wl.batch.total_rows} layers={wl.n_blocks * 3}")
+    dx, fg, tg, _, _ = _device(wl)
+    xs, gs, grads = _chained_layer_calls(wl)
+    np.testing.assert_array_equal(dx, gs[0])
+    per = 1 + wl.k_target
+    for l, g in enumerate(grads):
+        mine = fg[l // per] if l % per == 0 else tg[(l // per) * wl.k_target + l % per - 1]
+        for k in g:
+            np.testing.assert_array_equal(mine[k], g[k])
+    fw, tw = _rounded_weights(wl.full), _rounded_weights(wl.target)
+    r = Report(TOL_BF16)
+    for l in range(len(grads)):
+        if l % per == 0:
+            name, ref = f"full[{l // per}]", og.full_layer_bwd(wl.batch, xs[l], fw[l // per], wl.dims, gs[l + 1])
+        else:
+            t = (l // per) * wl.k_target + l % per - 1
+            name, ref = f"target[{t}]", og.target_layer_bwd(wl.batch, xs[l], tw[t], wl.dims, gs[l + 1])
+        r.close(f"layer {l} {name} dX", gs[l], ref["x"])
+        for k in grads[l]:
+            r.close(f"layer {l} {name} d{k}", grads[l][k], ref[k])
+    r.check()
+
+
+# End-to-end bar: to first order, the error of a layer's gradients is its own backward's error
+# (within TOL_BF16 given the same inputs: the layer-by-layer test) plus the effect of its inputs
+# (activations from the forward chain, within the activation bar TOL_BF16) differing from the
+# oracle's; hence two bars.
+TOL_CHAIN = 2 * TOL_BF16
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_backbone_backward_end_to_end(split):
+    """The same stack with the benchmark's weight scale (0.02, output projections 0.02 / sqrt(layers))
+    against the oracle's backward of the whole stack, both roundings at the layer boundaries mirrored
+    (bar TOL_CHAIN)."""
+    rng = np.random.default_rng(100 + split)
+    batch = synth.make_batch(rng, np.asarray(SMALL_LENS, np.int32), split)
+    dims = synth.Dims(512, 8, 2, 64)
+    x = rng.standard_normal((batch.total_rows, 512)).astype(np.float32)
+    wo = 0.02 / np.sqrt(6)
+    full = [synth.full_weights(rng, dims, 0.02, wo) for _ in range(2)]
+    tgt = [synth.target_weights(rng, dims, split, 0.02, wo) for _ in range(4)]
+    dy = rng.standard_normal((batch.total_rows, 512)).astype(np.float32)
+    wl = synth.Workload(f"bb_bwd_e2e_s{split}", batch, dims, "bf16", x, full=full, target=tgt, n_blocks=2,
+                        k_target=2, dy=dy)
+    dx, fg, tg, dy_dev, x_dev = _device(wl)
+    xr = om.bf16_round(wl.x)
+    np.testing.assert_array_equal(x_dev, xr)
+    ref = og.backbone_bwd(wl.batch, xr, _rounded_weights(wl.full), _rounded_weights(wl.target), wl.dims,
+                          wl.n_blocks, wl.k_target, dy_dev, boundary=om.bf16_round)
+    r = Report(TOL_CHAIN)
+    r.close("dX", dx, ref["x"])
+    for b, g in enumerate(fg):
+        for k in g:
+            r.close(f"full[{b}].d{k}", g[k], ref["full"][b][k])
+    for t, g in enumerate(tg):
+        for k in g:
+            r.close(f"target[{t}].d{k}", g[k], ref["target"][t][k])
+    r.check()
+
+
+def test_config3_training_backward_sampled_user():
+    """The 160-user, 16-layer batch (the timed training step): dX of one user against the oracle
+    (users are independent), every gradient finite, two runs bit-identical."""
+    wl3 = synth.config3()
+    rng = np.random.default_rng(33)
+    dy = rng.standard_normal((wl3.batch.total_rows, wl3.dims.d_model)).astype(np.float32)
+    wl = synth.Workload("cfg3_train", wl3.batch, wl3.dims, "bf16", wl3.x, full=wl3.full, target=wl3.target,
+                        n_blocks=wl3.n_blocks, k_target=wl3.k_target, dy=dy)
+    say(f"backbone backward: {wl.batch.n_users} users, {wl.batch.total_rows} rows, 16 layers")
+    dx1, fg1, tg1, dy_dev, x_dev = _device(wl)
+    for g in fg1 + tg1:
+        for k, v in g.items():
+            assert np.all(np.isfinite(v)), k
+    u = int(np.argmin(wl.batch.user_rows))   # the shortest user keeps the float64 oracle to seconds
+    rows = wl.batch.rows_of([u])
+    ref = og.backbone_bwd(wl.batch.subset([u]), x_dev[rows], _rounded_weights(wl.full),
+                          _rounded_weights(wl.target), wl.dims, wl.n_blocks, wl.k_target, dy_dev[rows],
+                          boundary=om.bf16_round)
+    r = Report(TOL_CHAIN)
+    r.close(f"dX user {u}", dx1[rows], ref["x"])
+    r.check()
+    dx2, fg2, tg2, _, _ = _device(wl)
+    np.testing.assert_array_equal(dx1, dx2)
+    for a, b in zip(fg1 + tg1, fg2 + tg2):
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k])
