@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--serve-steps", type=int, default=10,
+                    help="also time request-level serving: one context pass filling the K/V cache, then this many "
+                         "candidate passes over the cached context (0 skips)")
     ap.add_argument("--train-steps", type=int, default=3,
                     help="also time this many training gradient passes (mtfm_backbone_bwd: forward keeping the "
                          "layer inputs, then every layer's backward); 0 skips")
@@ -240,6 +243,61 @@ def main():
             f"user-samples/s")
         del ws_b, dy, dx, fg, tg
 
+    serve = None
+    if args.serve_steps > 0:
+        # the same users' context once into the K/V cache, then the batch's candidates (T rows) against it
+        lens_c = wl.batch.lens.copy()
+        lens_c[:, 2] = 0
+        cb = B.DeviceBatch(lens_c, wl.batch.split, wl.batch.ts_r, np.zeros(0, np.int32))
+        meta_c = B.mask_build(cb)
+        off = wl.batch.row_off
+        ctx_idx, t_idx = [], []
+        for u in range(wl.batch.n_users):
+            lh, lr, lt = (int(v) for v in wl.batch.lens[u])
+            ctx_idx.append(np.arange(off[u], off[u] + lh + lr))
+            t_idx.append(np.arange(off[u] + lh + lr, off[u + 1]))
+        ctx_idx = torch.as_tensor(np.concatenate(ctx_idx), device="cuda")
+        t_idx = torch.as_tensor(np.concatenate(t_idx), device="cuda")
+        cache = torch.empty(B.kv_cache_bytes(cb, dims, wl.n_blocks, wl.k_target), dtype=torch.uint8, device="cuda")
+        ws_c = torch.empty(B.serve_workspace_bytes(cb, dims, wl.k_target, B.SERVE_CONTEXT), dtype=torch.uint8,
+                           device="cuda")
+        ws_t = torch.empty(B.serve_workspace_bytes(batch, dims, wl.k_target, B.SERVE_TARGETS), dtype=torch.uint8,
+                           device="cuda")
+        x_c0, x_t0 = dw.x[ctx_idx].contiguous(), dw.x[t_idx].contiguous()
+        x_c, x_t = x_c0.clone(), x_t0.clone()
+
+        def ctx_pass():
+            x_c.copy_(x_c0)
+            B.mask_build(cb, meta_c)
+            B.serve_context(cb, dims, wl.n_blocks, wl.k_target, meta_c, dw.full, dw.target, x_c, cache, ws_c)
+
+        def cand_pass():
+            x_t.copy_(x_t0)
+            B.mask_build(batch, meta)
+            B.serve_targets(batch, dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, cache, x_t, ws_t)
+
+        ctx_pass()
+        cand_pass()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ctx_pass()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.serve_steps):
+            cand_pass()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        cand_ms = 1000.0 * (t2 - t1) / args.serve_steps
+        serve = {"what": "context pass (160 users' H/R rows through 16 layers, every layer's K/V^T cached) once; "
+                         "candidate pass (the batch's T rows through 16 layers against the cache) timed",
+                 "context_ms": 1000.0 * (t1 - t0), "candidate_pass_ms": cand_ms,
+                 "candidates_per_s": float(wl.batch.lens[:, 2].sum()) / (cand_ms * 1e-3),
+                 "t_rows": int(T), "kv_cache_GiB": cache.numel() / 2 ** 30,
+                 "vs_full_forward": ms_step / cand_ms}
+        log(f"serving: context {serve['context_ms']:.2f} ms once, candidates {cand_ms:.3f} ms/pass "
+            f"({serve['candidates_per_s']:.0f} candidates/s, {serve['vs_full_forward']:.1f}x the full forward)")
+        del cache, ws_c, ws_t, x_c, x_t, x_c0, x_t0
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
@@ -269,6 +327,7 @@ def main():
                      "traffic": recorded_traffic(), "flops_per_launch": attn_full_flops, "ms_per_launch": attn_ms},
         "breakdown": breakdown,
         "train": train,
+        "serve": serve,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -30,8 +30,10 @@ ENTRY_POINTS = [
     "mtfm_workspace_probe", "mtfm_attn_full", "mtfm_attn_target", "mtfm_backbone_fwd",
     "mtfm_attn_full_bwd", "mtfm_attn_target_bwd", "mtfm_timing_enable", "mtfm_timing_read",
     "mtfm_status_str", "mtfm_last_error", "mtfm_backbone_workspace_bytes",
-    "mtfm_backbone_bwd_workspace_bytes", "mtfm_backbone_bwd",
+    "mtfm_backbone_bwd_workspace_bytes", "mtfm_backbone_bwd", "mtfm_kv_cache_bytes", "mtfm_serve_workspace_bytes",
+    "mtfm_serve_context", "mtfm_serve_targets",
 ]
+SERVE_CONTEXT, SERVE_TARGETS = 0, 1
 K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD = range(9)
 
 
@@ -115,6 +117,15 @@ def lib():
                                     c_void_p, c_void_p, c_void_p, P(CFullGrad), P(CTargetGrad), c_void_p, c_size_t,
                                     c_void_p]
     L.mtfm_backbone_bwd.restype = c_int32
+    L.mtfm_kv_cache_bytes.argtypes = [P(CBatch), P(CDims), c_int32, c_int32]; L.mtfm_kv_cache_bytes.restype = c_size_t
+    L.mtfm_serve_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32, c_int32]
+    L.mtfm_serve_workspace_bytes.restype = c_size_t
+    L.mtfm_serve_context.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_void_p, P(CFullW), P(CTargetW),
+                                     c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
+    L.mtfm_serve_context.restype = c_int32
+    L.mtfm_serve_targets.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_void_p, P(CFullW), P(CTargetW),
+                                     c_void_p, c_size_t, c_void_p, c_void_p, c_size_t, c_void_p]
+    L.mtfm_serve_targets.restype = c_int32
     L.mtfm_timing_enable.argtypes = [ctypes.c_uint32]; L.mtfm_timing_enable.restype = c_int32
     L.mtfm_timing_read.argtypes = [c_int32, P(c_int64), P(ctypes.c_double)]; L.mtfm_timing_read.restype = c_int32
     L.mtfm_status_str.argtypes = [c_int32]; L.mtfm_status_str.restype = c_char_p
@@ -318,6 +329,37 @@ def backbone_bwd(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], tg
                                    _ptr(meta), fa, ta, _ptr(x_in), _ptr(dy), _ptr(dx), fg, tg, _ptr(ws), ws.numel(),
                                    _stream(stream)), "mtfm_backbone_bwd")
     return dx
+
+
+def kv_cache_bytes(batch: DeviceBatch, dims: CDims, n_blocks: int, k_target: int) -> int:
+    return int(lib().mtfm_kv_cache_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks), int(k_target)))
+
+
+def serve_workspace_bytes(batch: DeviceBatch, dims: CDims, k_target: int, phase: int) -> int:
+    return int(lib().mtfm_serve_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(k_target),
+                                                int(phase)))
+
+
+def serve_context(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], tgt: Sequence[Dict], x_inout,
+                  kv_cache, ws, stream=None):
+    """Context rows through the stack (in place) and every layer's K / V^T of them into kv_cache."""
+    fa = (CFullW * max(1, len(full)))(*[full_w(w) for w in full])
+    ta = (CTargetW * max(1, len(tgt)))(*[target_w(w) for w in tgt])
+    _check(lib().mtfm_serve_context(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks), int(k_target),
+                                    _ptr(meta), fa, ta, _ptr(x_inout), _ptr(kv_cache), kv_cache.numel(), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "mtfm_serve_context")
+    return x_inout
+
+
+def serve_targets(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], tgt: Sequence[Dict], kv_cache,
+                  x_t, ws, stream=None):
+    """T rows ([split * sum L_T][d], T-row order) through the stack (in place) against the cached context."""
+    fa = (CFullW * max(1, len(full)))(*[full_w(w) for w in full])
+    ta = (CTargetW * max(1, len(tgt)))(*[target_w(w) for w in tgt])
+    _check(lib().mtfm_serve_targets(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks), int(k_target),
+                                    _ptr(meta), fa, ta, _ptr(kv_cache), kv_cache.numel(), _ptr(x_t), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "mtfm_serve_targets")
+    return x_t
 
 
 def timing_enable(classes: Sequence[int]):

@@ -211,7 +211,7 @@ static int full_attn_half_tiles() {
 //   X~ = GLN1(X); [U|Q|K|V] = SiLU(X~ W^T); A = masked SiLU attention / n;
 //   X' = (GLN2(A) (.) U) W_o^T + X
 mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out,
-                     char* ws) {
+                     char* ws, const KvOut* kv) {
   const MetaPlan& p = c.plan;
   const int dt = d->dtype;
   const int64_t es = elem_size(dt);
@@ -240,6 +240,13 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   gp.dst[2] = z + 2 * hd * es; gp.ld[2] = zw; gp.cend[2] = zw; gp.scale[2] = 1.f;
   gp.cend[3] = zw;
   if (dt == MTFM_BF16) { gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd; }
+  if (kv) {
+    // K straight into the cache ([rows][gd]), V only transposed (bf16 path; no T rows, so
+    // no query reads its own row-major K/V)
+    gp.dst[2] = kv->k; gp.ld[2] = gd; gp.cend[2] = 2 * hd + gd;
+    gp.dst[3] = nullptr; gp.ld[3] = gd; gp.cend[3] = zw; gp.scale[3] = 1.f;
+    gp.vt = kv->vt; gp.ldvt = kv->ldvt;
+  }
   TRY(timed_gemm(MTFM_K_GEMM_UQKV, gp, dt, c.s));
 
   AttnArgs aa{};
@@ -248,6 +255,11 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   aa.v = z + (2 * hd + gd) * es; aa.ldv = zw;
   aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows;
   aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
+  if (kv) {
+    aa.k = kv->k; aa.ldk = gd; aa.v = nullptr; aa.ldv = 0;
+    aa.vt = kv->vt; aa.ldvt = kv->ldvt;
+    aa.kd = kv->k; aa.ldkd = gd; aa.vd = kv->k; aa.ldvd = gd;
+  }
   aa.a = a; aa.lda = hd;
   aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles; aa.half_tiles = full_attn_half_tiles();
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
@@ -368,7 +380,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
 // (T rows as zeros: their K/V are never read as keys), then each layer's K
 // and V^T over all packed rows.
 mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, int k, const void* x,
-                               char* ws, const BackboneWs& L) {
+                               char* ws, const BackboneWs& L, const KvOut* kv = nullptr) {
   const MetaPlan& p = c.plan;
   const int dt = d->dtype;
   const int64_t es = elem_size(dt);
@@ -388,9 +400,9 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
     gk.B[0] = w[l].w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
     gk.cmap = identity_map();
     gk.epi = EPI_SILU_SPLIT;
-    gk.dst[0] = ws + L.k[l]; gk.ld[0] = gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
+    gk.dst[0] = kv ? kv[l].k : ws + L.k[l]; gk.ld[0] = gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
     gk.dst[1] = nullptr; gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd; gk.scale[1] = 1.f;
-    gk.vt = ws + L.vt[l]; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
+    gk.vt = kv ? kv[l].vt : ws + L.vt[l]; gk.ldvt = kv ? kv[l].ldvt : L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
     TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s));
     (void)es;
   }
@@ -466,6 +478,164 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
 }
 
 // ---------------------------------------------------------------------------
+
+// ---------------------------------------------------------------------------
+// Request-level serving with user-side K/V reuse ([explainer] §5.2.3: K/V
+// cache sharing across serving micro-batches; [blog] §3.4 and §4: one
+// user-level sample shares the long-sequence attention among all of its
+// targets).  H and R rows never attend to T rows, so their values through the
+// whole stack, and every layer's K and V of them, do not depend on the
+// candidates: one context pass per user fills a cache of each layer's K and
+// V^T of the context rows; each candidate batch then runs only its T rows
+// through the 16 layers against that cache.
+namespace {
+
+struct KvCacheLayout {
+  int64_t ldvt = 0, k = 0, per_layer = 0, total = 0;
+};
+
+// Per layer: K [ctx rows][G*dh], then V^T [G*dh][ldvt] (bf16), 256-B aligned.
+KvCacheLayout kv_cache_layout(const MetaPlan& p, const mtfm_dims* d, int n_layers) {
+  const int64_t gd = (int64_t)d->n_kv_heads * d->head_dim;
+  KvCacheLayout c;
+  c.ldvt = vt_ld(p.n_ctx_rows);
+  c.k = align_up(p.n_ctx_rows * gd * 2, 256);
+  c.per_layer = c.k + align_up(gd * c.ldvt * 2, 256);
+  c.total = c.per_layer * n_layers;
+  return c;
+}
+
+KvOut kv_of(const KvCacheLayout& c, char* cache, int layer) {
+  KvOut o;
+  o.k = cache + layer * c.per_layer;
+  o.vt = cache + layer * c.per_layer + c.k;
+  o.ldvt = c.ldvt;
+  return o;
+}
+
+// Tile descriptors whose key base [7] is the user's first context row in the
+// cache (context rows of all users back to back) instead of its packed row.
+__global__ void rebase_tiles_kernel(const int32_t* in, int n, const int32_t* ctx_off, int32_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n * 8) return;
+  const int t = i >> 3, f = i & 7;
+  out[i] = f == TD_UROW0 ? ctx_off[in[8 * t + TD_USER]] : in[i];
+}
+
+struct ServeWs {
+  int64_t tiles = 0, xtt = 0, zt = 0, a = 0, y = 0, total = 0;
+};
+
+ServeWs serve_ws(const MetaPlan& p, const mtfm_dims* d) {
+  const int64_t hd = (int64_t)d->n_q_heads * d->head_dim, gd = (int64_t)d->n_kv_heads * d->head_dim;
+  const int64_t zw = 2 * hd + 2 * gd, T = p.n_t_rows;
+  ServeWs w;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
+  w.tiles = take(p.n_target_tiles * 8 * 4);
+  w.xtt = take(T * d->d_model * 2);
+  w.zt = take(T * zw * 2);
+  w.a = take(T * hd * 2);
+  w.y = take(T * hd * 2);
+  w.total = off;
+  return w;
+}
+
+// One layer over the T rows (T-row order: sub-token z of parent m at m * S + z)
+// against that layer's cached context K / V^T.  fw (a full layer: one U|Q|K|V
+// projection for every sub-token) or tw (a target layer: per-sub-token Q).
+mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, const mtfm_target_w* tw,
+                       const KvOut& kv, const int32_t* tiles, void* x, char* ws, const ServeWs& L) {
+  const MetaPlan& p = c.plan;
+  const int dt = MTFM_BF16;
+  const int64_t es = 2;
+  const int H = d->n_q_heads, G = d->n_kv_heads, dh = d->head_dim, D = d->d_model;
+  const int hd = H * dh, gd = G * dh, zw = 2 * hd + 2 * gd;
+  const int S = p.split;
+  char* xtt = ws + L.xtt;
+  char* zt = ws + L.zt;
+  char* a = ws + L.a;
+  char* y = ws + L.y;
+
+  GlnArgs g1{};
+  g1.rows = (int32_t)p.n_t_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = xtt; g1.ldy = D;
+  g1.gamma = fw ? fw->ln1_g : tw->ln1_g; g1.beta = fw ? fw->ln1_b : tw->ln1_b;
+  g1.type = nullptr; g1.type_const = TT_T; g1.eps = d->ln_eps;
+  TRY(timed_gln(g1, dt, c.s));
+
+  GemmArgs gt{};
+  gt.K = D; gt.A = xtt; gt.lda = D; gt.ldb = D;
+  gt.epi = EPI_SILU_SPLIT;
+  gt.dst[0] = zt; gt.ld[0] = zw; gt.cend[0] = hd; gt.scale[0] = 1.f;
+  gt.dst[1] = zt + hd * es; gt.ld[1] = zw; gt.cend[1] = 2 * hd; gt.scale[1] = q_scale(dh);
+  gt.dst[2] = zt + 2 * hd * es; gt.ld[2] = zw; gt.cend[2] = zw; gt.scale[2] = 1.f;
+  gt.cend[3] = zw;
+  gt.N = zw;
+  if (fw) {
+    gt.M = (int32_t)p.n_t_rows; gt.groups = 1;
+    gt.amap = identity_map(); gt.cmap = identity_map();
+    gt.B[0] = fw->w_uqkv; gt.bn[0] = zw;
+  } else {
+    gt.M = (int32_t)p.n_parents; gt.groups = S;
+    gt.amap = RowMap{nullptr, S, 0}; gt.amap_zadd = 1;
+    gt.cmap = RowMap{nullptr, S, 0}; gt.cmap_zadd = 1;
+    gt.B[0] = tw->w_u; gt.bn[0] = hd;
+    gt.B[1] = tw->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
+    gt.B[2] = tw->w_kv; gt.bn[2] = 2 * gd;
+  }
+  TRY(timed_gemm(MTFM_K_GEMM_T, gt, dt, c.s));
+
+  AttnArgs aa{};
+  aa.q = zt + hd * es; aa.ldq = zw;
+  aa.k = kv.k; aa.ldk = gd;
+  aa.v = nullptr; aa.ldv = 0;
+  aa.vt = kv.vt; aa.ldvt = kv.ldvt; aa.n_key_rows = (int32_t)p.n_ctx_rows;
+  aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
+  aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
+  aa.a = a; aa.lda = hd;
+  aa.tiles = tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
+  aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
+  aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+  TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
+
+  GlnArgs g2{};
+  g2.rows = (int32_t)p.n_t_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
+  g2.gate = zt; g2.ldg = zw;
+  g2.gamma = fw ? fw->ln2_g : tw->ln2_g; g2.beta = fw ? fw->ln2_b : tw->ln2_b;
+  g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;
+  TRY(timed_gln(g2, dt, c.s));
+
+  GemmArgs go{};
+  go.M = (int32_t)p.n_t_rows; go.N = D; go.K = hd; go.groups = 1;
+  go.A = y; go.lda = hd; go.amap = identity_map();
+  go.B[0] = fw ? fw->w_o : tw->w_o; go.bn[0] = D; go.ldb = hd;
+  go.cmap = identity_map();
+  go.epi = EPI_RESID; go.resid = x; go.ldr = D; go.out = x; go.ldo = D;
+  TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
+  return MTFM_OK;
+}
+
+mtfm_status serve_checks(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                         const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt, Ctx* c) {
+  if (n_blocks < 0 || k_target < 0) return MTFM_E_DIMS;
+  TRY(plan_meta(batch, &c->plan));
+  TRY(check_dims(dims));
+  if (dims->dtype != MTFM_BF16 || k_target > 4) return MTFM_E_UNSUPPORTED;
+  if (!meta_d) return MTFM_E_NULL;
+  TRY(check_batch_device(batch, c->plan));
+  if (n_blocks > 0 && !full) return MTFM_E_NULL;
+  if (n_blocks > 0 && k_target > 0 && !tgt) return MTFM_E_NULL;
+  for (int b = 0; b < n_blocks; ++b) {
+    TRY(check_full_w(&full[b]));
+    for (int t = 0; t < k_target; ++t) TRY(check_target_w(&tgt[b * k_target + t]));
+  }
+  c->b = batch;
+  c->meta = meta_ptrs(c->plan, meta_d);
+  return MTFM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t mtfm_meta_bytes(const mtfm_batch* batch) {
@@ -692,6 +862,82 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
     if (t == 0) TRY(run_full_bwd(c, dims, &full[b], input_of(l), g_in, g_out, &full_g[b], w + W.layer));
     else TRY(run_target_bwd(c, dims, &tgt[b * k_target + t - 1], input_of(l), g_in, g_out,
                             &tgt_g[b * k_target + t - 1], w + W.layer));
+  }
+  return MTFM_OK;
+}
+
+size_t mtfm_kv_cache_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target) {
+  MetaPlan p;
+  if (n_blocks < 0 || k_target < 0 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
+  if (dims->dtype != MTFM_BF16) return 0;
+  return (size_t)kv_cache_layout(p, dims, n_blocks * (1 + k_target)).total;
+}
+
+size_t mtfm_serve_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t k_target, int32_t phase) {
+  MetaPlan p;
+  if (k_target < 0 || k_target > 4 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
+  if (dims->dtype != MTFM_BF16) return 0;
+  if (phase == MTFM_SERVE_CONTEXT) return (size_t)backbone_ws(p, dims, k_target).total;
+  if (phase == MTFM_SERVE_TARGETS) return (size_t)serve_ws(p, dims).total;
+  return 0;
+}
+
+mtfm_status mtfm_serve_context(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                               const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                               void* x_inout, void* kv_cache, size_t cache_bytes, void* ws, size_t ws_bytes,
+                               void* stream) {
+  Ctx c;
+  TRY(serve_checks(batch, dims, n_blocks, k_target, meta_d, full, tgt, &c));
+  c.s = (hipStream_t)stream;
+  if (c.plan.n_t_rows != 0) {
+    set_last_error("mtfm_serve_context: the context batch must hold no T rows");
+    return MTFM_E_DIMS;
+  }
+  const KvCacheLayout K = kv_cache_layout(c.plan, dims, n_blocks * (1 + k_target));
+  const BackboneWs L = backbone_ws(c.plan, dims, k_target);
+  if (c.plan.n_rows > 0 && (!x_inout || !kv_cache || (L.total > 0 && !ws))) return MTFM_E_NULL;
+  if (cache_bytes < (size_t)K.total || ws_bytes < (size_t)L.total) return MTFM_E_WORKSPACE;
+  if (c.plan.n_rows == 0) return MTFM_OK;
+  char* w = (char*)ws;
+  char* cache = (char*)kv_cache;
+  const int per = 1 + k_target;
+  for (int b = 0; b < n_blocks; ++b) {
+    const KvOut kf = kv_of(K, cache, b * per);
+    TRY(run_full(c, dims, &full[b], x_inout, x_inout, w + L.full, &kf));
+    if (k_target == 0) continue;
+    KvOut kt[4];
+    for (int t = 0; t < k_target; ++t) kt[t] = kv_of(K, cache, b * per + 1 + t);
+    TRY(run_target_context(c, dims, &tgt[b * k_target], k_target, x_inout, w, L, kt));
+  }
+  return MTFM_OK;
+}
+
+mtfm_status mtfm_serve_targets(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                               const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                               const void* kv_cache, size_t cache_bytes, void* x_t, void* ws, size_t ws_bytes,
+                               void* stream) {
+  Ctx c;
+  TRY(serve_checks(batch, dims, n_blocks, k_target, meta_d, full, tgt, &c));
+  c.s = (hipStream_t)stream;
+  const KvCacheLayout K = kv_cache_layout(c.plan, dims, n_blocks * (1 + k_target));
+  const ServeWs L = serve_ws(c.plan, dims);
+  if (c.plan.n_t_rows > 0 && (!x_t || !kv_cache || !ws)) return MTFM_E_NULL;
+  if (cache_bytes < (size_t)K.total || ws_bytes < (size_t)L.total) return MTFM_E_WORKSPACE;
+  if (c.plan.n_t_rows == 0 || n_blocks == 0) return MTFM_OK;
+  char* w = (char*)ws;
+  int32_t* tiles = (int32_t*)(w + L.tiles);
+  {
+    const int n = (int)c.plan.n_target_tiles;
+    rebase_tiles_kernel<<<(n * 8 + 255) / 256, 256, 0, c.s>>>(c.meta.target_tiles, n,
+                                                               c.meta.user + UT_CTX * (c.plan.n_users + 1), tiles);
+    MTFM_LAUNCH_CHECK("rebase_tiles");
+  }
+  char* cache = (char*)kv_cache;
+  const int per = 1 + k_target;
+  for (int b = 0; b < n_blocks; ++b) {
+    TRY(serve_rows(c, dims, &full[b], nullptr, kv_of(K, cache, b * per), tiles, x_t, w, L));
+    for (int t = 0; t < k_target; ++t)
+      TRY(serve_rows(c, dims, nullptr, &tgt[b * k_target + t], kv_of(K, cache, b * per + 1 + t), tiles, x_t, w, L));
   }
   return MTFM_OK;
 }

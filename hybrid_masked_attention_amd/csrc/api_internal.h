@@ -41,7 +41,15 @@ struct Ctx {
 mtfm_status check_dims(const mtfm_dims* d);
 mtfm_status prepare(const mtfm_batch* b, const mtfm_dims* d, const void* meta_d, const void* x0, const void* x1,
                     void* ws, size_t ws_bytes, int op, Ctx* c, void* stream);
-mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out, char* ws);
+// Where a layer puts the K (row-major, [rows][G*dh]) and V^T ([G*dh][ldvt]) of
+// its rows when they are kept beyond the layer (bf16 serving cache).
+struct KvOut {
+  void* k = nullptr;
+  void* vt = nullptr;
+  int64_t ldvt = 0;
+};
+mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out, char* ws,
+                     const KvOut* kv = nullptr);
 mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in, void* x_out,
                        char* ws);
 

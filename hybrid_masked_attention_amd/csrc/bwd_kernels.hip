@@ -184,14 +184,26 @@ __global__ __launch_bounds__(256) void gln1_bwd_kernel(Gln1BwdArgs a) {
 }
 
 // out[which][c] = sum over blocks of pg[block][which][c], which in {dgamma x3, dbeta x3}.
+// A workgroup owns 64 consecutive outputs; each of its four waves sums a
+// contiguous quarter of the blocks, then the four sums are added in order
+// (fixed order: deterministic).
 __global__ __launch_bounds__(256) void param_reduce_kernel(const float* pg, int blocks, int D, float* dgamma,
                                                            float* dbeta) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= 6 * D) return;
+  __shared__ float part[4][64];
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + l;
   float s = 0.f;
-  for (int b = 0; b < blocks; ++b) s += pg[(int64_t)b * 6 * D + i];
-  if (i < 3 * D) dgamma[i] = s;
-  else dbeta[i - 3 * D] = s;
+  if (i < 6 * D) {
+    const int b0 = w * blocks / 4, b1 = (w + 1) * blocks / 4;
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) s += pg[(int64_t)b * 6 * D + i];
+  }
+  part[w][l] = s;
+  __syncthreads();
+  if (w != 0 || i >= 6 * D) return;
+  const float t = ((part[0][l] + part[1][l]) + part[2][l]) + part[3][l];
+  if (i < 3 * D) dgamma[i] = t;
+  else dbeta[i - 3 * D] = t;
 }
 
 // out[c][r] = in[r][c] for up to three row segments stacked along r.
@@ -261,7 +273,7 @@ mtfm_status launch_gln1_bwd(const Gln1BwdArgs& a, hipStream_t s) {
 }
 
 mtfm_status launch_param_reduce(const float* pg, int blocks, int D, float* dgamma, float* dbeta, hipStream_t s) {
-  param_reduce_kernel<<<(6 * D + 255) / 256, 256, 0, s>>>(pg, blocks, D, dgamma, dbeta);
+  param_reduce_kernel<<<(6 * D + 63) / 64, 256, 0, s>>>(pg, blocks, D, dgamma, dbeta);
   MTFM_LAUNCH_CHECK("param_reduce");
   return MTFM_OK;
 }

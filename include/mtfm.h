@@ -263,6 +263,47 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
                               const mtfm_target_grad* tgt_g, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Request-level serving with user-side K/V reuse ([explainer] §5.2.3: K/V
+ * cache sharing across serving micro-batches; [blog] §3.4 and §4: one
+ * user-level sample shares the long-sequence attention among its targets).
+ * H and R rows never attend to T rows, so the context rows' values through
+ * the stack and every layer's K and V of them do not depend on the
+ * candidates.  Split the backbone in two:
+ *
+ *   mtfm_serve_context: once per set of users.  `batch` holds the users'
+ *     context only (L_T = 0 for every user; lens and R timestamps as in the
+ *     candidate batches to come).  Runs the stack of mtfm_backbone_fwd over
+ *     the context rows (x_inout [n_rows][d_model], updated in place) and
+ *     writes each layer's K and V^T of those rows into kv_cache.
+ *   mtfm_serve_targets: per candidate batch.  `batch` holds the same users
+ *     with the same L_H, L_R and R timestamps, plus any number of candidate
+ *     parents L_T with their exposure times; meta_d is its mask metadata.
+ *     x_t is [split * sum L_T][d_model] in T-row order (sub-token z of parent
+ *     m at row m * split + z), updated in place through all layers, each T row
+ *     attending to the cached context K/V of its user (visible prefix from
+ *     the mask) and to itself.
+ *
+ * The T rows come out exactly as mtfm_backbone_fwd would leave them for the
+ * batch holding context and candidates together.  Cache layout, per layer l
+ * in stack order (block b's full layer, then its target layers): K
+ * [n_ctx_rows][G*dh], then V^T [G*dh][ldvt] with ldvt = n_ctx_rows rounded up
+ * to 64 (bf16, 256-byte aligned pieces); context rows of all users back to
+ * back, users in order.  bf16 only, k_target <= 4.  The caller owns the
+ * cache; overlapping calls on the same cache or workspace race. */
+typedef enum { MTFM_SERVE_CONTEXT = 0, MTFM_SERVE_TARGETS = 1 } mtfm_serve_phase;
+
+size_t mtfm_kv_cache_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target);
+size_t mtfm_serve_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t k_target, int32_t phase);
+mtfm_status mtfm_serve_context(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                               const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                               void* x_inout, void* kv_cache, size_t cache_bytes, void* ws, size_t ws_bytes,
+                               void* stream);
+mtfm_status mtfm_serve_targets(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                               const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                               const void* kv_cache, size_t cache_bytes, void* x_t, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing (measurement aid).  While a kernel class is enabled, each of
  * its launches is bracketed by two HIP events recorded on the stream the
  * kernel is launched on; nothing else changes.  mtfm_timing_read waits for

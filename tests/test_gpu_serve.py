@@ -1,0 +1,177 @@
+"""Request-level serving with user-side K/V reuse, on the GPU.
+
+mtfm_serve_context runs the users' context rows through the stack once and
+caches every layer's K and V^T of them; mtfm_serve_targets then runs a
+candidate batch's T rows through the stack against that cache.  Because H and
+R rows never attend to T rows, the split is exact in real arithmetic: both
+parts must match the oracle's backbone over the batch holding context and
+candidates together.  The device's key tiles are aligned to 64 rows of the
+buffer the keys live in, and the cache packs context rows without the T rows
+in between, so keys are grouped differently inside the fp32 attention sums
+than in mtfm_backbone_fwd: the two agree to rounding, not bit for bit.  Bar:
+the residual branch within 1e-2 of max|branch| after allowing one bf16
+rounding of the stored X per layer (as the backbone tests).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import model as om
+from tests._parity import TOL_BF16, Report, rounded_inputs, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(batch):
+    """Packed rows of the context (H, R) rows, users in order, and of the T rows in T-row order."""
+    off, S = batch.row_off, batch.split
+    ctx, trows = [], []
+    for u in range(batch.n_users):
+        lh, lr, lt = (int(v) for v in batch.lens[u])
+        ctx.append(np.arange(off[u], off[u] + lh + lr))
+        trows.append(np.arange(off[u] + lh + lr, off[u] + lh + lr + S * lt))
+    cat = lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.int64)
+    return cat(ctx), cat(trows)
+
+
+def _context_batch(batch):
+    lens = batch.lens.copy()
+    lens[:, 2] = 0
+    return synth.Batch(lens, batch.split, batch.ts_r, np.zeros(0, np.int32))
+
+
+def _small(split, seed, n_blocks=2, k_target=3, lens=None):
+    rng = np.random.default_rng(seed)
+    if lens is None:
+        lens = np.stack([rng.integers(40, 200, 7), rng.integers(0, 90, 7), rng.integers(0, 20, 7)], 1)
+        lens[2] = (70, 0, 5)
+        lens[4] = (30, 50, 0)
+        lens[5] = (0, 12, 3)
+    batch = synth.make_batch(rng, np.asarray(lens, np.int32), split)
+    dims = synth.Dims(512, 8, 2, 64)
+    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
+    full = [synth.full_weights(rng, dims, 0.02, 0.02) for _ in range(n_blocks)]
+    tgt = [synth.target_weights(rng, dims, split, 0.02, 0.02) for _ in range(n_blocks * k_target)]
+    return synth.Workload(f"serve_s{split}", batch, dims, "bf16", x, full=full, target=tgt, n_blocks=n_blocks,
+                          k_target=k_target)
+
+
+def _backbone(wl, dw, B, torch):
+    meta = B.mask_build(dw.batch)
+    ws = B.workspace(dw.batch, dw.dims, B.OP_BACKBONE, k_target=wl.k_target)
+    x = dw.x.clone()
+    B.backbone_fwd(dw.batch, dw.dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, x, ws)
+    return x
+
+
+def _serve_context(wl, dw, B, torch):
+    """Context pass on the context-only batch: (context rows after the stack, cache)."""
+    cb = B.DeviceBatch.from_synth(_context_batch(wl.batch))
+    meta = B.mask_build(cb)
+    cache = torch.empty(B.kv_cache_bytes(cb, dw.dims, wl.n_blocks, wl.k_target), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, B.serve_workspace_bytes(cb, dw.dims, wl.k_target, B.SERVE_CONTEXT)), dtype=torch.uint8,
+                     device="cuda")
+    ctx_rows, _ = _rows(wl.batch)
+    x = dw.x[torch.as_tensor(ctx_rows, device="cuda")].contiguous()
+    B.serve_context(cb, dw.dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, x, cache, ws)
+    return x, cache
+
+
+def _serve_targets(wl, dw, B, torch, cache, x_t):
+    meta = B.mask_build(dw.batch)
+    ws = torch.empty(max(1, B.serve_workspace_bytes(dw.batch, dw.dims, wl.k_target, B.SERVE_TARGETS)),
+                     dtype=torch.uint8, device="cuda")
+    B.serve_targets(dw.batch, dw.dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, cache, x_t, ws)
+    return x_t
+
+
+def _compare(r, name, got, ref_dev, ref_or, x0):
+    r.branch(f"{name} vs oracle", got, ref_or, x0, "bf16", roundings=16)
+    r.branch(f"{name} vs backbone", got, ref_dev, x0, "bf16", roundings=16)
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_serving_matches_backbone_and_oracle(split):
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    wl = _small(split, 120 + split)
+    say(f"serving: {wl.batch.n_users} users, {wl.batch.total_rows} rows, split {split}")
+    dw = DeviceWorkload(wl)
+    ref = to_np(_backbone(wl, dw, B, torch))
+    ctx_rows, t_rows = _rows(wl.batch)
+    x_ctx, cache = _serve_context(wl, dw, B, torch)
+    x_t = dw.x[torch.as_tensor(t_rows, device="cuda")].contiguous()
+    _serve_targets(wl, dw, B, torch, cache, x_t)
+    torch.cuda.synchronize()
+    xr, full, tgt = rounded_inputs(wl)
+    o = om.backbone(wl.batch, xr, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=om.bf16_round)
+    r = Report(TOL_BF16)
+    _compare(r, "context rows", to_np(x_ctx), ref[ctx_rows], o[ctx_rows], xr[ctx_rows])
+    _compare(r, "T rows", to_np(x_t), ref[t_rows], o[t_rows], xr[t_rows])
+    r.check()
+
+
+def test_serving_reuses_one_cache_for_other_candidates():
+    """Two candidate batches with different counts and exposure times over one context cache."""
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    wl = _small(4, 130)
+    dw = DeviceWorkload(wl)
+    x_ctx, cache = _serve_context(wl, dw, B, torch)
+    x_ctx = to_np(x_ctx)
+    rng = np.random.default_rng(131)
+    r = Report(TOL_BF16)
+    for trial in range(2):
+        lens = wl.batch.lens.copy()
+        lens[:, 2] = rng.integers(0, 25, wl.batch.n_users)
+        ts_t = rng.integers(0, synth.TS_HIGH, int(lens[:, 2].sum())).astype(np.int32)
+        cand = synth.Batch(lens, wl.batch.split, wl.batch.ts_r, ts_t)
+        ctx_rows, t_rows = _rows(cand)
+        x = np.zeros((cand.total_rows, wl.dims.d_model), np.float32)
+        x[ctx_rows] = wl.x[_rows(wl.batch)[0]]
+        x[t_rows] = rng.standard_normal((len(t_rows), wl.dims.d_model))
+        wc = synth.Workload("cand", cand, wl.dims, "bf16", x, full=wl.full, target=wl.target, n_blocks=wl.n_blocks,
+                            k_target=wl.k_target)
+        dwc = DeviceWorkload(wc)
+        ref = to_np(_backbone(wc, dwc, B, torch))
+        x_t = dwc.x[torch.as_tensor(t_rows, device="cuda")].contiguous()
+        _serve_targets(wc, dwc, B, torch, cache, x_t)
+        torch.cuda.synchronize()
+        say(f"  candidates {trial}: {len(t_rows)} T rows")
+        xr, full, tgt = rounded_inputs(wc)
+        o = om.backbone(cand, xr, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=om.bf16_round)
+        _compare(r, f"candidates {trial} T rows", to_np(x_t), ref[t_rows], o[t_rows], xr[t_rows])
+        _compare(r, f"candidates {trial} context rows", x_ctx, ref[ctx_rows], o[ctx_rows], xr[ctx_rows])
+    r.check()
+
+
+def test_config3_serving():
+    """The 160-user batch: serving against the backbone on every row, and one user's rows against
+    the oracle."""
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    wl = synth.config3()
+    dw = DeviceWorkload(wl)
+    ref = to_np(_backbone(wl, dw, B, torch))
+    ctx_rows, t_rows = _rows(wl.batch)
+    x_ctx, cache = _serve_context(wl, dw, B, torch)
+    x_t = dw.x[torch.as_tensor(t_rows, device="cuda")].contiguous()
+    _serve_targets(wl, dw, B, torch, cache, x_t)
+    torch.cuda.synchronize()
+    got_t, got_c = to_np(x_t), to_np(x_ctx)
+    xr, full, tgt = rounded_inputs(wl)
+    r = Report(TOL_BF16)
+    r.branch("T rows vs backbone", got_t, ref[t_rows], xr[t_rows], "bf16", roundings=16)
+    r.branch("context rows vs backbone", got_c, ref[ctx_rows], xr[ctx_rows], "bf16", roundings=16)
+    u = 7
+    o = om.backbone(wl.batch, xr, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=om.bf16_round, users=[u])
+    urows = wl.batch.rows_of([u])
+    mt, mc = np.isin(t_rows, urows), np.isin(ctx_rows, urows)
+    r.branch(f"T rows of user {u} vs oracle", got_t[mt], o[np.searchsorted(urows, t_rows[mt])], xr[t_rows[mt]],
+             "bf16", roundings=16)
+    r.branch(f"context rows of user {u} vs oracle", got_c[mc], o[np.searchsorted(urows, ctx_rows[mc])],
+             xr[ctx_rows[mc]], "bf16", roundings=16)
+    r.check()
