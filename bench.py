@@ -96,6 +96,10 @@ def main():
     ap.add_argument("--serve-steps", type=int, default=10,
                     help="also time request-level serving: one context pass filling the K/V cache, then this many "
                          "candidate passes over the cached context (0 skips)")
+    ap.add_argument("--v2-steps", type=int, default=5,
+                    help="also time the V2 target side on config 3's users (AutoSplit into 4 sub-tokens, the "
+                         "16-layer stack with a per-sub-token SwiGLU FFN and token mixing after every target "
+                         "layer, mean pooling); 0 skips")
     ap.add_argument("--train-steps", type=int, default=3,
                     help="also time this many training gradient passes (mtfm_backbone_bwd: forward keeping the "
                          "layer inputs, then every layer's backward); 0 skips")
@@ -298,6 +302,44 @@ def main():
             f"({serve['candidates_per_s']:.0f} candidates/s, {serve['vs_full_forward']:.1f}x the full forward)")
         del cache, ws_c, ws_t, x_c, x_t, x_c0, x_t0
 
+    v2 = None
+    if args.v2_steps > 0:
+        from hybrid_masked_attention_amd.tensors import to_device, weights_to_device
+        wl2, feats, w_split, ffn = synth.config3_v2()
+        dw2 = DeviceWorkload(wl2)
+        meta2 = B.mask_build(dw2.batch)
+        d_ff = ffn[0]["w_gate"].shape[1]
+        ws2 = torch.empty(B.backbone_v2_workspace_bytes(dw2.batch, dw2.dims, wl2.k_target, d_ff), dtype=torch.uint8,
+                          device="cuda")
+        fd, wd = to_device(feats, "bf16"), to_device(w_split, "bf16")
+        ffd = [weights_to_device(w, "bf16") for w in ffn]
+        n_par = feats.shape[0]
+        pooled = torch.empty((n_par, wl2.dims.d_model), dtype=torch.bfloat16, device="cuda")
+        x2 = dw2.x.clone()
+
+        def v2_step():
+            B.mask_build(dw2.batch, meta2)
+            B.autosplit(dw2.batch, dw2.dims, feats.shape[1], meta2, fd, wd, x2)
+            B.backbone_v2_fwd(dw2.batch, dw2.dims, wl2.n_blocks, wl2.k_target, d_ff, meta2, dw2.full, dw2.target,
+                              ffd, x2, ws2)
+            B.token_pool(dw2.batch, dw2.dims, meta2, x2, pooled)
+
+        v2_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.v2_steps):
+            v2_step()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        v2 = {"what": "V2 target side on config 3's 160 users: AutoSplit (feature width 512 -> 4 sub-tokens), "
+                      "16 layers with a per-sub-token SwiGLU FFN (hidden 1024) and token mixing after each target "
+                      "layer, mean pooling; metadata build included",
+              "rows": int(wl2.batch.total_rows), "t_rows": int(wl2.batch.total_t_rows), "steps": args.v2_steps,
+              "ms_per_step": 1000.0 * el / args.v2_steps,
+              "user_samples_per_s": wl2.batch.n_users * args.v2_steps / el}
+        log(f"V2 target side: {v2['ms_per_step']:.2f} ms/step, {v2['user_samples_per_s']:.1f} user-samples/s")
+        del dw2, ws2, x2, pooled, ffd
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
@@ -328,6 +370,7 @@ def main():
         "breakdown": breakdown,
         "train": train,
         "serve": serve,
+        "v2": v2,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

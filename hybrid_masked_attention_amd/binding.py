@@ -31,10 +31,11 @@ ENTRY_POINTS = [
     "mtfm_attn_full_bwd", "mtfm_attn_target_bwd", "mtfm_timing_enable", "mtfm_timing_read",
     "mtfm_status_str", "mtfm_last_error", "mtfm_backbone_workspace_bytes",
     "mtfm_backbone_bwd_workspace_bytes", "mtfm_backbone_bwd", "mtfm_kv_cache_bytes", "mtfm_serve_workspace_bytes",
-    "mtfm_serve_context", "mtfm_serve_targets",
+    "mtfm_serve_context", "mtfm_serve_targets", "mtfm_autosplit", "mtfm_token_ffn_workspace_bytes",
+    "mtfm_token_ffn", "mtfm_token_pool", "mtfm_backbone_v2_workspace_bytes", "mtfm_backbone_v2_fwd",
 ]
 SERVE_CONTEXT, SERVE_TARGETS = 0, 1
-K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD = range(9)
+K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD, K_V2 = range(10)
 
 
 class MtfmError(RuntimeError):
@@ -67,6 +68,10 @@ class CFullGrad(ctypes.Structure):
 
 class CTargetGrad(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o")]
+
+
+class CFfnW(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("ln_g", "ln_b", "w_gate", "w_up", "w_down")]
 
 
 class CMetaLayout(ctypes.Structure):
@@ -126,6 +131,20 @@ def lib():
     L.mtfm_serve_targets.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_void_p, P(CFullW), P(CTargetW),
                                      c_void_p, c_size_t, c_void_p, c_void_p, c_size_t, c_void_p]
     L.mtfm_serve_targets.restype = c_int32
+    L.mtfm_autosplit.argtypes = [P(CBatch), P(CDims), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.mtfm_autosplit.restype = c_int32
+    L.mtfm_token_ffn_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]
+    L.mtfm_token_ffn_workspace_bytes.restype = c_size_t
+    L.mtfm_token_ffn.argtypes = [P(CBatch), P(CDims), c_int32, c_void_p, P(CFfnW), c_void_p, c_void_p, c_size_t,
+                                 c_void_p]
+    L.mtfm_token_ffn.restype = c_int32
+    L.mtfm_token_pool.argtypes = [P(CBatch), P(CDims), c_void_p, c_void_p, c_void_p, c_void_p]
+    L.mtfm_token_pool.restype = c_int32
+    L.mtfm_backbone_v2_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32, c_int32]
+    L.mtfm_backbone_v2_workspace_bytes.restype = c_size_t
+    L.mtfm_backbone_v2_fwd.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_int32, c_void_p, P(CFullW),
+                                       P(CTargetW), P(CFfnW), c_void_p, c_void_p, c_size_t, c_void_p]
+    L.mtfm_backbone_v2_fwd.restype = c_int32
     L.mtfm_timing_enable.argtypes = [ctypes.c_uint32]; L.mtfm_timing_enable.restype = c_int32
     L.mtfm_timing_read.argtypes = [c_int32, P(c_int64), P(ctypes.c_double)]; L.mtfm_timing_read.restype = c_int32
     L.mtfm_status_str.argtypes = [c_int32]; L.mtfm_status_str.restype = c_char_p
@@ -360,6 +379,53 @@ def serve_targets(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], t
                                     _ptr(meta), fa, ta, _ptr(kv_cache), kv_cache.numel(), _ptr(x_t), _ptr(ws),
                                     ws.numel(), _stream(stream)), "mtfm_serve_targets")
     return x_t
+
+
+FFN_KEYS = ("ln_g", "ln_b", "w_gate", "w_up", "w_down")
+
+
+def ffn_w(w: Dict[str, "object"]) -> CFfnW:
+    return CFfnW(*[_ptr(w[n]) for n in FFN_KEYS])
+
+
+def autosplit(batch, dims, d_in, meta, feats, w_split, x, stream=None):
+    """The T rows of x from the parents' features ([n_parents][d_in]) through the AutoSplit map."""
+    _check(lib().mtfm_autosplit(ctypes.byref(batch.c), ctypes.byref(dims), int(d_in), _ptr(meta), _ptr(feats),
+                                _ptr(w_split), _ptr(x), _stream(stream)), "mtfm_autosplit")
+    return x
+
+
+def token_ffn_workspace_bytes(batch: DeviceBatch, dims: CDims, d_ff: int) -> int:
+    return int(lib().mtfm_token_ffn_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(d_ff)))
+
+
+def token_ffn(batch, dims, d_ff, meta, w: Dict, x, ws, stream=None):
+    cw = ffn_w(w)
+    _check(lib().mtfm_token_ffn(ctypes.byref(batch.c), ctypes.byref(dims), int(d_ff), _ptr(meta), ctypes.byref(cw),
+                                _ptr(x), _ptr(ws), ws.numel(), _stream(stream)), "mtfm_token_ffn")
+    return x
+
+
+def token_pool(batch, dims, meta, x, out, stream=None):
+    _check(lib().mtfm_token_pool(ctypes.byref(batch.c), ctypes.byref(dims), _ptr(meta), _ptr(x), _ptr(out),
+                                 _stream(stream)), "mtfm_token_pool")
+    return out
+
+
+def backbone_v2_workspace_bytes(batch: DeviceBatch, dims: CDims, k_target: int, d_ff: int) -> int:
+    return int(lib().mtfm_backbone_v2_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(k_target),
+                                                      int(d_ff)))
+
+
+def backbone_v2_fwd(batch, dims, n_blocks, k_target, d_ff, meta, full: Sequence[Dict], tgt: Sequence[Dict],
+                    ffn: Sequence[Dict], x_inout, ws, stream=None):
+    fa = (CFullW * max(1, len(full)))(*[full_w(w) for w in full])
+    ta = (CTargetW * max(1, len(tgt)))(*[target_w(w) for w in tgt])
+    fn = (CFfnW * max(1, len(ffn)))(*[ffn_w(w) for w in ffn])
+    _check(lib().mtfm_backbone_v2_fwd(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks), int(k_target),
+                                      int(d_ff), _ptr(meta), fa, ta, fn, _ptr(x_inout), _ptr(ws), ws.numel(),
+                                      _stream(stream)), "mtfm_backbone_v2_fwd")
+    return x_inout
 
 
 def timing_enable(classes: Sequence[int]):

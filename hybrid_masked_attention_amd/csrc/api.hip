@@ -11,6 +11,7 @@
 #include <string>
 
 #include "api_internal.h"
+#include "v2.h"
 
 thread_local std::string g_last_error;
 
@@ -480,6 +481,88 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
 // ---------------------------------------------------------------------------
 
 // ---------------------------------------------------------------------------
+// V2 target side ([blog] §3.3.2): AutoSplit, per-sub-token SwiGLU FFN with the
+// token mixing, mean pooling (readings in include/mtfm.h).
+namespace {
+
+struct FfnWs {
+  int64_t wgu = 0, xtt = 0, h = 0, total = 0;
+};
+
+FfnWs ffn_ws(const MetaPlan& p, const mtfm_dims* d, int d_ff) {
+  FfnWs w;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
+  w.wgu = take((int64_t)p.split * 2 * d_ff * d->d_model * 2);
+  w.xtt = take(p.n_t_rows * d->d_model * 2);
+  w.h = take(p.n_t_rows * (int64_t)d_ff * 2);
+  w.total = off;
+  return w;
+}
+
+mtfm_status v2_checks(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d, Ctx* c) {
+  TRY(plan_meta(batch, &c->plan));
+  TRY(check_dims(dims));
+  if (dims->dtype != MTFM_BF16) return MTFM_E_UNSUPPORTED;
+  if (!meta_d) return MTFM_E_NULL;
+  TRY(check_batch_device(batch, c->plan));
+  c->b = batch;
+  c->meta = meta_ptrs(c->plan, meta_d);
+  return MTFM_OK;
+}
+
+mtfm_status check_ffn(const mtfm_dims* d, int d_ff, int split, const mtfm_ffn_w* w) {
+  if (!w || !w->ln_g || !w->ln_b || !w->w_gate || !w->w_up || !w->w_down) return MTFM_E_NULL;
+  if (d_ff <= 0 || d_ff % 32 != 0) return MTFM_E_UNSUPPORTED;
+  if (split > 1 && (d->d_model % split != 0 || (d->d_model / split) % 8 != 0 || split * d->d_model / 8 > 1024))
+    return MTFM_E_UNSUPPORTED;
+  return MTFM_OK;
+}
+
+// Token FFN + mixing of one target layer on the T rows of x (packed, in place).
+mtfm_status run_token_ffn(const Ctx& c, const mtfm_dims* d, int d_ff, const mtfm_ffn_w* w, void* x, char* ws,
+                          const FfnWs& L) {
+  const MetaPlan& p = c.plan;
+  const int S = p.split, D = d->d_model;
+  if (p.n_t_rows == 0) return MTFM_OK;
+  {
+    RepackArgs r{};
+    r.gate = (const bf16*)w->w_gate; r.up = (const bf16*)w->w_up; r.out = (bf16*)(ws + L.wgu);
+    r.S = S; r.F = d_ff; r.D = D;
+    TimedLaunch t(MTFM_K_V2, c.s);
+    TRY(launch_repack_gate_up(r, c.s));
+  }
+  GlnArgs g1{};
+  g1.rows = (int32_t)p.n_t_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = ws + L.xtt; g1.ldy = D;
+  g1.xlist = c.meta.parent_row; g1.xdiv = S;
+  g1.gamma = w->ln_g; g1.beta = w->ln_b; g1.type = nullptr; g1.type_const = TT_T; g1.eps = d->ln_eps;
+  TRY(timed_gln(g1, MTFM_BF16, c.s));
+
+  GemmArgs gu{};
+  gu.M = (int32_t)p.n_parents; gu.N = 2 * d_ff; gu.K = D; gu.groups = S;
+  gu.A = ws + L.xtt; gu.lda = D; gu.amap = RowMap{nullptr, S, 0}; gu.amap_zadd = 1;
+  gu.B[0] = ws + L.wgu; gu.bn[0] = 2 * d_ff; gu.bz[0] = (int64_t)2 * d_ff * D; gu.ldb = D;
+  gu.cmap = RowMap{nullptr, S, 0}; gu.cmap_zadd = 1;
+  gu.epi = EPI_SWIGLU; gu.out = ws + L.h; gu.ldo = d_ff;
+  TRY(timed_gemm(MTFM_K_V2, gu, MTFM_BF16, c.s));
+
+  GemmArgs gd{};
+  gd.M = (int32_t)p.n_parents; gd.N = D; gd.K = d_ff; gd.groups = S;
+  gd.A = ws + L.h; gd.lda = d_ff; gd.amap = RowMap{nullptr, S, 0}; gd.amap_zadd = 1;
+  gd.B[0] = w->w_down; gd.bn[0] = D; gd.bz[0] = (int64_t)D * d_ff; gd.ldb = d_ff;
+  gd.cmap = RowMap{c.meta.parent_row, 0, 0}; gd.cmap_zadd = 1;
+  gd.epi = EPI_RESID; gd.resid = x; gd.ldr = D; gd.out = x; gd.ldo = D;
+  TRY(timed_gemm(MTFM_K_V2, gd, MTFM_BF16, c.s));
+
+  TokenRowsArgs m{};
+  m.x = (bf16*)x; m.ldx = D; m.parent_row = c.meta.parent_row; m.n_parents = (int32_t)p.n_parents; m.S = S; m.D = D;
+  TimedLaunch t(MTFM_K_V2, c.s);
+  return launch_token_mix(m, c.s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // Request-level serving with user-side K/V reuse ([explainer] §5.2.3: K/V
 // cache sharing across serving micro-batches; [blog] §3.4 and §4: one
 // user-level sample shares the long-sequence attention among all of its
@@ -862,6 +945,99 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
     if (t == 0) TRY(run_full_bwd(c, dims, &full[b], input_of(l), g_in, g_out, &full_g[b], w + W.layer));
     else TRY(run_target_bwd(c, dims, &tgt[b * k_target + t - 1], input_of(l), g_in, g_out,
                             &tgt_g[b * k_target + t - 1], w + W.layer));
+  }
+  return MTFM_OK;
+}
+
+mtfm_status mtfm_autosplit(const mtfm_batch* batch, const mtfm_dims* dims, int32_t d_in, const void* meta_d,
+                           const void* feats, const void* w_split, void* x, void* stream) {
+  Ctx c;
+  TRY(v2_checks(batch, dims, meta_d, &c));
+  c.s = (hipStream_t)stream;
+  if (d_in <= 0 || d_in % 32 != 0) return MTFM_E_UNSUPPORTED;
+  if (c.plan.n_parents == 0) return MTFM_OK;
+  if (!feats || !w_split || !x) return MTFM_E_NULL;
+  GemmArgs g{};
+  g.M = (int32_t)c.plan.n_parents; g.N = c.plan.split * dims->d_model; g.K = d_in; g.groups = 1;
+  g.A = feats; g.lda = d_in; g.amap = identity_map();
+  g.B[0] = w_split; g.bn[0] = g.N; g.ldb = d_in;
+  // output row m = parent m's S sub-token rows, contiguous in the packed matrix
+  g.cmap = RowMap{c.meta.parent_row, 0, 0};
+  g.epi = EPI_STORE; g.out = x; g.ldo = dims->d_model;
+  return timed_gemm(MTFM_K_V2, g, MTFM_BF16, c.s);
+}
+
+size_t mtfm_token_ffn_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t d_ff) {
+  MetaPlan p;
+  if (d_ff <= 0 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
+  return (size_t)ffn_ws(p, dims, d_ff).total;
+}
+
+mtfm_status mtfm_token_ffn(const mtfm_batch* batch, const mtfm_dims* dims, int32_t d_ff, const void* meta_d,
+                           const mtfm_ffn_w* w, void* x, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c;
+  TRY(v2_checks(batch, dims, meta_d, &c));
+  c.s = (hipStream_t)stream;
+  TRY(check_ffn(dims, d_ff, c.plan.split, w));
+  const FfnWs L = ffn_ws(c.plan, dims, d_ff);
+  if (c.plan.n_t_rows > 0 && (!x || !ws)) return MTFM_E_NULL;
+  if (ws_bytes < (size_t)L.total) return MTFM_E_WORKSPACE;
+  return run_token_ffn(c, dims, d_ff, w, x, (char*)ws, L);
+}
+
+mtfm_status mtfm_token_pool(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d, const void* x,
+                            void* out, void* stream) {
+  Ctx c;
+  TRY(v2_checks(batch, dims, meta_d, &c));
+  c.s = (hipStream_t)stream;
+  if (c.plan.n_parents == 0) return MTFM_OK;
+  if (!x || !out) return MTFM_E_NULL;
+  TokenRowsArgs a{};
+  a.x = (bf16*)x; a.ldx = dims->d_model; a.parent_row = c.meta.parent_row; a.n_parents = (int32_t)c.plan.n_parents;
+  a.S = c.plan.split; a.D = dims->d_model; a.out = (bf16*)out; a.ldo = dims->d_model;
+  TimedLaunch t(MTFM_K_V2, c.s);
+  return launch_token_pool(a, c.s);
+}
+
+size_t mtfm_backbone_v2_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t k_target,
+                                        int32_t d_ff) {
+  MetaPlan p;
+  if (k_target < 1 || k_target > 4 || d_ff <= 0 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK)
+    return 0;
+  return (size_t)(align_up(backbone_ws(p, dims, k_target).total, 256) + ffn_ws(p, dims, d_ff).total);
+}
+
+mtfm_status mtfm_backbone_v2_fwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                                 int32_t d_ff, const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                                 const mtfm_ffn_w* ffn, void* x_inout, void* ws, size_t ws_bytes, void* stream) {
+  Ctx c;
+  TRY(v2_checks(batch, dims, meta_d, &c));
+  c.s = (hipStream_t)stream;
+  if (n_blocks < 0) return MTFM_E_DIMS;
+  if (k_target < 1 || k_target > 4) return MTFM_E_UNSUPPORTED;
+  if (n_blocks > 0 && (!full || !tgt || !ffn)) return MTFM_E_NULL;
+  for (int b = 0; b < n_blocks; ++b) {
+    TRY(check_full_w(&full[b]));
+    for (int t = 0; t < k_target; ++t) {
+      TRY(check_target_w(&tgt[b * k_target + t]));
+      TRY(check_ffn(dims, d_ff, c.plan.split, &ffn[b * k_target + t]));
+    }
+  }
+  const BackboneWs L = backbone_ws(c.plan, dims, k_target);
+  const int64_t foff = align_up(L.total, 256);
+  const FfnWs F = ffn_ws(c.plan, dims, d_ff);
+  if (c.plan.n_rows > 0 && (!x_inout || !ws)) return MTFM_E_NULL;
+  if (ws_bytes < (size_t)(foff + F.total)) return MTFM_E_WORKSPACE;
+  char* w = (char*)ws;
+  for (int b = 0; b < n_blocks; ++b) {
+    TRY(run_full(c, dims, &full[b], x_inout, x_inout, w + L.full));
+    const mtfm_target_w* tw = &tgt[b * k_target];
+    if (c.plan.n_t_rows == 0) continue;   // target layers and FFNs change T rows only
+    TRY(run_target_context(c, dims, tw, k_target, x_inout, w, L));
+    for (int t = 0; t < k_target; ++t) {
+      TRY(run_target_rows(c, dims, &tw[t], x_inout, w, L, t));
+      TRY(run_token_ffn(c, dims, d_ff, &ffn[b * k_target + t], x_inout, w + foff, F));
+    }
   }
   return MTFM_OK;
 }

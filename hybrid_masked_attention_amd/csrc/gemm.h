@@ -22,7 +22,9 @@ enum GemmEpi {
   EPI_SILU_SPLIT = 0,  // v = SiLU(acc); columns [cend[r-1], cend[r]) -> dst[r] * scale[r] (row-major)
   EPI_RESID = 1,       // out[crow] = acc + resid[crow]
   EPI_STORE_F32 = 2,   // out (fp32) [crow] = acc  (+= if accumulate)
-  EPI_STORE = 3        // out (dtype) [crow] = acc
+  EPI_STORE = 3,       // out (dtype) [crow] = acc
+  EPI_SWIGLU = 4       // bf16: weight rows interleaved in blocks of 32 (gate units [32j, 32j + 32), then up
+                       // units [32j, 32j + 32)); out[crow][32j + i] = SiLU(gate) * up, width N / 2
 };
 
 struct GemmArgs {

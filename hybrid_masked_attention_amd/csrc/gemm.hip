@@ -393,6 +393,24 @@ __global__ __launch_bounds__(256, GShape<GBM>::WG_PER_CU) void gemm_bf16_kernel(
         }
       }
     }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // the wave tile's 32-column halves are the gate and up rows of the same 32 hidden
+    // units: a lane holds both for the same row and units, so it writes SiLU(g) * u
+    // as runs of four units
+    const int u0 = nw / 2;
+#pragma unroll
+    for (int a = 0; a < G_TM; ++a) {
+      const int m = mw + a * 32 + l32;
+      if (m >= g.M) continue;
+      bf16* orow = (bf16*)g.out + map_row(cmap, m) * g.ldo + u0 + 4 * hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (bf16)(silu_fast(acc[0][a][4 * j + q]) * acc[1][a][4 * j + q]);
+        *(bf16x4*)(orow + 8 * j) = v;
+      }
+    }
   } else if constexpr (EPI == EPI_STORE) {
 #pragma unroll
     for (int h = 0; h < G_WR / 64; ++h)
@@ -626,6 +644,8 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
         if (g.vt_col0 % G_WC != 0 || g.vt_cols % G_WC != 0 || !aligned16(g.vt) || g.ldvt % 64 != 0) return MTFM_E_UNSUPPORTED;
         if (g.ldvt < g.M) return MTFM_E_UNSUPPORTED;
       }
+    } else if (g.epi == EPI_SWIGLU) {
+      if (g.N % G_WC != 0 || ((uintptr_t)g.out & 7) || g.ldo % 4 != 0) return MTFM_E_UNSUPPORTED;
     } else {
       if (!aligned16(g.out) || g.ldo % 8 != 0) return MTFM_E_UNSUPPORTED;
       if (g.epi == EPI_RESID && (!aligned16(g.resid) || g.ldr % 8 != 0)) return MTFM_E_UNSUPPORTED;
@@ -646,10 +666,13 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
       case 2 * EPI_RESID + 1: gemm_bf16_kernel<EPI_RESID, 128><<<grid, 256, 0, s>>>(g); break;
       case 2 * EPI_STORE_F32: gemm_bf16_kernel<EPI_STORE_F32, 256><<<grid, 256, 0, s>>>(g); break;
       case 2 * EPI_STORE_F32 + 1: gemm_bf16_kernel<EPI_STORE_F32, 128><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_SWIGLU: gemm_bf16_kernel<EPI_SWIGLU, 256><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_SWIGLU + 1: gemm_bf16_kernel<EPI_SWIGLU, 128><<<grid, 256, 0, s>>>(g); break;
       case 2 * EPI_STORE: gemm_bf16_kernel<EPI_STORE, 256><<<grid, 256, 0, s>>>(g); break;
       default: gemm_bf16_kernel<EPI_STORE, 128><<<grid, 256, 0, s>>>(g); break;
     }
   } else {
+    if (g.epi == EPI_SWIGLU) return MTFM_E_UNSUPPORTED;
     const int64_t total = (int64_t)g.M * g.N;
     gemm_f32_kernel<<<dim3((unsigned)((total + 255) / 256), 1, g.groups), 256, 0, s>>>(g);
   }

@@ -263,6 +263,55 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
                               const mtfm_target_grad* tgt_g, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * V2 target side ([blog] §3.3.2 "Target Scale-Up"): a target becomes S = 4
+ * sub-token rows (AutoSplit), every target layer gives each sub-token its own
+ * SwiGLU FFN, RankMixer's zero-parameter token mixing crosses the sub-tokens,
+ * and mean pooling ends the target side.  The page gives no formulas; the
+ * readings: AutoSplit is a bias-free linear map of a parent's feature vector
+ * to S * d_model values, sub-token z taking columns [z d, (z + 1) d); the FFN
+ * is pre-normalised and residual,
+ *   X_T <- X_T + W_down[z] (SiLU(W_gate[z] X~) (.) (W_up[z] X~)),
+ *   X~ = LayerNorm(X_T) (biased variance, eps = dims->ln_eps) * ln_g[T] + ln_b[T],
+ * bias-free, hidden width d_ff, applied to the T rows after each target layer
+ * and followed by the mixing: each sub-token row is cut into S chunks of
+ * d_model / S, and sub-token c becomes the concatenation over z = 0..S-1 of
+ * chunk c of sub-token z (S = 1: nothing).  Pooling: one row per parent, the
+ * mean of its S sub-token rows.  bf16 only; d_ff a multiple of 32; d_model / S
+ * a multiple of 8. */
+typedef struct {
+  const float* ln_g; const float* ln_b;  /* [3][d_model]; the T row is used */
+  const void* w_gate;                    /* [split][d_ff][d_model] */
+  const void* w_up;                      /* [split][d_ff][d_model] */
+  const void* w_down;                    /* [split][d_model][d_ff] */
+} mtfm_ffn_w;
+
+/* AutoSplit: feats [n_parents][d_in] (parents in batch order), w_split
+ * [split * d_model][d_in] -> the T rows of x ([n_rows][d_model] packed rows;
+ * only T rows are written).  d_in a multiple of 32. */
+mtfm_status mtfm_autosplit(const mtfm_batch* batch, const mtfm_dims* dims, int32_t d_in, const void* meta_d,
+                           const void* feats, const void* w_split, void* x, void* stream);
+
+/* One target layer's token FFN and mixing on the T rows of x (packed rows, in
+ * place); ws: mtfm_token_ffn_workspace_bytes. */
+size_t mtfm_token_ffn_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t d_ff);
+mtfm_status mtfm_token_ffn(const mtfm_batch* batch, const mtfm_dims* dims, int32_t d_ff, const void* meta_d,
+                           const mtfm_ffn_w* w, void* x, void* ws, size_t ws_bytes, void* stream);
+
+/* Mean pooling of each parent's sub-token rows of x into out [n_parents][d_model]. */
+mtfm_status mtfm_token_pool(const mtfm_batch* batch, const mtfm_dims* dims, const void* meta_d, const void* x,
+                            void* out, void* stream);
+
+/* The V2 stack: mtfm_backbone_fwd's n_blocks x (1 full + k_target target
+ * layers) with, after every target layer, that layer's token FFN and mixing
+ * (ffn[b * k_target + t]).  1 <= k_target <= 4; ws:
+ * mtfm_backbone_v2_workspace_bytes. */
+size_t mtfm_backbone_v2_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t k_target,
+                                        int32_t d_ff);
+mtfm_status mtfm_backbone_v2_fwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                                 int32_t d_ff, const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                                 const mtfm_ffn_w* ffn, void* x_inout, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Request-level serving with user-side K/V reuse ([explainer] §5.2.3: K/V
  * cache sharing across serving micro-batches; [blog] §3.4 and §4: one
  * user-level sample shares the long-sequence attention among its targets).
@@ -321,7 +370,8 @@ typedef enum {
   MTFM_K_GEMM_T = 6,       /* target layer: U|Q|K|V projection of the T rows */
   MTFM_K_ATTN_TARGET = 7,  /* target layer: masked attention */
   MTFM_K_BWD = 8,          /* backward kernels */
-  MTFM_K_COUNT = 9
+  MTFM_K_V2 = 9,           /* V2 target side: AutoSplit, token FFN, mixing, pooling */
+  MTFM_K_COUNT = 10
 } mtfm_kernel_class;
 
 mtfm_status mtfm_timing_enable(uint32_t class_mask);  /* bit k enables class k; 0 disables all */

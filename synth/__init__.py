@@ -149,6 +149,16 @@ def target_weights(rng, dims: Dims, split: int, w_std: float, wo_std: float) -> 
             "ln2_g": p2["g"], "ln2_b": p2["b"]}
 
 
+def ffn_weights(rng, dims: Dims, split: int, d_ff: int, w_std: float, wo_std: float) -> Dict[str, np.ndarray]:
+    """Per-sub-token SwiGLU FFN of one target layer (V2): gate, up [split][d_ff][d], down [split][d][d_ff]."""
+    d = dims.d_model
+    p = gln_params(rng, d)
+    return {"ln_g": p["g"], "ln_b": p["b"],
+            "w_gate": (w_std * rng.standard_normal((split, d_ff, d))).astype(np.float32),
+            "w_up": (w_std * rng.standard_normal((split, d_ff, d))).astype(np.float32),
+            "w_down": (wo_std * rng.standard_normal((split, d, d_ff))).astype(np.float32)}
+
+
 # --------------------------------------------------------------------------
 # The five workloads.
 
@@ -232,6 +242,35 @@ def config4(seed: int = 4, n_users: int = 64, lens=(4096, 512, 256), arrays: boo
     dy = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
     return Workload("cfg4_long_fwd_bwd_bf16", batch, dims, "bf16", x, full=[full], target=[tgt],
                     n_blocks=1, k_target=1, dy=dy)
+
+
+def config3_v2(seed: int = 3, n_users: int = 160, n_blocks: int = 4, k_target: int = 3, d_in: int = 512,
+               d_ff: int = 1024):
+    """Config 3's users with the V2 target side: each parent a feature vector of width d_in split into
+    4 sub-tokens by AutoSplit, a per-sub-token SwiGLU FFN (hidden d_ff) after every target layer.
+    Returns (workload with the context rows of X filled, T rows zero; parent features; AutoSplit weight;
+    FFN weights per target layer)."""
+    rng = np.random.default_rng(seed)
+    lens = cfg3_lens(rng, n_users)
+    batch = make_batch(rng, lens, 4)
+    dims = Dims(512, 8, 2, 64)
+    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
+    n_layers = n_blocks * (1 + k_target)
+    wo = 0.02 / np.sqrt(n_layers)
+    full, tgt, ffn = [], [], []
+    for _ in range(n_blocks):
+        full.append(full_weights(rng, dims, 0.02, wo))
+        for _ in range(k_target):
+            tgt.append(target_weights(rng, dims, 4, 0.02, wo))
+            ffn.append(ffn_weights(rng, dims, 4, d_ff, 0.02, wo))
+    feats = rng.standard_normal((int(lens[:, 2].sum()), d_in))
+    w_split = (rng.standard_normal((4 * dims.d_model, d_in)) / np.sqrt(d_in)).astype(np.float32)
+    t_rows = np.concatenate([np.arange(batch.row_off[u] + lens[u, 0] + lens[u, 1], batch.row_off[u + 1])
+                             for u in range(n_users)])
+    x[t_rows] = 0.0
+    wl = Workload("cfg3_v2_backbone16_bf16", batch, dims, "bf16", x, full=full, target=tgt, n_blocks=n_blocks,
+                  k_target=k_target)
+    return wl, feats.astype(np.float32), w_split, ffn
 
 
 def random_small(rng, n_users: int, split: int, dims: Dims, max_h=12, max_r=8, max_t=5,
