@@ -225,25 +225,35 @@ __global__ __launch_bounds__(64 * R, AttnShape<QB>::WG_PER_CU) void attn_bf16_ke
   };
   // P chunk c of key block kb: keys kb*32 + 16c + {4hi + t, 8 + 4hi + t : t < 4}, the
   // order in which V^T holds them, so P^T is the B operand of O^T += V^T P^T as is.
-  auto silu_pv = [&](const char* st, int kb, const f32x16* sc, auto masked_tag, int lo, const int* lim,
+  // Masks (template MK): 0 none; 1 keys below lim visible; 2 keys in [lo, lim);
+  // 3 only key dsel (the diagonal tile).  The invisible scores are set to 0
+  // before SiLU (SiLU(0) = 0 exactly), so each mask costs one compare and one
+  // select per element and P still converts to bf16 in pairs.  Register i of
+  // this lane holds key kb*32 + kc(i) + 4*hi with the compile-time
+  // kc(i) = 8*(i/4) + i%4: the bounds are shifted by the lane part once.
+  auto silu_pv = [&](const char* st, int kb, const f32x16* sc, auto mask_tag, int lo, const int* lim,
                      const int* dsel) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int MK = decltype(mask_tag)::value;
     bf16x8 pf[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int shift = kb * 32 + 4 * hi;
+      const int lo_l = lo - shift;
+      const int lim_l = (MK == 1 || MK == 2) ? lim[qb] - shift : 0;
+      const int d_l = MK == 3 ? dsel[qb] - shift : 0;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * c + e;
-          float pv = silu_scaled(sc[qb][i]);
-          if constexpr (MASKED) {
-            const int key = kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const bool vis = (key >= lo && key < lim[qb]) || key == dsel[qb];
-            pv = vis ? pv : 0.f;
-          }
-          pf[qb][c][e] = (bf16)pv;
+          const int kc = 8 * (i >> 2) + (i & 3);
+          float sv = sc[qb][i];
+          if constexpr (MK == 1) sv = kc < lim_l ? sv : 0.f;
+          if constexpr (MK == 2) sv = (kc >= lo_l && kc < lim_l) ? sv : 0.f;
+          if constexpr (MK == 3) sv = kc == d_l ? sv : 0.f;
+          pf[qb][c][e] = (bf16)silu_scaled(sv);
         }
+    }
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -257,34 +267,39 @@ __global__ __launch_bounds__(64 * R, AttnShape<QB>::WG_PER_CU) void attn_bf16_ke
   // QB = 1 issues both key blocks' QK MFMAs before the first block's SiLU (more
   // independent MFMA work per wave); QB = 2 has enough of it per block already
   // and keeps fewer accumulators live.
-  auto tile_body = [&](const char* st, auto masked_tag, int lo, const int* lim, const int* dsel) {
+  auto tile_body = [&](const char* st, auto mask_tag, int lo, const int* lim, const int* dsel) {
     if constexpr (QB == 1) {
       f32x16 sc[2][QB];
       qk(st, 0, sc[0]);
       qk(st, 1, sc[1]);
-      silu_pv(st, 0, sc[0], masked_tag, lo, lim, dsel);
-      silu_pv(st, 1, sc[1], masked_tag, lo, lim, dsel);
+      silu_pv(st, 0, sc[0], mask_tag, lo, lim, dsel);
+      silu_pv(st, 1, sc[1], mask_tag, lo, lim, dsel);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 sc[QB];
         qk(st, kb, sc);
-        silu_pv(st, kb, sc, masked_tag, lo, lim, dsel);
+        silu_pv(st, kb, sc, mask_tag, lo, lim, dsel);
       }
     }
   };
+  using MaskNone = std::integral_constant<int, 0>;
+  using MaskUpper = std::integral_constant<int, 1>;
+  using MaskRange = std::integral_constant<int, 2>;
+  using MaskSelf = std::integral_constant<int, 3>;
 
   int stage = 0;
   for (int it = 0; it < n_main; ++it) {
     const char* st = lds + stage * A_STAGE;
     const int ts = T0 + it * 64;
     if (ts >= urow0 && ts + 64 <= kfull) {
-      tile_body(st, std::false_type{}, 0, nullptr, nullptr);
+      tile_body(st, MaskNone{}, 0, nullptr, nullptr);
     } else {
-      int lim[QB], dsel[QB];
+      int lim[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) { lim[qb] = urow0 + plim[qb] - ts; dsel[qb] = -1; }
-      tile_body(st, std::true_type{}, urow0 - ts, lim, dsel);
+      for (int qb = 0; qb < QB; ++qb) lim[qb] = urow0 + plim[qb] - ts;
+      if (ts >= urow0) tile_body(st, MaskUpper{}, 0, lim, nullptr);   // only the prefix end cuts this tile
+      else tile_body(st, MaskRange{}, urow0 - ts, lim, nullptr);      // the user's first tile
     }
     if (it + 1 < n_main) {
       // tile it + 1 has landed once at most AS - 2 newer tiles' DMA are in flight;
@@ -296,10 +311,10 @@ __global__ __launch_bounds__(64 * R, AttnShape<QB>::WG_PER_CU) void attn_bf16_ke
     }
   }
   if (has_diag) {
-    int lim[QB], dsel[QB];
+    int dsel[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) { lim[qb] = 0; dsel[qb] = selfq[qb] ? qb * 32 + l32 : -1; }
-    tile_body(dlds, std::true_type{}, 0, lim, dsel);
+    for (int qb = 0; qb < QB; ++qb) dsel[qb] = selfq[qb] ? qb * 32 + l32 : -1;
+    tile_body(dlds, MaskSelf{}, 0, nullptr, dsel);
   }
 
   // output: lane = query, four consecutive dims per register group
