@@ -205,118 +205,303 @@ __global__ __launch_bounds__(64 * R, 2) void attn_bwd_dq_kernel(AttnBwdArgs g) {
 }
 
 // --------------------------------------------------------------------------
+// dK / dV kernel.  One workgroup per (64-key context tile, group) with 2 HC
+// waves: wave w takes key half w % 2 (32 keys, lane = key) and head w / 2 of
+// the current chunk of HC heads (all R heads when R <= 4, two passes when
+// R = 8); every wave sums its heads into one dK, dV accumulator.  The user's
+// query tiles that see the keys are walked in stages of 32 queries: per head
+// Q', dA/n hi and lo (32 rows x 128 B each), plus the 32 prefix limits, are
+// brought into an LDS ring by buffer DMA two stages ahead.  S and dP come out
+// with lane = key, so P and dS feed the dV / dK MFMAs straight from registers;
+// the other operand (Q', dA/n with lane = head dimension, 8 queries per lane)
+// is read from the row-major stage with the transposing LDS read.
+constexpr int KV_NS = 3;                   // ring depth (stages)
+constexpr int KV_TENSOR = 32 * 128;        // one 32-row tensor of a head
+constexpr int KV_HEAD = 3 * KV_TENSOR;     // Q', dA/n hi, dA/n lo
+constexpr int KV_CPW = 6;                  // 1 KB DMA chunks per wave per stage
+
+template <int R> struct DkvShape {
+  static constexpr int HC = R < 4 ? R : 4;          // heads per pass
+  static constexpr int NW = 2 * HC;                 // waves
+  static constexpr int STAGE = HC * KV_HEAD + 256;  // + prefix limits (64 lanes x 4 B)
+};
+
+// 16-byte unit u of stage row r sits at slot u ^ kv_swz(r): conflict-free for
+// both the row reads (16 consecutive rows, one unit) and the transposing reads
+// (4 consecutive rows, 4 units).
+MTFM_DEV int kv_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+MTFM_DEV void kv_dma(__amdgpu_buffer_rsrc_t r, lds_void_t* dst, uint32_t voff, int bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (bytes == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+#endif
+}
+
+MTFM_DEV __amdgpu_buffer_rsrc_t kv_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+template <int N> MTFM_DEV void kv_wait_vm() { __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070); }
+MTFM_DEV void kv_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Transposing read ds_read_b64_tr_b16: lanes 4m + c of each 16-lane group
+// point at row m, 4 columns; lane j receives column j of the 4 rows.  The 16
+// reads of a stage (Q' and dA/n hi, 2 x 2 x 2 fragments) are issued together
+// and waited for inside the same block, so their results are complete when it
+// ends.  They are written as one block rather than as separate builtins because
+// the compiler cannot tell that they do not touch the stages still being filled
+// by DMA and would otherwise wait for the whole ring before each of them.
+// a[nb][h2] = LDS address of fragment (c = 0, nb, h2) of Q'; +2048 for c = 1,
+// +4096 for dA/n.
+MTFM_DEV void kv_tr16(const uint32_t (&a)[2][2], i16x4 (&q)[2][2][2], i16x4 (&d)[2][2][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %18\n\t"
+      "ds_read_b64_tr_b16 %3, %19\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %13, %17 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %14, %18 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0][0][0]), "=&v"(q[0][0][1]), "=&v"(q[0][1][0]), "=&v"(q[0][1][1]),
+        "=&v"(q[1][0][0]), "=&v"(q[1][0][1]), "=&v"(q[1][1][0]), "=&v"(q[1][1][1]),
+        "=&v"(d[0][0][0]), "=&v"(d[0][0][1]), "=&v"(d[0][1][0]), "=&v"(d[0][1][1]),
+        "=&v"(d[1][0][0]), "=&v"(d[1][0][1]), "=&v"(d[1][1][0]), "=&v"(d[1][1][1])
+      : "v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1])
+      : "memory");
+}
+
+// The 32 prefix limits of a stage's queries, in this lane's register order:
+// p[4j + t] = limit of query 8j + 4hi + t (a = LDS address of query 4hi).
+MTFM_DEV void kv_plim(uint32_t a, int4 (&p)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:32\n\t"
+      "ds_read_b128 %2, %4 offset:64\n\t"
+      "ds_read_b128 %3, %4 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3])
+      : "v"(a)
+      : "memory");
+}
+
+MTFM_DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
 template <int R>
-__global__ __launch_bounds__(64 * R, 2) void attn_bwd_dkv_kernel(AttnBwdArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16 stage[R][2][DH * VS];  // per wave: Q'^T, dAn^T
+__global__ __launch_bounds__(128 * DkvShape<R>::HC, 1) void attn_bwd_dkv_kernel(AttnBwdArgs g) {
+  using SH = DkvShape<R>;
+  constexpr int HC = SH::HC, NW = SH::NW, STAGE = SH::STAGE;
+  constexpr int NPASS = R / HC;
+  static_assert(12 * HC == KV_CPW * NW, "chunks per stage");
+  __shared__ __attribute__((aligned(1024))) char lds[KV_NS * STAGE];
 
-  const int n_key_tiles_total = g.user[UT_KTILE * (g.n_users + 1) + g.n_users];
-  const int nblocks = n_key_tiles_total * g.G * 2;
-  const int lb = xcd_remap(blockIdx.x, nblocks);
-  const int half = lb & 1;
-  const int ktg = (lb >> 1) / g.G, grp = (lb >> 1) % g.G;
+  // every index below is wave-uniform: readfirstlane keeps the descriptor reads
+  // on the scalar unit, away from the vector-memory counter that paces the ring
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  typedef __attribute__((address_space(4))) const int32_t cint;   // read-only for the whole launch
+  const cint* qtl = (const cint*)g.qtiles;
+  const int ntg = uni(g.user[UT_KTILE * (g.n_users + 1) + g.n_users]);
+  const int lb = xcd_remap(blockIdx.x, ntg * g.G);
+  const int ktg = lb / g.G, grp = lb % g.G;
   const int stride = g.n_users + 1;
-  const int u = upper_index(g.user + UT_KTILE * stride, g.n_users, ktg);
-  const int kt = ktg - g.user[UT_KTILE * stride + u];
-  const int lctx = g.lens[3 * u] + g.lens[3 * u + 1];
-  const int key0 = kt * 64 + half * 32;
-  const int nkeys = min(32, lctx - key0);
-  if (nkeys <= 0) return;
-  const int urow0 = g.user[UT_ROW * stride + u];
+  const int u = uni(upper_index(g.user + UT_KTILE * stride, g.n_users, ktg));
+  const int kt = uni(ktg - g.user[UT_KTILE * stride + u]);
+  const int lctx = uni(g.lens[3 * u] + g.lens[3 * u + 1]);
+  const int urow0 = uni(g.user[UT_ROW * stride + u]);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = grp * R + wave;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave & 1, hw = wave >> 1;
   const int l32 = lane & 31, hi = lane >> 5;
-  const bool kok = l32 < nkeys;
+  const int key0 = kt * 64 + kh * 32;
+  const int key = key0 + l32;                    // this lane's key (context index)
+  const bool kok = key < lctx;
 
   bf16x8 kf[4], vf[4];
   {
-    const bf16* ks = g.k + (int64_t)(urow0 + key0 + (kok ? l32 : 0)) * g.ldk + grp * DH + 8 * hi;
-    const bf16* vs = g.v + (int64_t)(urow0 + key0 + (kok ? l32 : 0)) * g.ldv + grp * DH + 8 * hi;
+    const int64_t row = urow0 + (kok ? key : 0);
+    const bf16* ks = g.k + row * g.ldk + grp * DH + 8 * hi;
+    const bf16* vs = g.v + row * g.ldv + grp * DH + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      kf[kk] = kok ? ld8(ks + kk * 16) : bf16x8{};
-      vf[kk] = kok ? ld8(vs + kk * 16) : bf16x8{};
+      kf[kk] = ld8(ks + kk * 16);
+      vf[kk] = ld8(vs + kk * 16);
     }
   }
-  f32x16 dk[2] = {f32x16{}, f32x16{}}, dv[2] = {f32x16{}, f32x16{}};
-  bf16* Qt = stage[wave][0];
-  bf16* Dt = stage[wave][1];
-  const int key = key0 + l32;  // this lane's key (context index)
 
-  const int qt0 = g.user[g.query_tiles_row * stride + u], qt1 = g.user[g.query_tiles_row * stride + u + 1];
-  for (int qt = qt0; qt < qt1; ++qt) {
-    const int32_t* td = g.qtiles + 8 * qt;
-    if (td[TD_END] <= kt) continue;  // no query of this tile sees the key tile
-    const int nrows = td[TD_NROWS], grow0 = td[TD_GROW0], qrow0 = td[TD_QROW0];
-    const bool masked = !(kt < td[TD_FULL_END] && (kt + 1) * 64 <= lctx);
-    // stage this head's Q'^T and dAn^T (64 queries x 64 dims) transposed
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = lane + 64 * i;            // (query pair, dim chunk)
-      const int qp = c & 31, kc = c >> 5, q = 2 * qp;
-      bf16x8 a0 = q < nrows ? ld8(g.q + (int64_t)(qrow0 + q) * g.ldq + h * DH + kc * 8) : bf16x8{};
-      bf16x8 a1 = q + 1 < nrows ? ld8(g.q + (int64_t)(qrow0 + q + 1) * g.ldq + h * DH + kc * 8) : bf16x8{};
-      bf16x8 b0 = q < nrows ? ld8(g.dan + (int64_t)(qrow0 + q) * g.lddan + h * DH + kc * 8) : bf16x8{};
-      bf16x8 b1 = q + 1 < nrows ? ld8(g.dan + (int64_t)(qrow0 + q + 1) * g.lddan + h * DH + kc * 8) : bf16x8{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        bf16x2 pa, pb;
-        pa[0] = a0[s]; pa[1] = a1[s];
-        pb[0] = b0[s]; pb[1] = b1[s];
-        *(bf16x2*)(&Qt[(kc * 8 + s) * VS + q]) = pa;
-        *(bf16x2*)(&Dt[(kc * 8 + s) * VS + q]) = pb;
-      }
+  // Stage cursor: pass (head chunk), query tile, 32-row half.  Tiles whose
+  // queries see none of the keys are skipped.
+  const int qt0 = uni(g.user[g.query_tiles_row * stride + u]);
+  const int qt1 = uni(g.user[g.query_tiles_row * stride + u + 1]);
+  auto next_tile = [&](int qt) {
+    while (qt < qt1 && uni(qtl[8 * qt + TD_END]) <= kt) qt = uni(qt + 1);
+    return qt;
+  };
+  struct Cur { int pass, qt, sub; };
+  auto advance = [&](Cur& c) {
+    if (c.sub == 0 && uni(qtl[8 * c.qt + TD_NROWS]) > 32) { c.sub = 1; return; }
+    c.sub = 0;
+    c.qt = next_tile(c.qt + 1);
+    if (c.qt >= qt1) { ++c.pass; c.qt = next_tile(qt0); }
+  };
+  const int first = next_tile(qt0);
+  Cur ci{first < qt1 ? 0 : NPASS, first, 0};   // issue cursor
+  Cur cc = ci;                                  // compute cursor
+
+  // DMA lane roles: chunk = 8 rows x 128 B; lane -> row 8 (chunk % 4) + lane / 8, slot lane % 8
+  const int rin = lane >> 3, slot = lane & 7;
+  auto issue = [&](int buf) {
+    // stages past the last one are issued as empty loads (zero-size resources),
+    // so that every wait sees the same number of DMA instructions in flight
+    const bool real = ci.pass < NPASS;
+    int rows = 0, grow = 0;
+    int64_t qrow = 0;
+    if (real) {
+      const cint* td = qtl + 8 * ci.qt;
+      rows = uni(min(32, td[TD_NROWS] - 32 * ci.sub));
+      qrow = uni(td[TD_QROW0] + 32 * ci.sub);
+      grow = uni(td[TD_GROW0] + 32 * ci.sub);
     }
-    __syncthreads();
+    const int hbase = grp * R + (real ? ci.pass : 0) * HC;
+    char* st = lds + buf * STAGE;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qi = qb * 32 + l32;
-      const bool qok = qi < nrows;
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 qa = qok ? ld8(g.q + (int64_t)(qrow0 + qi) * g.ldq + h * DH + kk * 16 + 8 * hi) : bf16x8{};
-        const int64_t doff = (int64_t)(qrow0 + qi) * g.lddan + h * DH + kk * 16 + 8 * hi;
-        const bf16x8 da = qok ? ld8(g.dan + doff) : bf16x8{};
-        const bf16x8 dl = qok ? ld8(g.dan_lo + doff) : bf16x8{};
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dl, vf[kk], dp, 0, 0, 0);
-      }
-      // layout: lane = key (l32), registers = queries qb*32 + 8(i/4) + 4hi + i%4
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 8 * c + e;
-          float pv, dsg;
-          silu_and_grad(s[i], &pv, &dsg);
-          float d = dp[i] * dsg;
-          if (masked) {
-            const int q = qb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const bool vis = q < nrows && key < g.p[grow0 + q];
-            pv = vis ? pv : 0.f;
-            d = vis ? d : 0.f;
-          }
-          pf[c][e] = (bf16)pv;
-          dsf[c][e] = (bf16)d;
-        }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const bf16x8 dt = tr_frag(Dt, nb * 32 + l32, qb * 32 + 16 * c + 4 * hi);
-          const bf16x8 qtf = tr_frag(Qt, nb * 32 + l32, qb * 32 + 16 * c + 4 * hi);
-          dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[c], dt, dv[nb], 0, 0, 0);
-          dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[c], qtf, dk[nb], 0, 0, 0);
-        }
+    for (int i = 0; i < KV_CPW; ++i) {
+      const int c = i * NW + wave;            // chunk of the stage
+      const int hh = c / 12, t = (c % 12) >> 2, rb = c & 3;
+      const bf16* src = t == 0 ? g.q : (t == 1 ? g.dan : g.dan_lo);
+      const int64_t ld = t == 0 ? g.ldq : g.lddan;
+      const __amdgpu_buffer_rsrc_t rs =
+          kv_rsrc(src + qrow * ld + (hbase + hh) * DH, (uint32_t)(rows * ld * 2));
+      const int r = rb * 8 + rin;
+      const uint32_t voff = (uint32_t)(r * ld * 2 + ((slot ^ kv_swz(r)) << 4));
+      kv_dma(rs, (lds_void_t*)(st + hh * KV_HEAD + t * KV_TENSOR + rb * 1024), voff, 16);
     }
+    if (wave == 0) {
+      const __amdgpu_buffer_rsrc_t rs = kv_rsrc(g.p + grow, (uint32_t)(rows * 4));
+      kv_dma(rs, (lds_void_t*)(st + HC * KV_HEAD), (uint32_t)(lane * 4), 4);
+    }
+    if (real) advance(ci);
+  };
+#pragma unroll
+  for (int s = 0; s < KV_NS - 1; ++s) issue(s);
+
+  f32x16 dk[2] = {f32x16{}, f32x16{}}, dv[2] = {f32x16{}, f32x16{}};
+  // row-read offset (A operands: query l32, dims kk*16 + 8hi) and transposing-read offsets
+  const int sw32 = kv_swz(l32);
+  // transposing reads of fragment (c, nb, h2): row 16c + 8h2 + 4hi + m, columns
+  // nb*32 + 16((lane/16)%2) + 4(lane%4) .. + 3, m = (lane/4)%4; c moves the row by 16
+  // (2048 B) without changing the swizzle
+  uint32_t tr_off[2][2];
+  {
+    const int tm = (lane >> 2) & 3, tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r = 8 * h2 + 4 * hi + tm;
+        const int col = nb * 32 + tcol;
+        tr_off[nb][h2] = (uint32_t)(r * 128 + (((col >> 3) ^ kv_swz(r)) << 4) + (col & 7) * 2);
+      }
   }
-  // sum the r heads in a fixed order through LDS, then apply SiLU' of the K / V pre-activations
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(&stage[0][0][0]);  // [R][2][32 keys][64 dims]
+  int it = 0;
+  while (cc.pass < NPASS) {
+    const int buf = it % KV_NS;
+    if (wave == 0) kv_wait_vm<(KV_NS - 2) * (KV_CPW + 1)>();
+    else kv_wait_vm<(KV_NS - 2) * KV_CPW>();
+    kv_barrier();
+    issue((it + KV_NS - 1) % KV_NS);
+    const char* st = lds + buf * STAGE;
+    const char* hb = st + hw * KV_HEAD;
+    const uint32_t hb_addr = lds_addr(hb);
+    const cint* td = qtl + 8 * cc.qt;
+    const bool masked = !(kt < uni(td[TD_FULL_END]) && (kt + 1) * 64 <= lctx);
+
+    f32x16 sc = {}, dp = {};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int off = l32 * 128 + (((2 * kk + hi) ^ sw32) << 4);
+      const bf16x8 qa = *(const bf16x8*)(hb + off);
+      const bf16x8 da = *(const bf16x8*)(hb + KV_TENSOR + off);
+      const bf16x8 dl = *(const bf16x8*)(hb + 2 * KV_TENSOR + off);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sc, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dl, vf[kk], dp, 0, 0, 0);
+    }
+    // layout: lane = key, registers = queries 8(i/4) + 4hi + i%4
+    int plim[16];
+    if (masked) {
+      int4 pv4[4];
+      kv_plim(lds_addr(st + HC * KV_HEAD + 16 * hi), pv4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        plim[4 * j] = pv4[j].x; plim[4 * j + 1] = pv4[j].y; plim[4 * j + 2] = pv4[j].z; plim[4 * j + 3] = pv4[j].w;
+      }
+    }
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * c + e;
+        float pv, dsg;
+        silu_and_grad(sc[i], &pv, &dsg);
+        float d = dp[i] * dsg;
+        if (masked) {
+          const bool vis = key < plim[i];
+          pv = vis ? pv : 0.f;
+          d = vis ? d : 0.f;
+        }
+        pf[c][e] = (bf16)pv;
+        dsf[c][e] = (bf16)d;
+      }
+    // dV += P^T dA/n, dK += dS^T Q' over this stage's 32 queries: k slot (hi, e) of
+    // pf[c] is query 16c + 8(e/4) + 4hi + e%4, the transposing reads match it
+    i16x4 q4[2][2][2], d4[2][2][2];
+    {
+      uint32_t ta[2][2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) ta[nb][h2] = hb_addr + tr_off[nb][h2];
+      kv_tr16(ta, q4, d4);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16x8 qt8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q4[c][nb][0], q4[c][nb][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 dt8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d4[c][nb][0], d4[c][nb][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[c], dt8, dv[nb], 0, 0, 0);
+        dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[c], qt8, dk[nb], 0, 0, 0);
+      }
+    advance(cc);
+    ++it;
+  }
+  // drain the ring (the last issued stages are empty), then sum the heads of
+  // each key half in a fixed order and apply SiLU' of the K / V pre-activations
+  kv_wait_vm<0>();
+  kv_barrier();
+  float* red = reinterpret_cast<float*>(lds);   // [NW][2][32 keys][64 dims]
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -326,15 +511,16 @@ __global__ __launch_bounds__(64 * R, 2) void attn_bwd_dkv_kernel(AttnBwdArgs g) 
       red[((wave * 2 + 1) * 32 + kr) * DH + nb * 32 + l32] = dv[nb][i];
     }
   __syncthreads();
-  for (int e = tid; e < 32 * DH; e += 64 * R) {
-    const int kr = e / DH, c = e % DH;
-    if (kr >= nkeys) continue;
+  for (int e = tid; e < 64 * DH; e += 64 * NW) {
+    const int kr64 = e / DH, c = e % DH;
+    const int half = kr64 >> 5, kr = kr64 & 31;
+    if (kt * 64 + kr64 >= lctx) continue;
     float sk = 0.f, sv = 0.f;
-    for (int w = 0; w < R; ++w) {
-      sk += red[((w * 2 + 0) * 32 + kr) * DH + c];
-      sv += red[((w * 2 + 1) * 32 + kr) * DH + c];
+    for (int w = 0; w < HC; ++w) {
+      sk += red[(((2 * w + half) * 2 + 0) * 32 + kr) * DH + c];
+      sv += red[(((2 * w + half) * 2 + 1) * 32 + kr) * DH + c];
     }
-    const int64_t row = urow0 + key0 + kr;
+    const int64_t row = urow0 + kt * 64 + kr64;
     const float hk = (float)g.hk[row * g.ldhk + grp * DH + c];
     const float hv = (float)g.hv[row * g.ldhv + grp * DH + c];
     g.dhk[row * g.lddhk + grp * DH + c] = (bf16)(sk * kLn2 * dsilu_f(hk));
@@ -381,7 +567,7 @@ mtfm_status launch_r(const AttnBwdArgs& a, int64_t n_key_tiles, hipStream_t s) {
     MTFM_LAUNCH_CHECK("attn_bwd_dq");
   }
   if (n_key_tiles > 0 && a.nqtiles > 0) {
-    attn_bwd_dkv_kernel<R><<<(unsigned)(n_key_tiles * a.G * 2), 64 * R, 0, s>>>(a);
+    attn_bwd_dkv_kernel<R><<<(unsigned)(n_key_tiles * a.G), 128 * DkvShape<R>::HC, 0, s>>>(a);
     MTFM_LAUNCH_CHECK("attn_bwd_dkv");
   }
   if (a.n_self_rows > 0) {
