@@ -50,6 +50,18 @@ MTFM_DEV void silu_and_grad(float sp, float* p, float* dp) {
   *dp = sg * (1.0f + x * (1.0f - sg));
 }
 
+// The same pair with SiLU scaled by 1/ln2 (callers fold ln2 in later), in
+// fewer operations: SiLU(x)/ln2 = s' sg and SiLU'(x) = sg + (s' sg) ln2 (1 - sg).
+// A masked pair is given the score kMaskedScore: 2^512 overflows to +inf, the
+// sigmoid is then exactly 0 and both results are 0.
+constexpr float kMaskedScore = -512.0f;
+MTFM_DEV void silu_grad_scaled(float sp, float* p_ln2, float* dp) {
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-sp));
+  const float q = sp * sg;
+  *p_ln2 = q;
+  *dp = __builtin_fmaf(q, __builtin_fmaf(-kLn2, sg, kLn2), sg);
+}
+
 MTFM_DEV bf16x8 ld8(const bf16* p) { return *(const bf16x8*)p; }
 
 MTFM_DEV bf16x8 tr_frag(const bf16* base, int row, int col) {
@@ -167,6 +179,12 @@ __global__ __launch_bounds__(64 * R, 2) void attn_bwd_dq_kernel(AttnBwdArgs g) {
         dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[kk], dpt, 0, 0, 0);
         dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dl[kk], dpt, 0, 0, 0);
       }
+      if (masked) {
+        // keys of register i: kb*32 + 8(i/4) + 4hi + i%4; shift the bound once
+        const int lim_l = lim - kb * 32 - 4 * hi;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[i] = 8 * (i >> 2) + (i & 3) < lim_l ? st[i] : kMaskedScore;
+      }
       bf16x8 dsf[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -174,13 +192,8 @@ __global__ __launch_bounds__(64 * R, 2) void attn_bwd_dq_kernel(AttnBwdArgs g) {
         for (int s = 0; s < 8; ++s) {
           const int i = 8 * c + s;
           float pv, dsg;
-          silu_and_grad(st[i], &pv, &dsg);
-          float d = dpt[i] * dsg;
-          if (masked) {
-            const int key = kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            d = key < lim ? d : 0.f;
-          }
-          dsf[c][s] = (bf16)d;
+          silu_grad_scaled(st[i], &pv, &dsg);
+          dsf[c][s] = (bf16)(dpt[i] * dsg);
         }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -448,7 +461,7 @@ __global__ __launch_bounds__(128 * DkvShape<R>::HC, 1) void attn_bwd_dkv_kernel(
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dl, vf[kk], dp, 0, 0, 0);
     }
     // layout: lane = key, registers = queries 8(i/4) + 4hi + i%4
-    int plim[16];
+    int plim[16] = {};
     if (masked) {
       int4 pv4[4];
       kv_plim(lds_addr(st + HC * KV_HEAD + 16 * hi), pv4);
@@ -457,6 +470,11 @@ __global__ __launch_bounds__(128 * DkvShape<R>::HC, 1) void attn_bwd_dkv_kernel(
         plim[4 * j] = pv4[j].x; plim[4 * j + 1] = pv4[j].y; plim[4 * j + 2] = pv4[j].z; plim[4 * j + 3] = pv4[j].w;
       }
     }
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = key < plim[i] ? sc[i] : kMaskedScore;
+    }
+    // P is kept as P / ln2 (ln2 applied to dV at the end)
     bf16x8 pf[2], dsf[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -464,15 +482,9 @@ __global__ __launch_bounds__(128 * DkvShape<R>::HC, 1) void attn_bwd_dkv_kernel(
       for (int e = 0; e < 8; ++e) {
         const int i = 8 * c + e;
         float pv, dsg;
-        silu_and_grad(sc[i], &pv, &dsg);
-        float d = dp[i] * dsg;
-        if (masked) {
-          const bool vis = key < plim[i];
-          pv = vis ? pv : 0.f;
-          d = vis ? d : 0.f;
-        }
+        silu_grad_scaled(sc[i], &pv, &dsg);
         pf[c][e] = (bf16)pv;
-        dsf[c][e] = (bf16)d;
+        dsf[c][e] = (bf16)(dp[i] * dsg);
       }
     // dV += P^T dA/n, dK += dS^T Q' over this stage's 32 queries: k slot (hi, e) of
     // pf[c] is query 16c + 8(e/4) + 4hi + e%4, the transposing reads match it
@@ -524,7 +536,7 @@ __global__ __launch_bounds__(128 * DkvShape<R>::HC, 1) void attn_bwd_dkv_kernel(
     const float hk = (float)g.hk[row * g.ldhk + grp * DH + c];
     const float hv = (float)g.hv[row * g.ldhv + grp * DH + c];
     g.dhk[row * g.lddhk + grp * DH + c] = (bf16)(sk * kLn2 * dsilu_f(hk));
-    g.dhv[row * g.lddhv + grp * DH + c] = (bf16)(sv * dsilu_f(hv));
+    g.dhv[row * g.lddhv + grp * DH + c] = (bf16)(sv * kLn2 * dsilu_f(hv));
   }
 }
 
