@@ -70,13 +70,14 @@ BwdWs bwd_layout(const MetaPlan& p, const mtfm_dims* d, int op) {
 
 RowMap list_map(const int32_t* list, int div = 1, int add = 0) { return RowMap{list, 0, add, div}; }
 
+// C = sum over r < R of A[am(r)]^T B[bm(r)]; a_rows, b_rows = rows of the A, B buffers
 mtfm_status tn(hipStream_t s, const BwdWs& L, char* ws, int M, int N, int R, const void* A, int64_t lda, RowMap am,
-               const void* B, int64_t ldb, RowMap bm, float* C, int accumulate, int groups = 1, int azadd = 0,
-               int bzadd = 0, int64_t czoff = 0) {
+               int64_t a_rows, const void* B, int64_t ldb, RowMap bm, int64_t b_rows, float* C, int accumulate,
+               int groups = 1, int azadd = 0, int bzadd = 0, int64_t czoff = 0) {
   GemmTNArgs t{};
   t.M = M; t.N = N; t.R = R; t.groups = groups;
-  t.A = A; t.lda = lda; t.amap = am; t.amap_zadd = azadd;
-  t.B = B; t.ldb = ldb; t.bmap = bm; t.bmap_zadd = bzadd;
+  t.A = A; t.lda = lda; t.amap = am; t.amap_zadd = azadd; t.a_rows = a_rows;
+  t.B = B; t.ldb = ldb; t.bmap = bm; t.bmap_zadd = bzadd; t.b_rows = b_rows;
   t.C = C; t.ldc = N; t.c_zoff = czoff; t.accumulate = accumulate;
   t.partial = (float*)(ws + L.part); t.partial_elems = L.part_elems;
   TimedLaunch tl(MTFM_K_BWD, s);
@@ -167,7 +168,7 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
   TRY(timed_gln(g2, MTFM_BF16, s));
 
   // ---- output projection
-  TRY(tn(s, L, ws, D, hd, R, dy, D, identity_map(), y, hd, identity_map(), gr->w_o, 0));
+  TRY(tn(s, L, ws, D, hd, R, dy, D, identity_map(), R, y, hd, identity_map(), R, gr->w_o, 0));
   TRY(transpose(s, w->w_o, D, nullptr, 0, nullptr, 0, hd, wot, D));
   {
     GemmArgs gd_{};
@@ -213,7 +214,7 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
     TRY(launch_dq_finish(f, s));
   }
   // ---- input projection and GLN1
-  TRY(tn(s, L, ws, zw, D, R, dh_, zw, identity_map(), xt, D, identity_map(), gr->w_uqkv, 0));
+  TRY(tn(s, L, ws, zw, D, R, dh_, zw, identity_map(), R, xt, D, identity_map(), R, gr->w_uqkv, 0));
   TRY(transpose(s, w->w_uqkv, zw, nullptr, 0, nullptr, 0, D, w1t, zw));
   {
     GemmArgs gx{};
@@ -319,7 +320,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
 
   // ---- output projection (T rows only; H/R rows pass dY through unchanged)
   if (T > 0) {
-    TRY(tn(s, L, ws, D, hd, T, dy, D, t_rows, y, hd, identity_map(), gr->w_o, 0));
+    TRY(tn(s, L, ws, D, hd, T, dy, D, t_rows, R, y, hd, identity_map(), T, gr->w_o, 0));
     TRY(transpose(s, w->w_o, D, nullptr, 0, nullptr, 0, hd, wot, D));
     GemmArgs gd_{};
     gd_.M = T; gd_.N = hd; gd_.K = D; gd_.groups = 1;
@@ -376,17 +377,17 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
 
   // ---- weight gradients of the input projections
   if (T > 0) {
-    TRY(tn(s, L, ws, hd, D, T, dht, zw, identity_map(), xt, D, t_rows, gr->w_u, 0));
+    TRY(tn(s, L, ws, hd, D, T, dht, zw, identity_map(), T, xt, D, t_rows, R, gr->w_u, 0));
     // W_q[k]: rows of sub-token k, T row S*m + k, packed row parent_row[m] + k
-    TRY(tn(s, L, ws, hd, D, P, dht + hd, zw, RowMap{nullptr, S, 0, 0}, xt, D, list_map(c.meta.parent_row), gr->w_q, 0,
+    TRY(tn(s, L, ws, hd, D, P, dht + hd, zw, RowMap{nullptr, S, 0, 0}, T, xt, D, list_map(c.meta.parent_row), R, gr->w_q, 0,
            S, 1, 1, (int64_t)hd * D));
   } else {
     hipError_t e = hipMemsetAsync(gr->w_u, 0, (size_t)hd * D * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(gr->w_q, 0, (size_t)S * hd * D * 4, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
   }
-  if (C > 0) TRY(tn(s, L, ws, 2 * gd, D, C, dhkv, 2 * gd, ctx_rows, xt, D, ctx_rows, gr->w_kv, 0));
-  if (T > 0) TRY(tn(s, L, ws, 2 * gd, D, T, dht + 2 * hd, zw, identity_map(), xt, D, t_rows, gr->w_kv, C > 0 ? 1 : 0));
+  if (C > 0) TRY(tn(s, L, ws, 2 * gd, D, C, dhkv, 2 * gd, ctx_rows, R, xt, D, ctx_rows, R, gr->w_kv, 0));
+  if (T > 0) TRY(tn(s, L, ws, 2 * gd, D, T, dht + 2 * hd, zw, identity_map(), T, xt, D, t_rows, R, gr->w_kv, C > 0 ? 1 : 0));
   if (C == 0 && T == 0) {
     hipError_t e = hipMemsetAsync(gr->w_kv, 0, (size_t)2 * gd * D * 4, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");

@@ -62,6 +62,7 @@ struct GemmTNArgs {
   const void* A; int64_t lda; RowMap amap; int32_t amap_zadd;
   int64_t a_zoff;                 // element offset per group
   const void* B; int64_t ldb; RowMap bmap; int32_t bmap_zadd;
+  int64_t a_rows, b_rows;         // rows of the A and B buffers (bounds the loads); 0 if unknown
   float* C; int64_t ldc; int64_t c_zoff; int32_t accumulate;
   float* partial; int64_t partial_elems;   // workspace for split partial sums
 };

@@ -541,6 +541,197 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(GemmTNArgs g, int n_spl
   }
 }
 
+// Weight-gradient GEMM, DMA form.  Same tiles, splits and partial layout as
+// above; the 32-row steps of A and B are copied row-major into a three-stage
+// LDS ring by buffer DMA (rows past the split's end and columns past M / N read
+// as zeros), and the MFMA operands -- 8 consecutive r of one column per lane --
+// come out of it through the transposing LDS read.  The split's row indices
+// (row maps applied) sit in a table of their own, so reading them never waits
+// for the DMA.
+constexpr int TD_NS = 3;
+static_assert(TN_ROWS_PER_SPLIT % 256 == 0, "row table fill");
+constexpr int TD_TILE = 32 * 256;     // 32 rows x 128 bf16 columns
+constexpr int TD_STAGE = 2 * TD_TILE;  // A, then B
+
+// 16-byte unit u of tile row r sits at slot u ^ 4 (r % 4): the four rows of one
+// transposing read then fall in four different quarters of the banks.
+MTFM_DEV int td_swz(int r) { return (r & 3) << 2; }
+
+typedef short td_i16x4 __attribute__((ext_vector_type(4)));
+
+// The 16 transposing reads of one stage for one wave: fragment f (0, 1: A
+// column blocks mb; 2, 3: B column blocks nb) at LDS address a[f], plus 4096 B
+// for the second 16 rows (kk = 1) and 1024 B for rows 4..7 of each 8 (h = 1).
+// One block with its own wait: the compiler would otherwise wait for every DMA
+// in flight before each read (it cannot tell which ring stage a read touches).
+MTFM_DEV void td_tr16(const uint32_t (&a)[4], td_i16x4 (&o)[2][4][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %10, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %12, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %13, %18 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:5120\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0][0][0]), "=&v"(o[0][0][1]), "=&v"(o[0][1][0]), "=&v"(o[0][1][1]),
+        "=&v"(o[0][2][0]), "=&v"(o[0][2][1]), "=&v"(o[0][3][0]), "=&v"(o[0][3][1]),
+        "=&v"(o[1][0][0]), "=&v"(o[1][0][1]), "=&v"(o[1][1][0]), "=&v"(o[1][1][1]),
+        "=&v"(o[1][2][0]), "=&v"(o[1][2][1]), "=&v"(o[1][3][0]), "=&v"(o[1][3][1])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
+__global__ __launch_bounds__(256, 2) void gemm_tn_dma_kernel(GemmTNArgs g, int n_split) {
+  __shared__ __attribute__((aligned(1024))) char ring[TD_NS * TD_STAGE];
+  __shared__ int32_t rowtab[2][TN_ROWS_PER_SPLIT];
+  const int z = blockIdx.z;
+  const int n_mt = (g.M + BM - 1) / BM, n_nt = (g.N + BN - 1) / BN;
+  const int tiles = n_mt * n_nt;
+  const int split = blockIdx.x / tiles, t = blockIdx.x % tiles;
+  const int mt = t / n_nt, nt = t % n_nt;
+  const int m0 = mt * BM, n0 = nt * BN;
+  RowMap amap = g.amap; amap.add += z * g.amap_zadd;
+  RowMap bmap = g.bmap; bmap.add += z * g.bmap_zadd;
+  const int r_begin = split * TN_ROWS_PER_SPLIT, r_end = min(g.R, r_begin + TN_ROWS_PER_SPLIT);
+  const int nrows = r_end - r_begin;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int hi = lane >> 5;
+
+  {
+    // all loads of the row lists first, then the table writes
+    constexpr int PER = TN_ROWS_PER_SPLIT / 256;
+    int32_t av[PER], bv[PER];
+    auto fill = [&](const RowMap& m, int32_t (&v)[PER]) {
+      if (m.list) {
+        const int dv = max(m.div, 1);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          const int r = r_begin + min(tid + 256 * k, nrows - 1);   // entries past the end unused
+          v[k] = m.list[r / dv] + r % dv + m.add;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[k] = (r_begin + tid + 256 * k) * m.mul + m.add;
+      }
+    };
+    if (nrows > 0) {
+      fill(amap, av);
+      fill(bmap, bv);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      rowtab[0][tid + 256 * k] = av[k];
+      rowtab[1][tid + 256 * k] = bv[k];
+    }
+  }
+  __syncthreads();
+
+  const int64_t a_shift = (int64_t)z * g.a_zoff;
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc((const bf16*)g.A + a_shift, (uint32_t)(g.a_rows * g.lda * 2 - a_shift * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)(g.b_rows * g.ldb * 2));
+  // DMA lanes: chunk c (of 8 per tile) = rows 4c .. 4c + 3; lane -> row 4c + lane/16,
+  // slot lane % 16, holding columns 8 (slot ^ swz(row)) .. + 7
+  const int rq = lane >> 4;
+  const int lu = (lane & 15) ^ td_swz(rq);
+  const bool a_col = m0 + 8 * lu < g.M, b_col = n0 + 8 * lu < g.N;
+  const int nst = (nrows + 31) >> 5;
+  auto issue = [&](int st_i) {
+    char* st = ring + (st_i % TD_NS) * TD_STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 4 + wave;
+      const int rr = st_i * 32 + 4 * c + rq;     // row within the split
+      const bool ok = st_i < nst && rr < nrows;
+      const uint32_t ao = ok && a_col ? (uint32_t)(rowtab[0][rr] * g.lda * 2 + (m0 + 8 * lu) * 2) : kOobOffset;
+      const uint32_t bo = ok && b_col ? (uint32_t)(rowtab[1][rr] * g.ldb * 2 + (n0 + 8 * lu) * 2) : kOobOffset;
+      lds_dma16(ra, (lds_void*)(st + c * 1024), ao, 0);
+      lds_dma16(rb, (lds_void*)(st + TD_TILE + c * 1024), bo, 0);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < TD_NS - 1; ++s) issue(s);
+
+  // transposing-read addresses: column block start + 16 ((lane/16) % 2) + 4 (lane % 4),
+  // rows 8 hi + (lane/4) % 4 (+ 16 kk + 4 h as immediates, which keep row % 4)
+  uint32_t tro[4];
+  {
+    const int r = 8 * hi + ((lane >> 2) & 3);
+    const int cw = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int col = (f < 2 ? wm * 64 + f * 32 : wn * 64 + (f - 2) * 32) + cw;
+      tro[f] = (uint32_t)((f < 2 ? 0 : TD_TILE) + r * 256 + (((col >> 3) ^ td_swz(r)) << 4) + (col & 7) * 2);
+    }
+  }
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)ring;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  for (int it = 0; it < nst; ++it) {
+    wait_vm_lgkm<(TD_NS - 2) * 4>();
+    barrier_only();
+    issue(it + TD_NS - 1);
+    uint32_t a4[4];
+    const uint32_t sb = ring_addr + (uint32_t)((it % TD_NS) * TD_STAGE);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) a4[f] = sb + tro[f];
+    td_i16x4 fr[2][4][2];
+    td_tr16(a4, fr);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 op[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        op[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(fr[kk][f][0], fr[kk][f][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      // C^T tiles: lane = m, registers = four consecutive n
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[2 + nb], op[mb], acc[nb][mb], 0, 0, 0);
+    }
+  }
+  wait_vm_lgkm<0>();   // the ring's trailing (empty) loads land before the workgroup ends
+  const int l32 = lane & 31;
+  float* P = g.partial + ((int64_t)z * n_split + split) * (int64_t)g.M * g.N;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = m0 + wm * 64 + mb * 32 + l32;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int nblk = n0 + wn * 64 + nb * 32;
+      if (nblk >= g.N) continue;
+      float* dst = P + (int64_t)m * g.N + nblk + 4 * hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[nb][mb][4 * j + q];
+        *(f32x4*)(dst + 8 * j) = v;
+      }
+    }
+  }
+}
+
 // C (+)= sum over splits of the partials, in split order.
 __global__ __launch_bounds__(256) void gemm_tn_reduce_kernel(GemmTNArgs g, int n_split) {
   const int z = blockIdx.y;
@@ -594,6 +785,8 @@ int device_cu_count() {
   return cached[dev];
 }
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 int64_t gemm_tn_partial_elems(int32_t M, int32_t N, int32_t R, int32_t groups) {
   const int64_t n_split = std::max<int64_t>(1, (R + TN_ROWS_PER_SPLIT - 1) / TN_ROWS_PER_SPLIT);
   return n_split * (int64_t)M * N * groups;
@@ -606,15 +799,23 @@ mtfm_status launch_gemm_tn(const GemmTNArgs& g, hipStream_t s) {
   const int n_split = std::max(1, (g.R + TN_ROWS_PER_SPLIT - 1) / TN_ROWS_PER_SPLIT);
   if (gemm_tn_partial_elems(g.M, g.N, g.R, g.groups) > g.partial_elems) return MTFM_E_WORKSPACE;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  gemm_tn_kernel<<<dim3(tiles * n_split, 1, g.groups), 256, 0, s>>>(g, n_split);
-  MTFM_LAUNCH_CHECK("gemm_tn");
+  // the DMA form needs the operands' row counts (its loads are bounded by them,
+  // with 32-bit offsets) and 16-byte aligned rows
+  const int64_t a_bytes = g.a_rows * g.lda * 2, b_bytes = g.b_rows * g.ldb * 2;
+  const bool dma = g.a_rows > 0 && g.b_rows > 0 && a_bytes < (int64_t)kOobOffset && b_bytes < (int64_t)kOobOffset &&
+                   g.a_zoff == 0 && aligned16(g.A) && aligned16(g.B);
+  if (dma) {
+    gemm_tn_dma_kernel<<<dim3(tiles * n_split, 1, g.groups), 256, 0, s>>>(g, n_split);
+    MTFM_LAUNCH_CHECK("gemm_tn_dma");
+  } else {
+    gemm_tn_kernel<<<dim3(tiles * n_split, 1, g.groups), 256, 0, s>>>(g, n_split);
+    MTFM_LAUNCH_CHECK("gemm_tn");
+  }
   const int64_t mn4 = ((int64_t)g.M * g.N) / 4;
   gemm_tn_reduce_kernel<<<dim3((unsigned)((mn4 + 255) / 256), g.groups), 256, 0, s>>>(g, n_split);
   MTFM_LAUNCH_CHECK("gemm_tn_reduce");
   return MTFM_OK;
 }
-
-static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.groups <= 0) return MTFM_OK;
