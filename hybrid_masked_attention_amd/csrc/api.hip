@@ -202,7 +202,7 @@ mtfm_status prepare(const mtfm_batch* b, const mtfm_dims* d, const void* meta_d,
 // default; MTFM_ATTN_FULL_QB=2 selects 64 queries per wave (half the
 // workgroups, more registers).  A tuning knob: both shapes compute the same.
 // Read at every call, so one process can run both shapes.
-static int full_attn_half_tiles() {
+int full_attn_half_tiles() {
   const char* e = std::getenv("MTFM_ATTN_FULL_QB");
   return (e && e[0] == '2') ? 0 : 1;
 }
@@ -212,7 +212,7 @@ static int full_attn_half_tiles() {
 //   X~ = GLN1(X); [U|Q|K|V] = SiLU(X~ W^T); A = masked SiLU attention / n;
 //   X' = (GLN2(A) (.) U) W_o^T + X
 mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out,
-                     char* ws, const KvOut* kv) {
+                     char* ws, const KvOut* kv, void* a_keep) {
   const MetaPlan& p = c.plan;
   const int dt = d->dtype;
   const int64_t es = elem_size(dt);
@@ -221,7 +221,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   const LayerWs L = layer_ws(p, d, MTFM_OP_FULL);
   char* xt = ws + L.xt;
   char* z = ws + L.z;
-  char* a = ws + L.a;
+  char* a = a_keep ? (char*)a_keep : ws + L.a;
   char* y = ws + L.y;
   if (p.n_rows == 0) return MTFM_OK;
 
@@ -290,7 +290,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
 //   [U_T|Q_T|K_T|V_T] = SiLU(X~_T [W_u; W_q[k]; W_kv]^T) per sub-token k;
 //   A_T = masked attention; X'_T = (GLN2(A_T) (.) U_T) W_o^T + X_T.
 mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in, void* x_out,
-                       char* ws) {
+                       char* ws, void* a_keep) {
   const MetaPlan& p = c.plan;
   const int dt = d->dtype;
   const int64_t es = elem_size(dt);
@@ -301,7 +301,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   char* xt = ws + L.xt;
   char* kv = ws + L.kv;
   char* zt = ws + L.z;
-  char* a = ws + L.a;
+  char* a = a_keep ? (char*)a_keep : ws + L.a;
   char* y = ws + L.y;
   if (x_out != x_in && p.n_rows > 0) {
     hipError_t e = hipMemcpyAsync(x_out, x_in, (size_t)p.n_rows * D * es, hipMemcpyDeviceToDevice, c.s);
@@ -858,16 +858,25 @@ mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims,
 // (bf16, as the forward hands it on), then the layers' backward run from the
 // last to the first, each taking the next layer's input gradient as its
 // upstream gradient.  Workspace: the largest single-layer workspace, the
-// inputs of layers 1 .. L-1, and one gradient buffer (the caller's dx is the
-// other one of the pair).
+// inputs of layers 1 .. L-1, one gradient buffer (the caller's dx is the
+// other one of the pair) and the attention outputs of layers 0 .. L-2.
 namespace {
 
+// Besides the layer inputs, the forward pass keeps each layer's attention
+// output A (packed rows for a full layer, T rows for a target layer), so the
+// backward does not recompute the attention.
 struct BackboneBwdWs {
-  int64_t layer = 0, stash = 0, xbytes = 0, gbuf = 0, total = 0;
+  int64_t layer = 0, stash = 0, xbytes = 0, gbuf = 0, astash = 0, afull = 0, atarget = 0, total = 0;
+  int per = 1;
+  int64_t a_off(int l) const {   // A of layer l (l < L - 1)
+    const int nf = (l + per - 1) / per;   // full layers before l
+    return astash + nf * afull + (l - nf) * atarget;
+  }
 };
 
-BackboneBwdWs backbone_bwd_ws(const MetaPlan& p, const mtfm_dims* d, int n_layers) {
+BackboneBwdWs backbone_bwd_ws(const MetaPlan& p, const mtfm_dims* d, int n_blocks, int k_target) {
   BackboneBwdWs w;
+  const int n_layers = n_blocks * (1 + k_target);
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
   const int64_t lw = std::max(std::max(layer_ws(p, d, MTFM_OP_FULL).total, layer_ws(p, d, MTFM_OP_TARGET).total),
@@ -876,6 +885,12 @@ BackboneBwdWs backbone_bwd_ws(const MetaPlan& p, const mtfm_dims* d, int n_layer
   w.xbytes = align_up(p.n_rows * d->d_model * elem_size(d->dtype), 256);
   w.stash = take(std::max(n_layers - 1, 0) * w.xbytes);
   w.gbuf = take(w.xbytes);
+  const int64_t hd = (int64_t)d->n_q_heads * d->head_dim;
+  w.per = 1 + k_target;
+  w.afull = align_up(p.n_rows * hd * 2, 256);
+  w.atarget = align_up(p.n_t_rows * hd * 2, 256);
+  w.astash = off;
+  if (n_layers > 1) off = align_up(w.a_off(n_layers - 1), 256);
   w.total = off;
   return w;
 }
@@ -887,7 +902,7 @@ size_t mtfm_backbone_bwd_workspace_bytes(const mtfm_batch* batch, const mtfm_dim
   MetaPlan p;
   if (n_blocks < 0 || k_target < 0 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
   if (bwd_ws_bytes(p, dims, MTFM_OP_FULL_BWD) == 0) return 0;   // shapes the backward does not support
-  return (size_t)backbone_bwd_ws(p, dims, n_blocks * (1 + k_target)).total;
+  return (size_t)backbone_bwd_ws(p, dims, n_blocks, k_target).total;
 }
 
 mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
@@ -915,7 +930,7 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
     }
   }
   const int L = n_blocks * (1 + k_target);
-  const BackboneBwdWs W = backbone_bwd_ws(c.plan, dims, L);
+  const BackboneBwdWs W = backbone_bwd_ws(c.plan, dims, n_blocks, k_target);
   if (W.total > 0 && !ws) return MTFM_E_NULL;
   if (ws_bytes < (size_t)W.total) return MTFM_E_WORKSPACE;
   c.b = batch;
@@ -932,19 +947,22 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
   auto input_of = [&](int l) -> const void* { return l == 0 ? x_in : (const void*)(w + W.stash + (l - 1) * W.xbytes); };
   // gradient buffers alternate so that layer 0 writes dx
   auto grad_buf = [&](int l) -> void* { return (l % 2 == 0) ? dx : (void*)(w + W.gbuf); };
+  // A of layer l as kept by the forward pass (none for the last layer, whose
+  // forward is not run here: its backward recomputes it)
+  auto a_of = [&](int l) -> char* { return l + 1 < L ? w + W.a_off(l) : nullptr; };
   for (int l = 0; l + 1 < L; ++l) {
     void* out = w + W.stash + l * W.xbytes;
     const int b = l / per, t = l % per;
-    if (t == 0) TRY(run_full(c, dims, &full[b], input_of(l), out, w + W.layer));
-    else TRY(run_target(c, dims, &tgt[b * k_target + t - 1], input_of(l), out, w + W.layer));
+    if (t == 0) TRY(run_full(c, dims, &full[b], input_of(l), out, w + W.layer, nullptr, a_of(l)));
+    else TRY(run_target(c, dims, &tgt[b * k_target + t - 1], input_of(l), out, w + W.layer, a_of(l)));
   }
   for (int l = L - 1; l >= 0; --l) {
     const void* g_in = l == L - 1 ? dy : grad_buf(l + 1);
     void* g_out = grad_buf(l);
     const int b = l / per, t = l % per;
-    if (t == 0) TRY(run_full_bwd(c, dims, &full[b], input_of(l), g_in, g_out, &full_g[b], w + W.layer));
+    if (t == 0) TRY(run_full_bwd(c, dims, &full[b], input_of(l), g_in, g_out, &full_g[b], w + W.layer, a_of(l)));
     else TRY(run_target_bwd(c, dims, &tgt[b * k_target + t - 1], input_of(l), g_in, g_out,
-                            &tgt_g[b * k_target + t - 1], w + W.layer));
+                            &tgt_g[b * k_target + t - 1], w + W.layer, a_of(l)));
   }
   return MTFM_OK;
 }

@@ -48,17 +48,24 @@ struct KvOut {
   void* vt = nullptr;
   int64_t ldvt = 0;
 };
+// a_keep: if set, the attention output A (query rows x H*dh, bf16) is written
+// there instead of the workspace, for a backward pass to reuse.
 mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out, char* ws,
-                     const KvOut* kv = nullptr);
+                     const KvOut* kv = nullptr, void* a_keep = nullptr);
 mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in, void* x_out,
-                       char* ws);
+                       char* ws, void* a_keep = nullptr);
+// Workgroup shape of the full-layer attention (1: 32 queries per wave); the
+// backward's recompute takes the same shape, so a kept A equals a recomputed one.
+int full_attn_half_tiles();
 
-// backward (bwd.hip)
+// backward (bwd.hip); a_pre: the layer's attention output from its forward pass
+// (as kept by run_full / run_target), else it is recomputed
 int64_t bwd_ws_bytes(const MetaPlan& p, const mtfm_dims* d, int op);
 mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, const void* dy,
-                         void* dx, const mtfm_full_grad* g, char* ws);
+                         void* dx, const mtfm_full_grad* g, char* ws, const void* a_pre = nullptr);
 mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in,
-                           const void* dy, void* dx, const mtfm_target_grad* g, char* ws);
+                           const void* dy, void* dx, const mtfm_target_grad* g, char* ws,
+                           const void* a_pre = nullptr);
 
 // RAII bracket of one launch with HIP events when its kernel class is enabled
 // (see mtfm_timing_enable); a no-op otherwise.

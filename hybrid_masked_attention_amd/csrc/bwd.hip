@@ -111,7 +111,7 @@ int64_t bwd_ws_bytes(const MetaPlan& p, const mtfm_dims* d, int op) {
 
 // ---------------------------------------------------------------------------
 mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, const void* dy,
-                         void* dx, const mtfm_full_grad* gr, char* ws) {
+                         void* dx, const mtfm_full_grad* gr, char* ws, const void* a_pre) {
   TRY(check_bwd_dims(d));
   const MetaPlan& p = c.plan;
   const hipStream_t s = c.s;
@@ -122,7 +122,7 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
   bf16* xt = (bf16*)(ws + L.xt);
   bf16* z = (bf16*)(ws + L.z);
   bf16* hpre = (bf16*)(ws + L.hpre);
-  bf16* a = (bf16*)(ws + L.a);
+  bf16* a = a_pre ? (bf16*)a_pre : (bf16*)(ws + L.a);
   bf16* y = (bf16*)(ws + L.y);
   bf16* wot = (bf16*)(ws + L.wot);
   bf16* w1t = (bf16*)(ws + L.w1t);
@@ -151,17 +151,19 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
   gp.dst[2] = z + 2 * hd; gp.ld[2] = zw; gp.cend[2] = zw; gp.scale[2] = 1.f;
   gp.cend[3] = zw;
   gp.pre = hpre; gp.ldpre = zw;
-  gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd;
+  if (!a_pre) { gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd; }
   TRY(timed_gemm(MTFM_K_GEMM_UQKV, gp, MTFM_BF16, s));
-  AttnArgs aa{};
-  aa.q = z + hd; aa.ldq = zw; aa.k = z + 2 * hd; aa.ldk = zw; aa.v = z + 2 * hd + gd; aa.ldv = zw;
-  aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
-  aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
-  aa.a = a; aa.lda = hd;
-  aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
-  aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
-  aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
-  TRY(timed_attention(MTFM_K_ATTN_FULL, aa, MTFM_BF16, s));
+  if (!a_pre) {
+    AttnArgs aa{};
+    aa.q = z + hd; aa.ldq = zw; aa.k = z + 2 * hd; aa.ldk = zw; aa.v = z + 2 * hd + gd; aa.ldv = zw;
+    aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
+    aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
+    aa.a = a; aa.lda = hd;
+    aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles; aa.half_tiles = full_attn_half_tiles();
+    aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
+    aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+    TRY(timed_attention(MTFM_K_ATTN_FULL, aa, MTFM_BF16, s));
+  }
   GlnArgs g2{};
   g2.rows = R; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd; g2.gate = z; g2.ldg = zw;
   g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = c.meta.type; g2.eps = d->ln_eps;
@@ -239,7 +241,7 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
 
 // ---------------------------------------------------------------------------
 mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in,
-                           const void* dy, void* dx, const mtfm_target_grad* gr, char* ws) {
+                           const void* dy, void* dx, const mtfm_target_grad* gr, char* ws, const void* a_pre) {
   TRY(check_bwd_dims(d));
   const MetaPlan& p = c.plan;
   const hipStream_t s = c.s;
@@ -252,7 +254,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
   bf16* ztpre = (bf16*)(ws + L.hpre);
   bf16* kv = (bf16*)(ws + L.kv);
   bf16* kvpre = (bf16*)(ws + L.kvpre);
-  bf16* a = (bf16*)(ws + L.a);
+  bf16* a = a_pre ? (bf16*)a_pre : (bf16*)(ws + L.a);
   bf16* y = (bf16*)(ws + L.y);
   bf16* wot = (bf16*)(ws + L.wot);
   bf16* wtk = (bf16*)(ws + L.w1t);   // [S][D][zw]: transposed [W_u; W_q[k]; W_kv]
@@ -284,7 +286,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = 2 * gd; gk.scale[0] = 1.f;
     gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd;
     gk.pre = kvpre; gk.ldpre = 2 * gd;
-    gk.vt = ws + L.vt; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
+    if (!a_pre) { gk.vt = ws + L.vt; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd; }
     TRY(timed_gemm(MTFM_K_GEMM_KV, gk, MTFM_BF16, s));
   }
   if (T > 0) {
@@ -303,15 +305,17 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     gt.cend[3] = zw;
     gt.pre = ztpre; gt.ldpre = zw;
     TRY(timed_gemm(MTFM_K_GEMM_T, gt, MTFM_BF16, s));
-    AttnArgs aa{};
-    aa.q = zt + hd; aa.ldq = zw; aa.k = kv; aa.ldk = 2 * gd; aa.v = kv + gd; aa.ldv = 2 * gd;
-    aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
-    aa.kd = zt + 2 * hd; aa.ldkd = zw; aa.vd = zt + 2 * hd + gd; aa.ldvd = zw;
-    aa.a = a; aa.lda = hd;
-    aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
-    aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
-    aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
-    TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, MTFM_BF16, s));
+    if (!a_pre) {
+      AttnArgs aa{};
+      aa.q = zt + hd; aa.ldq = zw; aa.k = kv; aa.ldk = 2 * gd; aa.v = kv + gd; aa.ldv = 2 * gd;
+      aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
+      aa.kd = zt + 2 * hd; aa.ldkd = zw; aa.vd = zt + 2 * hd + gd; aa.ldvd = zw;
+      aa.a = a; aa.lda = hd;
+      aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
+      aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
+      aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+      TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, MTFM_BF16, s));
+    }
     GlnArgs g2{};
     g2.rows = T; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd; g2.gate = zt; g2.ldg = zw;
     g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;

@@ -248,9 +248,11 @@ mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims,
  * dx = dL/dX_in and every layer's fp32 weight/GLN gradients (overwritten):
  * full_g[b] for the full layer of block b, tgt_g[b * k_target + t] for its
  * target layer t.  One forward pass keeps the inputs of layers 1 .. L-1 in
- * the workspace (bf16, as the forward passes them on); then each layer's
- * backward runs from the last to the first, the gradient handed between
- * layers stored in dims->dtype.  dx also serves as one of the two
+ * the workspace (bf16, as the forward passes them on) and the attention
+ * outputs of layers 0 .. L-2 (each layer's backward reuses it instead of
+ * recomputing the attention; the result is the same bit for bit); then each
+ * layer's backward runs from the last to the first, the gradient handed
+ * between layers stored in dims->dtype.  dx also serves as one of the two
  * intermediate gradient buffers, so it must not alias x_in or dy.
  * bf16 only (MTFM_E_UNSUPPORTED otherwise).  ws: at least
  * mtfm_backbone_bwd_workspace_bytes(batch, dims, n_blocks, k_target) bytes.
