@@ -88,7 +88,8 @@ def cpu_baseline(wl, seconds: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed forward steps (0: skip the forward timing, for profiling the other parts alone)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -150,6 +151,7 @@ def main():
     log("warmup done")
 
     # counters for the FLOP / byte model (from the device metadata of this batch)
+    B.mask_build(batch, meta)
     views = B.meta_views(meta, lay, wl.batch.n_users)
     n_host = views["n"].cpu().numpy().astype(np.int64)
     pairs_full, pairs_t = visible_pairs(n_host, wl.batch.lens.astype(np.int64), wl.batch.split)
@@ -167,26 +169,29 @@ def main():
     attn_t_bytes = 2.0 * (R * 2 * gd + 3 * T * hd)
 
     # ---- timed region: full-attention kernel bracketed by events on its stream
-    B.timing_enable([B.K_ATTN_FULL])
-    B.timing_read(B.K_ATTN_FULL)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    B.timing_enable([])
-    n_attn, ms_attn = B.timing_read(B.K_ATTN_FULL)
-    elapsed = t1 - t0
-    ms_step = 1000.0 * elapsed / args.steps
-    samples_s = wl.batch.n_users * args.steps / elapsed
-    attn_ms = ms_attn / max(1, n_attn)
-    attn_tflops = attn_full_flops / (attn_ms * 1e-3) / 1e12
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, {samples_s:.1f} user-samples/s; "
-        f"full attention {attn_ms:.3f} ms/launch -> {attn_tflops:.1f} TFLOP/s")
+    # (--steps 0 skips it: a profiling run of the training / serving / V2 parts alone)
+    ms_step = samples_s = attn_ms = attn_tflops = None
+    if args.steps > 0:
+        B.timing_enable([B.K_ATTN_FULL])
+        B.timing_read(B.K_ATTN_FULL)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        B.timing_enable([])
+        n_attn, ms_attn = B.timing_read(B.K_ATTN_FULL)
+        elapsed = t1 - t0
+        ms_step = 1000.0 * elapsed / args.steps
+        samples_s = wl.batch.n_users * args.steps / elapsed
+        attn_ms = ms_attn / max(1, n_attn)
+        attn_tflops = attn_full_flops / (attn_ms * 1e-3) / 1e12
+        log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, {samples_s:.1f} user-samples/s; "
+            f"full attention {attn_ms:.3f} ms/launch -> {attn_tflops:.1f} TFLOP/s")
 
     breakdown = None
-    if not args.no_breakdown:
+    if not args.no_breakdown and args.steps > 0:
         classes = [B.K_MASK, B.K_GLN, B.K_GEMM_UQKV, B.K_ATTN_FULL, B.K_GEMM_OUT, B.K_GEMM_KV, B.K_GEMM_T,
                    B.K_ATTN_TARGET]
         names = ["mask", "gln", "gemm_uqkv", "attn_full", "gemm_out", "gemm_kv", "gemm_t", "attn_target"]
@@ -238,8 +243,8 @@ def main():
             train_step()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        train = {"what": "mtfm_backbone_bwd: forward keeping 15 layer inputs + backward of all 16 layers "
-                         "(dX and every weight / GLN gradient), incl. mask build",
+        train = {"what": "mtfm_backbone_bwd: forward keeping 15 layer inputs and attention outputs + backward "
+                         "of all 16 layers (dX and every weight / GLN gradient), incl. mask build",
                  "steps": args.train_steps, "ms_per_step": 1000.0 * el / args.train_steps,
                  "user_samples_per_s": wl.batch.n_users * args.train_steps / el,
                  "workspace_GiB": nb / 2 ** 30}
@@ -297,9 +302,9 @@ def main():
                  "context_ms": 1000.0 * (t1 - t0), "candidate_pass_ms": cand_ms,
                  "candidates_per_s": float(wl.batch.lens[:, 2].sum()) / (cand_ms * 1e-3),
                  "t_rows": int(T), "kv_cache_GiB": cache.numel() / 2 ** 30,
-                 "vs_full_forward": ms_step / cand_ms}
+                 "vs_full_forward": ms_step / cand_ms if ms_step else None}
         log(f"serving: context {serve['context_ms']:.2f} ms once, candidates {cand_ms:.3f} ms/pass "
-            f"({serve['candidates_per_s']:.0f} candidates/s, {serve['vs_full_forward']:.1f}x the full forward)")
+            f"({serve['candidates_per_s']:.0f} candidates/s, {serve['vs_full_forward'] or 0:.1f}x the full forward)")
         del cache, ws_c, ws_t, x_c, x_t, x_c0, x_t0
 
     v2 = None
@@ -363,10 +368,12 @@ def main():
                                "N~U[1000,2000] 70/20/10 H/R/T, d 512, 8Q/2KV, dh 64",
                    "users": wl.batch.n_users, "rows": int(R), "t_rows": int(T), "parallelism": "single-gpu"},
         "step_algorithmic_TFLOP": step_flops / 1e12,
-        "step_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
+        "step_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12 if ms_step else None,
         "roofline": {"kernel": "attn_bf16_kernel (full layer)", "bound": "mfma", "achieved": attn_tflops,
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": recorded_traffic(), "flops_per_launch": attn_full_flops, "ms_per_launch": attn_ms},
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS if attn_tflops else None,
+                     "traffic": recorded_traffic(), "flops_per_launch": attn_full_flops,
+                     "ms_per_launch": attn_ms} if args.steps > 0 else None,
         "breakdown": breakdown,
         "train": train,
         "serve": serve,
