@@ -7,13 +7,16 @@
 // with dK, dV of a KV group summed over its r query heads ([explainer] §4.1
 // GQA).  Three kernels, none with atomics:
 //   * dq:  one workgroup per (32-row query slice, group), one wave per head;
-//          loops over the visible context key tiles like the forward (K, K^T
-//          and V tiles staged in LDS), S^T and dP^T accumulate with lane =
-//          query so dS feeds the dQ MFMA straight from registers.
-//   * dkv: one workgroup per (32-key context slice, group), one wave per head;
-//          loops over the user's query tiles that see the keys, S and dP with
-//          lane = key so P and dS feed the dV / dK MFMAs from registers; the r
-//          heads' dK, dV are summed through LDS in a fixed order.
+//          the visible context key tiles stream through an LDS ring of K and
+//          V tiles filled by buffer DMA; S^T and dP^T accumulate with lane =
+//          query so dS feeds dQ from registers, K^T through the transposing
+//          LDS read.
+//   * dkv: one workgroup per (64-key context tile, group), two waves per
+//          head (one per 32-key half); walks the user's query tiles that see
+//          the keys in 32-query stages brought in by buffer DMA, S and dP with
+//          lane = key so P and dS feed the dV / dK MFMAs from registers, Q' and
+//          dA/n through the transposing LDS read; the r heads' dK, dV are
+//          summed through LDS in a fixed order.
 //   * self: one wave per (T row, group): the T row's only T key is itself
 //          ([blog] §3.2), so its term is a few dot products.
 
@@ -22,8 +25,6 @@
 namespace {
 
 constexpr int DH = 64;
-constexpr int KS = DH + 8;  // row-major tile stride (144 B)
-constexpr int VS = 64 + 4;  // transposed tile stride (136 B)
 constexpr float kLn2 = 0.69314718055994530942f;
 
 MTFM_DEV int xcd_remap(int bid, int nblocks) {
@@ -64,180 +65,8 @@ MTFM_DEV void silu_grad_scaled(float sp, float* p_ln2, float* dp) {
 
 MTFM_DEV bf16x8 ld8(const bf16* p) { return *(const bf16x8*)p; }
 
-MTFM_DEV bf16x8 tr_frag(const bf16* base, int row, int col) {
-  // slots s < 4: columns col + s;  s >= 4: columns col + 8 + (s - 4)
-  const bf16x4 lo4 = *(const bf16x4*)(base + row * VS + col);
-  const bf16x4 hi4 = *(const bf16x4*)(base + row * VS + col + 8);
-  return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // --------------------------------------------------------------------------
-template <int R>
-__global__ __launch_bounds__(64 * R, 2) void attn_bwd_dq_kernel(AttnBwdArgs g) {
-  constexpr int NT = 64 * R;
-  constexpr int PPT = (256 + NT - 1) / NT;  // K (key pair, 8 dims) items per thread
-  constexpr int VPT = (512 + NT - 1) / NT;  // V 16-B chunks per thread
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[2][DH * VS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][64 * KS];
-
-  const int nblocks = g.nqtiles * g.G * 2;
-  const int lb = xcd_remap(blockIdx.x, nblocks);
-  const int slice = lb & 1;
-  const int tile = (lb >> 1) / g.G, grp = (lb >> 1) % g.G;
-  const int32_t* td = g.qtiles + 8 * tile;
-  const int u = td[TD_USER], tile_rows = td[TD_NROWS];
-  const int full_end = td[TD_FULL_END], key_end = td[TD_END];
-  const int qoff = slice * 32;
-  const int nrows = min(32, tile_rows - qoff);
-  if (nrows <= 0) return;
-  const int grow0 = td[TD_GROW0] + qoff, qrow0 = td[TD_QROW0] + qoff, urow0 = td[TD_UROW0];
-  const int lctx = g.lens[3 * u] + g.lens[3 * u + 1];
-  const int ntl = key_end;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = grp * R + wave;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const bool qok = l32 < nrows;
-
-  bf16x8 qf[4], df[4], dl[4];
-  {
-    const int64_t qrow = qrow0 + (qok ? l32 : 0);
-    const bf16* qs = g.q + qrow * g.ldq + h * DH + 8 * hi;
-    const bf16* ds = g.dan + qrow * g.lddan + h * DH + 8 * hi;
-    const bf16* dls = g.dan_lo + qrow * g.lddan + h * DH + 8 * hi;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      qf[kk] = qok ? ld8(qs + kk * 16) : bf16x8{};
-      df[kk] = qok ? ld8(ds + kk * 16) : bf16x8{};
-      dl[kk] = qok ? ld8(dls + kk * 16) : bf16x8{};
-    }
-  }
-  const int plim = qok ? g.p[grow0 + l32] : 0;
-
-  bf16x8 rk[PPT][2], rv[VPT];
-  auto load_tile = [&](int it) {
-    const int base = urow0 + it * 64;
-    const int lim = min(64, lctx - it * 64);
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int c = tid + NT * i;
-      const int jp = c & 31, kc = c >> 5, j = 2 * jp;
-      const bool in = c < 256;
-      rk[i][0] = (in && j < lim) ? ld8(g.k + (int64_t)(base + j) * g.ldk + grp * DH + kc * 8) : bf16x8{};
-      rk[i][1] = (in && j + 1 < lim) ? ld8(g.k + (int64_t)(base + j + 1) * g.ldk + grp * DH + kc * 8) : bf16x8{};
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + NT * i;
-      const int j = c >> 3, kc = c & 7;
-      rv[i] = (c < 512 && j < lim) ? ld8(g.v + (int64_t)(base + j) * g.ldv + grp * DH + kc * 8) : bf16x8{};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int c = tid + NT * i;
-      if (c >= 256) continue;
-      const int jp = c & 31, kc = c >> 5, j = 2 * jp;
-      *(bf16x8*)(&Ks[buf][j * KS + kc * 8]) = rk[i][0];
-      *(bf16x8*)(&Ks[buf][(j + 1) * KS + kc * 8]) = rk[i][1];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        bf16x2 pr;
-        pr[0] = rk[i][0][s];
-        pr[1] = rk[i][1][s];
-        *(bf16x2*)(&Kt[buf][(kc * 8 + s) * VS + j]) = pr;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + NT * i;
-      if (c < 512) *(bf16x8*)(&Vs[buf][(c >> 3) * KS + (c & 7) * 8]) = rv[i];
-    }
-  };
-
-  f32x16 dq[2] = {f32x16{}, f32x16{}};
-  if (ntl > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntl; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntl) load_tile(it + 1);
-    const bool masked = it >= full_end || (it + 1) * 64 > lctx;
-    const int lim = plim - it * 64;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 st = {}, dpt = {};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 kf = ld8(&Ks[buf][(kb * 32 + l32) * KS + kk * 16 + 8 * hi]);
-        const bf16x8 vf = ld8(&Vs[buf][(kb * 32 + l32) * KS + kk * 16 + 8 * hi]);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], st, 0, 0, 0);
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[kk], dpt, 0, 0, 0);
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dl[kk], dpt, 0, 0, 0);
-      }
-      if (masked) {
-        // keys of register i: kb*32 + 8(i/4) + 4hi + i%4; shift the bound once
-        const int lim_l = lim - kb * 32 - 4 * hi;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st[i] = 8 * (i >> 2) + (i & 3) < lim_l ? st[i] : kMaskedScore;
-      }
-      bf16x8 dsf[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int i = 8 * c + s;
-          float pv, dsg;
-          silu_grad_scaled(st[i], &pv, &dsg);
-          dsf[c][s] = (bf16)(dpt[i] * dsg);
-        }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const bf16x8 kt = tr_frag(Kt[buf], nb * 32 + l32, kb * 32 + 16 * c + 4 * hi);
-          dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[c], kt, dq[nb], 0, 0, 0);
-        }
-    }
-    if (it + 1 < ntl) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-  // dq layout: lane = dim nb*32 + l32, registers = queries 8(i/4) + 4hi + i%4
-  const int hd = g.H * DH;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qi = 8 * (i >> 2) + 4 * hi + (i & 3);
-      if (qi < nrows) g.dq[(int64_t)(qrow0 + qi) * hd + h * DH + nb * 32 + l32] = dq[nb][i];
-    }
-}
-
-// --------------------------------------------------------------------------
-// dK / dV kernel.  One workgroup per (64-key context tile, group) with 2 HC
-// waves: wave w takes key half w % 2 (32 keys, lane = key) and head w / 2 of
-// the current chunk of HC heads (all R heads when R <= 4, two passes when
-// R = 8); every wave sums its heads into one dK, dV accumulator.  The user's
-// query tiles that see the keys are walked in stages of 32 queries: per head
-// Q', dA/n hi and lo (32 rows x 128 B each), plus the 32 prefix limits, are
-// brought into an LDS ring by buffer DMA two stages ahead.  S and dP come out
-// with lane = key, so P and dS feed the dV / dK MFMAs straight from registers;
-// the other operand (Q', dA/n with lane = head dimension, 8 queries per lane)
-// is read from the row-major stage with the transposing LDS read.
-constexpr int KV_NS = 3;                   // ring depth (stages)
-constexpr int KV_TENSOR = 32 * 128;        // one 32-row tensor of a head
-constexpr int KV_HEAD = 3 * KV_TENSOR;     // Q', dA/n hi, dA/n lo
-constexpr int KV_CPW = 6;                  // 1 KB DMA chunks per wave per stage
-
-template <int R> struct DkvShape {
-  static constexpr int HC = R < 4 ? R : 4;          // heads per pass
-  static constexpr int NW = 2 * HC;                 // waves
-  static constexpr int STAGE = HC * KV_HEAD + 256;  // + prefix limits (64 lanes x 4 B)
-};
+// LDS ring helpers shared by the dQ and dK/dV kernels.
 
 // 16-byte unit u of stage row r sits at slot u ^ kv_swz(r): conflict-free for
 // both the row reads (16 consecutive rows, one unit) and the transposing reads
@@ -319,6 +148,224 @@ MTFM_DEV void kv_plim(uint32_t a, int4 (&p)[4]) {
 MTFM_DEV uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
 }
+
+// --------------------------------------------------------------------------
+// dQ kernel.  One workgroup per (32-row query slice, KV group), one wave per
+// head of the group (32 queries, lane = query).  The user's visible context
+// key tiles (64 keys, aligned to the user's first row) stream through a
+// three-stage LDS ring of K and V tiles (8 KB each, rows swizzled as kv_swz),
+// filled by buffer DMA two tiles ahead and shared by the r heads.  S^T = K Q'^T
+// and dP^T = V (dA/n)^T accumulate with lane = query, so dS feeds dQ += dS K
+// straight from registers; the K^T operand (8 consecutive keys of one head
+// dimension per lane) comes from the row-major K tile through the
+// transposing LDS read.
+constexpr int DQ_NS = 3;
+constexpr int DQ_TILE = 64 * 128;       // 64 key rows x 128 B
+constexpr int DQ_STAGE = 2 * DQ_TILE;   // K, then V
+
+// The 8 transposing reads of one 32-key block: fragment (c, nb, h2) at LDS
+// address a[nb][h2] (+2048 B for c = 1, the next 16 keys); one block with its
+// own wait, for the reason given at kv_tr16.
+MTFM_DEV void dq_tr8(const uint32_t (&a)[2][2], i16x4 (&o)[2][2][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %10 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0][0][0]), "=&v"(o[0][0][1]), "=&v"(o[0][1][0]), "=&v"(o[0][1][1]),
+        "=&v"(o[1][0][0]), "=&v"(o[1][0][1]), "=&v"(o[1][1][0]), "=&v"(o[1][1][1])
+      : "v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1])
+      : "memory");
+}
+
+template <int R>
+__global__ __launch_bounds__(64 * R, 3) void attn_bwd_dq_kernel(AttnBwdArgs g) {
+  constexpr int CPW = 16 / R;             // 1 KB DMA chunks per wave per stage
+  static_assert(CPW * R == 16, "chunks per stage");
+  __shared__ __attribute__((aligned(1024))) char lds[DQ_NS * DQ_STAGE];
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  typedef __attribute__((address_space(4))) const int32_t cint;
+
+  const int nblocks = g.nqtiles * g.G * 2;
+  const int lb = xcd_remap(blockIdx.x, nblocks);
+  const int slice = lb & 1;
+  const int tile = (lb >> 1) / g.G, grp = (lb >> 1) % g.G;
+  const cint* td = (const cint*)g.qtiles + 8 * tile;
+  const int u = uni(td[TD_USER]), tile_rows = uni(td[TD_NROWS]);
+  const int full_end = uni(td[TD_FULL_END]), ntl = uni(td[TD_END]);
+  const int qoff = slice * 32;
+  const int nrows = min(32, tile_rows - qoff);
+  if (nrows <= 0) return;
+  const int grow0 = uni(td[TD_GROW0]) + qoff, qrow0 = uni(td[TD_QROW0]) + qoff, urow0 = uni(td[TD_UROW0]);
+  const cint* lens = (const cint*)g.lens;
+  const int lctx = uni(lens[3 * u] + lens[3 * u + 1]);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = grp * R + wave;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const bool qok = l32 < nrows;
+
+  // this wave's queries (B operands, lane = query, dims kk*16 + 8hi): loaded
+  // before the first DMA so that waiting for them never waits for the ring
+  bf16x8 qf[4], df[4], dl[4];
+  {
+    const int64_t qrow = qrow0 + (qok ? l32 : 0);
+    const bf16* qs = g.q + qrow * g.ldq + h * DH + 8 * hi;
+    const bf16* ds = g.dan + qrow * g.lddan + h * DH + 8 * hi;
+    const bf16* dls = g.dan_lo + qrow * g.lddan + h * DH + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      qf[kk] = ld8(qs + kk * 16);
+      df[kk] = ld8(ds + kk * 16);
+      dl[kk] = ld8(dls + kk * 16);
+    }
+  }
+  const int plim_raw = g.p[grow0 + (qok ? l32 : 0)];
+
+  // DMA: chunk c (16 per stage) = tensor c / 8 (K, V), rows 8 (c % 8) + lane / 8,
+  // slot lane % 8 holding the 16-byte unit slot ^ kv_swz(row).  Tiles past the
+  // last one are issued as empty loads so that every wait sees the same count.
+  const int rin = lane >> 3, slot = lane & 7;
+  auto issue = [&](int it, int buf) {
+    const bool real = it < ntl;
+    const int valid = real ? min(64, lctx - it * 64) : 0;
+    const int64_t row0 = urow0 + (real ? it * 64 : 0);
+    const __amdgpu_buffer_rsrc_t rk = kv_rsrc(g.k + row0 * g.ldk + grp * DH, (uint32_t)(valid * g.ldk * 2));
+    const __amdgpu_buffer_rsrc_t rv = kv_rsrc(g.v + row0 * g.ldv + grp * DH, (uint32_t)(valid * g.ldv * 2));
+    char* st = lds + buf * DQ_STAGE;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int c = i * R + wave;
+      const int t = c >> 3, r = (c & 7) * 8 + rin;
+      const int64_t ld = t ? g.ldv : g.ldk;
+      const uint32_t voff = (uint32_t)(r * ld * 2 + ((slot ^ kv_swz(r)) << 4));
+      kv_dma(t ? rv : rk, (lds_void_t*)(st + t * DQ_TILE + (c & 7) * 1024), voff, 16);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < DQ_NS - 1; ++s) issue(s, s);
+
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    qf[kk] = qok ? qf[kk] : bf16x8{};
+    df[kk] = qok ? df[kk] : bf16x8{};
+    dl[kk] = qok ? dl[kk] : bf16x8{};
+  }
+  const int plim = qok ? plim_raw : 0;
+  // row reads: key kb*32 + l32, unit 2kk + hi; transposing reads of fragment
+  // (c, nb, h2): keys kb*32 + 16c + 8h2 + 4hi + (lane/4)%4, dims nb*32 +
+  // 16((lane/16)%2) + 4(lane%4) .. + 3 (kb and c only move the row by 32 / 16)
+  const int sw32 = kv_swz(l32);
+  uint32_t tro[2][2];
+  {
+    const int tm = (lane >> 2) & 3, tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r = 8 * h2 + 4 * hi + tm;
+        const int col = nb * 32 + tcol;
+        tro[nb][h2] = (uint32_t)(r * 128 + (((col >> 3) ^ kv_swz(r)) << 4) + (col & 7) * 2);
+      }
+  }
+  const uint32_t lds0 = lds_addr(lds);
+
+  f32x16 dq[2] = {f32x16{}, f32x16{}};
+  for (int it = 0; it < ntl; ++it) {
+    kv_wait_vm<(DQ_NS - 2) * CPW>();
+    kv_barrier();
+    issue(it + DQ_NS - 1, (it + DQ_NS - 1) % DQ_NS);
+    const int buf = it % DQ_NS;
+    const char* st = lds + buf * DQ_STAGE;
+    const bool masked = it >= full_end || (it + 1) * 64 > lctx;
+    const int lim = plim - it * 64;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T, dP^T: lane = query, registers = keys kb*32 + 8(i/4) + 4hi + i%4
+      f32x16 sc = {}, dpt = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = (kb * 32 + l32) * 128 + (((2 * kk + hi) ^ sw32) << 4);
+        const bf16x8 kf = *(const bf16x8*)(st + off);
+        const bf16x8 vf = *(const bf16x8*)(st + DQ_TILE + off);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[kk], dpt, 0, 0, 0);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dl[kk], dpt, 0, 0, 0);
+      }
+      if (masked) {
+        const int lim_l = lim - kb * 32 - 4 * hi;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = 8 * (i >> 2) + (i & 3) < lim_l ? sc[i] : kMaskedScore;
+      }
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * c + e;
+          float pv, dsg;
+          silu_grad_scaled(sc[i], &pv, &dsg);
+          dsf[c][e] = (bf16)(dpt[i] * dsg);
+        }
+      i16x4 kt4[2][2][2];
+      {
+        uint32_t ta[2][2];
+        const uint32_t base = lds0 + (uint32_t)(buf * DQ_STAGE + kb * 4096);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) ta[nb][h2] = base + tro[nb][h2];
+        dq_tr8(ta, kt4);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const bf16x8 kt8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(kt4[c][nb][0], kt4[c][nb][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[c], kt8, dq[nb], 0, 0, 0);
+        }
+    }
+  }
+  kv_wait_vm<0>();   // the ring's trailing (empty) loads land before the workgroup ends
+  // dq layout: lane = dim nb*32 + l32, registers = queries 8(i/4) + 4hi + i%4
+  const int hd = g.H * DH;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int qi = 8 * (i >> 2) + 4 * hi + (i & 3);
+      if (qi < nrows) g.dq[(int64_t)(qrow0 + qi) * hd + h * DH + nb * 32 + l32] = dq[nb][i];
+    }
+}
+
+
+// --------------------------------------------------------------------------
+// dK / dV kernel.  One workgroup per (64-key context tile, group) with 2 HC
+// waves: wave w takes key half w % 2 (32 keys, lane = key) and head w / 2 of
+// the current chunk of HC heads (all R heads when R <= 4, two passes when
+// R = 8); every wave sums its heads into one dK, dV accumulator.  The user's
+// query tiles that see the keys are walked in stages of 32 queries: per head
+// Q', dA/n hi and lo (32 rows x 128 B each), plus the 32 prefix limits, are
+// brought into an LDS ring by buffer DMA two stages ahead.  S and dP come out
+// with lane = key, so P and dS feed the dV / dK MFMAs straight from registers;
+// the other operand (Q', dA/n with lane = head dimension, 8 queries per lane)
+// is read from the row-major stage with the transposing LDS read.
+constexpr int KV_NS = 3;                   // ring depth (stages)
+constexpr int KV_TENSOR = 32 * 128;        // one 32-row tensor of a head
+constexpr int KV_HEAD = 3 * KV_TENSOR;     // Q', dA/n hi, dA/n lo
+constexpr int KV_CPW = 6;                  // 1 KB DMA chunks per wave per stage
+
+template <int R> struct DkvShape {
+  static constexpr int HC = R < 4 ? R : 4;          // heads per pass
+  static constexpr int NW = 2 * HC;                 // waves
+  static constexpr int STAGE = HC * KV_HEAD + 256;  // + prefix limits (64 lanes x 4 B)
+};
 
 template <int R>
 __global__ __launch_bounds__(128 * DkvShape<R>::HC, 1) void attn_bwd_dkv_kernel(AttnBwdArgs g) {
