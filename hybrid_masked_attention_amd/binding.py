@@ -30,7 +30,7 @@ ENTRY_POINTS = [
     "mtfm_workspace_probe", "mtfm_attn_full", "mtfm_attn_target", "mtfm_backbone_fwd",
     "mtfm_attn_full_bwd", "mtfm_attn_target_bwd", "mtfm_timing_enable", "mtfm_timing_read",
     "mtfm_status_str", "mtfm_last_error", "mtfm_backbone_workspace_bytes",
-    "mtfm_backbone_bwd_workspace_bytes", "mtfm_backbone_bwd", "mtfm_kv_cache_bytes", "mtfm_serve_workspace_bytes",
+    "mtfm_backbone_bwd_workspace_bytes", "mtfm_backbone_bwd_min_workspace_bytes", "mtfm_backbone_bwd", "mtfm_kv_cache_bytes", "mtfm_serve_workspace_bytes",
     "mtfm_serve_context", "mtfm_serve_targets", "mtfm_autosplit", "mtfm_token_ffn_workspace_bytes",
     "mtfm_token_ffn", "mtfm_token_pool", "mtfm_backbone_v2_workspace_bytes", "mtfm_backbone_v2_fwd",
 ]
@@ -118,6 +118,8 @@ def lib():
     L.mtfm_attn_target_bwd.restype = c_int32
     L.mtfm_backbone_bwd_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32, c_int32]
     L.mtfm_backbone_bwd_workspace_bytes.restype = c_size_t
+    L.mtfm_backbone_bwd_min_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32, c_int32]
+    L.mtfm_backbone_bwd_min_workspace_bytes.restype = c_size_t
     L.mtfm_backbone_bwd.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_void_p, P(CFullW), P(CTargetW),
                                     c_void_p, c_void_p, c_void_p, P(CFullGrad), P(CTargetGrad), c_void_p, c_size_t,
                                     c_void_p]
@@ -333,6 +335,12 @@ TARGET_GRAD_KEYS = ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w
 def backbone_bwd_workspace_bytes(batch: DeviceBatch, dims: CDims, n_blocks: int, k_target: int) -> int:
     return int(lib().mtfm_backbone_bwd_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks),
                                                        int(k_target)))
+
+
+def backbone_bwd_min_workspace_bytes(batch: DeviceBatch, dims: CDims, n_blocks: int, k_target: int) -> int:
+    """Smallest workspace mtfm_backbone_bwd accepts (each layer backward then recomputes its intermediates)."""
+    return int(lib().mtfm_backbone_bwd_min_workspace_bytes(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks),
+                                                           int(k_target)))
 
 
 def backbone_bwd(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], tgt: Sequence[Dict], x_in, dy, dx,

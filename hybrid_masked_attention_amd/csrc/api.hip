@@ -212,16 +212,16 @@ int full_attn_half_tiles() {
 //   X~ = GLN1(X); [U|Q|K|V] = SiLU(X~ W^T); A = masked SiLU attention / n;
 //   X' = (GLN2(A) (.) U) W_o^T + X
 mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out,
-                     char* ws, const KvOut* kv, void* a_keep) {
+                     char* ws, const KvOut* kv, const FwdKeep* keep) {
   const MetaPlan& p = c.plan;
   const int dt = d->dtype;
   const int64_t es = elem_size(dt);
   const int H = d->n_q_heads, G = d->n_kv_heads, dh = d->head_dim, D = d->d_model;
   const int hd = H * dh, gd = G * dh, zw = 2 * hd + 2 * gd;
   const LayerWs L = layer_ws(p, d, MTFM_OP_FULL);
-  char* xt = ws + L.xt;
-  char* z = ws + L.z;
-  char* a = a_keep ? (char*)a_keep : ws + L.a;
+  char* xt = keep ? keep->xt : ws + L.xt;
+  char* z = keep ? keep->z : ws + L.z;
+  char* a = keep ? keep->a : ws + L.a;
   char* y = ws + L.y;
   if (p.n_rows == 0) return MTFM_OK;
 
@@ -241,6 +241,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   gp.dst[2] = z + 2 * hd * es; gp.ld[2] = zw; gp.cend[2] = zw; gp.scale[2] = 1.f;
   gp.cend[3] = zw;
   if (dt == MTFM_BF16) { gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd; }
+  if (keep) { gp.pre = keep->hpre; gp.ldpre = zw; }
   if (kv) {
     // K straight into the cache ([rows][gd]), V only transposed (bf16 path; no T rows, so
     // no query reads its own row-major K/V)
@@ -290,7 +291,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
 //   [U_T|Q_T|K_T|V_T] = SiLU(X~_T [W_u; W_q[k]; W_kv]^T) per sub-token k;
 //   A_T = masked attention; X'_T = (GLN2(A_T) (.) U_T) W_o^T + X_T.
 mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in, void* x_out,
-                       char* ws, void* a_keep) {
+                       char* ws, const FwdKeep* keep) {
   const MetaPlan& p = c.plan;
   const int dt = d->dtype;
   const int64_t es = elem_size(dt);
@@ -298,10 +299,10 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   const int hd = H * dh, gd = G * dh, zw = 2 * hd + 2 * gd;
   const int S = p.split;
   const LayerWs L = layer_ws(p, d, MTFM_OP_TARGET);
-  char* xt = ws + L.xt;
-  char* kv = ws + L.kv;
-  char* zt = ws + L.z;
-  char* a = a_keep ? (char*)a_keep : ws + L.a;
+  char* xt = keep ? keep->xt : ws + L.xt;
+  char* kv = keep ? keep->kv : ws + L.kv;
+  char* zt = keep ? keep->z : ws + L.z;
+  char* a = keep ? keep->a : ws + L.a;
   char* y = ws + L.y;
   if (x_out != x_in && p.n_rows > 0) {
     hipError_t e = hipMemcpyAsync(x_out, x_in, (size_t)p.n_rows * D * es, hipMemcpyDeviceToDevice, c.s);
@@ -327,6 +328,10 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
     gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
     gk.dst[1] = dt == MTFM_BF16 ? nullptr : kv + gd * es; gk.ld[1] = 2 * gd; gk.cend[1] = 2 * gd; gk.scale[1] = 1.f;
     gk.cend[2] = gk.cend[3] = 2 * gd;
+    if (keep) {   // the backward also needs V row-major and the pre-activations
+      gk.cend[0] = 2 * gd; gk.dst[1] = nullptr;
+      gk.pre = keep->kvpre; gk.ldpre = 2 * gd;
+    }
     if (dt == MTFM_BF16) { gk.vt = ws + L.vt; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd; }
     TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s));
   }
@@ -344,6 +349,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   gt.dst[1] = zt + hd * es; gt.ld[1] = zw; gt.cend[1] = 2 * hd; gt.scale[1] = q_scale(dh);
   gt.dst[2] = zt + 2 * hd * es; gt.ld[2] = zw; gt.cend[2] = zw; gt.scale[2] = 1.f;
   gt.cend[3] = zw;
+  if (keep) { gt.pre = keep->hpre; gt.ldpre = zw; }
   TRY(timed_gemm(MTFM_K_GEMM_T, gt, dt, c.s));
 
   AttnArgs aa{};
@@ -719,6 +725,72 @@ mtfm_status serve_checks(const mtfm_batch* batch, const mtfm_dims* dims, int32_t
 
 }  // namespace
 
+// Backward through the whole stack: one forward pass keeps every layer's input
+// (bf16, as the forward hands it on), then the layers' backward run from the
+// last to the first, each taking the next layer's input gradient as its
+// upstream gradient.  Workspace: the largest single-layer workspace, the
+// inputs of layers 1 .. L-1, one gradient buffer (the caller's dx is the
+// other one of the pair), then (full size only) the kept intermediates of
+// layers 0 .. L-2.
+namespace {
+
+// With the full workspace the forward pass also keeps each layer's
+// intermediates (X~, the projections and their pre-activations, the
+// attention output), so no layer backward recomputes them; with only the
+// minimum (the regions before `keep`) every layer backward recomputes them.
+struct BackboneBwdWs {
+  int64_t layer = 0, stash = 0, xbytes = 0, gbuf = 0, keep = 0, total = 0;
+  int per = 1;
+  int64_t R = 0, T = 0, D = 0, hd = 0, gd2 = 0, zw = 0;
+  static int64_t al(int64_t b) { return align_up(std::max<int64_t>(b, 0), 256); }
+  int64_t kfull() const { return al(R * D * 2) + 2 * al(R * zw * 2) + al(R * hd * 2); }
+  int64_t ktarget() const { return al(R * D * 2) + 2 * al(R * gd2 * 2) + 2 * al(T * zw * 2) + al(T * hd * 2); }
+  int64_t keep_off(int l) const {   // kept intermediates of layer l (l < L - 1)
+    const int nf = (l + per - 1) / per;   // full layers before l
+    return keep + nf * kfull() + (l - nf) * ktarget();
+  }
+  FwdKeep keep_of(char* w, int l) const {
+    FwdKeep k;
+    char* b = w + keep_off(l);
+    k.xt = b; b += al(R * D * 2);
+    if (l % per == 0) {
+      k.z = b; b += al(R * zw * 2);
+      k.hpre = b; b += al(R * zw * 2);
+      k.a = b;
+    } else {
+      k.kv = b; b += al(R * gd2 * 2);
+      k.kvpre = b; b += al(R * gd2 * 2);
+      k.z = b; b += al(T * zw * 2);
+      k.hpre = b; b += al(T * zw * 2);
+      k.a = b;
+    }
+    return k;
+  }
+};
+
+BackboneBwdWs backbone_bwd_ws(const MetaPlan& p, const mtfm_dims* d, int n_blocks, int k_target) {
+  BackboneBwdWs w;
+  const int n_layers = n_blocks * (1 + k_target);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
+  const int64_t lw = std::max(std::max(layer_ws(p, d, MTFM_OP_FULL).total, layer_ws(p, d, MTFM_OP_TARGET).total),
+                              std::max(bwd_ws_bytes(p, d, MTFM_OP_FULL_BWD), bwd_ws_bytes(p, d, MTFM_OP_TARGET_BWD)));
+  w.layer = take(lw);
+  w.xbytes = align_up(p.n_rows * d->d_model * elem_size(d->dtype), 256);
+  w.stash = take(std::max(n_layers - 1, 0) * w.xbytes);
+  w.gbuf = take(w.xbytes);
+  w.per = 1 + k_target;
+  w.R = p.n_rows; w.T = p.n_t_rows; w.D = d->d_model;
+  w.hd = (int64_t)d->n_q_heads * d->head_dim;
+  w.gd2 = 2 * (int64_t)d->n_kv_heads * d->head_dim;
+  w.zw = 2 * w.hd + w.gd2;
+  w.keep = off;
+  w.total = n_layers > 1 ? w.keep_off(n_layers - 1) : off;
+  return w;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t mtfm_meta_bytes(const mtfm_batch* batch) {
@@ -854,48 +926,7 @@ mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims,
 }
 
 // ---------------------------------------------------------------------------
-// Backward through the whole stack: one forward pass keeps every layer's input
-// (bf16, as the forward hands it on), then the layers' backward run from the
-// last to the first, each taking the next layer's input gradient as its
-// upstream gradient.  Workspace: the largest single-layer workspace, the
-// inputs of layers 1 .. L-1, one gradient buffer (the caller's dx is the
-// other one of the pair) and the attention outputs of layers 0 .. L-2.
-namespace {
 
-// Besides the layer inputs, the forward pass keeps each layer's attention
-// output A (packed rows for a full layer, T rows for a target layer), so the
-// backward does not recompute the attention.
-struct BackboneBwdWs {
-  int64_t layer = 0, stash = 0, xbytes = 0, gbuf = 0, astash = 0, afull = 0, atarget = 0, total = 0;
-  int per = 1;
-  int64_t a_off(int l) const {   // A of layer l (l < L - 1)
-    const int nf = (l + per - 1) / per;   // full layers before l
-    return astash + nf * afull + (l - nf) * atarget;
-  }
-};
-
-BackboneBwdWs backbone_bwd_ws(const MetaPlan& p, const mtfm_dims* d, int n_blocks, int k_target) {
-  BackboneBwdWs w;
-  const int n_layers = n_blocks * (1 + k_target);
-  int64_t off = 0;
-  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
-  const int64_t lw = std::max(std::max(layer_ws(p, d, MTFM_OP_FULL).total, layer_ws(p, d, MTFM_OP_TARGET).total),
-                              std::max(bwd_ws_bytes(p, d, MTFM_OP_FULL_BWD), bwd_ws_bytes(p, d, MTFM_OP_TARGET_BWD)));
-  w.layer = take(lw);
-  w.xbytes = align_up(p.n_rows * d->d_model * elem_size(d->dtype), 256);
-  w.stash = take(std::max(n_layers - 1, 0) * w.xbytes);
-  w.gbuf = take(w.xbytes);
-  const int64_t hd = (int64_t)d->n_q_heads * d->head_dim;
-  w.per = 1 + k_target;
-  w.afull = align_up(p.n_rows * hd * 2, 256);
-  w.atarget = align_up(p.n_t_rows * hd * 2, 256);
-  w.astash = off;
-  if (n_layers > 1) off = align_up(w.a_off(n_layers - 1), 256);
-  w.total = off;
-  return w;
-}
-
-}  // namespace
 
 size_t mtfm_backbone_bwd_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks,
                                          int32_t k_target) {
@@ -903,6 +934,14 @@ size_t mtfm_backbone_bwd_workspace_bytes(const mtfm_batch* batch, const mtfm_dim
   if (n_blocks < 0 || k_target < 0 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
   if (bwd_ws_bytes(p, dims, MTFM_OP_FULL_BWD) == 0) return 0;   // shapes the backward does not support
   return (size_t)backbone_bwd_ws(p, dims, n_blocks, k_target).total;
+}
+
+size_t mtfm_backbone_bwd_min_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks,
+                                             int32_t k_target) {
+  MetaPlan p;
+  if (n_blocks < 0 || k_target < 0 || plan_meta(batch, &p) != MTFM_OK || check_dims(dims) != MTFM_OK) return 0;
+  if (bwd_ws_bytes(p, dims, MTFM_OP_FULL_BWD) == 0) return 0;
+  return (size_t)backbone_bwd_ws(p, dims, n_blocks, k_target).keep;
 }
 
 mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
@@ -931,8 +970,9 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
   }
   const int L = n_blocks * (1 + k_target);
   const BackboneBwdWs W = backbone_bwd_ws(c.plan, dims, n_blocks, k_target);
-  if (W.total > 0 && !ws) return MTFM_E_NULL;
-  if (ws_bytes < (size_t)W.total) return MTFM_E_WORKSPACE;
+  if (W.keep > 0 && !ws) return MTFM_E_NULL;
+  if (ws_bytes < (size_t)W.keep) return MTFM_E_WORKSPACE;
+  const bool keep_mode = ws_bytes >= (size_t)W.total;
   c.b = batch;
   c.meta = meta_ptrs(c.plan, meta_d);
   c.s = (hipStream_t)stream;
@@ -947,22 +987,27 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
   auto input_of = [&](int l) -> const void* { return l == 0 ? x_in : (const void*)(w + W.stash + (l - 1) * W.xbytes); };
   // gradient buffers alternate so that layer 0 writes dx
   auto grad_buf = [&](int l) -> void* { return (l % 2 == 0) ? dx : (void*)(w + W.gbuf); };
-  // A of layer l as kept by the forward pass (none for the last layer, whose
-  // forward is not run here: its backward recomputes it)
-  auto a_of = [&](int l) -> char* { return l + 1 < L ? w + W.a_off(l) : nullptr; };
+  // intermediates of layer l kept by the forward pass (keep mode; none for the
+  // last layer, whose forward is not run here: its backward recomputes them)
+  FwdKeep kl;
+  auto keep_of = [&](int l) -> const FwdKeep* {
+    if (!keep_mode || l + 1 >= L) return nullptr;
+    kl = W.keep_of(w, l);
+    return &kl;
+  };
   for (int l = 0; l + 1 < L; ++l) {
     void* out = w + W.stash + l * W.xbytes;
     const int b = l / per, t = l % per;
-    if (t == 0) TRY(run_full(c, dims, &full[b], input_of(l), out, w + W.layer, nullptr, a_of(l)));
-    else TRY(run_target(c, dims, &tgt[b * k_target + t - 1], input_of(l), out, w + W.layer, a_of(l)));
+    if (t == 0) TRY(run_full(c, dims, &full[b], input_of(l), out, w + W.layer, nullptr, keep_of(l)));
+    else TRY(run_target(c, dims, &tgt[b * k_target + t - 1], input_of(l), out, w + W.layer, keep_of(l)));
   }
   for (int l = L - 1; l >= 0; --l) {
     const void* g_in = l == L - 1 ? dy : grad_buf(l + 1);
     void* g_out = grad_buf(l);
     const int b = l / per, t = l % per;
-    if (t == 0) TRY(run_full_bwd(c, dims, &full[b], input_of(l), g_in, g_out, &full_g[b], w + W.layer, a_of(l)));
+    if (t == 0) TRY(run_full_bwd(c, dims, &full[b], input_of(l), g_in, g_out, &full_g[b], w + W.layer, keep_of(l)));
     else TRY(run_target_bwd(c, dims, &tgt[b * k_target + t - 1], input_of(l), g_in, g_out,
-                            &tgt_g[b * k_target + t - 1], w + W.layer, a_of(l)));
+                            &tgt_g[b * k_target + t - 1], w + W.layer, keep_of(l)));
   }
   return MTFM_OK;
 }

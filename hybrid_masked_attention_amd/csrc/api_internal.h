@@ -48,24 +48,37 @@ struct KvOut {
   void* vt = nullptr;
   int64_t ldvt = 0;
 };
-// a_keep: if set, the attention output A (query rows x H*dh, bf16) is written
-// there instead of the workspace, for a backward pass to reuse.
+// Intermediates of one layer's forward pass kept for its backward (bf16,
+// caller-placed).  Full layer: X~ [R][d], Z = U|Q'|K|V [R][zw] and its
+// pre-activations [R][zw], A [R][H*dh].  Target layer: X~ [R][d], K|V and
+// pre-activations [R][2 G*dh] (every packed row), Z_T and pre-activations
+// [T][zw], A_T [T][H*dh].  A forward given one writes them there (and the
+// pre-activations, which it otherwise does not produce); a backward given one
+// reads them instead of recomputing GLN1, the projections and the attention.
+// Both passes use the same kernels and shapes, so the values are the same.
+struct FwdKeep {
+  char* xt = nullptr;
+  char* z = nullptr;
+  char* hpre = nullptr;
+  char* kv = nullptr;
+  char* kvpre = nullptr;
+  char* a = nullptr;
+};
 mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, void* x_out, char* ws,
-                     const KvOut* kv = nullptr, void* a_keep = nullptr);
+                     const KvOut* kv = nullptr, const FwdKeep* keep = nullptr);
 mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in, void* x_out,
-                       char* ws, void* a_keep = nullptr);
+                       char* ws, const FwdKeep* keep = nullptr);
 // Workgroup shape of the full-layer attention (1: 32 queries per wave); the
-// backward's recompute takes the same shape, so a kept A equals a recomputed one.
+// backward's recompute takes the same shape, so kept and recomputed A agree.
 int full_attn_half_tiles();
 
-// backward (bwd.hip); a_pre: the layer's attention output from its forward pass
-// (as kept by run_full / run_target), else it is recomputed
+// backward (bwd.hip)
 int64_t bwd_ws_bytes(const MetaPlan& p, const mtfm_dims* d, int op);
 mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, const void* dy,
-                         void* dx, const mtfm_full_grad* g, char* ws, const void* a_pre = nullptr);
+                         void* dx, const mtfm_full_grad* g, char* ws, const FwdKeep* keep = nullptr);
 mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in,
                            const void* dy, void* dx, const mtfm_target_grad* g, char* ws,
-                           const void* a_pre = nullptr);
+                           const FwdKeep* keep = nullptr);
 
 // RAII bracket of one launch with HIP events when its kernel class is enabled
 // (see mtfm_timing_enable); a no-op otherwise.

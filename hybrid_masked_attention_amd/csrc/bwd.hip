@@ -111,7 +111,7 @@ int64_t bwd_ws_bytes(const MetaPlan& p, const mtfm_dims* d, int op) {
 
 // ---------------------------------------------------------------------------
 mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, const void* x_in, const void* dy,
-                         void* dx, const mtfm_full_grad* gr, char* ws, const void* a_pre) {
+                         void* dx, const mtfm_full_grad* gr, char* ws, const FwdKeep* keep) {
   TRY(check_bwd_dims(d));
   const MetaPlan& p = c.plan;
   const hipStream_t s = c.s;
@@ -119,10 +119,10 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
   const int hd = H * dh, gd = G * dh, zw = 2 * hd + 2 * gd;
   const int R = (int)p.n_rows;
   const BwdWs L = bwd_layout(p, d, MTFM_OP_FULL_BWD);
-  bf16* xt = (bf16*)(ws + L.xt);
-  bf16* z = (bf16*)(ws + L.z);
-  bf16* hpre = (bf16*)(ws + L.hpre);
-  bf16* a = a_pre ? (bf16*)a_pre : (bf16*)(ws + L.a);
+  bf16* xt = (bf16*)(keep ? keep->xt : ws + L.xt);
+  bf16* z = (bf16*)(keep ? keep->z : ws + L.z);
+  bf16* hpre = (bf16*)(keep ? keep->hpre : ws + L.hpre);
+  bf16* a = (bf16*)(keep ? keep->a : ws + L.a);
   bf16* y = (bf16*)(ws + L.y);
   bf16* wot = (bf16*)(ws + L.wot);
   bf16* w1t = (bf16*)(ws + L.w1t);
@@ -135,34 +135,36 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
   float* pg = (float*)(ws + L.pg);
   if (R == 0) return MTFM_OK;
 
-  // ---- forward recompute (keeps pre-activations)
-  GlnArgs g1{};
-  g1.rows = R; g1.D = D; g1.x = x_in; g1.ldx = D; g1.y = xt; g1.ldy = D;
-  g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
-  TRY(timed_gln(g1, MTFM_BF16, s));
-  GemmArgs gp{};
-  gp.M = R; gp.N = zw; gp.K = D; gp.groups = 1;
-  gp.A = xt; gp.lda = D; gp.amap = identity_map();
-  gp.B[0] = w->w_uqkv; gp.bn[0] = zw; gp.ldb = D;
-  gp.cmap = identity_map();
-  gp.epi = EPI_SILU_SPLIT;
-  gp.dst[0] = z; gp.ld[0] = zw; gp.cend[0] = hd; gp.scale[0] = 1.f;
-  gp.dst[1] = z + hd; gp.ld[1] = zw; gp.cend[1] = 2 * hd; gp.scale[1] = q_scale(dh);
-  gp.dst[2] = z + 2 * hd; gp.ld[2] = zw; gp.cend[2] = zw; gp.scale[2] = 1.f;
-  gp.cend[3] = zw;
-  gp.pre = hpre; gp.ldpre = zw;
-  if (!a_pre) { gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd; }
-  TRY(timed_gemm(MTFM_K_GEMM_UQKV, gp, MTFM_BF16, s));
-  if (!a_pre) {
-    AttnArgs aa{};
-    aa.q = z + hd; aa.ldq = zw; aa.k = z + 2 * hd; aa.ldk = zw; aa.v = z + 2 * hd + gd; aa.ldv = zw;
-    aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
-    aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
-    aa.a = a; aa.lda = hd;
-    aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles; aa.half_tiles = full_attn_half_tiles();
-    aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
-    aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
-    TRY(timed_attention(MTFM_K_ATTN_FULL, aa, MTFM_BF16, s));
+  // ---- forward recompute (keeps pre-activations), unless the forward pass kept it
+  if (!keep) {
+    GlnArgs g1{};
+    g1.rows = R; g1.D = D; g1.x = x_in; g1.ldx = D; g1.y = xt; g1.ldy = D;
+    g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
+    TRY(timed_gln(g1, MTFM_BF16, s));
+    GemmArgs gp{};
+    gp.M = R; gp.N = zw; gp.K = D; gp.groups = 1;
+    gp.A = xt; gp.lda = D; gp.amap = identity_map();
+    gp.B[0] = w->w_uqkv; gp.bn[0] = zw; gp.ldb = D;
+    gp.cmap = identity_map();
+    gp.epi = EPI_SILU_SPLIT;
+    gp.dst[0] = z; gp.ld[0] = zw; gp.cend[0] = hd; gp.scale[0] = 1.f;
+    gp.dst[1] = z + hd; gp.ld[1] = zw; gp.cend[1] = 2 * hd; gp.scale[1] = q_scale(dh);
+    gp.dst[2] = z + 2 * hd; gp.ld[2] = zw; gp.cend[2] = zw; gp.scale[2] = 1.f;
+    gp.cend[3] = zw;
+    gp.pre = hpre; gp.ldpre = zw;
+    gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd;
+    TRY(timed_gemm(MTFM_K_GEMM_UQKV, gp, MTFM_BF16, s));
+    {
+      AttnArgs aa{};
+      aa.q = z + hd; aa.ldq = zw; aa.k = z + 2 * hd; aa.ldk = zw; aa.v = z + 2 * hd + gd; aa.ldv = zw;
+      aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
+      aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
+      aa.a = a; aa.lda = hd;
+      aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles; aa.half_tiles = full_attn_half_tiles();
+      aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
+      aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+      TRY(timed_attention(MTFM_K_ATTN_FULL, aa, MTFM_BF16, s));
+    }
   }
   GlnArgs g2{};
   g2.rows = R; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd; g2.gate = z; g2.ldg = zw;
@@ -241,7 +243,7 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
 
 // ---------------------------------------------------------------------------
 mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in,
-                           const void* dy, void* dx, const mtfm_target_grad* gr, char* ws, const void* a_pre) {
+                           const void* dy, void* dx, const mtfm_target_grad* gr, char* ws, const FwdKeep* keep) {
   TRY(check_bwd_dims(d));
   const MetaPlan& p = c.plan;
   const hipStream_t s = c.s;
@@ -249,12 +251,13 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
   const int hd = H * dh, gd = G * dh, zw = 2 * hd + 2 * gd;
   const int R = (int)p.n_rows, T = (int)p.n_t_rows, P = (int)p.n_parents, C = (int)p.n_ctx_rows, S = p.split;
   const BwdWs L = bwd_layout(p, d, MTFM_OP_TARGET_BWD);
-  bf16* xt = (bf16*)(ws + L.xt);
-  bf16* zt = (bf16*)(ws + L.z);
-  bf16* ztpre = (bf16*)(ws + L.hpre);
-  bf16* kv = (bf16*)(ws + L.kv);
-  bf16* kvpre = (bf16*)(ws + L.kvpre);
-  bf16* a = a_pre ? (bf16*)a_pre : (bf16*)(ws + L.a);
+  if (keep && p.n_t_rows == 0) keep = nullptr;   // the forward kept nothing for a layer without T rows
+  bf16* xt = (bf16*)(keep ? keep->xt : ws + L.xt);
+  bf16* zt = (bf16*)(keep ? keep->z : ws + L.z);
+  bf16* ztpre = (bf16*)(keep ? keep->hpre : ws + L.hpre);
+  bf16* kv = (bf16*)(keep ? keep->kv : ws + L.kv);
+  bf16* kvpre = (bf16*)(keep ? keep->kvpre : ws + L.kvpre);
+  bf16* a = (bf16*)(keep ? keep->a : ws + L.a);
   bf16* y = (bf16*)(ws + L.y);
   bf16* wot = (bf16*)(ws + L.wot);
   bf16* wtk = (bf16*)(ws + L.w1t);   // [S][D][zw]: transposed [W_u; W_q[k]; W_kv]
@@ -271,12 +274,14 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
   const RowMap ctx_rows = list_map(c.meta.ctx_rows);
   if (R == 0) return MTFM_OK;
 
-  // ---- forward recompute
-  GlnArgs g1{};
-  g1.rows = R; g1.D = D; g1.x = x_in; g1.ldx = D; g1.y = xt; g1.ldy = D;
-  g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
-  TRY(timed_gln(g1, MTFM_BF16, s));
-  if (C > 0) {
+  // ---- forward recompute, unless the forward pass kept it
+  if (!keep) {
+    GlnArgs g1{};
+    g1.rows = R; g1.D = D; g1.x = x_in; g1.ldx = D; g1.y = xt; g1.ldy = D;
+    g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
+    TRY(timed_gln(g1, MTFM_BF16, s));
+  }
+  if (C > 0 && !keep) {
     // K, V (and their pre-activations) of every packed row, V also transposed
     GemmArgs gk{};
     gk.M = R; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
@@ -286,10 +291,10 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = 2 * gd; gk.scale[0] = 1.f;
     gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd;
     gk.pre = kvpre; gk.ldpre = 2 * gd;
-    if (!a_pre) { gk.vt = ws + L.vt; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd; }
+    gk.vt = ws + L.vt; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
     TRY(timed_gemm(MTFM_K_GEMM_KV, gk, MTFM_BF16, s));
   }
-  if (T > 0) {
+  if (T > 0 && !keep) {
     GemmArgs gt{};
     gt.M = P; gt.N = zw; gt.K = D; gt.groups = S;
     gt.A = xt; gt.lda = D; gt.amap = list_map(c.meta.parent_row); gt.amap_zadd = 1; gt.a_rows = c.plan.n_rows;
@@ -305,7 +310,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     gt.cend[3] = zw;
     gt.pre = ztpre; gt.ldpre = zw;
     TRY(timed_gemm(MTFM_K_GEMM_T, gt, MTFM_BF16, s));
-    if (!a_pre) {
+    {
       AttnArgs aa{};
       aa.q = zt + hd; aa.ldq = zw; aa.k = kv; aa.ldk = 2 * gd; aa.v = kv + gd; aa.ldv = 2 * gd;
       aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
@@ -316,6 +321,8 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
       aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
       TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, MTFM_BF16, s));
     }
+  }
+  if (T > 0) {
     GlnArgs g2{};
     g2.rows = T; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd; g2.gate = zt; g2.ldg = zw;
     g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;

@@ -248,17 +248,24 @@ mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims,
  * dx = dL/dX_in and every layer's fp32 weight/GLN gradients (overwritten):
  * full_g[b] for the full layer of block b, tgt_g[b * k_target + t] for its
  * target layer t.  One forward pass keeps the inputs of layers 1 .. L-1 in
- * the workspace (bf16, as the forward passes them on) and the attention
- * outputs of layers 0 .. L-2 (each layer's backward reuses it instead of
- * recomputing the attention; the result is the same bit for bit); then each
- * layer's backward runs from the last to the first, the gradient handed
- * between layers stored in dims->dtype.  dx also serves as one of the two
+ * the workspace (bf16, as the forward passes them on); then each layer's
+ * backward runs from the last to the first, the gradient handed between
+ * layers stored in dims->dtype.  dx also serves as one of the two
  * intermediate gradient buffers, so it must not alias x_in or dy.
- * bf16 only (MTFM_E_UNSUPPORTED otherwise).  ws: at least
- * mtfm_backbone_bwd_workspace_bytes(batch, dims, n_blocks, k_target) bytes.
+ * bf16 only (MTFM_E_UNSUPPORTED otherwise).
+ * Workspace, two sizes: with at least
+ * mtfm_backbone_bwd_workspace_bytes(batch, dims, n_blocks, k_target) bytes the
+ * forward pass also keeps each layer's intermediates (normalised input,
+ * projections and their pre-activations, attention output; about 14 GB for
+ * 160 users of ~1,500 rows), so no layer backward recomputes them; with at
+ * least mtfm_backbone_bwd_min_workspace_bytes(...) bytes (but less than the
+ * full size) each layer backward recomputes them.  Both give the same
+ * gradients bit for bit.  Fewer bytes than the minimum: MTFM_E_WORKSPACE.
  * Stream-ordered, no host synchronisation. */
 size_t mtfm_backbone_bwd_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks,
                                          int32_t k_target);
+size_t mtfm_backbone_bwd_min_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks,
+                                             int32_t k_target);
 mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
                               const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
                               const void* x_in, const void* dy, void* dx, const mtfm_full_grad* full_g,

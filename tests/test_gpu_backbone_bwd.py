@@ -1,7 +1,8 @@
 """GPU parity of the whole-backbone backward (the training step's gradient pass).
 
-mtfm_backbone_bwd keeps every layer's input from one forward pass and runs
-the layers' backward from the last to the first.  The device stores those
+mtfm_backbone_bwd keeps every layer's input (and, with the full workspace,
+its intermediates) from one forward pass and runs the layers' backward from
+the last to the first.  The device stores those
 activations and the gradient handed from layer to layer in bf16; the oracle
 (float64, same bf16-rounded inputs) mirrors both roundings at the layer
 boundaries.  Every gradient tensor -- dX and each layer's weights and GLN
@@ -37,14 +38,19 @@ def _grad_like(w, keys):
     return {k: torch.full(tuple(w[k].shape), float("nan"), dtype=torch.float32, device="cuda") for k in keys}
 
 
-def _device(wl):
+def _device(wl, min_workspace=False):
+    """mtfm_backbone_bwd on the device; min_workspace: the smallest accepted workspace (every layer
+    backward recomputes its intermediates) instead of the full one (the forward keeps them)."""
     import torch
     from hybrid_masked_attention_amd import binding as B
     from hybrid_masked_attention_amd.tensors import DeviceWorkload, to_device
     dw = DeviceWorkload(wl)
     meta = B.mask_build(dw.batch)
     n = B.backbone_bwd_workspace_bytes(dw.batch, dw.dims, wl.n_blocks, wl.k_target)
-    assert n > 0
+    n_min = B.backbone_bwd_min_workspace_bytes(dw.batch, dw.dims, wl.n_blocks, wl.k_target)
+    assert 0 < n_min < n
+    if min_workspace:
+        n = n_min
     ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     dy = to_device(wl.dy, "bf16")
     dx = torch.empty_like(dw.x)
@@ -134,6 +140,19 @@ def test_backbone_backward_layer_by_layer(split):
         for k in grads[l]:
             r.close(f"layer {l} {name} d{k}", grads[l][k], ref[k])
     r.check()
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_backbone_backward_kept_and_recomputed_intermediates_agree(split):
+    """With the full workspace the forward keeps every layer's intermediates, with the minimum each
+    layer backward recomputes them: the same kernels and shapes, so the gradients agree bit for bit."""
+    wl = _workload(split, 90 + split, 2, 2, SMALL_LENS, f"bb_bwd_modes_s{split}")
+    dx_k, fg_k, tg_k, _, _ = _device(wl)
+    dx_r, fg_r, tg_r, _, _ = _device(wl, min_workspace=True)
+    np.testing.assert_array_equal(dx_k, dx_r)
+    for a, b in zip(fg_k + tg_k, fg_r + tg_r):
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k])
 
 
 # End-to-end bar: to first order, the error of a layer's gradients is its own backward's error
