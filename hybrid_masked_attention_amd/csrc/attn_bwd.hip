@@ -348,8 +348,8 @@ __global__ __launch_bounds__(64 * R, 3) void attn_bwd_dq_kernel(AttnBwdArgs g) {
 // --------------------------------------------------------------------------
 // dK / dV kernel.  One workgroup per (64-key context tile, group) with 2 HC
 // waves: wave w takes key half w % 2 (32 keys, lane = key) and head w / 2 of
-// the current chunk of HC heads (all R heads when R <= 4, two passes when
-// R = 8); every wave sums its heads into one dK, dV accumulator.  The user's
+// the current chunk of HC heads (R / HC passes over the query stages); every
+// wave sums its heads into one dK, dV accumulator.  The user's
 // query tiles that see the keys are walked in stages of 32 queries: per head
 // Q', dA/n hi and lo (32 rows x 128 B each), plus the 32 prefix limits, are
 // brought into an LDS ring by buffer DMA two stages ahead.  S and dP come out
@@ -361,14 +361,17 @@ constexpr int KV_TENSOR = 32 * 128;        // one 32-row tensor of a head
 constexpr int KV_HEAD = 3 * KV_TENSOR;     // Q', dA/n hi, dA/n lo
 constexpr int KV_CPW = 6;                  // 1 KB DMA chunks per wave per stage
 
+// Two heads per pass (74.5 KB of LDS) let two workgroups share a CU, so one
+// workgroup's barrier waits and prologue / epilogue overlap the other's work;
+// measured faster than four heads per pass (one workgroup per CU) and than one.
 template <int R> struct DkvShape {
-  static constexpr int HC = R < 4 ? R : 4;          // heads per pass
+  static constexpr int HC = R < 2 ? R : 2;          // heads per pass
   static constexpr int NW = 2 * HC;                 // waves
   static constexpr int STAGE = HC * KV_HEAD + 256;  // + prefix limits (64 lanes x 4 B)
 };
 
 template <int R>
-__global__ __launch_bounds__(128 * DkvShape<R>::HC, 1) void attn_bwd_dkv_kernel(AttnBwdArgs g) {
+__global__ __launch_bounds__(128 * DkvShape<R>::HC, 2) void attn_bwd_dkv_kernel(AttnBwdArgs g) {
   using SH = DkvShape<R>;
   constexpr int HC = SH::HC, NW = SH::NW, STAGE = SH::STAGE;
   constexpr int NPASS = R / HC;
