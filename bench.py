@@ -243,8 +243,9 @@ def main():
             train_step()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        train = {"what": "mtfm_backbone_bwd: forward keeping 15 layer inputs and attention outputs + backward "
-                         "of all 16 layers (dX and every weight / GLN gradient), incl. mask build",
+        train = {"what": "mtfm_backbone_bwd with the full workspace: forward keeping 15 layers' inputs and "
+                         "intermediates + backward of all 16 layers (dX and every weight / GLN gradient), "
+                         "incl. mask build",
                  "steps": args.train_steps, "ms_per_step": 1000.0 * el / args.train_steps,
                  "user_samples_per_s": wl.batch.n_users * args.train_steps / el,
                  "workspace_GiB": nb / 2 ** 30}
