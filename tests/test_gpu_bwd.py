@@ -71,10 +71,10 @@ def _check(wl, kind, dy_np, users=None):
     return dx, grads
 
 
-def _small(lens, split, seed):
+def _small(lens, split, seed, heads=(8, 2)):
     rng = np.random.default_rng(seed)
     batch = synth.make_batch(rng, np.asarray(lens, np.int32), split)
-    dims = synth.Dims(512, 8, 2, 64)
+    dims = synth.Dims(512, heads[0], heads[1], 64)
     x = rng.standard_normal((batch.total_rows, 512)).astype(np.float32)
     wf = synth.full_weights(rng, dims, 0.05, 0.05)
     wt = synth.target_weights(rng, dims, split, 0.05, 0.05)
@@ -89,6 +89,15 @@ SMALL_LENS = [[130, 64, 17], [1, 0, 1], [63, 1, 0], [0, 0, 3], [65, 63, 33], [5,
 @pytest.mark.parametrize("kind", ["full", "target"])
 def test_backward_small_ragged(kind, split):
     wl = _small(SMALL_LENS, split, 70 + split)
+    _check(wl, kind, wl.dy)
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (8, 4), (8, 1)])
+@pytest.mark.parametrize("kind", ["full", "target"])
+def test_backward_other_gqa_ratios(kind, heads):
+    """r = H/G of 1, 2 and 8 query heads per KV group: the dQ kernel's DMA split over r waves and
+    the dK/dV kernel's head passes (one head per pass at r = 1, four passes at r = 8)."""
+    wl = _small(SMALL_LENS, 4, 75 + heads[1], heads)
     _check(wl, kind, wl.dy)
 
 
