@@ -9,6 +9,7 @@
 // and hit its L2.
 
 #include <algorithm>
+#include <cstdlib>
 
 #include "gemm.h"
 
@@ -802,8 +803,12 @@ mtfm_status launch_gemm_tn(const GemmTNArgs& g, hipStream_t s) {
   // the DMA form needs the operands' row counts (its loads are bounded by them,
   // with 32-bit offsets) and 16-byte aligned rows
   const int64_t a_bytes = g.a_rows * g.lda * 2, b_bytes = g.b_rows * g.ldb * 2;
-  const bool dma = g.a_rows > 0 && g.b_rows > 0 && a_bytes < (int64_t)kOobOffset && b_bytes < (int64_t)kOobOffset &&
-                   g.a_zoff == 0 && aligned16(g.A) && aligned16(g.B);
+  // (MTFM_GEMM_TN_STAGED=1 forces the register-staged kernel: both accumulate the
+  // same rows in the same order, so they agree bit for bit)
+  const char* forced = std::getenv("MTFM_GEMM_TN_STAGED");
+  const bool dma = !(forced && forced[0] == '1') && g.a_rows > 0 && g.b_rows > 0 &&
+                   a_bytes < (int64_t)kOobOffset && b_bytes < (int64_t)kOobOffset && g.a_zoff == 0 &&
+                   aligned16(g.A) && aligned16(g.B);
   if (dma) {
     gemm_tn_dma_kernel<<<dim3(tiles * n_split, 1, g.groups), 256, 0, s>>>(g, n_split);
     MTFM_LAUNCH_CHECK("gemm_tn_dma");

@@ -102,6 +102,20 @@ def test_backward_other_gqa_ratios(kind, heads):
 
 
 @pytest.mark.parametrize("kind", ["full", "target"])
+def test_weight_gradient_gemm_paths_agree(kind, monkeypatch):
+    """The register-staged weight-gradient GEMM (used for operands past 2 GiB, forced here by
+    MTFM_GEMM_TN_STAGED=1) and the DMA one accumulate the same rows in the same order: every
+    gradient agrees bit for bit."""
+    wl = _small(SMALL_LENS, 4, 79)
+    dx1, g1 = _device_bwd(wl, kind, wl.dy)[:2]
+    monkeypatch.setenv("MTFM_GEMM_TN_STAGED", "1")
+    dx2, g2 = _device_bwd(wl, kind, wl.dy)[:2]
+    np.testing.assert_array_equal(dx1, dx2)
+    for k in g1:
+        np.testing.assert_array_equal(g1[k], g2[k])
+
+
+@pytest.mark.parametrize("kind", ["full", "target"])
 def test_backward_config4_two_user_slice(kind):
     """Config 4's shapes (4096 H + 512 R + 256 x 4 T rows, d 1024, 16Q/4KV) on its first two users."""
     full = synth.config4()
