@@ -333,15 +333,24 @@ __global__ __launch_bounds__(64 * R, 3) void attn_bwd_dq_kernel(AttnBwdArgs g) {
     }
   }
   kv_wait_vm<0>();   // the ring's trailing (empty) loads land before the workgroup ends
-  // dq layout: lane = dim nb*32 + l32, registers = queries 8(i/4) + 4hi + i%4
+  // dq layout: lane = dim nb*32 + l32, registers = queries 8(i/4) + 4hi + i%4.  A row
+  // with a self key (a T row) adds the self kernel's term, written before this kernel.
   const int hd = g.H * DH;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int i = 0; i < 16; ++i) {
+    const int qi = 8 * (i >> 2) + 4 * hi + (i & 3);
+    if (qi >= nrows) continue;
+    const int64_t qr = qrow0 + qi;
+    const bool self = g.n[grow0 + qi] - g.p[grow0 + qi] > 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qi = 8 * (i >> 2) + 4 * hi + (i & 3);
-      if (qi < nrows) g.dq[(int64_t)(qrow0 + qi) * hd + h * DH + nb * 32 + l32] = dq[nb][i];
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = h * DH + nb * 32 + l32;
+      float v = dq[nb][i];
+      if (self) v += g.dq[qr * hd + col];
+      const float hqv = (float)g.hq[qr * g.ldhq + col];
+      g.dhq[qr * g.lddhq + col] = (bf16)(v * g.dq_scale * dsilu_f(hqv));
     }
+  }
 }
 
 
@@ -612,7 +621,7 @@ __global__ __launch_bounds__(256) void attn_bwd_self_kernel(AttnBwdArgs g) {
     float pv, dsg;
     silu_and_grad(sp, &pv, &dsg);
     const float ds = dpv * dsg;
-    g.dq[qs * hd + h * DH + c] += ds * k;
+    g.dq[qs * hd + h * DH + c] = ds * k;   // added by the dQ kernel, which runs next
     dk += ds * q * kLn2;
     dv += pv * da;
   }
@@ -624,6 +633,11 @@ __global__ __launch_bounds__(256) void attn_bwd_self_kernel(AttnBwdArgs g) {
 
 template <int R>
 mtfm_status launch_r(const AttnBwdArgs& a, int64_t n_key_tiles, hipStream_t s) {
+  // the self term first: the dQ kernel adds it to the T rows' dQ
+  if (a.n_self_rows > 0) {
+    attn_bwd_self_kernel<<<(unsigned)((a.n_self_rows * a.G + 3) / 4), 256, 0, s>>>(a);
+    MTFM_LAUNCH_CHECK("attn_bwd_self");
+  }
   if (a.nqtiles > 0) {
     attn_bwd_dq_kernel<R><<<(unsigned)(a.nqtiles * a.G * 2), 64 * R, 0, s>>>(a);
     MTFM_LAUNCH_CHECK("attn_bwd_dq");
@@ -631,10 +645,6 @@ mtfm_status launch_r(const AttnBwdArgs& a, int64_t n_key_tiles, hipStream_t s) {
   if (n_key_tiles > 0 && a.nqtiles > 0) {
     attn_bwd_dkv_kernel<R><<<(unsigned)(n_key_tiles * a.G), 128 * DkvShape<R>::HC, 0, s>>>(a);
     MTFM_LAUNCH_CHECK("attn_bwd_dkv");
-  }
-  if (a.n_self_rows > 0) {
-    attn_bwd_self_kernel<<<(unsigned)((a.n_self_rows * a.G + 3) / 4), 256, 0, s>>>(a);
-    MTFM_LAUNCH_CHECK("attn_bwd_self");
   }
   return MTFM_OK;
 }

@@ -210,12 +210,9 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
     b.ks = z + 2 * hd; b.ldks = zw; b.vs = z + 2 * hd + gd; b.ldvs = zw;
     b.hks = hpre + 2 * hd; b.ldhks = zw; b.hvs = hpre + 2 * hd + gd; b.ldhvs = zw;
     b.dhks = dh_ + 2 * hd; b.lddhks = zw; b.dhvs = dh_ + 2 * hd + gd; b.lddhvs = zw;
+    b.hq = hpre + hd; b.ldhq = zw; b.dhq = dh_ + hd; b.lddhq = zw; b.dq_scale = 1.0f / std::sqrt((float)dh);
     TimedLaunch tl(MTFM_K_BWD, s);
     TRY(launch_attn_bwd(b, p.n_key_tiles, s));
-    DqFinishArgs f{};
-    f.rows = R; f.width = hd; f.dq = dq; f.hq = hpre + hd; f.ldh = zw; f.dhq = dh_ + hd; f.lddh = zw;
-    f.scale = 1.0f / std::sqrt((float)dh);
-    TRY(launch_dq_finish(f, s));
   }
   // ---- input projection and GLN1
   TRY(tn(s, L, ws, zw, D, R, dh_, zw, identity_map(), R, xt, D, identity_map(), R, gr->w_uqkv, 0));
@@ -376,14 +373,11 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     b.ks = zt + 2 * hd; b.ldks = zw; b.vs = zt + 2 * hd + gd; b.ldvs = zw;
     b.hks = ztpre + 2 * hd; b.ldhks = zw; b.hvs = ztpre + 2 * hd + gd; b.ldhvs = zw;
     b.dhks = dht + 2 * hd; b.lddhks = zw; b.dhvs = dht + 2 * hd + gd; b.lddhvs = zw;
+    b.hq = ztpre + hd; b.ldhq = zw; b.dhq = dht + hd; b.lddhq = zw; b.dq_scale = 1.0f / std::sqrt((float)dh);
     {
       TimedLaunch tl(MTFM_K_BWD, s);
       TRY(launch_attn_bwd(b, p.n_key_tiles, s));
     }
-    DqFinishArgs f{};
-    f.rows = T; f.width = hd; f.dq = dq; f.hq = ztpre + hd; f.ldh = zw; f.dhq = dht + hd; f.lddh = zw;
-    f.scale = 1.0f / std::sqrt((float)dh);
-    TRY(launch_dq_finish(f, s));
   }
 
   // ---- weight gradients of the input projections

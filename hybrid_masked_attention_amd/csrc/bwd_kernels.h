@@ -44,20 +44,11 @@ struct TransposeArgs {
   bf16* out; int64_t ldo;           // out[c][r]
 };
 
-struct DqFinishArgs {
-  int32_t rows, width;
-  const float* dq;                  // [rows][width] accumulated sum_j dS_ij k_j
-  const bf16* hq; int64_t ldh;      // pre-activation of Q
-  bf16* dhq; int64_t lddh;          // out
-  float scale;                      // 1 / sqrt(dh)
-};
-
 int gln_bwd_grid(int rows);
 mtfm_status launch_gln2_bwd(const Gln2BwdArgs& a, hipStream_t s);
 mtfm_status launch_gln1_bwd(const Gln1BwdArgs& a, hipStream_t s);
 mtfm_status launch_param_reduce(const float* pg, int blocks, int D, float* dgamma, float* dbeta, hipStream_t s);
 mtfm_status launch_transpose(const TransposeArgs& a, hipStream_t s);
-mtfm_status launch_dq_finish(const DqFinishArgs& a, hipStream_t s);
 
 // Attention backward ([explainer] §4.1 attention, differentiated; [blog]
 // §6.1 lists the FA2-style backward of the masked attention).  Inputs are the
@@ -77,8 +68,11 @@ struct AttnBwdArgs {
   const int32_t* p; const int32_t* n;
   const int32_t* lens;
   int32_t H, G;
-  // dQ kernel
-  float* dq;                        // out [query rows][H*dh] (fp32): sum_j dS_ij k_j
+  // dQ kernel: dhq = (sum_j dS_ij k_j + self term) / sqrt(dh) * SiLU'(hq), bf16
+  float* dq;                        // [query rows][H*dh] fp32: the self kernel's term of T rows
+  const bf16* hq; int64_t ldhq;     // pre-activation of Q (query space)
+  bf16* dhq; int64_t lddhq;         // out
+  float dq_scale;                   // 1 / sqrt(dh)
   // dK / dV kernel (context keys)
   const bf16* hk; int64_t ldhk;     // pre-activations of K, V of context rows (packed rows)
   const bf16* hv; int64_t ldhv;

@@ -229,14 +229,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
 }
 
 // dH_Q = dQ * scale * SiLU'(h_Q)   (fp32 accumulator -> bf16 pre-activation gradient)
-__global__ __launch_bounds__(256) void dq_finish_kernel(DqFinishArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)a.rows * a.width) return;
-  const int row = (int)(i / a.width), c = (int)(i % a.width);
-  const float h = (float)a.hq[(int64_t)row * a.ldh + c];
-  a.dhq[(int64_t)row * a.lddh + c] = (bf16)(a.dq[(int64_t)row * a.width + c] * a.scale * dsilu(h));
-}
-
 template <int VPL>
 int gln_bwd_blocks(int rows) {
   return std::max(1, std::min(1024, (rows + 3) / 4));
@@ -286,10 +278,3 @@ mtfm_status launch_transpose(const TransposeArgs& a, hipStream_t s) {
   return MTFM_OK;
 }
 
-mtfm_status launch_dq_finish(const DqFinishArgs& a, hipStream_t s) {
-  const int64_t total = (int64_t)a.rows * a.width;
-  if (total <= 0) return MTFM_OK;
-  dq_finish_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);
-  MTFM_LAUNCH_CHECK("dq_finish");
-  return MTFM_OK;
-}
