@@ -361,18 +361,20 @@ __global__ __launch_bounds__(64 * R, 3) void attn_bwd_dq_kernel(AttnBwdArgs g) {
 // wave sums its heads into one dK, dV accumulator.  The user's
 // query tiles that see the keys are walked in stages of 32 queries: per head
 // Q', dA/n hi and lo (32 rows x 128 B each), plus the 32 prefix limits, are
-// brought into an LDS ring by buffer DMA two stages ahead.  S and dP come out
+// brought into an LDS ring by buffer DMA one stage ahead.  S and dP come out
 // with lane = key, so P and dS feed the dV / dK MFMAs straight from registers;
 // the other operand (Q', dA/n with lane = head dimension, 8 queries per lane)
 // is read from the row-major stage with the transposing LDS read.
-constexpr int KV_NS = 3;                   // ring depth (stages)
+constexpr int KV_NS = 2;                   // ring depth (stages)
 constexpr int KV_TENSOR = 32 * 128;        // one 32-row tensor of a head
 constexpr int KV_HEAD = 3 * KV_TENSOR;     // Q', dA/n hi, dA/n lo
 constexpr int KV_CPW = 6;                  // 1 KB DMA chunks per wave per stage
 
-// Two heads per pass (74.5 KB of LDS) let two workgroups share a CU, so one
-// workgroup's barrier waits and prologue / epilogue overlap the other's work;
-// measured faster than four heads per pass (one workgroup per CU) and than one.
+// Two heads per pass and a two-stage ring (49.7 KB of LDS, at most 170 VGPRs)
+// let three workgroups share a CU, so one workgroup's barrier waits, DMA waits
+// and prologue / epilogue overlap the others' work: measured faster than four
+// heads per pass (one workgroup per CU), one head per pass, and two heads with
+// a three-stage ring (two workgroups per CU).
 template <int R> struct DkvShape {
   static constexpr int HC = R < 2 ? R : 2;          // heads per pass
   static constexpr int NW = 2 * HC;                 // waves
@@ -380,7 +382,7 @@ template <int R> struct DkvShape {
 };
 
 template <int R>
-__global__ __launch_bounds__(128 * DkvShape<R>::HC, 2) void attn_bwd_dkv_kernel(AttnBwdArgs g) {
+__global__ __launch_bounds__(128 * DkvShape<R>::HC, 3) void attn_bwd_dkv_kernel(AttnBwdArgs g) {
   using SH = DkvShape<R>;
   constexpr int HC = SH::HC, NW = SH::NW, STAGE = SH::STAGE;
   constexpr int NPASS = R / HC;
@@ -569,33 +571,39 @@ __global__ __launch_bounds__(128 * DkvShape<R>::HC, 2) void attn_bwd_dkv_kernel(
     ++it;
   }
   // drain the ring (the last issued stages are empty), then sum the heads of
-  // each key half in a fixed order and apply SiLU' of the K / V pre-activations
+  // each key half in a fixed order and apply SiLU' of the K / V pre-activations:
+  // dK first, then dV, each through a [NW][32 keys][64 dims] fp32 buffer in the
+  // (then idle) ring
+  static_assert(NW * 32 * DH * 4 <= KV_NS * STAGE, "reduction buffer fits in the ring");
   kv_wait_vm<0>();
   kv_barrier();
-  float* red = reinterpret_cast<float*>(lds);   // [NW][2][32 keys][64 dims]
+  float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int part = 0; part < 2; ++part) {
+    const f32x16* acc = part ? dv : dk;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kr = 8 * (i >> 2) + 4 * hi + (i & 3);
-      red[((wave * 2 + 0) * 32 + kr) * DH + nb * 32 + l32] = dk[nb][i];
-      red[((wave * 2 + 1) * 32 + kr) * DH + nb * 32 + l32] = dv[nb][i];
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kr = 8 * (i >> 2) + 4 * hi + (i & 3);
+        red[(wave * 32 + kr) * DH + nb * 32 + l32] = acc[nb][i];
+      }
+    __syncthreads();
+    const bf16* hsrc = part ? g.hv : g.hk;
+    const int64_t ldh = part ? g.ldhv : g.ldhk;
+    bf16* dst = part ? g.dhv : g.dhk;
+    const int64_t ldd = part ? g.lddhv : g.lddhk;
+    for (int e = tid; e < 64 * DH; e += 64 * NW) {
+      const int kr64 = e / DH, c = e % DH;
+      const int half = kr64 >> 5, kr = kr64 & 31;
+      if (kt * 64 + kr64 >= lctx) continue;
+      float sum = 0.f;
+      for (int w = 0; w < HC; ++w) sum += red[((2 * w + half) * 32 + kr) * DH + c];
+      const int64_t row = urow0 + kt * 64 + kr64;
+      const float h = (float)hsrc[row * ldh + grp * DH + c];
+      dst[row * ldd + grp * DH + c] = (bf16)(sum * kLn2 * dsilu_f(h));
     }
-  __syncthreads();
-  for (int e = tid; e < 64 * DH; e += 64 * NW) {
-    const int kr64 = e / DH, c = e % DH;
-    const int half = kr64 >> 5, kr = kr64 & 31;
-    if (kt * 64 + kr64 >= lctx) continue;
-    float sk = 0.f, sv = 0.f;
-    for (int w = 0; w < HC; ++w) {
-      sk += red[(((2 * w + half) * 2 + 0) * 32 + kr) * DH + c];
-      sv += red[(((2 * w + half) * 2 + 1) * 32 + kr) * DH + c];
-    }
-    const int64_t row = urow0 + kt * 64 + kr64;
-    const float hk = (float)g.hk[row * g.ldhk + grp * DH + c];
-    const float hv = (float)g.hv[row * g.ldhv + grp * DH + c];
-    g.dhk[row * g.lddhk + grp * DH + c] = (bf16)(sk * kLn2 * dsilu_f(hk));
-    g.dhv[row * g.lddhv + grp * DH + c] = (bf16)(sv * kLn2 * dsilu_f(hv));
+    __syncthreads();
   }
 }
 
