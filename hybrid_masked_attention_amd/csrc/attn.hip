@@ -81,7 +81,9 @@ MTFM_DEV int perm16(int r) { return (r & ~15) | (r & 3) | (((r >> 3) & 1) << 2) 
 template <int QB> struct AttnShape { static constexpr int AS = QB == 1 ? 2 : 3, WG_PER_CU = QB == 1 ? 3 : 2; };
 
 template <int R, int QB>
-__global__ __launch_bounds__(64 * R, AttnShape<QB>::WG_PER_CU) void attn_bf16_kernel(AttnArgs g) {
+// (the second bound is waves per SIMD: with one wave per head, fewer than four
+// heads per group leave the SIMDs a wave per workgroup or less)
+__global__ __launch_bounds__(64 * R, R >= 4 ? AttnShape<QB>::WG_PER_CU : 1) void attn_bf16_kernel(AttnArgs g) {
   constexpr int AS = AttnShape<QB>::AS;
   constexpr int NT = 64 * R;
   constexpr int CPW = 8 / R;                // 1 KB DMA chunks per wave per 8 KB tile

@@ -184,7 +184,7 @@ MTFM_DEV void dq_tr8(const uint32_t (&a)[2][2], i16x4 (&o)[2][2][2]) {
 }
 
 template <int R>
-__global__ __launch_bounds__(64 * R, 3) void attn_bwd_dq_kernel(AttnBwdArgs g) {
+__global__ __launch_bounds__(64 * R, R >= 4 ? 3 : 1) void attn_bwd_dq_kernel(AttnBwdArgs g) {
   constexpr int CPW = 16 / R;             // 1 KB DMA chunks per wave per stage
   static_assert(CPW * R == 16, "chunks per stage");
   __shared__ __attribute__((aligned(1024))) char lds[DQ_NS * DQ_STAGE];
