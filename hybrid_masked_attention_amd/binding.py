@@ -30,10 +30,13 @@ ENTRY_POINTS = [
     "mtfm_workspace_probe", "mtfm_attn_full", "mtfm_attn_target", "mtfm_backbone_fwd",
     "mtfm_attn_full_bwd", "mtfm_attn_target_bwd", "mtfm_timing_enable", "mtfm_timing_read",
     "mtfm_status_str", "mtfm_last_error", "mtfm_backbone_workspace_bytes",
-    "mtfm_backbone_bwd_workspace_bytes", "mtfm_backbone_bwd_min_workspace_bytes", "mtfm_backbone_bwd", "mtfm_kv_cache_bytes", "mtfm_serve_workspace_bytes",
+    "mtfm_backbone_bwd_workspace_bytes", "mtfm_backbone_bwd_min_workspace_bytes", "mtfm_backbone_bwd",
+    "mtfm_kv_cache_bytes", "mtfm_serve_workspace_bytes",
     "mtfm_serve_context", "mtfm_serve_targets", "mtfm_autosplit", "mtfm_token_ffn_workspace_bytes",
     "mtfm_token_ffn", "mtfm_token_pool", "mtfm_backbone_v2_workspace_bytes", "mtfm_backbone_v2_fwd",
+    "mtfm_mask_dense", "mtfm_validate_batch",
 ]
+BAD_ACTION_ORDER, BAD_LENGTHS = 1, 2
 SERVE_CONTEXT, SERVE_TARGETS = 0, 1
 K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD, K_V2 = range(10)
 
@@ -96,6 +99,9 @@ def lib():
     L.mtfm_meta_bytes.argtypes = [P(CBatch)]; L.mtfm_meta_bytes.restype = c_size_t
     L.mtfm_meta_layout_of.argtypes = [P(CBatch), P(CMetaLayout)]; L.mtfm_meta_layout_of.restype = c_int32
     L.mtfm_mask_build.argtypes = [P(CBatch), c_void_p, c_size_t, c_void_p]; L.mtfm_mask_build.restype = c_int32
+    L.mtfm_mask_dense.argtypes = [P(CBatch), c_void_p, c_int32, c_void_p, c_void_p]
+    L.mtfm_mask_dense.restype = c_int32
+    L.mtfm_validate_batch.argtypes = [P(CBatch), c_void_p, c_void_p]; L.mtfm_validate_batch.restype = c_int32
     L.mtfm_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]; L.mtfm_workspace_bytes.restype = c_size_t
     L.mtfm_backbone_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]
     L.mtfm_backbone_workspace_bytes.restype = c_size_t
@@ -231,6 +237,25 @@ def mask_build(batch: DeviceBatch, meta=None, stream=None):
         meta = torch.empty(max(nb, 1), dtype=torch.uint8, device=batch.lens_d.device)
     _check(lib().mtfm_mask_build(ctypes.byref(batch.c), _ptr(meta), meta.numel(), _stream(stream)), "mtfm_mask_build")
     return meta
+
+
+def mask_dense(batch: DeviceBatch, meta, user: int, stream=None):
+    """Debug: the dense [N][N] uint8 visibility matrix of one user (device tensor), from the metadata."""
+    import torch
+    lh, lr, lt = (int(v) for v in batch.lens_h[user])
+    n = lh + lr + batch.split * lt
+    out = torch.empty((n, n), dtype=torch.uint8, device=batch.lens_d.device)
+    _check(lib().mtfm_mask_dense(ctypes.byref(batch.c), _ptr(meta), int(user), _ptr(out) if n else None,
+                                 _stream(stream)), "mtfm_mask_dense")
+    return out
+
+
+def validate_batch(batch: DeviceBatch, stream=None) -> int:
+    """Debug: bit mask of the data-level contract violations of the batch (0 = none); reads the flag back."""
+    import torch
+    flags = torch.full((1,), -1, dtype=torch.int32, device=batch.lens_d.device)
+    _check(lib().mtfm_validate_batch(ctypes.byref(batch.c), _ptr(flags), _stream(stream)), "mtfm_validate_batch")
+    return int(flags.item())
 
 
 def meta_views(meta, layout: CMetaLayout, n_users: int) -> Dict[str, "object"]:

@@ -172,6 +172,28 @@ mtfm_status mtfm_meta_layout_of(const mtfm_batch* batch, mtfm_meta_layout* layou
  * lengths, split not 1 or 4, more than 2^31 - 1 rows), E_WORKSPACE, E_HIP. */
 mtfm_status mtfm_mask_build(const mtfm_batch* batch, void* meta_d, size_t meta_bytes, void* stream);
 
+/* Debug, tiny batches only: the dense visibility matrix of one user,
+ * mask_d[i * N + j] = 1 if query row i of the user sees key row j (rows in the
+ * user's packed order H, R, T; N = L_H + L_R + split * L_T), from the
+ * metadata alone: a context key j < L_H + L_R is visible iff j < p_i, a T key
+ * only to itself ([explainer] §8.2's worked matrix; [blog] §3.2).  mask_d:
+ * device uint8 [N][N], caller-owned.  Errors: E_NULL, E_DIMS (no such user,
+ * N^2 too large), E_HIP. */
+mtfm_status mtfm_mask_dense(const mtfm_batch* batch, const void* meta_d, int32_t user, uint8_t* mask_d,
+                            void* stream);
+
+/* Debug: checks the batch's data-level contracts on the device and writes a
+ * bit mask of the violations found to *flags_d (device int32; 0 = none):
+ * MTFM_BAD_ACTION_ORDER if some user's action times do not ascend,
+ * MTFM_BAD_LENGTHS if the device lengths differ from the host lengths (a
+ * negative length, another total, or a mismatch of an order-sensitive hash of
+ * the per-user lengths).  Reads only within the sizes the host lengths give,
+ * whatever the device holds.  One workgroup; not meant for the hot path.
+ * Errors: E_NULL, E_DIMS, E_HIP. */
+#define MTFM_BAD_ACTION_ORDER 1
+#define MTFM_BAD_LENGTHS 2
+mtfm_status mtfm_validate_batch(const mtfm_batch* batch, int32_t* flags_d, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Layers.  x_in / x_out: device [n_rows][d_model] of dims->dtype.  meta_d:
  * the output of mtfm_mask_build for the same batch.  ws: device workspace of
