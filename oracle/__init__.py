@@ -20,10 +20,13 @@ Modules:
   model  - group LayerNorm, the full-attention layer, the target-attention
            layer and the hybrid backbone (forward).
   grad   - hand-derived backward of both layer types.
+  v2     - the V2 target side (AutoSplit, per-sub-token SwiGLU FFN, token
+           mixing, mean pooling).
+  sparse - 2:4 structured pruning of the projection weights.
 
 Parity status: every function here is pinned by the not-gpu tests (worked
 example from [explainer] §8.2, brute force, closed forms, invariants, library
 special cases, finite differences).  Absolute activation values are printed
 nowhere on the pages, so they are pinned only through those properties.
 """
-from . import mask, model, grad  # noqa: F401
+from . import mask, model, grad, v2, sparse  # noqa: F401
