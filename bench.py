@@ -101,6 +101,8 @@ def main():
                     help="also time the V2 target side on config 3's users (AutoSplit into 4 sub-tokens, the "
                          "16-layer stack with a per-sub-token SwiGLU FFN and token mixing after every target "
                          "layer, mean pooling); 0 skips")
+    ap.add_argument("--sparse-steps", type=int, default=5,
+                    help="timed forward steps with 2:4 structured-sparse projections (0 skips)")
     ap.add_argument("--train-steps", type=int, default=3,
                     help="also time this many training gradient passes (mtfm_backbone_bwd: forward keeping the "
                          "layer inputs, then every layer's backward); 0 skips")
@@ -346,6 +348,53 @@ def main():
         log(f"V2 target side: {v2['ms_per_step']:.2f} ms/step, {v2['user_samples_per_s']:.1f} user-samples/s")
         del dw2, ws2, x2, pooled, ffd
 
+    sparse = None
+    if args.sparse_steps > 0:
+        # the same forward with every projection 2:4-pruned and packed (inference weights)
+        t0 = time.perf_counter()
+        full_s = [dict(w, **B.pack_full_s24(w)) for w in dw.full]
+        tgt_s = [dict(w, **B.pack_target_s24(w, wl.batch.split)) for w in dw.target]
+        torch.cuda.synchronize()
+        pack_ms = 1000.0 * (time.perf_counter() - t0)
+
+        def sparse_step():
+            B.mask_build(batch, meta)
+            B.backbone_fwd(batch, dims, wl.n_blocks, wl.k_target, meta, full_s, tgt_s, x, ws)
+
+        for _ in range(2):
+            sparse_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.sparse_steps):
+            sparse_step()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        proj = [B.K_GEMM_UQKV, B.K_GEMM_OUT, B.K_GEMM_KV, B.K_GEMM_T]
+        B.timing_enable(proj)
+        for k in proj:
+            B.timing_read(k)
+        for _ in range(2):
+            sparse_step()
+        torch.cuda.synchronize()
+        B.timing_enable([])
+        proj_ms = sum(B.timing_read(k)[1] for k in proj) / 2
+        proj_flops = layers_full * proj_full_flops + layers_t * proj_t_flops
+        sparse = {"what": "the config-3 forward with every projection (U|Q|K|V, K|V, T rows, output) 2:4-pruned "
+                          "and run on the sparse MFMA (mtfm_s24_pack'ed weights); metadata build included",
+                  "steps": args.sparse_steps, "ms_per_step": 1000.0 * el / args.sparse_steps,
+                  "user_samples_per_s": wl.batch.n_users * args.sparse_steps / el,
+                  "pack_ms_all_layers": pack_ms,
+                  "projection_ms_per_step": proj_ms,
+                  "projection_dense_equiv_TFLOPs": proj_flops / (proj_ms * 1e-3) / 1e12 if proj_ms > 0 else None}
+        if breakdown:
+            dense_proj = sum(breakdown[k]["ms_per_step"] for k in ("gemm_uqkv", "gemm_out", "gemm_kv", "gemm_t"))
+            sparse["projection_dense_ms_per_step"] = dense_proj
+            sparse["projection_speedup"] = dense_proj / proj_ms if proj_ms > 0 else None
+        if ms_step:
+            sparse["vs_dense_forward"] = ms_step / sparse["ms_per_step"]
+        log("sparse projections: " + json.dumps(sparse))
+        del full_s, tgt_s
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
@@ -379,6 +428,7 @@ def main():
         "train": train,
         "serve": serve,
         "v2": v2,
+        "sparse": sparse,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

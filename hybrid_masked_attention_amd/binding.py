@@ -34,7 +34,7 @@ ENTRY_POINTS = [
     "mtfm_kv_cache_bytes", "mtfm_serve_workspace_bytes",
     "mtfm_serve_context", "mtfm_serve_targets", "mtfm_autosplit", "mtfm_token_ffn_workspace_bytes",
     "mtfm_token_ffn", "mtfm_token_pool", "mtfm_backbone_v2_workspace_bytes", "mtfm_backbone_v2_fwd",
-    "mtfm_mask_dense", "mtfm_validate_batch",
+    "mtfm_mask_dense", "mtfm_validate_batch", "mtfm_s24_pack_bytes", "mtfm_s24_pack",
 ]
 BAD_ACTION_ORDER, BAD_LENGTHS = 1, 2
 SERVE_CONTEXT, SERVE_TARGETS = 0, 1
@@ -57,12 +57,16 @@ class CDims(ctypes.Structure):
                 ("ln_eps", c_float), ("dtype", c_int32)]
 
 
+FULL_W = ("ln1_g", "ln1_b", "w_uqkv", "ln2_g", "ln2_b", "w_o", "w_uqkv_s24", "w_o_s24")
+TARGET_W = ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o", "w_t_s24", "w_kv_s24", "w_o_s24")
+
+
 class CFullW(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in ("ln1_g", "ln1_b", "w_uqkv", "ln2_g", "ln2_b", "w_o")]
+    _fields_ = [(n, c_void_p) for n in FULL_W]
 
 
 class CTargetW(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o")]
+    _fields_ = [(n, c_void_p) for n in TARGET_W]
 
 
 class CFullGrad(ctypes.Structure):
@@ -102,6 +106,9 @@ def lib():
     L.mtfm_mask_dense.argtypes = [P(CBatch), c_void_p, c_int32, c_void_p, c_void_p]
     L.mtfm_mask_dense.restype = c_int32
     L.mtfm_validate_batch.argtypes = [P(CBatch), c_void_p, c_void_p]; L.mtfm_validate_batch.restype = c_int32
+    L.mtfm_s24_pack_bytes.argtypes = [c_int32, c_int32]; L.mtfm_s24_pack_bytes.restype = c_size_t
+    L.mtfm_s24_pack.argtypes = [P(c_void_p), P(c_int32), c_int32, c_int32, c_void_p, c_size_t, c_void_p]
+    L.mtfm_s24_pack.restype = c_int32
     L.mtfm_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]; L.mtfm_workspace_bytes.restype = c_size_t
     L.mtfm_backbone_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]
     L.mtfm_backbone_workspace_bytes.restype = c_size_t
@@ -304,11 +311,45 @@ def workspace_probe(batch: DeviceBatch, dims: CDims, op: int):
 
 
 def full_w(w: Dict[str, "object"]) -> CFullW:
-    return CFullW(*[_ptr(w[n]) for n in ("ln1_g", "ln1_b", "w_uqkv", "ln2_g", "ln2_b", "w_o")])
+    """Weight struct of a full layer; the packed 2:4 fields are taken when the dict has them."""
+    return CFullW(*[_ptr(w.get(n)) for n in FULL_W])
 
 
 def target_w(w: Dict[str, "object"]) -> CTargetW:
-    return CTargetW(*[_ptr(w[n]) for n in ("ln1_g", "ln1_b", "w_u", "w_q", "w_kv", "ln2_g", "ln2_b", "w_o")])
+    """Weight struct of a target layer; the packed 2:4 fields are taken when the dict has them."""
+    return CTargetW(*[_ptr(w.get(n)) for n in TARGET_W])
+
+
+def s24_pack_bytes(rows: int, k: int) -> int:
+    return int(lib().mtfm_s24_pack_bytes(int(rows), int(k)))
+
+
+def s24_pack(segs, stream=None):
+    """2:4-prune and pack bf16 device matrices [rows_i][k] (stacked in order) -> uint8 device tensor."""
+    import torch
+    k = int(segs[0].shape[-1])
+    rows = [int(t.shape[0]) for t in segs]
+    assert all(t.dtype == torch.bfloat16 and t.is_contiguous() and int(t.shape[-1]) == k for t in segs)
+    nbytes = s24_pack_bytes(sum(rows), k)
+    out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=segs[0].device)
+    ptrs = (c_void_p * len(segs))(*[t.data_ptr() for t in segs])
+    nrows = (c_int32 * len(segs))(*rows)
+    _check(lib().mtfm_s24_pack(ptrs, nrows, len(segs), k, _ptr(out), nbytes, _stream(stream)), "mtfm_s24_pack")
+    return out
+
+
+def pack_full_s24(w: Dict[str, "object"], stream=None) -> Dict[str, "object"]:
+    """The packed 2:4 projections of a full layer (keys w_uqkv_s24, w_o_s24)."""
+    return {"w_uqkv_s24": s24_pack([w["w_uqkv"]], stream), "w_o_s24": s24_pack([w["w_o"]], stream)}
+
+
+def pack_target_s24(w: Dict[str, "object"], split: int, stream=None) -> Dict[str, "object"]:
+    """The packed 2:4 projections of a target layer (keys w_t_s24, w_kv_s24, w_o_s24); w_q is [split][H*dh][d]."""
+    segs = []
+    for z in range(split):
+        segs += [w["w_u"], w["w_q"][z], w["w_kv"]]
+    return {"w_t_s24": s24_pack(segs, stream), "w_kv_s24": s24_pack([w["w_kv"]], stream),
+            "w_o_s24": s24_pack([w["w_o"]], stream)}
 
 
 def attn_full(batch, dims, meta, w, x_in, x_out, ws, stream=None):

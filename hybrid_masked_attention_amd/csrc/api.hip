@@ -234,6 +234,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   gp.M = (int32_t)p.n_rows; gp.N = zw; gp.K = D; gp.groups = 1;
   gp.A = xt; gp.lda = D; gp.amap = identity_map();
   gp.B[0] = w->w_uqkv; gp.bn[0] = zw; gp.ldb = D;
+  gp.bs24 = w->w_uqkv_s24; gp.bs24_rows = zw;
   gp.cmap = identity_map();
   gp.epi = EPI_SILU_SPLIT;
   gp.dst[0] = z; gp.ld[0] = zw; gp.cend[0] = hd; gp.scale[0] = 1.f;
@@ -278,6 +279,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   go.M = (int32_t)p.n_rows; go.N = D; go.K = hd; go.groups = 1;
   go.A = y; go.lda = hd; go.amap = identity_map();
   go.B[0] = w->w_o; go.bn[0] = D; go.ldb = hd;
+  go.bs24 = w->w_o_s24; go.bs24_rows = D;
   go.cmap = identity_map();
   go.epi = EPI_RESID; go.resid = x_in; go.ldr = D; go.out = x_out; go.ldo = D;
   TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
@@ -323,6 +325,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
     gk.M = (int32_t)p.n_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
     gk.A = xt; gk.lda = D; gk.amap = identity_map();
     gk.B[0] = w->w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
+    gk.bs24 = w->w_kv_s24; gk.bs24_rows = 2 * gd;
     gk.cmap = identity_map();
     gk.epi = EPI_SILU_SPLIT;
     gk.dst[0] = kv; gk.ld[0] = 2 * gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
@@ -343,6 +346,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   gt.B[1] = w->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
   gt.B[2] = w->w_kv; gt.bn[2] = 2 * gd;
   gt.ldb = D;
+  gt.bs24 = w->w_t_s24; gt.bs24_rows = S * zw; gt.bs24_zrows = zw;
   gt.cmap = RowMap{nullptr, S, 0}; gt.cmap_zadd = 1;
   gt.epi = EPI_SILU_SPLIT;
   gt.dst[0] = zt; gt.ld[0] = zw; gt.cend[0] = hd; gt.scale[0] = 1.f;
@@ -375,6 +379,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   go.M = (int32_t)p.n_parents; go.N = D; go.K = hd; go.groups = S;
   go.A = y; go.lda = hd; go.amap = RowMap{nullptr, S, 0}; go.amap_zadd = 1;
   go.B[0] = w->w_o; go.bn[0] = D; go.ldb = hd;
+  go.bs24 = w->w_o_s24; go.bs24_rows = D;
   go.cmap = RowMap{c.meta.parent_row, 0, 0}; go.cmap_zadd = 1;
   go.epi = EPI_RESID; go.resid = x_in; go.ldr = D; go.out = x_out; go.ldo = D;
   TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
@@ -405,6 +410,7 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
     gk.M = (int32_t)p.n_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
     gk.A = ws + L.xt[l]; gk.lda = D; gk.amap = identity_map();
     gk.B[0] = w[l].w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
+    gk.bs24 = w[l].w_kv_s24; gk.bs24_rows = 2 * gd;
     gk.cmap = identity_map();
     gk.epi = EPI_SILU_SPLIT;
     gk.dst[0] = kv ? kv[l].k : ws + L.k[l]; gk.ld[0] = gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
@@ -447,6 +453,7 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   gt.B[1] = w->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
   gt.B[2] = w->w_kv; gt.bn[2] = 2 * gd;
   gt.ldb = D;
+  gt.bs24 = w->w_t_s24; gt.bs24_rows = S * zw; gt.bs24_zrows = zw;
   gt.cmap = RowMap{nullptr, S, 0}; gt.cmap_zadd = 1;
   gt.epi = EPI_SILU_SPLIT;
   gt.dst[0] = zt; gt.ld[0] = zw; gt.cend[0] = hd; gt.scale[0] = 1.f;
@@ -478,6 +485,7 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   go.M = (int32_t)p.n_parents; go.N = D; go.K = hd; go.groups = S;
   go.A = y; go.lda = hd; go.amap = RowMap{nullptr, S, 0}; go.amap_zadd = 1;
   go.B[0] = w->w_o; go.bn[0] = D; go.ldb = hd;
+  go.bs24 = w->w_o_s24; go.bs24_rows = D;
   go.cmap = RowMap{c.meta.parent_row, 0, 0}; go.cmap_zadd = 1;
   go.epi = EPI_RESID; go.resid = x; go.ldr = D; go.out = x; go.ldo = D;
   TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
@@ -664,6 +672,7 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
     gt.M = (int32_t)p.n_t_rows; gt.groups = 1;
     gt.amap = identity_map(); gt.cmap = identity_map();
     gt.B[0] = fw->w_uqkv; gt.bn[0] = zw;
+    gt.bs24 = fw->w_uqkv_s24; gt.bs24_rows = zw;
   } else {
     gt.M = (int32_t)p.n_parents; gt.groups = S;
     gt.amap = RowMap{nullptr, S, 0}; gt.amap_zadd = 1;
@@ -671,6 +680,7 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
     gt.B[0] = tw->w_u; gt.bn[0] = hd;
     gt.B[1] = tw->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
     gt.B[2] = tw->w_kv; gt.bn[2] = 2 * gd;
+    gt.bs24 = tw->w_t_s24; gt.bs24_rows = S * zw; gt.bs24_zrows = zw;
   }
   TRY(timed_gemm(MTFM_K_GEMM_T, gt, dt, c.s));
 
@@ -698,6 +708,7 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   go.M = (int32_t)p.n_t_rows; go.N = D; go.K = hd; go.groups = 1;
   go.A = y; go.lda = hd; go.amap = identity_map();
   go.B[0] = fw ? fw->w_o : tw->w_o; go.bn[0] = D; go.ldb = hd;
+  go.bs24 = fw ? fw->w_o_s24 : tw->w_o_s24; go.bs24_rows = D;
   go.cmap = identity_map();
   go.epi = EPI_RESID; go.resid = x; go.ldr = D; go.out = x; go.ldo = D;
   TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
@@ -998,8 +1009,16 @@ mtfm_status mtfm_backbone_bwd(const mtfm_batch* batch, const mtfm_dims* dims, in
   for (int l = 0; l + 1 < L; ++l) {
     void* out = w + W.stash + l * W.xbytes;
     const int b = l / per, t = l % per;
-    if (t == 0) TRY(run_full(c, dims, &full[b], input_of(l), out, w + W.layer, nullptr, keep_of(l)));
-    else TRY(run_target(c, dims, &tgt[b * k_target + t - 1], input_of(l), out, w + W.layer, keep_of(l)));
+    // the training pass computes with the dense weights (packed sparse ones are inference-only)
+    if (t == 0) {
+      mtfm_full_w fw = full[b];
+      fw.w_uqkv_s24 = fw.w_o_s24 = nullptr;
+      TRY(run_full(c, dims, &fw, input_of(l), out, w + W.layer, nullptr, keep_of(l)));
+    } else {
+      mtfm_target_w tw = tgt[b * k_target + t - 1];
+      tw.w_t_s24 = tw.w_kv_s24 = tw.w_o_s24 = nullptr;
+      TRY(run_target(c, dims, &tw, input_of(l), out, w + W.layer, keep_of(l)));
+    }
   }
   for (int l = L - 1; l >= 0; --l) {
     const void* g_in = l == L - 1 ? dy : grad_buf(l + 1);

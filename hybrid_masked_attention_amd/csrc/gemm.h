@@ -47,6 +47,10 @@ struct GemmArgs {
   // rows past M as zeros; perm16 permutes rows within aligned groups of 16 as
   // {0-3, 8-11, 4-7, 12-15} (the key order of the attention's P V operand).
   void* vt; int64_t ldvt; int32_t vt_col0, vt_cols;
+  // bf16 only: if set, B is not read; the weights are 2:4-pruned and packed
+  // (mtfm_s24_pack layout) as bs24_rows stacked rows, output column n of
+  // group z taking packed row z * bs24_zrows + n; run on the sparse MFMA
+  const void* bs24; int32_t bs24_rows, bs24_zrows;
 };
 
 mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s);

@@ -182,12 +182,45 @@ MTFM_DEV bf16x8 pack8(const float (&v)[8]) {
   return o;
 }
 
-template <int EPI, int GBM>
-__global__ __launch_bounds__(256, GShape<GBM>::WG_PER_CU) void gemm_bf16_kernel(GemmArgs g) {
+// ---------------------------------------------------------------------------
+// 2:4 structured-sparse kernel (gfx950 v_smfmac_f32_32x32x32_bf16): the
+// pruned weights, packed by s24_pack below, are the instruction's sparse
+// operand and the activations its dense one, so each instruction covers a K
+// step of 32 at the MFMA cost of 16.  Tiles, row maps, the XCD-aware order
+// and the epilogues are the dense kernel's.  The LDS ring holds activations
+// only (three stages); each lane loads its packed weight slices (16 bytes of
+// kept values and a 16-bit position word per K step and column block)
+// straight from global memory into registers, two K steps ahead, so every
+// load has two steps of MFMA work to land.
+#ifndef S24_AHEAD
+#define S24_AHEAD 2
+#endif
+#ifndef S24_WG256
+#define S24_WG256 2
+#endif
+#ifndef S24_WG128
+#define S24_WG128 3
+#endif
+constexpr int S24_NS = 3;                 // activation ring stages (loaded two K steps ahead)
+constexpr int S24_WA = S24_AHEAD;         // weight slices are loaded this many K steps ahead
+constexpr int S24_WS = S24_WA + 1;        // weight register sets
+constexpr int S24_U = S24_WS == S24_NS ? S24_NS : S24_NS * S24_WS;   // unroll: stage and set indexes constant
+constexpr int S24_WL = 2 * G_TN;          // weight load instructions per wave per K step
+
+template <int BM> struct S24Shape {
+  static constexpr int STAGE = BM * GBK * 2;
+  static constexpr int LDS = S24_NS * STAGE > GNW * G_EP_BYTES ? S24_NS * STAGE : GNW * G_EP_BYTES;
+  static constexpr int WG_PER_CU = BM == 256 ? S24_WG256 : S24_WG128;
+};
+
+typedef __attribute__((__vector_size__(16 * sizeof(__bf16)))) __bf16 bf16x16;
+
+template <int EPI, int GBM, bool SP>
+__global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::WG_PER_CU) void gemm_bf16_kernel(GemmArgs g) {
   using SH = GShape<GBM>;
   constexpr int G_LA = SH::LA, G_TM = SH::TM, G_WR = SH::WR, G_STAGE = SH::STAGE, G_VMC0 = SH::VMC0;
   constexpr int G_VMC = (GS - 2) * (G_LA + G_LB);
-  __shared__ __attribute__((aligned(1024))) char lds[SH::LDS];
+  __shared__ __attribute__((aligned(1024))) char lds[SP ? S24Shape<GBM>::LDS : SH::LDS];
 
   const int n_mt = (g.M + GBM - 1) / GBM, n_nt = (g.N + GBN - 1) / GBN;
   const int tiles_per_group = n_mt * n_nt;
@@ -223,103 +256,185 @@ __global__ __launch_bounds__(256, GShape<GBM>::WG_PER_CU) void gemm_bf16_kernel(
       aoff[i] = (uint32_t)(rin * amap.mul * g.lda * 2) + cb;
     }
   }
-  // B: the weight rows of a chunk lie in one segment (segment sizes are multiples of 16)
-  __amdgpu_buffer_rsrc_t rb[G_LB];
-  uint32_t boff[G_LB];
-#pragma unroll
-  for (int i = 0; i < G_LB; ++i) {
-    const int rs = (i * GNW + wave) * G_RPC;
-    const int r = rs + rin, n = n0 + rs;
-    const int valid = min(max(g.N - n, 0), G_RPC);
-    // (explicit selects keep the segment pointer in scalar registers)
-    const void* bseg = g.B[0];
-    int64_t bz = g.bz[0];
-    int nn = n;
-    if (nn >= g.bn[0]) {
-      nn -= g.bn[0]; bseg = g.B[1]; bz = g.bz[1];
-      if (nn >= g.bn[1]) { nn -= g.bn[1]; bseg = g.B[2]; bz = g.bz[2]; }
-    }
-    const bf16* base = (const bf16*)bseg + (int64_t)z * bz + (int64_t)nn * g.ldb;
-    rb[i] = make_rsrc(valid ? base : (const bf16*)g.B[0], valid ? (uint32_t)(((int64_t)(valid - 1) * g.ldb + g.K) * 2) : 0u);
-    boff[i] = (uint32_t)(rin * g.ldb * 2 + (slot ^ g_swz(r)) * 16);
-  }
-  auto issue = [&](int step, int stage) {
-    char* base = lds + stage * G_STAGE;
-    const uint32_t so = (uint32_t)step * GBK * 2;
-#pragma unroll
-    for (int i = 0; i < G_LA; ++i) lds_dma16(ra[i], (lds_void*)(base + (i * GNW + wave) * 1024), aoff[i], so);
-#pragma unroll
-    for (int i = 0; i < G_LB; ++i)
-      lds_dma16(rb[i], (lds_void*)(base + GBM * GBK * 2 + (i * GNW + wave) * 1024), boff[i], so);
-  };
-
-  // fragment offsets within a stage: chunk (2 kk + hi) of row r sits at slot chunk ^ f(r)
-  int arow[G_TM], af[G_TM], brow[G_TN], bfo[G_TN];
-#pragma unroll
-  for (int i = 0; i < G_TM; ++i) {
-    const int r = wm * G_WR + i * 32 + l32;
-    arow[i] = r * GBK * 2; af[i] = hi ^ g_swz(r);
-  }
-#pragma unroll
-  for (int i = 0; i < G_TN; ++i) {
-    const int r = wn * G_WC + i * 32 + l32;
-    brow[i] = GBM * GBK * 2 + r * GBK * 2; bfo[i] = hi ^ g_swz(r);
-  }
-  bf16x8 fa[2][G_TM], fb[2][G_TN];
-  auto read = [&](int stage, int kk, int buf) {
-    const char* st = lds + stage * G_STAGE;
-#pragma unroll
-    for (int i = 0; i < G_TM; ++i) fa[buf][i] = *(const bf16x8*)(st + arow[i] + (((2 * kk) ^ af[i]) << 4));
-#pragma unroll
-    for (int i = 0; i < G_TN; ++i) fb[buf][i] = *(const bf16x8*)(st + brow[i] + (((2 * kk) ^ bfo[i]) << 4));
-  };
   f32x16 acc[G_TN][G_TM];
 #pragma unroll
   for (int b = 0; b < G_TN; ++b)
 #pragma unroll
     for (int a = 0; a < G_TM; ++a) acc[b][a] = f32x16{};
-  auto mma = [&](int buf) {   // C^T tiles: weights as the A operand, so a lane holds 4 consecutive columns
+  if constexpr (!SP) {
+    // B: the weight rows of a chunk lie in one segment (segment sizes are multiples of 16)
+    __amdgpu_buffer_rsrc_t rb[G_LB];
+    uint32_t boff[G_LB];
 #pragma unroll
-    for (int b = 0; b < G_TN; ++b)
+    for (int i = 0; i < G_LB; ++i) {
+      const int rs = (i * GNW + wave) * G_RPC;
+      const int r = rs + rin, n = n0 + rs;
+      const int valid = min(max(g.N - n, 0), G_RPC);
+      // (explicit selects keep the segment pointer in scalar registers)
+      const void* bseg = g.B[0];
+      int64_t bz = g.bz[0];
+      int nn = n;
+      if (nn >= g.bn[0]) {
+        nn -= g.bn[0]; bseg = g.B[1]; bz = g.bz[1];
+        if (nn >= g.bn[1]) { nn -= g.bn[1]; bseg = g.B[2]; bz = g.bz[2]; }
+      }
+      const bf16* base = (const bf16*)bseg + (int64_t)z * bz + (int64_t)nn * g.ldb;
+      rb[i] = make_rsrc(valid ? base : (const bf16*)g.B[0], valid ? (uint32_t)(((int64_t)(valid - 1) * g.ldb + g.K) * 2) : 0u);
+      boff[i] = (uint32_t)(rin * g.ldb * 2 + (slot ^ g_swz(r)) * 16);
+    }
+    auto issue = [&](int step, int stage) {
+      char* base = lds + stage * G_STAGE;
+      const uint32_t so = (uint32_t)step * GBK * 2;
 #pragma unroll
-      for (int a = 0; a < G_TM; ++a)
-        acc[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][b], fa[buf][a], acc[b][a], 0, 0, 0);
-  };
+      for (int i = 0; i < G_LA; ++i) lds_dma16(ra[i], (lds_void*)(base + (i * GNW + wave) * 1024), aoff[i], so);
+#pragma unroll
+      for (int i = 0; i < G_LB; ++i)
+        lds_dma16(rb[i], (lds_void*)(base + GBM * GBK * 2 + (i * GNW + wave) * 1024), boff[i], so);
+    };
 
-  const int nk = g.K / GBK;
+    // fragment offsets within a stage: chunk (2 kk + hi) of row r sits at slot chunk ^ f(r)
+    int arow[G_TM], af[G_TM], brow[G_TN], bfo[G_TN];
 #pragma unroll
-  for (int s = 0; s < GS; ++s)
-    if (s < nk) issue(s, s);
-  if (GS - 1 < nk) wait_vm<G_VMC0>();
-  else wait_vm<0>();
-  barrier_only();
-  read(0, 0, 0);
-  int stage = 0;
-  for (int s = 0; s < nk - 1; ++s) {
+    for (int i = 0; i < G_TM; ++i) {
+      const int r = wm * G_WR + i * 32 + l32;
+      arow[i] = r * GBK * 2; af[i] = hi ^ g_swz(r);
+    }
+#pragma unroll
+    for (int i = 0; i < G_TN; ++i) {
+      const int r = wn * G_WC + i * 32 + l32;
+      brow[i] = GBM * GBK * 2 + r * GBK * 2; bfo[i] = hi ^ g_swz(r);
+    }
+    bf16x8 fa[2][G_TM], fb[2][G_TN];
+    auto read = [&](int stage, int kk, int buf) {
+      const char* st = lds + stage * G_STAGE;
+#pragma unroll
+      for (int i = 0; i < G_TM; ++i) fa[buf][i] = *(const bf16x8*)(st + arow[i] + (((2 * kk) ^ af[i]) << 4));
+#pragma unroll
+      for (int i = 0; i < G_TN; ++i) fb[buf][i] = *(const bf16x8*)(st + brow[i] + (((2 * kk) ^ bfo[i]) << 4));
+    };
+    auto mma = [&](int buf) {   // C^T tiles: weights as the A operand, so a lane holds 4 consecutive columns
+#pragma unroll
+      for (int b = 0; b < G_TN; ++b)
+#pragma unroll
+        for (int a = 0; a < G_TM; ++a)
+          acc[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][b], fa[buf][a], acc[b][a], 0, 0, 0);
+    };
+
+    const int nk = g.K / GBK;
+#pragma unroll
+    for (int s = 0; s < GS; ++s)
+      if (s < nk) issue(s, s);
+    if (GS - 1 < nk) wait_vm<G_VMC0>();
+    else wait_vm<0>();
+    barrier_only();
+    read(0, 0, 0);
+    int stage = 0;
+    for (int s = 0; s < nk - 1; ++s) {
+#pragma unroll
+      for (int kk = 0; kk < G_KK; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < G_KK) {
+          read(stage, kk + 1, cur ^ 1);
+        } else {
+          // step s + 1 has landed once at most G_VMC newer DMA instructions are
+          // outstanding; the barrier also tells every wave that this stage has
+          // been read (lgkmcnt(0)) so it can be refilled with step s + GS
+          if (s + GS - 1 < nk) wait_vm_lgkm<G_VMC>();
+          else wait_vm_lgkm<0>();
+          barrier_only();
+          if (s + GS < nk) issue(s + GS, stage);
+          stage = (stage + 1 == GS) ? 0 : stage + 1;
+          read(stage, 0, cur ^ 1);
+        }
+        mma(cur);
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < G_KK; ++kk) {
       const int cur = kk & 1;
-      if (kk + 1 < G_KK) {
-        read(stage, kk + 1, cur ^ 1);
-      } else {
-        // step s + 1 has landed once at most G_VMC newer DMA instructions are
-        // outstanding; the barrier also tells every wave that this stage has
-        // been read (lgkmcnt(0)) so it can be refilled with step s + GS
-        if (s + GS - 1 < nk) wait_vm_lgkm<G_VMC>();
-        else wait_vm_lgkm<0>();
-        barrier_only();
-        if (s + GS < nk) issue(s + GS, stage);
-        stage = (stage + 1 == GS) ? 0 : stage + 1;
-        read(stage, 0, cur ^ 1);
-      }
+      if (kk + 1 < G_KK) read(stage, kk + 1, cur ^ 1);
       mma(cur);
     }
-  }
+
+  } else {
+    constexpr int STAGE = S24Shape<GBM>::STAGE;
+    // loads issued after step t's: step t + 1's (weights first, then activations)
+    constexpr int VMC = S24_WA == 2 ? S24_WL + G_LA : G_LA;
+    auto issue = [&](int step, int stage) {
+      char* base = lds + stage * STAGE;
+      const uint32_t so = (uint32_t)step * GBK * 2;
 #pragma unroll
-  for (int kk = 0; kk < G_KK; ++kk) {
-    const int cur = kk & 1;
-    if (kk + 1 < G_KK) read(stage, kk + 1, cur ^ 1);
-    mma(cur);
+      for (int i = 0; i < G_LA; ++i) lds_dma16(ra[i], (lds_void*)(base + (i * GNW + wave) * 1024), aoff[i], so);
+    };
+
+    // packed weights: slice (step, row, half) of this lane's output column in
+    // each 32-column block; columns past N repeat row N - 1 (never stored)
+    const char* wvals = (const char*)g.bs24;
+    const int64_t wrows = g.bs24_rows;
+    const char* widx = wvals + wrows * g.K;
+    int64_t wslice[G_TN];
+#pragma unroll
+    for (int b = 0; b < G_TN; ++b) {
+      const int n = min(n0 + wn * G_WC + b * 32 + l32, g.N - 1);
+      wslice[b] = ((int64_t)z * g.bs24_zrows + n) * 2 + hi;
+    }
+    bf16x8 wv[S24_WS][G_TN];
+    int wi[S24_WS][G_TN];
+    auto wload = [&](int step, int set) {
+#pragma unroll
+      for (int b = 0; b < G_TN; ++b) {
+        const int64_t e = (int64_t)step * wrows * 2 + wslice[b];
+        wv[set][b] = *(const bf16x8*)(wvals + e * 16);
+        wi[set][b] = *(const uint16_t*)(widx + e * 2);
+      }
+    };
+
+    // B operand of the sparse instruction: lane (row, half h) holds K entries
+    // 16 h .. 16 h + 15 of its activation row = LDS chunks 2 h and 2 h + 1
+    int arow[G_TM], af[G_TM];
+#pragma unroll
+    for (int i = 0; i < G_TM; ++i) {
+      const int r = wm * G_WR + i * 32 + l32;
+      arow[i] = r * GBK * 2; af[i] = g_swz(r);
+    }
+
+    // Issue order: activations of step 0, then per step j the weights of step
+    // j + S24_WA and the activations of step j + 2, so that a step's loads are
+    // followed only by the next step's.  Every step issues the same loads
+    // (steps past the end re-read the last one into a stage no longer read):
+    // with no branches around them the compiler's own wait counting stays as
+    // loose as the explicit waits below.
+    const int nk = g.K / GBK;
+    issue(0, 0);
+#pragma unroll
+    for (int j = 0; j < S24_WA; ++j) wload(min(j, nk - 1), j);
+    issue(min(1, nk - 1), 1);
+    for (int s0 = 0; s0 < nk; s0 += S24_U) {
+#pragma unroll
+      for (int u = 0; u < S24_U; ++u) {
+        const int t = s0 + u;
+        if (t >= nk) break;
+        const int st = u % S24_NS, ws = u % S24_WS;   // constants once the loop is unrolled
+        // step t has landed once only step t + 1's loads may be outstanding;
+        // the barrier also tells every wave that the previous stage has been
+        // read, so it can take step t + 2
+        wait_vm_lgkm<VMC>();
+        barrier_only();
+        wload(min(t + S24_WA, nk - 1), (u + S24_WA) % S24_WS);
+        issue(min(t + 2, nk - 1), (u + 2) % S24_NS);
+        const char* sb = lds + st * STAGE;
+#pragma unroll
+        for (int a = 0; a < G_TM; ++a) {
+          const bf16x8 lo = *(const bf16x8*)(sb + arow[a] + (((2 * hi) ^ af[a]) << 4));
+          const bf16x8 up = *(const bf16x8*)(sb + arow[a] + (((2 * hi + 1) ^ af[a]) << 4));
+          const bf16x16 fa = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+#pragma unroll
+          for (int b = 0; b < G_TN; ++b)
+            acc[b][a] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(wv[ws][b], fa, acc[b][a], wi[ws][b], 0, 0);
+        }
+      }
+    }
+    wait_vm<0>();   // the tail's loads land before the epilogue reuses the ring
   }
 
   // ---- epilogue: the ring is free once every wave has finished its reads
@@ -447,6 +562,8 @@ __global__ __launch_bounds__(256, GShape<GBM>::WG_PER_CU) void gemm_bf16_kernel(
     }
   }
 }
+
+
 
 // ---------------------------------------------------------------------------
 // Weight-gradient GEMM.  Block tile 128 (m) x 128 (n), 32 rows of r per step:
@@ -828,9 +945,17 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
     // K in whole steps; 16-byte rows and stores; weight segments in whole DMA
     // chunks; output segments aligned to the 64-column wave tile
     if (g.K % GBK != 0 || g.N % 8 != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0) return MTFM_E_UNSUPPORTED;
-    if (!aligned16(g.A) || !aligned16(g.B[0])) return MTFM_E_UNSUPPORTED;
-    if (g.N > g.bn[0] && (g.bn[0] % G_RPC != 0 || !aligned16(g.B[1]))) return MTFM_E_UNSUPPORTED;
-    if (g.N > g.bn[0] + g.bn[1] && (g.bn[1] % G_RPC != 0 || !aligned16(g.B[2]))) return MTFM_E_UNSUPPORTED;
+    if (!aligned16(g.A)) return MTFM_E_UNSUPPORTED;
+    if (g.bs24) {
+      // every group's rows inside the packed matrix
+      if (!aligned16(g.bs24) || g.bs24_rows <= 0 || g.bs24_zrows < 0 ||
+          (int64_t)(g.groups - 1) * g.bs24_zrows + g.N > g.bs24_rows)
+        return MTFM_E_UNSUPPORTED;
+    } else {
+      if (!aligned16(g.B[0])) return MTFM_E_UNSUPPORTED;
+      if (g.N > g.bn[0] && (g.bn[0] % G_RPC != 0 || !aligned16(g.B[1]))) return MTFM_E_UNSUPPORTED;
+      if (g.N > g.bn[0] + g.bn[1] && (g.bn[1] % G_RPC != 0 || !aligned16(g.B[2]))) return MTFM_E_UNSUPPORTED;
+    }
     if (g.amap.list) {
       // gathered rows address the whole A buffer through one 31-bit offset
       if (g.a_rows <= 0 || g.a_rows * g.lda * 2 + (int64_t)g.K * 2 >= (int64_t)kOobOffset) {
@@ -865,20 +990,31 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
     const int64_t tiles = (int64_t)((g.M + bm - 1) / bm) * n_nt * g.groups;
     if (tiles > 0x7fffffff) return MTFM_E_UNSUPPORTED;
     const dim3 grid((unsigned)tiles, 1, 1);
+    if (g.bs24) {
+      switch (g.epi * 2 + (small ? 1 : 0)) {
+        case 2 * EPI_SILU_SPLIT: gemm_bf16_kernel<EPI_SILU_SPLIT, 256, true><<<grid, 256, 0, s>>>(g); break;
+        case 2 * EPI_SILU_SPLIT + 1: gemm_bf16_kernel<EPI_SILU_SPLIT, 128, true><<<grid, 256, 0, s>>>(g); break;
+        case 2 * EPI_RESID: gemm_bf16_kernel<EPI_RESID, 256, true><<<grid, 256, 0, s>>>(g); break;
+        case 2 * EPI_RESID + 1: gemm_bf16_kernel<EPI_RESID, 128, true><<<grid, 256, 0, s>>>(g); break;
+        default: return MTFM_E_UNSUPPORTED;   // the forward projections use these two epilogues
+      }
+      MTFM_LAUNCH_CHECK("gemm_s24");
+      return MTFM_OK;
+    }
     switch (g.epi * 2 + (small ? 1 : 0)) {
-      case 2 * EPI_SILU_SPLIT: gemm_bf16_kernel<EPI_SILU_SPLIT, 256><<<grid, 256, 0, s>>>(g); break;
-      case 2 * EPI_SILU_SPLIT + 1: gemm_bf16_kernel<EPI_SILU_SPLIT, 128><<<grid, 256, 0, s>>>(g); break;
-      case 2 * EPI_RESID: gemm_bf16_kernel<EPI_RESID, 256><<<grid, 256, 0, s>>>(g); break;
-      case 2 * EPI_RESID + 1: gemm_bf16_kernel<EPI_RESID, 128><<<grid, 256, 0, s>>>(g); break;
-      case 2 * EPI_STORE_F32: gemm_bf16_kernel<EPI_STORE_F32, 256><<<grid, 256, 0, s>>>(g); break;
-      case 2 * EPI_STORE_F32 + 1: gemm_bf16_kernel<EPI_STORE_F32, 128><<<grid, 256, 0, s>>>(g); break;
-      case 2 * EPI_SWIGLU: gemm_bf16_kernel<EPI_SWIGLU, 256><<<grid, 256, 0, s>>>(g); break;
-      case 2 * EPI_SWIGLU + 1: gemm_bf16_kernel<EPI_SWIGLU, 128><<<grid, 256, 0, s>>>(g); break;
-      case 2 * EPI_STORE: gemm_bf16_kernel<EPI_STORE, 256><<<grid, 256, 0, s>>>(g); break;
-      default: gemm_bf16_kernel<EPI_STORE, 128><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_SILU_SPLIT: gemm_bf16_kernel<EPI_SILU_SPLIT, 256, false><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_SILU_SPLIT + 1: gemm_bf16_kernel<EPI_SILU_SPLIT, 128, false><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_RESID: gemm_bf16_kernel<EPI_RESID, 256, false><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_RESID + 1: gemm_bf16_kernel<EPI_RESID, 128, false><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_STORE_F32: gemm_bf16_kernel<EPI_STORE_F32, 256, false><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_STORE_F32 + 1: gemm_bf16_kernel<EPI_STORE_F32, 128, false><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_SWIGLU: gemm_bf16_kernel<EPI_SWIGLU, 256, false><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_SWIGLU + 1: gemm_bf16_kernel<EPI_SWIGLU, 128, false><<<grid, 256, 0, s>>>(g); break;
+      case 2 * EPI_STORE: gemm_bf16_kernel<EPI_STORE, 256, false><<<grid, 256, 0, s>>>(g); break;
+      default: gemm_bf16_kernel<EPI_STORE, 128, false><<<grid, 256, 0, s>>>(g); break;
     }
   } else {
-    if (g.epi == EPI_SWIGLU) return MTFM_E_UNSUPPORTED;
+    if (g.epi == EPI_SWIGLU || g.bs24) return MTFM_E_UNSUPPORTED;
     const int64_t total = (int64_t)g.M * g.N;
     gemm_f32_kernel<<<dim3((unsigned)((total + 255) / 256), 1, g.groups), 256, 0, s>>>(g);
   }

@@ -56,3 +56,13 @@ class DeviceWorkload:
         self.full: List[Dict] = [weights_to_device(w, wl.dtype, device, _FULL_KEYS) for w in wl.full]
         self.target: List[Dict] = [weights_to_device(w, wl.dtype, device, _TARGET_KEYS) for w in wl.target]
         self.device = device
+        self.split = int(wl.batch.split)
+
+    def pack_s24(self, stream=None):
+        """Add every layer's packed 2:4 projections to its weights: the forward and serving
+        entry points then compute those projections with the pruned weights (bf16)."""
+        for w in self.full:
+            w.update(B.pack_full_s24(w, stream))
+        for w in self.target:
+            w.update(B.pack_target_s24(w, self.split, stream))
+        return self

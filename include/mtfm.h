@@ -92,6 +92,14 @@ typedef struct {
   const void* w_uqkv;                      /* [2*H*dh + 2*G*dh][d_model], rows U|Q|K|V, heads contiguous */
   const float* ln2_g; const float* ln2_b;  /* [3][H*dh] */
   const void* w_o;                         /* [d_model][H*dh] */
+  /* Optional 2:4 structured-sparse projections ([explainer] §5.2.1; bf16
+   * only): if set, the forward and serving entry points compute that
+   * projection with the pruned weights on the sparse matrix instructions
+   * instead of reading the dense matrix.  Each is mtfm_s24_pack of the dense
+   * matrix above (the pack prunes).  NULL = dense.  The backward entry points
+   * ignore them (training keeps dense weights). */
+  const void* w_uqkv_s24;                  /* pack of w_uqkv ([2*H*dh + 2*G*dh] rows, K = d_model) */
+  const void* w_o_s24;                     /* pack of w_o ([d_model] rows, K = H*dh) */
 } mtfm_full_w;
 
 /* Target-attention layer weights ([explainer] §4.2; [blog] §3.3.2 per-sub-token Q):
@@ -105,6 +113,11 @@ typedef struct {
   const void* w_kv;                        /* [2*G*dh][d_model], rows K|V */
   const float* ln2_g; const float* ln2_b;  /* [3][H*dh] */
   const void* w_o;                         /* [d_model][H*dh] */
+  /* Optional 2:4 structured-sparse projections, as in mtfm_full_w: */
+  const void* w_t_s24;                     /* pack of the T-row stack, per sub-token k = 0 .. split-1 the
+                                              segments w_u, w_q[k], w_kv (split * (2*H*dh + 2*G*dh) rows) */
+  const void* w_kv_s24;                    /* pack of w_kv (context rows' K|V) */
+  const void* w_o_s24;                     /* pack of w_o */
 } mtfm_target_w;
 
 /* Gradients written by the backward entry points.  Weight and GLN-parameter
@@ -413,6 +426,34 @@ const char* mtfm_status_str(int32_t status);
 
 /* Last HIP error text recorded by this thread (empty if none). */
 const char* mtfm_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * 2:4 structured pruning and packing ([explainer] §5.2.1: in the linear
+ * projections, of every 4 consecutive weights the 2 smaller are set to zero
+ * for sparse matrix hardware).
+ *
+ * Groups of 4 run along a weight row (the reduction axis of y = x W^T).  A
+ * group keeps its 2 entries of largest magnitude; of equal magnitudes the
+ * lower position is kept.  The packed matrix holds, for the rows of the
+ * given segments stacked in order (R rows, K columns, bf16, row-major, each
+ * segment 16-byte aligned), the kept values and their positions in the
+ * operand order of the sparse matrix instruction (K step ks = k / 32, slice
+ * i = (ks * R + r) * 2 + h for half h = 0, 1 covering the groups q of the step
+ * with q % 4 in {2h, 2h + 1}):
+ *   byte i * 16: 8 bf16, the two kept entries of each of those 4 groups in
+ *                ascending q, each pair in ascending position;
+ *   byte R * K + i * 2: uint16, 2 bits per kept entry (its position 0..3 in
+ *                its group), entry j at bits 2j .. 2j + 1.
+ * The layout is what the forward kernels read; it is stated so that tests
+ * can decode it.  K % 32 == 0, at most 16 segments. */
+size_t mtfm_s24_pack_bytes(int32_t rows, int32_t k);   /* R * K * 9 / 8; 0 if k % 32 != 0 or a size <= 0 */
+/* w_segs / seg_rows: host arrays of n_segs device pointers and row counts.
+ * packed: device buffer of at least mtfm_s24_pack_bytes(sum rows, k) bytes
+ * (else E_WORKSPACE), 16-byte aligned; caller-owned.  Enqueued on stream; the
+ * sources must stay valid until it runs.  E_NULL, E_DIMS (k % 32, segment
+ * count or rows), E_UNSUPPORTED (alignment), E_HIP. */
+mtfm_status mtfm_s24_pack(const void* const* w_segs, const int32_t* seg_rows, int32_t n_segs, int32_t k,
+                          void* packed, size_t packed_bytes, void* stream);
 
 #ifdef __cplusplus
 }

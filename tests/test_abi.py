@@ -145,3 +145,28 @@ def test_workspace_sizes_grow_with_rows(B):
     for op in (B.OP_FULL, B.OP_TARGET, B.OP_BACKBONE):
         assert 0 < B.workspace_bytes(small, d, op) < B.workspace_bytes(big, d, op)
     assert B.workspace_bytes(small, B.make_dims(500, 8, 2, 64), B.OP_FULL) == 0   # invalid dims -> 0
+
+
+def test_s24_pack_sizes_and_argument_checks(B):
+    """2:4 packing ([explainer] §5.2.1): 9/8 byte per weight (8 bf16 kept values and one 16-bit
+    position word per 32 weights); argument errors are reported before anything is enqueued."""
+    L = B.lib()
+    assert B.s24_pack_bytes(1280, 512) == 1280 * 512 * 9 // 8
+    assert B.s24_pack_bytes(512, 512) == 512 * 512 + 512 * 512 // 8
+    assert B.s24_pack_bytes(16, 48) == 0 and B.s24_pack_bytes(0, 64) == 0 and B.s24_pack_bytes(8, -32) == 0
+    segs = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    rows = (ctypes.c_int32 * 2)(64, 32)
+    need = B.s24_pack_bytes(96, 64)
+
+    def call(k=64, n=2, out=0x40000, nbytes=need, s=segs, r=rows):
+        return L.mtfm_s24_pack(s, r, n, k, ctypes.c_void_p(out) if out else None, nbytes, None)
+    assert call(k=48) == B.E_DIMS
+    assert call(n=0) == B.E_DIMS and call(n=17) == B.E_DIMS
+    assert call(out=0) == B.E_NULL
+    assert call(s=None) == B.E_NULL
+    assert call(nbytes=need - 1) == B.E_WORKSPACE
+    assert call(out=0x40008) == B.E_UNSUPPORTED                          # 16-byte alignment
+    assert call(s=(ctypes.c_void_p * 2)(0x10000, 0x20004)) == B.E_UNSUPPORTED
+    assert call(r=(ctypes.c_int32 * 2)(64, -1)) == B.E_DIMS
+    assert call(s=(ctypes.c_void_p * 2)(0x10000, None)) == B.E_NULL
+    assert call(r=(ctypes.c_int32 * 2)(0, 0)) == B.OK                   # nothing to pack
