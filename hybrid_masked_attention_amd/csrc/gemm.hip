@@ -127,6 +127,9 @@ MTFM_DEV void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 MTFM_DEV void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 typedef __attribute__((__vector_size__(2 * sizeof(int64_t)))) int64_t i64x2;
+// The staged rows are written as bf16 and read back as 8-byte words: reads
+// through this type may alias any store (no type-based reordering).
+typedef int64_t __attribute__((may_alias)) i64_any;
 
 // One pass of the staged epilogue: the wave's fp32 accumulators of MFMA row
 // blocks [a0, a0 + NA) go through LDS as bf16 (OUTF32 = false; 136-byte rows)
@@ -165,7 +168,7 @@ MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][TM], int a0, int l
 #pragma unroll
       for (int q = 0; q < 4; ++q) { v[q] = x0[q]; v[4 + q] = x1[q]; }
     } else {
-      const int64_t* src = (const int64_t*)(ep + r * RS + c * 2);
+      const i64_any* src = (const i64_any*)(ep + r * RS + c * 2);
       i64x2 raw; raw[0] = src[0]; raw[1] = src[1];
       const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
 #pragma unroll
@@ -496,8 +499,8 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
         for (int i = 0; i < G_WC / 8; ++i) {
           const int col = i * 8 + (lane >> 3), sc = lane & 7;      // 8 lanes per column, 8 slots each
           const int r0 = (sc >> 1) * 16 + 4 * (sc & 1);
-          const int64_t* s0 = (const int64_t*)(ep + col * RT + r0 * 2);
-          const int64_t* s1 = (const int64_t*)(ep + col * RT + (r0 + 8) * 2);
+          const i64_any* s0 = (const i64_any*)(ep + col * RT + r0 * 2);
+          const i64_any* s1 = (const i64_any*)(ep + col * RT + (r0 + 8) * 2);
           i64x2 v; v[0] = *s0; v[1] = *s1;
           const int64_t slot0 = (int64_t)mw + pass * 64 + sc * 8;
           if (slot0 < g.ldvt && nw + col < g.N)
