@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "api_internal.h"
@@ -170,15 +171,25 @@ mtfm_status check_batch_device(const mtfm_batch* b, const MetaPlan& p) {
   return MTFM_OK;
 }
 
-mtfm_status check_full_w(const mtfm_full_w* w) {
-  if (!w || !w->ln1_g || !w->ln1_b || !w->w_uqkv || !w->ln2_g || !w->ln2_b || !w->w_o) return MTFM_E_NULL;
+// Packed 2:4 projections are read by the bf16 forward only and must be
+// 16-byte aligned; fwd_dims = nullptr (backward) skips the check, the
+// backward ignores them.
+mtfm_status check_packed(const mtfm_dims* fwd_dims, std::initializer_list<const void*> packed) {
+  if (!fwd_dims) return MTFM_OK;
+  for (const void* p : packed)
+    if (p && (fwd_dims->dtype != MTFM_BF16 || ((uintptr_t)p & 15) != 0)) return MTFM_E_UNSUPPORTED;
   return MTFM_OK;
 }
 
-mtfm_status check_target_w(const mtfm_target_w* w) {
+mtfm_status check_full_w(const mtfm_full_w* w, const mtfm_dims* fwd_dims = nullptr) {
+  if (!w || !w->ln1_g || !w->ln1_b || !w->w_uqkv || !w->ln2_g || !w->ln2_b || !w->w_o) return MTFM_E_NULL;
+  return check_packed(fwd_dims, {w->w_uqkv_s24, w->w_o_s24});
+}
+
+mtfm_status check_target_w(const mtfm_target_w* w, const mtfm_dims* fwd_dims = nullptr) {
   if (!w || !w->ln1_g || !w->ln1_b || !w->w_u || !w->w_q || !w->w_kv || !w->ln2_g || !w->ln2_b || !w->w_o)
     return MTFM_E_NULL;
-  return MTFM_OK;
+  return check_packed(fwd_dims, {w->w_t_s24, w->w_kv_s24, w->w_o_s24});
 }
 
 }  // namespace
@@ -726,8 +737,8 @@ mtfm_status serve_checks(const mtfm_batch* batch, const mtfm_dims* dims, int32_t
   if (n_blocks > 0 && !full) return MTFM_E_NULL;
   if (n_blocks > 0 && k_target > 0 && !tgt) return MTFM_E_NULL;
   for (int b = 0; b < n_blocks; ++b) {
-    TRY(check_full_w(&full[b]));
-    for (int t = 0; t < k_target; ++t) TRY(check_target_w(&tgt[b * k_target + t]));
+    TRY(check_full_w(&full[b], dims));
+    for (int t = 0; t < k_target; ++t) TRY(check_target_w(&tgt[b * k_target + t], dims));
   }
   c->b = batch;
   c->meta = meta_ptrs(c->plan, meta_d);
@@ -859,7 +870,7 @@ mtfm_status mtfm_attn_full(const mtfm_batch* batch, const mtfm_dims* dims, const
                            const void* x_in, void* x_out, void* ws, size_t ws_bytes, void* stream) {
   Ctx c;
   TRY(prepare(batch, dims, meta_d, x_in, x_out, ws, ws_bytes, MTFM_OP_FULL, &c, stream));
-  TRY(check_full_w(w));
+  TRY(check_full_w(w, dims));
   return run_full(c, dims, w, x_in, x_out, (char*)ws);
 }
 
@@ -868,7 +879,7 @@ mtfm_status mtfm_attn_target(const mtfm_batch* batch, const mtfm_dims* dims, con
                              void* stream) {
   Ctx c;
   TRY(prepare(batch, dims, meta_d, x_in, x_out, ws, ws_bytes, MTFM_OP_TARGET, &c, stream));
-  TRY(check_target_w(w));
+  TRY(check_target_w(w, dims));
   return run_target(c, dims, w, x_in, x_out, (char*)ws);
 }
 
@@ -881,8 +892,8 @@ mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, in
   if (n_blocks > 0 && !full) return MTFM_E_NULL;
   if (n_blocks > 0 && k_target > 0 && !tgt) return MTFM_E_NULL;
   for (int b = 0; b < n_blocks; ++b) {
-    TRY(check_full_w(&full[b]));
-    for (int t = 0; t < k_target; ++t) TRY(check_target_w(&tgt[b * k_target + t]));
+    TRY(check_full_w(&full[b], dims));
+    for (int t = 0; t < k_target; ++t) TRY(check_target_w(&tgt[b * k_target + t], dims));
   }
   const bool hoist = dims->dtype == MTFM_BF16 && k_target >= 1 && k_target <= 4 &&
                      ws_bytes >= (size_t)backbone_ws(c.plan, dims, k_target).total;
@@ -1099,9 +1110,9 @@ mtfm_status mtfm_backbone_v2_fwd(const mtfm_batch* batch, const mtfm_dims* dims,
   if (k_target < 1 || k_target > 4) return MTFM_E_UNSUPPORTED;
   if (n_blocks > 0 && (!full || !tgt || !ffn)) return MTFM_E_NULL;
   for (int b = 0; b < n_blocks; ++b) {
-    TRY(check_full_w(&full[b]));
+    TRY(check_full_w(&full[b], dims));
     for (int t = 0; t < k_target; ++t) {
-      TRY(check_target_w(&tgt[b * k_target + t]));
+      TRY(check_target_w(&tgt[b * k_target + t], dims));
       TRY(check_ffn(dims, d_ff, c.plan.split, &ffn[b * k_target + t]));
     }
   }

@@ -96,8 +96,10 @@ typedef struct {
    * only): if set, the forward and serving entry points compute that
    * projection with the pruned weights on the sparse matrix instructions
    * instead of reading the dense matrix.  Each is mtfm_s24_pack of the dense
-   * matrix above (the pack prunes).  NULL = dense.  The backward entry points
-   * ignore them (training keeps dense weights). */
+   * matrix above (the pack prunes).  NULL = dense.  A set field must be
+   * 16-byte aligned and needs bf16 dims (else E_UNSUPPORTED, checked before
+   * anything is enqueued).  The backward entry points ignore them (training
+   * keeps dense weights). */
   const void* w_uqkv_s24;                  /* pack of w_uqkv ([2*H*dh + 2*G*dh] rows, K = d_model) */
   const void* w_o_s24;                     /* pack of w_o ([d_model] rows, K = H*dh) */
 } mtfm_full_w;

@@ -170,3 +170,28 @@ def test_s24_pack_sizes_and_argument_checks(B):
     assert call(r=(ctypes.c_int32 * 2)(64, -1)) == B.E_DIMS
     assert call(s=(ctypes.c_void_p * 2)(0x10000, None)) == B.E_NULL
     assert call(r=(ctypes.c_int32 * 2)(0, 0)) == B.OK                   # nothing to pack
+
+
+def test_packed_weights_need_bf16_and_alignment(B):
+    """A packed 2:4 projection in the weight structs is read by the bf16 forward only: fp32 dims or
+    a misaligned pointer is rejected before anything is enqueued."""
+    L = B.lib()
+    b = _with_fake_device(_host_batch(B, [[5, 3, 2]]))
+    fake = ctypes.c_void_p(0x1000)
+    f32 = B.make_dims(512, 8, 2, 64, dtype=B.F32)
+    bf = B.make_dims(512, 8, 2, 64, dtype=B.BF16)
+
+    def full(dims, w):
+        need = B.workspace_bytes(b, dims, B.OP_FULL)
+        return L.mtfm_attn_full(ctypes.byref(b.c), ctypes.byref(dims), fake, ctypes.byref(w), fake, fake, fake,
+                                need, None)
+
+    def target(dims, w):
+        need = B.workspace_bytes(b, dims, B.OP_TARGET)
+        return L.mtfm_attn_target(ctypes.byref(b.c), ctypes.byref(dims), fake, ctypes.byref(w), fake, fake, fake,
+                                  need, None)
+    assert full(f32, B.CFullW(*([0x5000] * 6), 0x6000, None)) == B.E_UNSUPPORTED
+    assert full(f32, B.CFullW(*([0x5000] * 6), None, 0x6000)) == B.E_UNSUPPORTED
+    assert full(bf, B.CFullW(*([0x5000] * 6), 0x6008, None)) == B.E_UNSUPPORTED
+    assert target(f32, B.CTargetW(*([0x5000] * 8), 0x6000, None, None)) == B.E_UNSUPPORTED
+    assert target(bf, B.CTargetW(*([0x5000] * 8), None, 0x6004, None)) == B.E_UNSUPPORTED
