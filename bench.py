@@ -85,6 +85,20 @@ def cpu_baseline(wl, seconds: float):
                       f"{el:.1f} s"}
 
 
+def oracle_rate(fn, n_users: int, seconds: float, what: str):
+    """Time fn(u) (the oracle on user u) on users 0, 1, ... until `seconds` pass."""
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        fn(done)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= n_users:
+            break
+    return {"value": done / el, "unit": "user-samples/s", "kind": "oracle",
+            "sample": f"first {done} of {n_users} users, {what}, float64 numpy, {el:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +268,23 @@ def main():
         log(f"training gradient pass: {train['ms_per_step']:.2f} ms/step, {train['user_samples_per_s']:.1f} "
             f"user-samples/s")
         del ws_b, dy, dx, fg, tg
+        if not args.no_cpu_baseline:
+            # the oracle's gradient pass on single users of the same batch
+            from oracle import grad as og
+            from oracle import model as om
+            r = om.bf16_round
+            full_r = [{k: (v if k.startswith("ln") else r(v)) for k, v in w.items()} for w in wl.full]
+            tgt_r = [{k: (v if k.startswith("ln") else r(v)) for k, v in w.items()} for w in wl.target]
+            dy_h = np.random.default_rng(33).standard_normal((wl.batch.total_rows, wl.dims.d_model))
+
+            def train_user(u):
+                rows = wl.batch.rows_of([u])
+                og.backbone_bwd(wl.batch.subset([u]), wl.x[rows], full_r, tgt_r, wl.dims, wl.n_blocks,
+                                wl.k_target, dy_h[rows], boundary=r)
+
+            train["cpu_oracle"] = oracle_rate(train_user, wl.batch.n_users, min(args.cpu_seconds, 10.0),
+                                              "16-layer forward + backward (oracle.grad.backbone_bwd)")
+            log(f"training oracle: {train['cpu_oracle']}")
 
     serve = None
     if args.serve_steps > 0:
@@ -347,6 +378,17 @@ def main():
               "user_samples_per_s": wl2.batch.n_users * args.v2_steps / el}
         log(f"V2 target side: {v2['ms_per_step']:.2f} ms/step, {v2['user_samples_per_s']:.1f} user-samples/s")
         del dw2, ws2, x2, pooled, ffd
+        if not args.no_cpu_baseline:
+            from oracle import model as om
+            from oracle import v2 as ov2
+            r = om.bf16_round
+            f2 = [{k: (v if k.startswith("ln") else r(v)) for k, v in w.items()} for w in wl2.full]
+            t2 = [{k: (v if k.startswith("ln") else r(v)) for k, v in w.items()} for w in wl2.target]
+            v2["cpu_oracle"] = oracle_rate(
+                lambda u: ov2.backbone_v2(wl2.batch, wl2.x, f2, t2, ffn, wl2.dims, wl2.n_blocks, wl2.k_target,
+                                          boundary=r, users=[u]),
+                wl2.batch.n_users, min(args.cpu_seconds, 10.0), "V2 16-layer stack with token FFNs (oracle.v2)")
+            log(f"V2 oracle: {v2['cpu_oracle']}")
 
     sparse = None
     if args.sparse_steps > 0:
