@@ -245,3 +245,35 @@ def test_backward_ignores_packed_weights():
 
     for a, b in zip(run(False), run(True)):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_v2_stack_sparse(split):
+    """The V2 stack (token FFNs after every target layer) with every projection packed: the
+    projections use the pruned weights, the FFNs stay dense ([explainer] §5.2.1 names the U, V, Q,
+    K and output projections)."""
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    from oracle import v2 as ov
+    from tests.test_gpu_v2 import _ffn_dev, _round_ffn, _small_v2
+    wl, ffn = _small_v2(split, 640 + split)
+    say(f"sparse V2 stack: {wl.batch.n_users} users, {wl.batch.total_rows} rows, split {split}")
+    dw = DeviceWorkload(wl).pack_s24()
+    meta = B.mask_build(dw.batch)
+    ws = torch.empty(B.backbone_v2_workspace_bytes(dw.batch, dw.dims, wl.k_target, 256), dtype=torch.uint8,
+                     device="cuda")
+    x = dw.x.clone()
+    B.backbone_v2_fwd(dw.batch, dw.dims, wl.n_blocks, wl.k_target, 256, meta, dw.full, dw.target,
+                      [_ffn_dev(w) for w in ffn], x, ws)
+    torch.cuda.synchronize()
+    got = to_np(x)
+    xr, full, tgt = rounded_inputs(wl)
+    ref = ov.backbone_v2(wl.batch, xr, _pruned(full, osp.prune_full_weights), _pruned(tgt, osp.prune_target_weights),
+                         [_round_ffn(w) for w in ffn], wl.dims, 2, 3, boundary=om.bf16_round)
+    tr = ov.t_rows(wl.batch)
+    ctx = np.setdiff1d(np.arange(wl.batch.total_rows), tr)
+    r = Report(TOL_BF16)
+    r.branch("context rows", got[ctx], ref[ctx], xr[ctx], "bf16", roundings=8)
+    r.branch("T rows", got[tr], ref[tr], xr[tr], "bf16", roundings=14)
+    r.check()
