@@ -277,3 +277,17 @@ def test_v2_stack_sparse(split):
     r.branch("context rows", got[ctx], ref[ctx], xr[ctx], "bf16", roundings=8)
     r.branch("T rows", got[tr], ref[tr], xr[tr], "bf16", roundings=14)
     r.check()
+
+
+def test_sparse_layers_are_deterministic():
+    """Two runs of the sparse-projection layers on the same inputs are bit-identical."""
+    rng = np.random.default_rng(700)
+    batch = synth.make_batch(rng, np.asarray(EDGE_LENS, np.int32), 4)
+    dims = synth.Dims(512, 8, 2, 64)
+    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
+    wl = synth.Workload("det_s24", batch, dims, "bf16", x, full=[synth.full_weights(rng, dims, 0.05, 0.05)],
+                        target=[synth.target_weights(rng, dims, 4, 0.05, 0.05)])
+    for kind in ("full", "target"):
+        a, b = _run_layer(wl, kind), _run_layer(wl, kind)
+        for u, v in zip(a, b):
+            np.testing.assert_array_equal(u, v)
