@@ -329,7 +329,9 @@ def s24_pack(segs, stream=None):
     import torch
     k = int(segs[0].shape[-1])
     rows = [int(t.shape[0]) for t in segs]
-    assert all(t.dtype == torch.bfloat16 and t.is_contiguous() and int(t.shape[-1]) == k for t in segs)
+    if not all(t.dtype == torch.bfloat16 and t.is_contiguous() and t.dim() == 2 and int(t.shape[-1]) == k
+               for t in segs):
+        raise ValueError("s24_pack: segments must be contiguous 2-D bf16 tensors of one width")
     nbytes = s24_pack_bytes(sum(rows), k)
     out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=segs[0].device)
     ptrs = (c_void_p * len(segs))(*[t.data_ptr() for t in segs])

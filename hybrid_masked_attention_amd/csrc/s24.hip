@@ -99,6 +99,7 @@ mtfm_status mtfm_s24_pack(const void* const* w_segs, const int32_t* seg_rows, in
   }
   a.n_segs = n_segs; a.rows = (int32_t)rows; a.K = k; a.out = (char*)packed;
   const int64_t slices = rows * (k / 32) * 2;
+  if (slices > ((int64_t)1 << 32) - 256) return MTFM_E_DIMS;   // one thread per slice, 32-bit grid
   s24_pack_kernel<<<(unsigned)((slices + 255) / 256), 256, 0, (hipStream_t)stream>>>(a);
   MTFM_LAUNCH_CHECK("s24_pack");
   return MTFM_OK;
