@@ -191,17 +191,19 @@ MTFM_DEV bf16x8 pack8(const float (&v)[8]) {
 // are the instruction's sparse operand and the activations its dense one,
 // so each instruction covers a K step of 32 at the MFMA cost of 16.  Row
 // maps, the XCD-aware order and the epilogues are the dense kernel's.  The
-// LDS ring holds activations only (three stages); each lane loads its packed
-// weight slices (16 bytes of kept values and a 16-bit position word per K
-// step and column block) straight from global memory into registers, two K
-// steps ahead, so every load has two steps of MFMA work to land.
+// LDS ring holds activations only (three stages, filled two K steps ahead);
+// each lane loads its packed weight slices (16 bytes of kept values and a
+// 16-bit position word per K step and column block) straight from global
+// memory into registers.
 // Tile rows as in the dense kernel (256 for large M, 128 when that would
-// leave CUs idle).  The three-stage ring and three register sets of weights
-// take 189 registers at 256 rows (two workgroups per CU) and 122 at 128
-// (four); at 256 rows two workgroups measured faster than 128-row tiles at
-// four on the 241535-row projections.
+// leave CUs idle).  Weights are loaded one K step ahead into two register
+// sets: 168 registers at 256 rows (three workgroups per CU, as the dense
+// kernel) and 110 at 128 (four).  Two steps ahead in three sets needs 189
+// registers at 256 rows, i.e. two workgroups per CU, and measured 8 % slower
+// on the 241535-row projections: loads in flight per CU matter more here
+// than the weights' prefetch depth.
 constexpr int S24_NS = 3;                 // activation ring stages (loaded two K steps ahead)
-constexpr int S24_WA = 2;                 // weight slices are loaded this many K steps ahead
+constexpr int S24_WA = 1;                 // weight slices are loaded this many K steps ahead
 constexpr int S24_WS = S24_WA + 1;        // weight register sets
 constexpr int S24_U = S24_WS == S24_NS ? S24_NS : S24_NS * S24_WS;   // unroll: stage and set indexes constant
 constexpr int S24_WL = 2 * G_TN;          // weight load instructions per wave per K step
@@ -209,7 +211,7 @@ constexpr int S24_WL = 2 * G_TN;          // weight load instructions per wave p
 template <int BM> struct S24Shape {
   static constexpr int STAGE = BM * GBK * 2;
   static constexpr int LDS = S24_NS * STAGE > GNW * G_EP_BYTES ? S24_NS * STAGE : GNW * G_EP_BYTES;
-  static constexpr int WG_PER_CU = BM == 256 ? 2 : 4;
+  static constexpr int WG_PER_CU = BM == 256 ? 3 : 4;
 };
 
 typedef __attribute__((__vector_size__(16 * sizeof(__bf16)))) __bf16 bf16x16;
