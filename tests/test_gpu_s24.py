@@ -58,7 +58,7 @@ def test_pack_matches_oracle_pruning():
     from hybrid_masked_attention_amd import binding as B
     rng = np.random.default_rng(31)
     k = 160
-    segs = [_bf16_matrix(rng, r, k) for r in (48, 16, 200)]
+    segs = [_bf16_matrix(rng, r, k) for r in (48, 0, 16, 200)]     # an empty segment is skipped
     say(f"s24 pack: segments {[s.shape for s in segs]}")
     dev = [torch.as_tensor(s, dtype=torch.float32).to(torch.bfloat16).cuda() for s in segs]
     packed = B.s24_pack(dev)
