@@ -123,3 +123,87 @@ def test_batch_meta_concatenates_users():
         np.testing.assert_array_equal(meta["p"][r0:r1], one["p"])
         sel = meta["full_tiles"][:, 0] == u
         np.testing.assert_array_equal(meta["full_tiles"][sel][:, 1:], one["full_tiles"][:, 1:])
+
+
+# Hand-derived block classes ([blog] §6.2: the mask is pre-scanned into an index
+# of the key blocks worth computing; here "skip" = 0, "partial" = 1, "full" = 2).
+# Each expectation below was worked out by hand from the matrix it names, key
+# tiles covering only the context columns [0, L_H + L_R) and the last key tile
+# short when L_H + L_R is not a multiple of bn.
+#
+# Golden user ([explainer] §8.2 matrix, tests/golden): context columns 0..4,
+#   rows 0-2 see cols 0-2, row 3 cols 0-3, rows 4-6 cols 0-4.
+# Second user (L_H 2, L_R 3 at times 10/20/30, two targets exposed at 25 and 5):
+#   rows 0-1 see cols 0-1, row 2 cols 0-2, row 3 cols 0-3, row 4 cols 0-4,
+#   row 5 (exposure 25: actions 10, 20) cols 0-3, row 6 (exposure 5) cols 0-1.
+_SECOND = dict(l_h=2, l_r=3, l_t=2, ts_r=[10, 20, 30], ts_t=[25, 5])
+
+_HAND_CLASSES = [
+    # (user, begin, bm, bn, classes per query tile)
+    ("golden", 0, 2, 2, [[2, 1, 0], [2, 1, 0], [2, 2, 2], [2, 2, 2]]),
+    ("golden", 5, 2, 2, [[2, 2, 2]]),
+    ("golden", 0, 3, 2, [[2, 1, 0], [2, 2, 1], [2, 2, 2]]),
+    ("golden", 5, 3, 2, [[2, 2, 2]]),
+    ("golden", 0, 7, 5, [[1]]),
+    ("golden", 0, 4, 3, [[2, 1], [2, 2]]),
+    ("second", 0, 2, 2, [[2, 0, 0], [2, 1, 0], [2, 2, 1], [2, 0, 0]]),
+    ("second", 5, 2, 2, [[2, 1, 0]]),
+    ("second", 0, 3, 2, [[2, 1, 0], [2, 2, 1], [2, 0, 0]]),
+    ("second", 5, 1, 4, [[2, 0], [1, 0]]),
+]
+
+
+def _hand_user(which):
+    if which == "golden":
+        return om.dense_mask(3, 2, 2, 1, ts_r=[10, 20], ts_t=[30, 40]), 5
+    s = _SECOND
+    return om.dense_mask(s["l_h"], s["l_r"], s["l_t"], 1, s["ts_r"], s["ts_t"]), s["l_h"] + s["l_r"]
+
+
+@pytest.mark.parametrize("which,begin,bm,bn,expect", _HAND_CLASSES)
+def test_tile_classes_hand_derived(which, begin, bm, bn, expect):
+    m, l_ctx = _hand_user(which)
+    cls = om.tile_classes(m, begin, l_ctx, bm, bn)
+    np.testing.assert_array_equal(cls, np.array(expect, np.int8))
+
+
+# (leading full key tiles, one past the last non-skip key tile) per query tile,
+# read off the hand-derived classes above
+_HAND_DESC = {
+    ("golden", 0, 2, 2): [(1, 2), (1, 2), (3, 3), (3, 3)],
+    ("golden", 0, 3, 2): [(1, 2), (2, 3), (3, 3)],
+    ("golden", 0, 7, 5): [(0, 1)],
+    ("second", 0, 2, 2): [(1, 1), (1, 2), (2, 3), (1, 1)],
+    ("second", 5, 2, 2): [(1, 2)],
+    ("second", 5, 1, 4): [(1, 1), (0, 1)],
+}
+
+
+@pytest.mark.parametrize("key", sorted(_HAND_DESC))
+def test_tile_desc_hand_derived(key):
+    which, begin, bm, bn = key
+    m, l_ctx = _hand_user(which)
+    desc = om.tile_desc_from_classes(om.tile_classes(m, begin, l_ctx, bm, bn))
+    np.testing.assert_array_equal(desc, np.array(_HAND_DESC[key], np.int32))
+
+
+def test_tile_desc_worked_rows():
+    # rows of classes written out directly: an all-skip row, an all-full row, a
+    # row ending in partial tiles, a row with no key tiles at all
+    cls = np.array([[0, 0, 0], [2, 2, 2], [2, 1, 1], [1, 0, 0]], np.int8)
+    np.testing.assert_array_equal(om.tile_desc_from_classes(cls), [[0, 0], [3, 3], [1, 3], [0, 1]])
+    assert om.tile_desc_from_classes(np.zeros((2, 0), np.int8)).tolist() == [[0, 0], [0, 0]]
+    with pytest.raises(AssertionError):
+        om.tile_desc_from_classes(np.array([[2, 0, 1]], np.int8))   # a visible tile after a skipped one
+
+
+def test_batch_meta_tile_tables_hand_derived():
+    # the two users above as one batch at 2 x 2 tiles: the tables are
+    # (user, first row in the user, rows, leading full tiles, key-tile end)
+    b = synth.Batch(np.array([[3, 2, 2], [2, 3, 2]], np.int32), 1,
+                    np.array([10, 20, 10, 20, 30], np.int32), np.array([30, 40, 25, 5], np.int32))
+    meta = om.batch_meta(b, 2, 2)
+    np.testing.assert_array_equal(meta["full_tiles"], [
+        [0, 0, 2, 1, 2], [0, 2, 2, 1, 2], [0, 4, 2, 3, 3], [0, 6, 1, 3, 3],
+        [1, 0, 2, 1, 1], [1, 2, 2, 1, 2], [1, 4, 2, 2, 3], [1, 6, 1, 1, 1]])
+    np.testing.assert_array_equal(meta["target_tiles"], [[0, 5, 2, 3, 3], [1, 5, 2, 1, 2]])
