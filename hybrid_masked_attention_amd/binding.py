@@ -35,6 +35,7 @@ ENTRY_POINTS = [
     "mtfm_serve_context", "mtfm_serve_targets", "mtfm_autosplit", "mtfm_token_ffn_workspace_bytes",
     "mtfm_token_ffn", "mtfm_token_pool", "mtfm_backbone_v2_workspace_bytes", "mtfm_backbone_v2_fwd",
     "mtfm_mask_dense", "mtfm_validate_batch", "mtfm_s24_pack_bytes", "mtfm_s24_pack",
+    "mtfm_serve_targets_noalloc_max_bytes", "mtfm_serve_targets_noalloc",
 ]
 BAD_ACTION_ORDER, BAD_LENGTHS = 1, 2
 SERVE_CONTEXT, SERVE_TARGETS = 0, 1
@@ -146,6 +147,10 @@ def lib():
     L.mtfm_serve_targets.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_void_p, P(CFullW), P(CTargetW),
                                      c_void_p, c_size_t, c_void_p, c_void_p, c_size_t, c_void_p]
     L.mtfm_serve_targets.restype = c_int32
+    L.mtfm_serve_targets_noalloc_max_bytes.argtypes = []; L.mtfm_serve_targets_noalloc_max_bytes.restype = c_size_t
+    L.mtfm_serve_targets_noalloc.argtypes = [P(CBatch), P(CDims), c_int32, c_int32, c_void_p, P(CFullW),
+                                             P(CTargetW), c_void_p, c_size_t, c_void_p, c_void_p]
+    L.mtfm_serve_targets_noalloc.restype = c_int32
     L.mtfm_autosplit.argtypes = [P(CBatch), P(CDims), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     L.mtfm_autosplit.restype = c_int32
     L.mtfm_token_ffn_workspace_bytes.argtypes = [P(CBatch), P(CDims), c_int32]
@@ -454,6 +459,21 @@ def serve_targets(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], t
     _check(lib().mtfm_serve_targets(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks), int(k_target),
                                     _ptr(meta), fa, ta, _ptr(kv_cache), kv_cache.numel(), _ptr(x_t), _ptr(ws),
                                     ws.numel(), _stream(stream)), "mtfm_serve_targets")
+    return x_t
+
+
+def serve_targets_noalloc_max_bytes() -> int:
+    return int(lib().mtfm_serve_targets_noalloc_max_bytes())
+
+
+def serve_targets_noalloc(batch, dims, n_blocks, k_target, meta, full: Sequence[Dict], tgt: Sequence[Dict],
+                          kv_cache, x_t, stream=None):
+    """serve_targets with the library's static per-GPU scratch instead of a workspace (allocates nothing)."""
+    fa = (CFullW * max(1, len(full)))(*[full_w(w) for w in full])
+    ta = (CTargetW * max(1, len(tgt)))(*[target_w(w) for w in tgt])
+    _check(lib().mtfm_serve_targets_noalloc(ctypes.byref(batch.c), ctypes.byref(dims), int(n_blocks), int(k_target),
+                                            _ptr(meta), fa, ta, _ptr(kv_cache), kv_cache.numel(), _ptr(x_t),
+                                            _stream(stream)), "mtfm_serve_targets_noalloc")
     return x_t
 
 

@@ -747,6 +747,44 @@ mtfm_status serve_checks(const mtfm_batch* batch, const mtfm_dims* dims, int32_t
 
 }  // namespace
 
+// Argument checks of the candidate pass (everything but the workspace).
+mtfm_status serve_targets_check(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                                const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                                const void* kv_cache, size_t cache_bytes, const void* x_t, Ctx* c) {
+  TRY(serve_checks(batch, dims, n_blocks, k_target, meta_d, full, tgt, c));
+  const KvCacheLayout K = kv_cache_layout(c->plan, dims, n_blocks * (1 + k_target));
+  if (c->plan.n_t_rows > 0 && (!x_t || !kv_cache)) return MTFM_E_NULL;
+  if (cache_bytes < (size_t)K.total) return MTFM_E_WORKSPACE;
+  return MTFM_OK;
+}
+
+int64_t serve_targets_ws_bytes(const MetaPlan& p, const mtfm_dims* d) { return serve_ws(p, d).total; }
+
+// The candidate pass on checked arguments with a workspace of at least
+// serve_targets_ws_bytes bytes.
+mtfm_status serve_targets_run(const Ctx& c, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                              const mtfm_full_w* full, const mtfm_target_w* tgt, const void* kv_cache, void* x_t,
+                              char* w) {
+  if (c.plan.n_t_rows == 0 || n_blocks == 0) return MTFM_OK;
+  const KvCacheLayout K = kv_cache_layout(c.plan, dims, n_blocks * (1 + k_target));
+  const ServeWs L = serve_ws(c.plan, dims);
+  int32_t* tiles = (int32_t*)(w + L.tiles);
+  {
+    const int n = (int)c.plan.n_target_tiles;
+    rebase_tiles_kernel<<<(n * 8 + 255) / 256, 256, 0, c.s>>>(c.meta.target_tiles, n,
+                                                               c.meta.user + UT_CTX * (c.plan.n_users + 1), tiles);
+    MTFM_LAUNCH_CHECK("rebase_tiles");
+  }
+  char* cache = (char*)kv_cache;
+  const int per = 1 + k_target;
+  for (int b = 0; b < n_blocks; ++b) {
+    TRY(serve_rows(c, dims, &full[b], nullptr, kv_of(K, cache, b * per), tiles, x_t, w, L));
+    for (int t = 0; t < k_target; ++t)
+      TRY(serve_rows(c, dims, nullptr, &tgt[b * k_target + t], kv_of(K, cache, b * per + 1 + t), tiles, x_t, w, L));
+  }
+  return MTFM_OK;
+}
+
 // Backward through the whole stack: one forward pass keeps every layer's input
 // (bf16, as the forward hands it on), then the layers' backward run from the
 // last to the first, each taking the next layer's input gradient as its
@@ -1186,29 +1224,11 @@ mtfm_status mtfm_serve_targets(const mtfm_batch* batch, const mtfm_dims* dims, i
                                const void* kv_cache, size_t cache_bytes, void* x_t, void* ws, size_t ws_bytes,
                                void* stream) {
   Ctx c;
-  TRY(serve_checks(batch, dims, n_blocks, k_target, meta_d, full, tgt, &c));
+  TRY(serve_targets_check(batch, dims, n_blocks, k_target, meta_d, full, tgt, kv_cache, cache_bytes, x_t, &c));
+  if (c.plan.n_t_rows > 0 && !ws) return MTFM_E_NULL;
+  if (ws_bytes < (size_t)serve_ws(c.plan, dims).total) return MTFM_E_WORKSPACE;
   c.s = (hipStream_t)stream;
-  const KvCacheLayout K = kv_cache_layout(c.plan, dims, n_blocks * (1 + k_target));
-  const ServeWs L = serve_ws(c.plan, dims);
-  if (c.plan.n_t_rows > 0 && (!x_t || !kv_cache || !ws)) return MTFM_E_NULL;
-  if (cache_bytes < (size_t)K.total || ws_bytes < (size_t)L.total) return MTFM_E_WORKSPACE;
-  if (c.plan.n_t_rows == 0 || n_blocks == 0) return MTFM_OK;
-  char* w = (char*)ws;
-  int32_t* tiles = (int32_t*)(w + L.tiles);
-  {
-    const int n = (int)c.plan.n_target_tiles;
-    rebase_tiles_kernel<<<(n * 8 + 255) / 256, 256, 0, c.s>>>(c.meta.target_tiles, n,
-                                                               c.meta.user + UT_CTX * (c.plan.n_users + 1), tiles);
-    MTFM_LAUNCH_CHECK("rebase_tiles");
-  }
-  char* cache = (char*)kv_cache;
-  const int per = 1 + k_target;
-  for (int b = 0; b < n_blocks; ++b) {
-    TRY(serve_rows(c, dims, &full[b], nullptr, kv_of(K, cache, b * per), tiles, x_t, w, L));
-    for (int t = 0; t < k_target; ++t)
-      TRY(serve_rows(c, dims, nullptr, &tgt[b * k_target + t], kv_of(K, cache, b * per + 1 + t), tiles, x_t, w, L));
-  }
-  return MTFM_OK;
+  return serve_targets_run(c, dims, n_blocks, k_target, full, tgt, kv_cache, x_t, (char*)ws);
 }
 
 const char* mtfm_status_str(int32_t status) {

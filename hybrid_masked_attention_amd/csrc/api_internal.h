@@ -95,6 +95,26 @@ class TimedLaunch {
   hipEvent_t start_ = nullptr, stop_ = nullptr;
 };
 
+// While one of these lives, launches on this thread are not timed (no events
+// are created or recorded): for the entry point that must not allocate.
+class TimingOff {
+ public:
+  TimingOff();
+  ~TimingOff();
+  TimingOff(const TimingOff&) = delete;
+  TimingOff& operator=(const TimingOff&) = delete;
+};
+
+// Serving candidate pass (api.hip): argument checks without the workspace,
+// the workspace size, and the pass itself on checked arguments.
+mtfm_status serve_targets_check(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                                const void* meta_d, const mtfm_full_w* full, const mtfm_target_w* tgt,
+                                const void* kv_cache, size_t cache_bytes, const void* x_t, Ctx* c);
+int64_t serve_targets_ws_bytes(const MetaPlan& p, const mtfm_dims* d);
+mtfm_status serve_targets_run(const Ctx& c, const mtfm_dims* dims, int32_t n_blocks, int32_t k_target,
+                              const mtfm_full_w* full, const mtfm_target_w* tgt, const void* kv_cache, void* x_t,
+                              char* ws);
+
 // Launch helpers that time themselves under a kernel class.
 inline mtfm_status timed_gemm(int kclass, const GemmArgs& g, int dt, hipStream_t s) {
   TimedLaunch t(kclass, s);

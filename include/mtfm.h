@@ -398,6 +398,26 @@ mtfm_status mtfm_serve_targets(const mtfm_batch* batch, const mtfm_dims* dims, i
                                const void* kv_cache, size_t cache_bytes, void* x_t, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * candidate pass of mtfm_serve_targets with the same arguments except the
+ * workspace, which comes from a static device array inside the library, one
+ * per GPU, of mtfm_serve_targets_noalloc_max_bytes() bytes (64 MiB: about
+ * 11,900 T rows at d_model = H*dh = 512, G*dh = 128).  Computes exactly what
+ * mtfm_serve_targets computes (same kernels and shapes, bit for bit).  Calls
+ * no allocating routine; kernel timing (mtfm_timing_enable) is suspended
+ * during the call.  A batch needing more than the array holds returns
+ * MTFM_E_WORKSPACE before anything is enqueued.  The array is looked up on
+ * the first call on each device; `stream` must belong to the current device
+ * (else MTFM_E_UNSUPPORTED).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other host threads or streams) race; calls
+ * ordered on one stream do not. */
+size_t mtfm_serve_targets_noalloc_max_bytes(void);
+mtfm_status mtfm_serve_targets_noalloc(const mtfm_batch* batch, const mtfm_dims* dims, int32_t n_blocks,
+                                       int32_t k_target, const void* meta_d, const mtfm_full_w* full,
+                                       const mtfm_target_w* tgt, const void* kv_cache, size_t cache_bytes, void* x_t,
+                                       void* stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel timing (measurement aid).  While a kernel class is enabled, each of
  * its launches is bracketed by two HIP events recorded on the stream the

@@ -195,3 +195,30 @@ def test_packed_weights_need_bf16_and_alignment(B):
     assert full(bf, B.CFullW(*([0x5000] * 6), 0x6008, None)) == B.E_UNSUPPORTED
     assert target(f32, B.CTargetW(*([0x5000] * 8), 0x6000, None, None)) == B.E_UNSUPPORTED
     assert target(bf, B.CTargetW(*([0x5000] * 8), None, 0x6004, None)) == B.E_UNSUPPORTED
+
+
+def test_serve_targets_noalloc_rejects_batches_beyond_its_scratch(B):
+    """The entry point without a workspace has a fixed per-GPU scratch array; a candidate batch that
+    needs more is refused on the host (MTFM_E_WORKSPACE) before any device call."""
+    L = B.lib()
+    cap = B.serve_targets_noalloc_max_bytes()
+    assert cap == 64 << 20
+    d = B.make_dims(512, 8, 2, 64, dtype=B.BF16)
+    fake = ctypes.c_void_p(0x1000)
+    fw = (B.CFullW * 1)(B.CFullW(*([0x5000] * 6)))
+    tws = (B.CTargetW * 1)(B.CTargetW(*([0x5000] * 8)))
+    # 12,000 candidate rows at d 512 need ~66 MB of scratch; 2,000 need ~11 MB
+    for n_t, fits in ((3000, False), (500, True)):
+        b = _with_fake_device(_host_batch(B, [[100, 20, n_t]], split=4))
+        need = B.serve_workspace_bytes(b, d, 1, B.SERVE_TARGETS)
+        assert (need <= cap) == fits
+        cache = B.kv_cache_bytes(b, d, 1, 1)
+        if not fits:
+            assert L.mtfm_serve_targets_noalloc(ctypes.byref(b.c), ctypes.byref(d), 1, 1, fake, fw, tws, fake,
+                                                cache, fake, None) == B.E_WORKSPACE
+        # no layers: every host check passes and nothing is enqueued (no device call either)
+        assert L.mtfm_serve_targets_noalloc(ctypes.byref(b.c), ctypes.byref(d), 0, 1, fake, fw, tws, fake,
+                                            B.kv_cache_bytes(b, d, 0, 1), fake, None) == (B.OK if fits else
+                                                                                           B.E_WORKSPACE)
+        assert L.mtfm_serve_targets_noalloc(ctypes.byref(b.c), ctypes.byref(d), 1, 1, fake, fw, tws, fake,
+                                            cache - 1, fake, None) == B.E_WORKSPACE
