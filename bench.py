@@ -181,8 +181,9 @@ def main():
     proj_t_flops = 2.0 * R * D * 2 * gd + 2.0 * T * D * 2 * hd + 2.0 * T * hd * D
     layers_full, layers_t = wl.n_blocks, wl.n_blocks * wl.k_target
     step_flops = layers_full * (attn_full_flops + proj_full_flops) + layers_t * (attn_t_flops + proj_t_flops)
-    # target attention algorithmic bytes: K and V of every row read once, Q and U of T rows in, Y out
-    attn_t_bytes = 2.0 * (R * 2 * gd + 3 * T * hd)
+    # bytes the target-attention kernel must move: K and V of every packed row once (context rows as key
+    # tiles, each T row's own for its self term), Q of the T rows in, A of the T rows out
+    attn_t_bytes = 2.0 * (R * 2 * gd + 2 * T * hd)
 
     # ---- timed region: full-attention kernel bracketed by events on its stream
     # (--steps 0 skips it: a profiling run of the training / serving / V2 parts alone)

@@ -96,7 +96,9 @@ mtfm_status check_dims(const mtfm_dims* d) {
   } else {
     if (d->head_dim != 32 && d->head_dim != 64) return MTFM_E_UNSUPPORTED;
   }
-  if (d->d_model % 64 != 0 || hd % 64 != 0 || d->d_model > 1024 || hd > 1024) return MTFM_E_UNSUPPORTED;
+  // row kernels hold a row in one wave as 1, 2, 4, 8 or 16 values per lane
+  auto row_width_ok = [](int w) { return w == 64 || w == 128 || w == 256 || w == 512 || w == 1024; };
+  if (!row_width_ok(d->d_model) || !row_width_ok(hd)) return MTFM_E_UNSUPPORTED;
   return MTFM_OK;
 }
 

@@ -34,12 +34,6 @@ namespace {
 
 constexpr int DH = 64;
 
-MTFM_DEV int xcd_remap(int bid, int nblocks) {
-  const int q = nblocks >> 3, r = nblocks & 7;
-  const int x = bid & 7, k = bid >> 3;
-  return x * q + min(x, r) + k;
-}
-
 MTFM_DEV float silu_scaled(float s) {
   // s = x log2(e); returns SiLU(x) / ln2 = s / (1 + 2^-s)
   return s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-s));

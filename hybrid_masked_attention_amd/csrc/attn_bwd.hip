@@ -27,12 +27,6 @@ namespace {
 constexpr int DH = 64;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-MTFM_DEV int xcd_remap(int bid, int nblocks) {
-  const int q = nblocks >> 3, r = nblocks & 7;
-  const int x = bid & 7, k = bid >> 3;
-  return x * q + min(x, r) + k;
-}
-
 MTFM_DEV int64_t map_b(const RowMapB& r, int m) {
   if (r.list) return (int64_t)r.list[m / r.div] + m % r.div;
   return m;

@@ -98,7 +98,9 @@ mtfm_status transpose(hipStream_t s, const void* a, int ra, const void* b, int r
 mtfm_status check_bwd_dims(const mtfm_dims* d) {
   if (d->dtype != MTFM_BF16) return MTFM_E_UNSUPPORTED;  // the backward runs on the bf16 path only
   const int hd = d->n_q_heads * d->head_dim;
-  if (d->d_model % 256 != 0 || hd % 256 != 0) return MTFM_E_UNSUPPORTED;  // row kernels: 4..16 values per lane
+  // row kernels: 4, 8 or 16 values per lane
+  auto ok = [](int w) { return w == 256 || w == 512 || w == 1024; };
+  if (!ok(d->d_model) || !ok(hd)) return MTFM_E_UNSUPPORTED;
   return MTFM_OK;
 }
 

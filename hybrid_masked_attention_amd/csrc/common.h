@@ -52,6 +52,25 @@ MTFM_DEV int wave_max(int v) {
   return v;
 }
 
+// Logical block index such that blocks sharing an XCD get consecutive ids:
+// the hardware hands consecutive workgroup ids to the 8 XCDs round-robin, so
+// logical neighbours (which share operands) land on one XCD and its L2.
+MTFM_DEV int xcd_remap(int bid, int nblocks) {
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int x = bid & 7, k = bid >> 3;
+  return x * q + min(x, r) + k;
+}
+
+// Orders one wave's LDS accesses across lanes: its earlier LDS writes before
+// its later reads of what other lanes wrote, and its earlier reads before
+// later overwrites.  A wave-scope release / acquire pair around a wave
+// barrier; it also keeps the compiler from moving LDS accesses across it.
+MTFM_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Largest i in [0, n) with off[i] <= x (off ascending, off[0] <= x).
 MTFM_DEV int upper_index(const int32_t* off, int n, int x) {
   int lo = 0, hi = n - 1;

@@ -26,14 +26,6 @@ MTFM_DEV int64_t map_row(const RowMap& r, int m) {
   return (int64_t)m * r.mul + r.add;
 }
 
-// Logical block index such that blocks sharing an XCD (hardware dispatches
-// consecutive workgroup ids round-robin over 8 XCDs) get consecutive ids.
-MTFM_DEV int xcd_remap(int bid, int nblocks) {
-  const int q = nblocks >> 3, r = nblocks & 7;
-  const int x = bid & 7, k = bid >> 3;
-  return x * q + min(x, r) + k;
-}
-
 template <typename T>
 MTFM_DEV const T* b_row_ptr(const GemmArgs& g, int z, int n) {
   if (n < g.bn[0]) return (const T*)g.B[0] + (int64_t)z * g.bz[0] + (int64_t)n * g.ldb;
@@ -138,6 +130,7 @@ typedef int64_t __attribute__((may_alias)) i64_any;
 template <bool OUTF32, int NA, int TM, typename F>
 MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][TM], int a0, int l32, int hi, int lane, F&& f) {
   constexpr int RS = OUTF32 ? G_WC * 4 + 16 : G_WC * 2 + 8;
+  wave_lds_sync();   // the previous pass's reads of this buffer are done
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -157,6 +150,7 @@ MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][TM], int a0, int l
           *(bf16x4*)d = v;
         }
       }
+  wave_lds_sync();   // every lane's writes land before other lanes read them
   // read back: 8 lanes per row (8 columns each), 8 rows per round
 #pragma unroll
   for (int i = 0; i < NA * 32 / 8; ++i) {
@@ -488,6 +482,7 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
       const int64_t col0 = nw - g.vt_col0;
 #pragma unroll
       for (int pass = 0; pass < G_WR / 64; ++pass) {
+        wave_lds_sync();   // earlier passes' reads of the staging buffer are done
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -497,6 +492,7 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
               const int col = b * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
               *(bf16*)(ep + col * RT + (a * 32 + l32) * 2) = (bf16)acc[b][2 * pass + a][e];
             }
+        wave_lds_sync();   // the transposed tile is complete before lanes read columns
 #pragma unroll
         for (int i = 0; i < G_WC / 8; ++i) {
           const int col = i * 8 + (lane >> 3), sc = lane & 7;      // 8 lanes per column, 8 slots each

@@ -213,9 +213,11 @@ mtfm_status mtfm_validate_batch(const mtfm_batch* batch, int32_t* flags_d, void*
  * Layers.  x_in / x_out: device [n_rows][d_model] of dims->dtype.  meta_d:
  * the output of mtfm_mask_build for the same batch.  ws: device workspace of
  * at least mtfm_workspace_bytes(batch, dims, op) bytes.
- * Supported: head_dim 64 with bf16 (MFMA path), head_dim 32 or 64 with fp32;
- * d_model a multiple of 64 (bf16) or 4 (fp32); H % G == 0.  Other shapes
- * return MTFM_E_UNSUPPORTED.
+ * Supported: head_dim 64 with bf16 (MFMA path; H / G of 1, 2, 4 or 8),
+ * head_dim 32 or 64 with fp32; d_model and H * dh each one of 64, 128, 256,
+ * 512 or 1024; H % G == 0.  Other shapes return MTFM_E_UNSUPPORTED before
+ * anything is enqueued.  The backward entry points (bf16 only) further need
+ * d_model and H * dh in {256, 512, 1024}.
  */
 typedef enum {
   MTFM_OP_FULL = 0, MTFM_OP_TARGET = 1, MTFM_OP_BACKBONE = 2,
@@ -293,8 +295,9 @@ mtfm_status mtfm_attn_target_bwd(const mtfm_batch* batch, const mtfm_dims* dims,
  * Workspace, two sizes: with at least
  * mtfm_backbone_bwd_workspace_bytes(batch, dims, n_blocks, k_target) bytes the
  * forward pass also keeps each layer's intermediates (normalised input,
- * projections and their pre-activations, attention output; about 14 GB for
- * 160 users of ~1,500 rows), so no layer backward recomputes them; with at
+ * projections and their pre-activations, attention output; about 21 GiB for
+ * 160 users of ~1,500 rows at d_model 512), so no layer backward recomputes
+ * them; with at
  * least mtfm_backbone_bwd_min_workspace_bytes(...) bytes (but less than the
  * full size) each layer backward recomputes them.  Both give the same
  * gradients bit for bit.  Fewer bytes than the minimum: MTFM_E_WORKSPACE.

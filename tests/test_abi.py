@@ -122,6 +122,11 @@ def test_layer_argument_checks(B):
     assert call(B.make_dims(512, 8, 2, 48)) == B.E_UNSUPPORTED      # head_dim
     assert call(B.make_dims(512, 8, 2, 32, dtype=B.BF16)) == B.E_UNSUPPORTED
     assert call(B.make_dims(500, 8, 2, 64)) == B.E_UNSUPPORTED      # d_model % 64
+    for width in (192, 384, 768, 2048):                              # row kernels: 64 * 2^k up to 1024
+        assert call(B.make_dims(width, 8, 2, 64)) == B.E_UNSUPPORTED, width
+        assert call(B.make_dims(512, width // 64, 1, 64)) == B.E_UNSUPPORTED, width   # H * dh
+    assert B.workspace_bytes(b, B.make_dims(512, 12, 4, 64), B.OP_FULL) == 0       # H * dh = 768
+    assert B.workspace_bytes(b, B.make_dims(128, 8, 2, 64), B.OP_FULL_BWD) == 0    # backward: d_model >= 256
     assert call(B.make_dims(0, 8, 2, 64)) == B.E_DIMS
     assert call(B.make_dims(512, 8, 2, 64, ln_eps=0.0)) == B.E_DIMS
     assert call(B.make_dims(512, 8, 2, 64, dtype=7)) == B.E_UNSUPPORTED
