@@ -82,7 +82,7 @@ def cpu_baseline(wl, seconds: float):
     cores = int(max(threads)) if threads else 1
     return {"value": done / el, "unit": "user-samples/s", "cores": cores, "kind": "oracle",
             "sample": f"first {done} of {wl.batch.n_users} users, 16-layer backbone forward, float64 numpy, "
-                      f"{el:.1f} s"}
+                      f"{el:.1f} s", "cpu": cpu_model()}
 
 
 def oracle_rate(fn, n_users: int, seconds: float, what: str):
@@ -97,6 +97,168 @@ def oracle_rate(fn, n_users: int, seconds: float, what: str):
             break
     return {"value": done / el, "unit": "user-samples/s", "kind": "oracle",
             "sample": f"first {done} of {n_users} users, {what}, float64 numpy, {el:.1f} s"}
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return int(max(threads)) if threads else 1
+def time_launches(fn, n, torch):
+    """Mean milliseconds of fn() over n back-to-back calls on the current stream (events around them)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def config_sections(args, B, torch, synth, np):
+    """Configs 1, 2 (split 1 and 4) and 4 in their own launch shapes, each with the oracle timed beside it."""
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload, to_device
+    from oracle import grad as og
+    from oracle import model as om
+    n = args.config_steps
+    out = {}
+    r = om.bf16_round
+
+    def rw(w):
+        return {k: (v if k.startswith("ln") else r(v)) for k, v in w.items()}
+
+    def flops_bytes(wl, lay, meta, kind):
+        views = B.meta_views(meta, lay, wl.batch.n_users)
+        nn = views["n"].cpu().numpy().astype(np.int64)
+        pf, pt = visible_pairs(nn, wl.batch.lens.astype(np.int64), wl.batch.split)
+        d = wl.dims
+        hd, gd, D = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim, d.d_model
+        R, T = lay.n_rows, lay.n_t_rows
+        if kind == "full":
+            return 4.0 * d.head_dim * d.n_q_heads * pf, 2.0 * R * D * (2 * hd + 2 * gd) + 2.0 * R * hd * D, None
+        attn = 4.0 * d.head_dim * d.n_q_heads * pt
+        proj = 2.0 * R * D * 2 * gd + 2.0 * T * D * 2 * hd + 2.0 * T * hd * D
+        return attn, proj, 2.0 * (R * 2 * gd + 2 * T * hd)
+
+    def layer_case(wl, kind, label):
+        dw = DeviceWorkload(wl)
+        lay = B.meta_layout(dw.batch)
+        meta = B.mask_build(dw.batch)
+        op = B.OP_FULL if kind == "full" else B.OP_TARGET
+        ws = B.workspace(dw.batch, dw.dims, op)
+        x_out = torch.empty_like(dw.x)
+        fn = B.attn_full if kind == "full" else B.attn_target
+        w = dw.full[0] if kind == "full" else dw.target[0]
+        run = lambda: fn(dw.batch, dw.dims, meta, w, dw.x, x_out, ws)
+        for _ in range(3):
+            run()
+        layer_ms = time_launches(run, n, torch)
+        kc = B.K_ATTN_FULL if kind == "full" else B.K_ATTN_TARGET
+        B.timing_enable([kc])
+        B.timing_read(kc)
+        for _ in range(n):
+            run()
+        torch.cuda.synchronize()
+        B.timing_enable([])
+        cnt, ms = B.timing_read(kc)
+        attn_ms = ms / max(1, cnt)
+        attn, proj, abytes = flops_bytes(wl, lay, meta, kind)
+        res = {"rows": int(lay.n_rows), "t_rows": int(lay.n_t_rows), "launches": n,
+               "layer_us": 1000.0 * layer_ms, "attn_us": 1000.0 * attn_ms,
+               "layer_masked_TFLOPs": (attn + proj) / (layer_ms * 1e-3) / 1e12,
+               "attn_TFLOPs": attn / (attn_ms * 1e-3) / 1e12}
+        res["layer_mfma_frac"] = res["layer_masked_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+        if abytes is not None:
+            res["attn_GBs"] = abytes / (attn_ms * 1e-3) / 1e9
+            res["attn_hbm_frac"] = res["attn_GBs"] / HBM_PEAK_GBS
+            res["attn_bytes"] = abytes
+        if not args.no_cpu_baseline:
+            xr = r(wl.x)
+            wr = rw(wl.full[0] if kind == "full" else wl.target[0])
+            ofn = om.full_layer if kind == "full" else om.target_layer
+
+            def one(u):
+                rows = wl.batch.rows_of([u])
+                ofn(wl.batch.subset([u]), xr[rows], wr, wl.dims)
+            rate = oracle_rate(one, wl.batch.n_users, 4.0, f"one {kind} layer (oracle.model)")
+            rate["ms_per_layer_batch"] = 1000.0 * wl.batch.n_users / rate["value"]
+            rate["cores"] = blas_threads()
+            res["cpu_oracle"] = rate
+            if label == "config1":
+                from threadpoolctl import threadpool_limits
+                with threadpool_limits(1):
+                    one1 = oracle_rate(one, wl.batch.n_users, 4.0, f"one {kind} layer (oracle.model), 1 thread")
+                one1["ms_per_layer_batch"] = 1000.0 * wl.batch.n_users / one1["value"]
+                one1["cores"] = 1
+                res["cpu_oracle_1core"] = one1
+        log(f"{label}: " + json.dumps({k: v for k, v in res.items() if not isinstance(v, dict)}))
+        return res
+
+    out["config1"] = layer_case(synth.config1(), "full", "config1")
+    for s in (1, 4):
+        out[f"config2_s{s}"] = layer_case(synth.config2(s), "target", f"config2_s{s}")
+
+    # config 4: forward and backward of one full and one target layer, 64 users of 5632 rows, d 1024
+    wl = synth.config4()
+    dw = DeviceWorkload(wl)
+    meta = B.mask_build(dw.batch)
+    dy = to_device(wl.dy, "bf16")
+    ws_f = B.workspace(dw.batch, dw.dims, B.OP_FULL)
+    ws_t = B.workspace(dw.batch, dw.dims, B.OP_TARGET)
+    ws_fb = B.workspace(dw.batch, dw.dims, B.OP_FULL_BWD)
+    ws_tb = B.workspace(dw.batch, dw.dims, B.OP_TARGET_BWD)
+    x1, x2 = torch.empty_like(dw.x), torch.empty_like(dw.x)
+    dx1, dx2 = torch.empty_like(dw.x), torch.empty_like(dw.x)
+    fg = {k: torch.empty(tuple(dw.full[0][k].shape), dtype=torch.float32, device="cuda") for k in B.FULL_GRAD_KEYS}
+    tg = {k: torch.empty(tuple(dw.target[0][k].shape), dtype=torch.float32, device="cuda")
+          for k in B.TARGET_GRAD_KEYS}
+
+    def fwd():
+        B.attn_full(dw.batch, dw.dims, meta, dw.full[0], dw.x, x1, ws_f)
+        B.attn_target(dw.batch, dw.dims, meta, dw.target[0], x1, x2, ws_t)
+
+    def bwd():
+        B.attn_target_bwd(dw.batch, dw.dims, meta, dw.target[0], x1, dy, dx2, tg, ws_tb)
+        B.attn_full_bwd(dw.batch, dw.dims, meta, dw.full[0], dw.x, dx2, dx1, fg, ws_fb)
+
+    fwd(); bwd()
+    k4 = max(2, n // 4)
+    fwd_ms = time_launches(fwd, k4, torch)
+    bwd_ms = time_launches(bwd, k4, torch)
+    c4 = {"users": wl.batch.n_users, "rows": int(wl.batch.total_rows), "steps": k4,
+          "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "fwd_bwd_ms": fwd_ms + bwd_ms,
+          "what": "forward of one full + one target layer, then both layers' backward (dX and every weight / "
+                  "GLN gradient), d 1024, 16Q/4KV, split 4"}
+    if not args.no_cpu_baseline:
+        xr = r(wl.x)
+        wf, wt = rw(wl.full[0]), rw(wl.target[0])
+
+        def one(u):
+            rows = wl.batch.rows_of([u])
+            sub = wl.batch.subset([u])
+            x_1 = om.full_layer(sub, xr[rows], wf, wl.dims)
+            g = og.target_layer_bwd(sub, r(x_1), wt, wl.dims, wl.dy[rows])
+            og.full_layer_bwd(sub, xr[rows], wf, wl.dims, r(g["x"]))
+        rate = oracle_rate(one, wl.batch.n_users, 1.0, "forward of the full layer, backward of both layers, "
+                                                         "one user")
+        rate["ms_per_batch"] = 1000.0 * wl.batch.n_users / rate["value"]
+        rate["cores"] = blas_threads()
+        c4["cpu_oracle"] = rate
+    log("config4: " + json.dumps({k: v for k, v in c4.items() if not isinstance(v, dict)}))
+    out["config4"] = c4
+    del dw, ws_f, ws_t, ws_fb, ws_tb, x1, x2, dx1, dx2, fg, tg, dy
+    return out
 
 
 def main():
@@ -120,6 +282,10 @@ def main():
     ap.add_argument("--train-steps", type=int, default=3,
                     help="also time this many training gradient passes (mtfm_backbone_bwd: forward keeping the "
                          "layer inputs, then every layer's backward); 0 skips")
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="also time config 1 (one full layer, 32 users), config 2 (one target layer, split 1 and 4) "
+                         "and config 4 (forward + backward of one full and one target layer, 64 long users) in their "
+                         "own shapes, this many launches each, with the oracle beside each; 0 skips")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (calibrates PMC byte counters)")
     args = ap.parse_args()
@@ -438,6 +604,10 @@ def main():
         log("sparse projections: " + json.dumps(sparse))
         del full_s, tgt_s
 
+    configs = None
+    if args.config_steps > 0:
+        configs = config_sections(args, B, torch, synth, np)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
@@ -472,6 +642,7 @@ def main():
         "serve": serve,
         "v2": v2,
         "sparse": sparse,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -211,13 +211,30 @@ mtfm_status prepare(const mtfm_batch* b, const mtfm_dims* d, const void* meta_d,
   return MTFM_OK;
 }
 
-// Workgroup shape of the full-layer attention kernel: 32 queries per wave by
-// default; MTFM_ATTN_FULL_QB=2 selects 64 queries per wave (half the
-// workgroups, more registers).  A tuning knob: both shapes compute the same.
-// Read at every call, so one process can run both shapes.
-int full_attn_half_tiles() {
-  const char* e = std::getenv("MTFM_ATTN_FULL_QB");
-  return (e && e[0] == '2') ? 0 : 1;
+// Fused epilogue of the bf16 attention (the gated group LayerNorm, written as
+// Y); A itself only where something reads it afterwards.
+static void fuse_gated_gln(AttnArgs& aa, const Ctx& c, const mtfm_dims* d, const float* g2, const float* b2,
+                           const void* u, int64_t ldu, void* y, int64_t ldy, void* a_keep) {
+  aa.y = y; aa.ldy = ldy;
+  aa.u = u; aa.ldu = ldu;
+  aa.ln_g = g2; aa.ln_b = b2;
+  aa.type = c.meta.type; aa.eps = d->ln_eps;
+  aa.a = (c.write_a || a_keep) ? aa.a : nullptr;
+}
+
+// Gated group LayerNorm of the T rows after the target attention (their A,
+// T-row order): the target layer's query rows are too few to fill the GPU
+// with one workgroup per 32 rows and every head, so its attention runs one
+// workgroup per KV group and the normalisation, which needs every head of a
+// row, follows as a pass over the T rows alone.
+static mtfm_status target_gated_gln(const Ctx& c, const mtfm_dims* d, const float* g2, const float* b2,
+                                    const void* a, const void* u, int64_t ldu, void* y, int dt) {
+  const int hd = d->n_q_heads * d->head_dim;
+  GlnArgs g{};
+  g.rows = (int32_t)c.plan.n_t_rows; g.D = hd; g.x = a; g.ldx = hd; g.y = y; g.ldy = hd;
+  g.gate = u; g.ldg = ldu;
+  g.gamma = g2; g.beta = b2; g.type = nullptr; g.type_const = TT_T; g.eps = d->ln_eps;
+  return timed_gln(g, dt, c.s);
 }
 
 // ---------------------------------------------------------------------------
@@ -277,16 +294,19 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
     aa.kd = kv->k; aa.ldkd = gd; aa.vd = kv->k; aa.ldvd = gd;
   }
   aa.a = a; aa.lda = hd;
-  aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles; aa.half_tiles = full_attn_half_tiles();
+  aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+  if (dt == MTFM_BF16) fuse_gated_gln(aa, c, d, w->ln2_g, w->ln2_b, z, zw, y, hd, keep ? keep->a : nullptr);
   TRY(timed_attention(MTFM_K_ATTN_FULL, aa, dt, c.s));
 
-  GlnArgs g2{};
-  g2.rows = (int32_t)p.n_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
-  g2.gate = z; g2.ldg = zw;
-  g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = c.meta.type; g2.eps = d->ln_eps;
-  TRY(timed_gln(g2, dt, c.s));
+  if (dt != MTFM_BF16) {
+    GlnArgs g2{};
+    g2.rows = (int32_t)p.n_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
+    g2.gate = z; g2.ldg = zw;
+    g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = c.meta.type; g2.eps = d->ln_eps;
+    TRY(timed_gln(g2, dt, c.s));
+  }
 
   GemmArgs go{};
   go.M = (int32_t)p.n_rows; go.N = D; go.K = hd; go.groups = 1;
@@ -377,16 +397,19 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
-  aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
+  aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+  aa.per_group = 1;
   TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
 
-  GlnArgs g2{};
-  g2.rows = (int32_t)p.n_t_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
-  g2.gate = zt; g2.ldg = zw;
-  g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;
-  TRY(timed_gln(g2, dt, c.s));
+  {
+    GlnArgs g2{};
+    g2.rows = (int32_t)p.n_t_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
+    g2.gate = zt; g2.ldg = zw;
+    g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;
+    TRY(timed_gln(g2, dt, c.s));
+  }
 
   GemmArgs go{};
   go.M = (int32_t)p.n_parents; go.N = D; go.K = hd; go.groups = S;
@@ -483,16 +506,13 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
-  aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
+  aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+  aa.per_group = 1;
   TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
 
-  GlnArgs g2{};
-  g2.rows = (int32_t)p.n_t_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
-  g2.gate = zt; g2.ldg = zw;
-  g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;
-  TRY(timed_gln(g2, dt, c.s));
+  TRY(target_gated_gln(c, d, w->ln2_g, w->ln2_b, a, zt, zw, y, dt));
 
   GemmArgs go{};
   go.M = (int32_t)p.n_parents; go.N = D; go.K = hd; go.groups = S;
@@ -705,17 +725,13 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
-  aa.tiles = tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
+  aa.tiles = tiles; aa.ntiles = (int32_t)p.n_target_tiles;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
+  aa.per_group = 1;
   TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
 
-  GlnArgs g2{};
-  g2.rows = (int32_t)p.n_t_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
-  g2.gate = zt; g2.ldg = zw;
-  g2.gamma = fw ? fw->ln2_g : tw->ln2_g; g2.beta = fw ? fw->ln2_b : tw->ln2_b;
-  g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;
-  TRY(timed_gln(g2, dt, c.s));
+  TRY(target_gated_gln(c, d, fw ? fw->ln2_g : tw->ln2_g, fw ? fw->ln2_b : tw->ln2_b, a, zt, zw, y, dt));
 
   GemmArgs go{};
   go.M = (int32_t)p.n_t_rows; go.N = D; go.K = hd; go.groups = 1;
@@ -911,6 +927,7 @@ mtfm_status mtfm_attn_full(const mtfm_batch* batch, const mtfm_dims* dims, const
   Ctx c;
   TRY(prepare(batch, dims, meta_d, x_in, x_out, ws, ws_bytes, MTFM_OP_FULL, &c, stream));
   TRY(check_full_w(w, dims));
+  c.write_a = true;
   return run_full(c, dims, w, x_in, x_out, (char*)ws);
 }
 
@@ -920,6 +937,7 @@ mtfm_status mtfm_attn_target(const mtfm_batch* batch, const mtfm_dims* dims, con
   Ctx c;
   TRY(prepare(batch, dims, meta_d, x_in, x_out, ws, ws_bytes, MTFM_OP_TARGET, &c, stream));
   TRY(check_target_w(w, dims));
+  c.write_a = true;
   return run_target(c, dims, w, x_in, x_out, (char*)ws);
 }
 

@@ -36,6 +36,7 @@ struct Ctx {
   MetaPlan plan;
   MetaPtrs meta{};
   hipStream_t s = nullptr;
+  bool write_a = false;   // the bf16 forward also stores A in the workspace (single-layer calls: the probe reads it)
 };
 
 mtfm_status check_dims(const mtfm_dims* d);
@@ -68,9 +69,6 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
                      const KvOut* kv = nullptr, const FwdKeep* keep = nullptr);
 mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, const void* x_in, void* x_out,
                        char* ws, const FwdKeep* keep = nullptr);
-// Workgroup shape of the full-layer attention (1: 32 queries per wave); the
-// backward's recompute takes the same shape, so kept and recomputed A agree.
-int full_attn_half_tiles();
 
 // backward (bwd.hip)
 int64_t bwd_ws_bytes(const MetaPlan& p, const mtfm_dims* d, int op);

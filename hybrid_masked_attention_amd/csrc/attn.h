@@ -27,13 +27,23 @@ struct AttnArgs {
   int32_t n_key_rows;            // packed rows in k (rows past it read as zero)
   const void* kd; int64_t ldkd;  // the query rows' own keys / values (query space)
   const void* vd; int64_t ldvd;
-  void* a; int64_t lda;          // output [query row][H*dh]
+  void* a; int64_t lda;          // output [query row][H*dh]; optional on the bf16 path (nullptr: not written)
   const int32_t* tiles; int32_t ntiles;
   const int32_t* p; const int32_t* n;  // per packed row
   const int32_t* lens;
   int32_t H, G, dh;
   float out_scale;               // ln 2
-  int32_t half_tiles;            // bf16: 1 = one workgroup per 32-row half tile (more workgroups)
+  // bf16 path, optional fused epilogue (y != nullptr): the gated group
+  // LayerNorm after attention, y[row] = (LN(A[row]) * ln_g[t] + ln_b[t]) (.) u[row]
+  // over the row's H*dh values, t = type[packed row] (ln_g / ln_b [3][H*dh] fp32)
+  void* y; int64_t ldy;
+  const void* u; int64_t ldu;
+  const float* ln_g; const float* ln_b;
+  const uint8_t* type;
+  float eps;
+  // bf16 path: one workgroup per KV group of a query half instead of one per
+  // query half (G times the workgroups; A only, no fused epilogue)
+  int32_t per_group;
 };
 
 mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s);

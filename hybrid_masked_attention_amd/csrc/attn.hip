@@ -1,29 +1,34 @@
 // Masked pointwise-SiLU attention kernels for gfx950.
 //
-// bf16 kernel: one workgroup per (query tile slice, KV group g) with one wave
-// per query head of the group (r waves).  The group's K and V tiles (64 keys
-// x 64 dims) are shared by the r heads in LDS ([explainer] §4.1 GQA: r query
-// heads share a KV head).  They arrive through a ring of LDS stages filled by
-// buffer loads straight into LDS: K from its row-major rows, V from a
-// transposed copy (V^T, written by the projection GEMM) whose keys are
-// permuted within groups of 16.  Per 32-key block each wave computes
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulate; lane = query,
-// registers = keys), applies SiLU pointwise, rounds P to bf16 and accumulates
-// O^T += V^T P^T on MFMA: the S^T registers are already the B operand in the
-// permuted key order, so P never leaves registers and every fragment is one
-// 16-byte LDS read.
+// bf16 kernel: one workgroup per 32 query rows of a query tile and all H
+// heads, one wave per head of the KV groups in flight.  The K and V tiles
+// (64 keys x 64 dims) of a group are shared by its r heads in LDS
+// ([explainer] §4.1 GQA: r query heads share a KV head).  They arrive through
+// a ring of LDS stages filled by buffer loads straight into LDS: K from its
+// row-major rows, V from a transposed copy (V^T, written by the projection
+// GEMM) whose keys are permuted within groups of 16.  Per 32-key block each
+// wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulate;
+// lane = query, registers = keys), applies SiLU pointwise, rounds P to bf16
+// and accumulates O^T += V^T P^T on MFMA: the S^T registers are already the B
+// operand in the permuted key order, so P never leaves registers and every
+// fragment is one 16-byte LDS read.
 //
 // Key tiles are aligned to 64 packed rows (aligned DMA); a tile is visited
 // only when it holds a key visible to some query of the slice ([blog] §6.2:
 // compute only key blocks holding a valid key), and the mask compare runs only
 // on tiles not entirely inside every query's visible prefix (separate
 // straight-line bodies).  T columns are never tiled ([blog] §6.2: the
-// user-to-item direction is skipped): a T row's self term is one extra
-// "diagonal" tile built from the query slice's own K/V rows.
+// user-to-item direction is skipped): a T row's self term is one dot product
+// and one value update in registers.
 //
-// Every visible pair costs one exp and one reciprocal on the VALU, so the
-// kernel keeps two workgroups per CU to overlap one wave's SiLU with another's
-// MFMAs.  QB = 1 gives each wave 32 queries, QB = 2 gives 64.
+// With every head of its rows in one workgroup, the kernel finishes the layer's
+// attention branch itself: A = O ln2 / n, then the gated group LayerNorm
+// Y = GLN2(A) (.) U over the row ([blog] §6.1, GLN fused with the gating), so
+// neither A nor Y makes a round trip through HBM before the output projection.
+//
+// Every visible pair costs one exp and one reciprocal on the VALU; MFMA and
+// VALU work overlap across the waves resident on a SIMD (four per SIMD here),
+// not within one wave.
 //
 // fp32 kernel: one thread per (query row, head), plain loops; the fp32
 // correctness path.
@@ -69,40 +74,48 @@ MTFM_DEV void a_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // Slot of packed row r inside its aligned group of 16 (the P V key order).
 MTFM_DEV int perm16(int r) { return (r & ~15) | (r & 3) | (((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 3); }
 
-// Ring depth and workgroups per CU: 32 queries per wave fit three workgroups
-// (two-stage ring + diagonal tile, 48 KB), 64 queries per wave two (three
-// stages, 64 KB).
-template <int QB> struct AttnShape { static constexpr int AS = QB == 1 ? 2 : 3, WG_PER_CU = QB == 1 ? 3 : 2; };
+// Workgroup shape.  One workgroup takes 32 query rows and every head of them,
+// one wave per head of GPP KV groups at a time; the heads of further groups
+// are further passes over the key tiles (P = G / GPP passes, each wave then
+// holding P heads).  A ring stage holds GPP x (K + V^T) of 64 keys; two
+// stages: 64 KB at GPP = 2 (two workgroups per CU, four waves per SIMD at
+// r = 4), 128 KB at GPP = 4 (one workgroup of 16 waves per CU).
+template <int R, int GPP> struct FusedShape {
+  static constexpr int W = R * GPP;                  // waves per workgroup
+  static constexpr int STAGE = GPP * A_STAGE;
+  static constexpr int AS = 2;                       // ring stages
+  static constexpr int CPW = 16 * GPP / W;           // 1 KB DMA chunks per wave per stage
+  static constexpr int WG_PER_CU = (160 * 1024) / (AS * STAGE) >= 2 ? 2 : 1;
+  static constexpr int WAVES_PER_SIMD = W * WG_PER_CU / 4 < 1 ? 1 : (W * WG_PER_CU / 4 > 4 ? 4 : W * WG_PER_CU / 4);
+};
 
-template <int R, int QB>
-// (the second bound is waves per SIMD: with one wave per head, fewer than four
-// heads per group leave the SIMDs a wave per workgroup or less)
-__global__ __launch_bounds__(64 * R, R >= 4 ? AttnShape<QB>::WG_PER_CU : 1) void attn_bf16_kernel(AttnArgs g) {
-  constexpr int AS = AttnShape<QB>::AS;
-  constexpr int NT = 64 * R;
-  constexpr int CPW = 8 / R;                // 1 KB DMA chunks per wave per 8 KB tile
-  constexpr int DMA_PER_TILE = 2 * CPW;     // K + V^T instructions per wave per tile
-  constexpr int SLICES = 2 / QB;            // workgroups per 64-row query tile
-  __shared__ __attribute__((aligned(1024))) char lds[AS * A_STAGE + A_STAGE];   // ring + diagonal tile
-  char* const dlds = lds + AS * A_STAGE;
+template <int R, int GPP, int P>
+__global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD)) void attn_bf16_kernel(AttnArgs g) {
+  using SH = FusedShape<R, GPP>;
+  constexpr int W = SH::W, AS = SH::AS, STAGE = SH::STAGE, CPW = SH::CPW;
+  __shared__ __attribute__((aligned(1024))) char lds[AS * STAGE];
 
-  const int nblocks = g.ntiles * g.G * SLICES;
+  // logical block: (query tile, 32-row half[, KV group]); with per_group the
+  // workgroup takes one group's heads (the grid has G times the blocks)
+  const int ngrp = g.per_group ? g.G : 1;
+  const int nblocks = g.ntiles * 2 * ngrp;
   const int lb = xcd_remap(blockIdx.x, nblocks);
-  const int slice = lb % SLICES;
-  const int tile = (lb / SLICES) / g.G, grp = (lb / SLICES) % g.G;
+  const int gsel = lb % ngrp, sid = lb / ngrp;
+  const int slice = sid & 1, tile = sid >> 1;
   const int32_t* td = g.tiles + 8 * tile;
   const int u = td[TD_USER], row0 = td[TD_ROW0], tile_rows = td[TD_NROWS];
-  const int qoff = slice * 32 * QB;
-  const int nrows = min(32 * QB, tile_rows - qoff);
+  const int qoff = slice * 32;
+  const int nrows = min(32, tile_rows - qoff);
   if (nrows <= 0) return;                      // empty half of a short tile (whole workgroup)
   const int grow0 = td[TD_GROW0] + qoff, qrow0 = td[TD_QROW0] + qoff, urow0 = td[TD_UROW0];
   const int lctx = g.lens[3 * u] + g.lens[3 * u + 1];
-  const bool has_diag = row0 + qoff + nrows > lctx;
+  const bool any_self = row0 + qoff + nrows > lctx;   // some row of the slice is a T row (sees itself)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = grp * R + wave;
+  const int gl = wave / R;                     // group within the pass
   const int l32 = lane & 31, hi = lane >> 5;
+  const int hd = g.H * DH;
 
   // Key tiles are aligned to 64 packed rows: tile it covers rows ts = T0 + 64 it
   // .. ts + 63.  The descriptor bounds the user's visible keys: rows below
@@ -114,222 +127,274 @@ __global__ __launch_bounds__(64 * R, R >= 4 ? AttnShape<QB>::WG_PER_CU : 1) void
   const int n_main = key_end > 0 ? (kend - T0 + 63) >> 6 : 0;
   const int kfull = urow0 + min(64 * td[TD_FULL_END], lctx);
 
-  // DMA lanes: chunk c = 8 rows of 128 B; lane -> row 8c + lane/8, slot lane%8
+  // DMA: the stage's 16 GPP chunks of 1 KB (per group: 8 of K rows, 8 of V^T
+  // rows, 8 rows of 128 B each); wave w issues chunks w + W i.  Lane -> row
+  // 8 rb + lane / 8, 16-byte slot lane % 8 (read from the swizzled chunk).
   const int rin = lane >> 3, slot = lane & 7;
-  uint32_t koff[CPW], voff[CPW];
+  uint32_t doff[CPW];
+  int dlds[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
-    const int r = (i * R + wave) * 8 + rin;
-    const int c = slot ^ a_swz(r);
-    koff[i] = (uint32_t)(r * g.ldk * 2 + grp * DH * 2 + c * 16);
-    voff[i] = (uint32_t)((grp * DH + r) * g.ldvt * 2 + c * 16);
+    const int c = wave + W * i;
+    const int cg = c >> 4, kind = (c >> 3) & 1, rb = c & 7;
+    const int r = rb * 8 + rin;
+    const int sw = slot ^ a_swz(r);
+    doff[i] = kind == 0 ? (uint32_t)(r * g.ldk * 2 + cg * DH * 2 + sw * 16)
+                        : (uint32_t)((cg * DH + r) * g.ldvt * 2 + sw * 16);
+    dlds[i] = cg * A_STAGE + kind * A_TILE + rb * 1024;
   }
   const bf16* kbase = (const bf16*)g.k;
   const bf16* vtbase = (const bf16*)g.vt;
   const int64_t vt_elems = (int64_t)g.G * DH * g.ldvt;
   // Tiles past the last one are issued as empty loads (zero-size resources), so
   // that the number of DMA instructions in flight is a constant at every wait.
-  auto issue = [&](int it, int stage) {
+  auto issue = [&](int gbase, int it, int stage) {
     const bool real = it < n_main;
     const int ts = real ? T0 + it * 64 : T0;
     const int valid = real ? min(64, g.n_key_rows - ts) : 0;
-    const __amdgpu_buffer_rsrc_t kr = a_rsrc(kbase + (int64_t)ts * g.ldk, (uint32_t)(max(valid, 0) * g.ldk * 2));
-    const __amdgpu_buffer_rsrc_t vr = a_rsrc(vtbase + ts, real ? (uint32_t)((vt_elems - ts) * 2) : 0u);
-    char* st = lds + stage * A_STAGE;
+    const __amdgpu_buffer_rsrc_t kr =
+        a_rsrc(kbase + (int64_t)ts * g.ldk + gbase * DH, (uint32_t)(max(valid, 0) * g.ldk * 2));
+    const int64_t vt0 = (int64_t)gbase * DH * g.ldvt + ts;
+    const __amdgpu_buffer_rsrc_t vr = a_rsrc(vtbase + vt0, real ? (uint32_t)((vt_elems - vt0) * 2) : 0u);
+    char* st = lds + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-      lds_dma16(kr, (lds_void*)(st + (i * R + wave) * 1024), koff[i]);
-      lds_dma16(vr, (lds_void*)(st + A_TILE + (i * R + wave) * 1024), voff[i]);
+      const int c = wave + W * i;
+      lds_dma16(((c >> 3) & 1) ? vr : kr, (lds_void*)(st + dlds[i]), doff[i]);
     }
   };
-#pragma unroll
-  for (int s = 0; s < AS; ++s) issue(s, s);
 
-  // Q fragments (B operand of S^T = K Q^T): query qb*32 + l32, dims kk*16 + 8*hi + [0, 8)
-  // (all loads first, uses after: the counters drain in issue order)
-  bf16x8 qf[QB][4];
-  int pl[QB], nl[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qb * 32 + l32;
-    const bool ok = qi < nrows;
-    const int qr = ok ? qi : 0;
-    const bf16* src = (const bf16*)g.q + (int64_t)(qrow0 + qr) * g.ldq + h * DH + 8 * hi;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = *(const bf16x8*)(src + kk * 16);
-    pl[qb] = g.p[grow0 + qr];
-    nl[qb] = g.n[grow0 + qr];
-  }
-  // diagonal tile (T rows' own keys): registers -> LDS in the ring's layout
-  constexpr int DPT = (512 + NT - 1) / NT;
-  bf16x8 dk[DPT], dv[DPT];
-  if (has_diag) {
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-      const int c = tid + NT * i, r = c >> 3, cc = c & 7;
-      const int rr = (c < 512 && r < nrows) ? r : 0;
-      dk[i] = *(const bf16x8*)((const bf16*)g.kd + (int64_t)(qrow0 + rr) * g.ldkd + grp * DH + cc * 8);
-      dv[i] = *(const bf16x8*)((const bf16*)g.vd + (int64_t)(qrow0 + rr) * g.ldvd + grp * DH + cc * 8);
-    }
-  }
-  int plim[QB], selfq[QB];
-  float rq[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const bool ok = qb * 32 + l32 < nrows;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = ok ? qf[qb][kk] : bf16x8{};
-    plim[qb] = ok ? pl[qb] : 0;
-    selfq[qb] = ok ? nl[qb] - pl[qb] : 0;
-    rq[qb] = ok ? g.out_scale / (float)nl[qb] : 0.f;
-  }
-  if (has_diag) {
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-      const int c = tid + NT * i, r = c >> 3, cc = c & 7;
-      if (c >= 512) continue;
-      if (r >= nrows) { dk[i] = bf16x8{}; dv[i] = bf16x8{}; }
-      *(bf16x8*)(dlds + r * 128 + ((cc ^ a_swz(r)) << 4)) = dk[i];
-      const int ps = perm16(r);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = cc * 8 + e;
-        *(bf16*)(dlds + A_TILE + d * 128 + (((ps >> 3) ^ a_swz(d)) << 4) + (ps & 7) * 2) = dv[i][e];
-      }
-    }
-  }
-  // the ring's first tiles, the query rows and the diagonal tile are in place
-  a_wait_vm_lgkm<0>();
-  a_barrier();
+  // per query row: visible context prefix, self flag, output scale
+  const bool ok = l32 < nrows;
+  const int qr = ok ? l32 : 0;
+  const int plim = ok ? g.p[grow0 + qr] : 0;
+  const int nl = ok ? g.n[grow0 + qr] : 1;
+  const int selfq = ok ? nl - plim : 0;
+  const float rq = ok ? g.out_scale / (float)nl : 0.f;
 
-  f32x16 o[2][QB];   // O^T: lane = query, registers = dims mb*32 + 8(i/4) + 4hi + i%4
+  f32x16 o[P][2];   // O^T per pass: lane = query, registers = dims mb*32 + 8(i/4) + 4hi + i%4
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < QB; ++b) o[a][b] = f32x16{};
+  for (int pp = 0; pp < P; ++pp) { o[pp][0] = f32x16{}; o[pp][1] = f32x16{}; }
 
   const int xk = hi ^ a_swz(l32);   // fragment slot = (even chunk) ^ xk for K and V^T rows
-  auto qk = [&](const char* st, int kb, f32x16* sc) {
+  using MaskNone = std::integral_constant<int, 0>;
+  using MaskUpper = std::integral_constant<int, 1>;
+  using MaskRange = std::integral_constant<int, 2>;
+
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sc[qb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 af = *(const bf16x8*)(st + (kb * 32 + l32) * 128 + (((2 * kk) ^ xk) << 4));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][kk], sc[qb], 0, 0, 0);
+  for (int pp = 0; pp < P; ++pp) {
+    const int gbase = (gsel + pp) * GPP;
+    const int grp = gbase + gl;
+    const int h = grp * R + wave % R;
+    if (pp > 0) {
+      a_wait_vm_lgkm<0>();
+      a_barrier();                             // every wave is done with the previous pass's ring
     }
-  };
-  // P chunk c of key block kb: keys kb*32 + 16c + {4hi + t, 8 + 4hi + t : t < 4}, the
-  // order in which V^T holds them, so P^T is the B operand of O^T += V^T P^T as is.
-  // Masks (template MK): 0 none; 1 keys below lim visible; 2 keys in [lo, lim);
-  // 3 only key dsel (the diagonal tile).  The invisible scores are set to 0
-  // before SiLU (SiLU(0) = 0 exactly), so each mask costs one compare and one
-  // select per element and P still converts to bf16 in pairs.  Register i of
-  // this lane holds key kb*32 + kc(i) + 4*hi with the compile-time
-  // kc(i) = 8*(i/4) + i%4: the bounds are shifted by the lane part once.
-  auto silu_pv = [&](const char* st, int kb, const f32x16* sc, auto mask_tag, int lo, const int* lim,
-                     const int* dsel) {
-    constexpr int MK = decltype(mask_tag)::value;
-    bf16x8 pf[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int s = 0; s < AS; ++s) issue(gbase, s, s);
+    // Q fragments (B operand of S^T = K Q^T): query l32, dims kk*16 + 8*hi + [0, 8)
+    bf16x8 qf[4];
+    {
+      const bf16* src = (const bf16*)g.q + (int64_t)(qrow0 + qr) * g.ldq + h * DH + 8 * hi;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qf[kk] = ok ? *(const bf16x8*)(src + kk * 16) : bf16x8{};
+    }
+    const char* gl_lds = lds + gl * A_STAGE;   // this wave's group inside a stage
+    a_wait_vm_lgkm<0>();
+    a_barrier();                               // the ring's first tiles are in place
+
+    auto qk = [&](const char* st, int kb, f32x16& sc) {
+      sc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 af = *(const bf16x8*)(st + (kb * 32 + l32) * 128 + (((2 * kk) ^ xk) << 4));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], sc, 0, 0, 0);
+      }
+    };
+    // P chunk c of key block kb: keys kb*32 + 16c + {4hi + t, 8 + 4hi + t : t < 4}, the
+    // order in which V^T holds them, so P^T is the B operand of O^T += V^T P^T as is.
+    // Masks (template MK): 0 none; 1 keys below lim visible; 2 keys in [lo, lim).
+    // The invisible scores are set to 0 before SiLU (SiLU(0) = 0 exactly), so a
+    // mask costs one compare and one select per element and P still converts to
+    // bf16 in pairs.  Register i of this lane holds key kb*32 + kc(i) + 4*hi with
+    // the compile-time kc(i) = 8*(i/4) + i%4: the bounds are shifted once.
+    auto silu_pv = [&](const char* st, int kb, const f32x16& sc, auto mask_tag, int lo, int lim) {
+      constexpr int MK = decltype(mask_tag)::value;
+      bf16x8 pf[2];
       const int shift = kb * 32 + 4 * hi;
-      const int lo_l = lo - shift;
-      const int lim_l = (MK == 1 || MK == 2) ? lim[qb] - shift : 0;
-      const int d_l = MK == 3 ? dsel[qb] - shift : 0;
+      const int lo_l = lo - shift, lim_l = lim - shift;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * c + e;
           const int kc = 8 * (i >> 2) + (i & 3);
-          float sv = sc[qb][i];
+          float sv = sc[i];
           if constexpr (MK == 1) sv = kc < lim_l ? sv : 0.f;
           if constexpr (MK == 2) sv = (kc >= lo_l && kc < lim_l) ? sv : 0.f;
-          if constexpr (MK == 3) sv = kc == d_l ? sv : 0.f;
-          pf[qb][c][e] = (bf16)silu_scaled(sv);
+          pf[c][e] = (bf16)silu_scaled(sv);
         }
-    }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 vf = *(const bf16x8*)(st + A_TILE + (mb * 32 + l32) * 128 + (((4 * kb + 2 * c) ^ xk) << 4));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[mb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][c], o[mb][qb], 0, 0, 0);
-      }
-  };
-  // QB = 1 issues both key blocks' QK MFMAs before the first block's SiLU (more
-  // independent MFMA work per wave); QB = 2 has enough of it per block already
-  // and keeps fewer accumulators live.
-  auto tile_body = [&](const char* st, auto mask_tag, int lo, const int* lim, const int* dsel) {
-    if constexpr (QB == 1) {
-      f32x16 sc[2][QB];
-      qk(st, 0, sc[0]);
-      qk(st, 1, sc[1]);
-      silu_pv(st, 0, sc[0], mask_tag, lo, lim, dsel);
-      silu_pv(st, 1, sc[1], mask_tag, lo, lim, dsel);
-    } else {
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8 vf = *(const bf16x8*)(st + A_TILE + (mb * 32 + l32) * 128 + (((4 * kb + 2 * c) ^ xk) << 4));
+          o[pp][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[pp][mb], 0, 0, 0);
+        }
+    };
+    // one 32-key block at a time (a wave gets no MFMA / VALU overlap within
+    // itself, only with the other waves of its SIMD, so holding one block's
+    // scores keeps four waves per SIMD within their registers)
+    auto tile_body = [&](const char* st, auto mask_tag, int lo, int lim) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sc[QB];
+        f32x16 sc;
         qk(st, kb, sc);
-        silu_pv(st, kb, sc, mask_tag, lo, lim, dsel);
+        silu_pv(st, kb, sc, mask_tag, lo, lim);
+      }
+    };
+
+    int stage = 0;
+    for (int it = 0; it < n_main; ++it) {
+      const char* st = gl_lds + stage * STAGE;
+      const int ts = T0 + it * 64;
+      if (ts >= urow0 && ts + 64 <= kfull) {
+        tile_body(st, MaskNone{}, 0, 0);
+      } else {
+        const int lim = urow0 + plim - ts;
+        if (ts >= urow0) tile_body(st, MaskUpper{}, 0, lim);   // only the prefix end cuts this tile
+        else tile_body(st, MaskRange{}, urow0 - ts, lim);      // the user's first tile
+      }
+      if (it + 1 < n_main) {
+        // tile it + 1 has landed once at most AS - 2 newer tiles' DMA are in flight;
+        // after the barrier every wave is done with this stage and it is refilled
+        a_wait_vm_lgkm<(AS - 2) * CPW>();
+        a_barrier();
+        issue(gbase, it + AS, stage);
+        stage = stage + 1 == AS ? 0 : stage + 1;
       }
     }
-  };
-  using MaskNone = std::integral_constant<int, 0>;
-  using MaskUpper = std::integral_constant<int, 1>;
-  using MaskRange = std::integral_constant<int, 2>;
-  using MaskSelf = std::integral_constant<int, 3>;
 
-  int stage = 0;
-  for (int it = 0; it < n_main; ++it) {
-    const char* st = lds + stage * A_STAGE;
-    const int ts = T0 + it * 64;
-    if (ts >= urow0 && ts + 64 <= kfull) {
-      tile_body(st, MaskNone{}, 0, nullptr, nullptr);
-    } else {
-      int lim[QB];
+    // A T row's only T key is itself ([explainer] §8.2 matrix; the user-to-item
+    // direction is never tiled): its score and value term in registers.  The
+    // lane holds half of the query's dims (kk*16 + 8hi + [0, 8)); the other half
+    // is in lane ^ 32.
+    if (any_self) {
+      const bf16* krow = (const bf16*)g.kd + (int64_t)(qrow0 + qr) * g.ldkd + grp * DH + 8 * hi;
+      float part = 0.f;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) lim[qb] = urow0 + plim[qb] - ts;
-      if (ts >= urow0) tile_body(st, MaskUpper{}, 0, lim, nullptr);   // only the prefix end cuts this tile
-      else tile_body(st, MaskRange{}, urow0 - ts, lim, nullptr);      // the user's first tile
-    }
-    if (it + 1 < n_main) {
-      // tile it + 1 has landed once at most AS - 2 newer tiles' DMA are in flight;
-      // after the barrier every wave is done with this stage and it is refilled
-      a_wait_vm_lgkm<(AS - 2) * DMA_PER_TILE>();
-      a_barrier();
-      issue(it + AS, stage);
-      stage = stage + 1 == AS ? 0 : stage + 1;
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 kv = *(const bf16x8*)(krow + kk * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf((float)qf[kk][e], (float)kv[e], part);
+      }
+      part += __shfl_xor(part, 32, 64);
+      const float ps = selfq ? (float)(bf16)silu_scaled(part) : 0.f;
+      const bf16* vrow = (const bf16*)g.vd + (int64_t)(qrow0 + qr) * g.ldvd + grp * DH + 4 * hi;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x4 vv = *(const bf16x4*)(vrow + mb * 32 + 8 * j);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) o[pp][mb][4 * j + t] = fmaf(ps, (float)vv[t], o[pp][mb][4 * j + t]);
+        }
     }
   }
-  if (has_diag) {
-    int dsel[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) dsel[qb] = selfq[qb] ? qb * 32 + l32 : -1;
-    tile_body(dlds, MaskSelf{}, 0, nullptr, dsel);
-  }
 
-  // output: lane = query, four consecutive dims per register group
-  bf16* out = (bf16*)g.a;
+  // A = O ln2 / n_i; wave w holds heads w + W pp
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qb * 32 + l32;
-    if (qi >= nrows) continue;
-    bf16* orow = out + (int64_t)(qrow0 + qi) * g.lda + h * DH + 4 * hi;
+  for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[pp][mb][i] *= rq;
+  if (g.a && ok) {
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp) {
+      bf16* orow = (bf16*)g.a + (int64_t)(qrow0 + l32) * g.lda + ((gsel + pp) * W + wave) * DH + 4 * hi;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = (bf16)o[pp][mb][4 * j + t];
+          *(bf16x4*)(orow + mb * 32 + 8 * j) = v;
+        }
+    }
+  }
+  if (!g.y) return;
+
+  // Fused epilogue ([blog] §6.1, the gated group LayerNorm after attention):
+  //   Y = (LayerNorm(A) * gamma[type] + beta[type]) (.) U
+  // over the row's H*dh values, fp32 two-pass statistics: per lane over its
+  // 32 P values, with lane ^ 32 (the other half of each head), then across the
+  // W waves through LDS (the ring is free once every wave is past its loop).
+  float* red = (float*)lds;
+  float s1 = 0.f;
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s1 += o[pp][mb][i];
+  s1 += __shfl_xor(s1, 32, 64);
+  a_wait_vm_lgkm<0>();
+  a_barrier();
+  if (hi == 0) red[wave * 32 + l32] = s1;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) tot += red[w * 32 + l32];
+  const float mean = tot / (float)hd;
+  float s2 = 0.f;
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float dv = o[pp][mb][i] - mean;
+        o[pp][mb][i] = dv;
+        s2 += dv * dv;
+      }
+  s2 += __shfl_xor(s2, 32, 64);
+  if (hi == 0) red[(W + wave) * 32 + l32] = s2;
+  __syncthreads();
+  float var = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) var += red[(W + w) * 32 + l32];
+  const float rstd = rsqrtf(var / (float)hd + g.eps);
+  if (!ok) return;
+  const int t = g.type[grow0 + qr];
+  const float* gam = g.ln_g + (int64_t)t * hd;
+  const float* bet = g.ln_b + (int64_t)t * hd;
+  const bool gb_vec = (((uintptr_t)g.ln_g | (uintptr_t)g.ln_b) & 15) == 0;   // 16-byte loads where aligned
+  const bf16* urow = (const bf16*)g.u + (int64_t)(qrow0 + l32) * g.ldu;
+  bf16* yrow = (bf16*)g.y + (int64_t)(qrow0 + l32) * g.ldy;
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const int d0 = (pp * W + wave) * DH + mb * 32 + 8 * j + 4 * hi;
+        float gm[4], bt[4];
+        if (gb_vec) {
+          const f32x4 g4 = *(const f32x4*)(gam + d0), b4 = *(const f32x4*)(bet + d0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { gm[q] = g4[q]; bt[q] = b4[q]; }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { gm[q] = gam[d0 + q]; bt[q] = bet[d0 + q]; }
+        }
+        const bf16x4 uu = *(const bf16x4*)(urow + d0);
         bf16x4 v;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = (bf16)(o[mb][qb][4 * j + t] * rq[qb]);
-        *(bf16x4*)(orow + mb * 32 + 8 * j) = v;
+        for (int q = 0; q < 4; ++q) v[q] = (bf16)((o[pp][mb][4 * j + q] * rstd * gm[q] + bt[q]) * (float)uu[q]);
+        *(bf16x4*)(yrow + d0) = v;
       }
-  }
 }
 
 // fp32 path: thread = (query row of the tile, head).
@@ -364,14 +429,53 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs g) {
   for (int c = 0; c < D; ++c) out[c] = acc[c] * sc;
 }
 
-template <int QB>
+template <int R, int GPP, int P>
+void launch_fused(const AttnArgs& a, hipStream_t s) {
+  const unsigned blocks = (unsigned)(a.ntiles * 2 * (a.per_group ? a.G : 1));
+  attn_bf16_kernel<R, GPP, P><<<blocks, 64 * R * GPP, 0, s>>>(a);
+}
+
+// Groups per ring stage GPP = min(G, 4, 16 / r) (at most 16 waves and a 64 KB
+// stage) and passes G / GPP, for H = r G query heads (H <= 16).
 mtfm_status launch_bf16(const AttnArgs& a, int r, hipStream_t s) {
-  const unsigned blocks = (unsigned)(a.ntiles * a.G * (2 / QB));
+  const int G = a.G;
+  if (a.per_group) {   // one group per workgroup: r waves, a single pass
+    switch (r) {
+      case 1: launch_fused<1, 1, 1>(a, s); break;
+      case 2: launch_fused<2, 1, 1>(a, s); break;
+      case 4: launch_fused<4, 1, 1>(a, s); break;
+      case 8: launch_fused<8, 1, 1>(a, s); break;
+      default: return MTFM_E_UNSUPPORTED;
+    }
+    return MTFM_OK;
+  }
   switch (r) {
-    case 1: attn_bf16_kernel<1, QB><<<blocks, 64, 0, s>>>(a); break;
-    case 2: attn_bf16_kernel<2, QB><<<blocks, 128, 0, s>>>(a); break;
-    case 4: attn_bf16_kernel<4, QB><<<blocks, 256, 0, s>>>(a); break;
-    case 8: attn_bf16_kernel<8, QB><<<blocks, 512, 0, s>>>(a); break;
+    case 1:
+      if (G == 1) launch_fused<1, 1, 1>(a, s);
+      else if (G == 2) launch_fused<1, 2, 1>(a, s);
+      else if (G == 4) launch_fused<1, 4, 1>(a, s);
+      else if (G == 8) launch_fused<1, 4, 2>(a, s);
+      else if (G == 16) launch_fused<1, 4, 4>(a, s);
+      else return MTFM_E_UNSUPPORTED;
+      break;
+    case 2:
+      if (G == 1) launch_fused<2, 1, 1>(a, s);
+      else if (G == 2) launch_fused<2, 2, 1>(a, s);
+      else if (G == 4) launch_fused<2, 4, 1>(a, s);
+      else if (G == 8) launch_fused<2, 4, 2>(a, s);
+      else return MTFM_E_UNSUPPORTED;
+      break;
+    case 4:
+      if (G == 1) launch_fused<4, 1, 1>(a, s);
+      else if (G == 2) launch_fused<4, 1, 2>(a, s);
+      else if (G == 4) launch_fused<4, 1, 4>(a, s);
+      else return MTFM_E_UNSUPPORTED;
+      break;
+    case 8:
+      if (G == 1) launch_fused<8, 1, 1>(a, s);
+      else if (G == 2) launch_fused<8, 2, 1>(a, s);
+      else return MTFM_E_UNSUPPORTED;
+      break;
     default: return MTFM_E_UNSUPPORTED;
   }
   return MTFM_OK;
@@ -389,7 +493,11 @@ mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
       return MTFM_E_UNSUPPORTED;
     // 32-bit buffer offsets: the whole V^T and one 64-row K tile
     if ((int64_t)a.G * 64 * a.ldvt * 2 >= (int64_t)1 << 32 || 64 * a.ldk * 2 >= (int64_t)1 << 31) return MTFM_E_UNSUPPORTED;
-    mtfm_status st = a.half_tiles ? launch_bf16<1>(a, r, s) : launch_bf16<2>(a, r, s);
+    if (a.per_group && a.y) return MTFM_E_UNSUPPORTED;   // the gated epilogue needs every head of a row
+    if (a.y && (!a.u || !a.ln_g || !a.ln_b || !a.type || a.ldy % 4 != 0 || a.ldu % 4 != 0 ||
+                ((uintptr_t)a.y & 7) || ((uintptr_t)a.u & 7)))
+      return MTFM_E_UNSUPPORTED;
+    mtfm_status st = launch_bf16(a, r, s);
     if (st != MTFM_OK) return st;
   } else {
     dim3 grid((unsigned)a.ntiles, (unsigned)a.H);

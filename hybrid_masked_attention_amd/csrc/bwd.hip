@@ -162,7 +162,7 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
       aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
       aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
       aa.a = a; aa.lda = hd;
-      aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles; aa.half_tiles = full_attn_half_tiles();
+      aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
       aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
       aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
       TRY(timed_attention(MTFM_K_ATTN_FULL, aa, MTFM_BF16, s));
@@ -315,7 +315,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
       aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
       aa.kd = zt + 2 * hd; aa.ldkd = zw; aa.vd = zt + 2 * hd + gd; aa.ldvd = zw;
       aa.a = a; aa.lda = hd;
-      aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles; aa.half_tiles = 1;
+      aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
       aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
       aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
       TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, MTFM_BF16, s));

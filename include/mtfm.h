@@ -228,9 +228,12 @@ size_t mtfm_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int3
 
 /* Byte offsets, inside the workspace, of the attention output A (before
  * GLN2, already divided by n) and of the gated Y = GLN2(A) (.) U left by the
- * last forward call: [n_rows][H*dh] for the full layer, [n_t_rows][H*dh] in
- * T-row order for the target layer, in dims->dtype.  Lets a caller check
- * the attention and gating branches separately.  Host only. */
+ * last mtfm_attn_full / mtfm_attn_target call: [n_rows][H*dh] for the full
+ * layer, [n_t_rows][H*dh] in T-row order for the target layer, in
+ * dims->dtype.  Lets a caller check the attention and gating branches
+ * separately.  (On the bf16 path the full layer's attention kernel applies
+ * the gated GLN2 itself and stores A only for these single-layer calls.)
+ * Host only. */
 mtfm_status mtfm_workspace_probe(const mtfm_batch* batch, const mtfm_dims* dims, int32_t op,
                                  int64_t* off_a, int64_t* off_y);
 

@@ -228,12 +228,3 @@ def test_small_v2_backbone_against_oracle():
     r.close("X'", got, ref)
     r.branch("dX (8 roundings allowed)", got, ref, xr, "bf16", roundings=8)
     r.check()
-
-
-@pytest.mark.parametrize("case", ["config1", "edge"])
-def test_full_layer_64_query_wave_shape(case, monkeypatch):
-    # The full-layer attention kernel has two workgroup shapes (32 or 64 query
-    # rows per wave, selected by MTFM_ATTN_FULL_QB); both must match the oracle.
-    monkeypatch.setenv("MTFM_ATTN_FULL_QB", "2")
-    wl = synth.config1() if case == "config1" else _small_workload(EDGE_LENS, 1, "bf16", 53)
-    _compare(wl, "full", _run_layer(wl, "full"), TOL_BF16)

@@ -192,8 +192,12 @@ def test_config3_v2_sampled_user():
     r.branch(f"user {u} context rows", got_u[c_u], ref[c_u], xin_u[c_u], "bf16", roundings=16)
     r.branch(f"user {u} T rows", got_u[t_u], ref[t_u], xin_u[t_u], "bf16", roundings=28)
     r.check()
-    # pooling at full size: every parent's pooled row is the mean of the device's own sub-token rows
-    # (fp32 sum, exact 1/4, one bf16 rounding: within half an ulp); the rows themselves are pinned above
-    ref_pool = ov.mean_pool(x1[tr_all], 4)
-    half = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref_pool), 1e-30))) - 8)
-    assert np.all(np.abs(pooled1 - ref_pool) <= half + 1e-30)
+    # pooling at full size: every parent's pooled row is the mean of the device's own sub-token rows:
+    # an fp32 sum of 4 terms (rounding error at most 3 * 2^-24 * sum|x|), an exact 1/4, one bf16
+    # rounding (half an ulp of the result); the rows themselves are pinned above
+    subs = x1[tr_all].reshape(-1, 4, x1.shape[1])
+    ref_pool = subs.mean(axis=1)
+    big = np.maximum(np.abs(ref_pool), np.abs(pooled1))
+    half = np.exp2(np.floor(np.log2(np.maximum(big, 1e-30))) - 8)
+    fp32_sum = 3 * 2.0 ** -24 * np.abs(subs).sum(axis=1) / 4
+    assert np.all(np.abs(pooled1 - ref_pool) <= half + fp32_sum + 1e-30)
