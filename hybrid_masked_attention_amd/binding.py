@@ -15,7 +15,9 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmtfm.so")
+# MTFM_LIB selects another build of the library (the host-sanitizer build of
+# the argument-checking tests); the default is the in-tree libmtfm.so.
+LIB_PATH = os.environ.get("MTFM_LIB") or os.path.join(_HERE, "libmtfm.so")
 
 OK, E_NULL, E_DIMS, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1

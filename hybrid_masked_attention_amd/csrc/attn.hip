@@ -110,6 +110,10 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
   const int grow0 = td[TD_GROW0] + qoff, qrow0 = td[TD_QROW0] + qoff, urow0 = td[TD_UROW0];
   const int lctx = g.lens[3 * u] + g.lens[3 * u + 1];
   const bool any_self = row0 + qoff + nrows > lctx;   // some row of the slice is a T row (sees itself)
+  MTFM_DCHECK_UNIFORM(tile_rows <= 64 && row0 % 64 == 0 && u >= 0 && urow0 >= 0, "attention tile descriptor");
+  MTFM_DCHECK_UNIFORM(urow0 + lctx <= g.n_key_rows, "attention keys within the key rows");
+  MTFM_DCHECK_UNIFORM(td[TD_FULL_END] <= td[TD_END] && 64 * (td[TD_END] - 1) < max(lctx, 1),
+                      "attention key-tile bounds within the user's context");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

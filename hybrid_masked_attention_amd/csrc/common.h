@@ -15,6 +15,31 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 #define MTFM_DEV __device__ __forceinline__
 
+// Debug builds (MTFM_DEBUG, build.py --debug) check the indexing assumptions
+// of the kernels.  MTFM_DCHECK_UNIFORM is for conditions every thread of the
+// workgroup evaluates alike (read from a tile descriptor, say): a violation is
+// reported and the whole workgroup leaves before any barrier, reading nothing
+// out of bounds.  MTFM_DCHECK_LANE only reports (the caller keeps the access
+// in bounds).  Release builds compile both away.
+#ifdef MTFM_DEBUG
+#define MTFM_DCHECK_UNIFORM(cond, what)                                                     \
+  do {                                                                                      \
+    if (!(cond)) {                                                                          \
+      if (threadIdx.x == 0) printf("mtfm debug: %s failed (%s:%d, block %u)\n", what, __FILE__, __LINE__, \
+                                   blockIdx.x);                                             \
+      return;                                                                               \
+    }                                                                                       \
+  } while (0)
+#define MTFM_DCHECK_LANE(cond, what)                                                        \
+  do {                                                                                      \
+    if (!(cond)) printf("mtfm debug: %s failed (%s:%d, block %u thread %u)\n", what, __FILE__, __LINE__, \
+                        blockIdx.x, threadIdx.x);                                           \
+  } while (0)
+#else
+#define MTFM_DCHECK_UNIFORM(cond, what) do {} while (0)
+#define MTFM_DCHECK_LANE(cond, what) do {} while (0)
+#endif
+
 // Tile edge of the mask metadata and of the attention kernels.
 static constexpr int kTile = MTFM_TILE;
 

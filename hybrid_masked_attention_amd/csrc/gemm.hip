@@ -242,6 +242,7 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
     const uint32_t cb = (uint32_t)((slot ^ g_swz(r)) * 16);
     if (amap.list) {
       ra[i] = make_rsrc(g.A, (uint32_t)(g.a_rows * g.lda * 2));
+      MTFM_DCHECK_LANE(m >= g.M || (map_row(amap, m) >= 0 && map_row(amap, m) < g.a_rows), "GEMM gathered row");
       aoff[i] = m < g.M ? (uint32_t)(map_row(amap, m) * g.lda * 2) + cb : kOobOffset;
     } else {
       const int valid = min(max(g.M - (m0 + rs), 0), G_RPC);
