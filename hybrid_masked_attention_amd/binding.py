@@ -88,7 +88,8 @@ class CMetaLayout(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in (
         "n_rows", "n_t_rows", "n_parents", "n_ctx_rows", "n_full_tiles", "n_target_tiles", "n_key_tiles",
         "off_user", "off_p",
-        "off_n", "off_type", "off_full_tiles", "off_target_tiles", "off_ctx_rows", "off_parent_row", "total_bytes")]
+        "off_n", "off_type", "off_full_tiles", "off_target_tiles", "off_ctx_rows", "off_parent_row",
+        "n_full_order", "n_target_order", "off_full_order", "off_target_order", "total_bytes")]
 
 
 _lib = None
@@ -290,6 +291,8 @@ def meta_views(meta, layout: CMetaLayout, n_users: int) -> Dict[str, "object"]:
         "target_tiles": view(L.off_target_tiles, L.n_target_tiles * 8, torch.int32, (L.n_target_tiles, 8)),
         "ctx_rows": view(L.off_ctx_rows, L.n_ctx_rows, torch.int32),
         "parent_row": view(L.off_parent_row, L.n_parents, torch.int32),
+        "full_order": view(L.off_full_order, L.n_full_order, torch.int32),
+        "target_order": view(L.off_target_order, L.n_target_order, torch.int32),
     }
 
 

@@ -10,6 +10,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <string>
+#include <vector>
 
 #include "api_internal.h"
 #include "v2.h"
@@ -27,6 +28,23 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------------------
 // Metadata plan: totals from the host lengths, array offsets in the buffer.
+
+// Entries of a layer's attention work order: 8 x the longest XCD list, from
+// the same ranking and dealing the device performs (users by estimated work,
+// descending, ties by index; rank r goes to XCD order_xcd(r)).
+static int64_t order_entries(const int32_t* lens, int n_users, int split, int layer) {
+  if (n_users <= 0 || n_users > kOrderMaxUsers) return 0;
+  std::vector<int64_t> work(n_users);
+  std::vector<int32_t> idx(n_users);
+  for (int u = 0; u < n_users; ++u) {
+    work[u] = order_user_work(lens, u, split, layer);
+    idx[u] = u;
+  }
+  std::sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return work[a] != work[b] ? work[a] > work[b] : a < b; });
+  int64_t count[8] = {};
+  for (int r = 0; r < n_users; ++r) count[order_xcd(r)] += order_slices(lens, idx[r], split, layer);
+  return 8 * *std::max_element(count, count + 8);
+}
 mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan) {
   if (!b || !plan) return MTFM_E_NULL;
   if (b->n_users < 0) return MTFM_E_DIMS;
@@ -50,6 +68,8 @@ mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan) {
     p.max_t_rows = (int32_t)std::min<int64_t>(std::max<int64_t>(p.max_t_rows, b->split * lt), INT32_MAX);
     if (p.n_rows > INT32_MAX - 4096) return MTFM_E_DIMS;
   }
+  p.n_full_order = order_entries(b->lens_h, b->n_users, b->split, OL_FULL);
+  p.n_target_order = order_entries(b->lens_h, b->n_users, b->split, OL_TARGET);
   mtfm_meta_layout& l = p.lay;
   l.n_rows = p.n_rows; l.n_t_rows = p.n_t_rows; l.n_parents = p.n_parents; l.n_ctx_rows = p.n_ctx_rows;
   l.n_full_tiles = p.n_full_tiles; l.n_target_tiles = p.n_target_tiles; l.n_key_tiles = p.n_key_tiles;
@@ -63,6 +83,9 @@ mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan) {
   l.off_target_tiles = take(p.n_target_tiles * 32);
   l.off_ctx_rows = take(p.n_ctx_rows * 4);
   l.off_parent_row = take(p.n_parents * 4);
+  l.n_full_order = p.n_full_order; l.n_target_order = p.n_target_order;
+  l.off_full_order = take(p.n_full_order * 4);
+  l.off_target_order = take(p.n_target_order * 4);
   l.total_bytes = off;
   *plan = p;
   return MTFM_OK;
@@ -79,6 +102,8 @@ MetaPtrs meta_ptrs(const MetaPlan& plan, const void* meta_d) {
   m.target_tiles = reinterpret_cast<const int32_t*>(base + plan.lay.off_target_tiles);
   m.ctx_rows = reinterpret_cast<const int32_t*>(base + plan.lay.off_ctx_rows);
   m.parent_row = reinterpret_cast<const int32_t*>(base + plan.lay.off_parent_row);
+  m.full_order = plan.n_full_order ? reinterpret_cast<const int32_t*>(base + plan.lay.off_full_order) : nullptr;
+  m.target_order = plan.n_target_order ? reinterpret_cast<const int32_t*>(base + plan.lay.off_target_order) : nullptr;
   return m;
 }
 
@@ -295,6 +320,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   }
   aa.a = a; aa.lda = hd;
   aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
+  aa.order = c.meta.full_order; aa.n_order = (int32_t)p.n_full_order;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   if (dt == MTFM_BF16) fuse_gated_gln(aa, c, d, w->ln2_g, w->ln2_b, z, zw, y, hd, keep ? keep->a : nullptr);
@@ -398,6 +424,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
   aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
+  aa.order = c.meta.target_order; aa.n_order = (int32_t)p.n_target_order;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   aa.per_group = 1;
@@ -507,6 +534,7 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
   aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
+  aa.order = c.meta.target_order; aa.n_order = (int32_t)p.n_target_order;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   aa.per_group = 1;
@@ -726,6 +754,7 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
   aa.tiles = tiles; aa.ntiles = (int32_t)p.n_target_tiles;
+  aa.order = c.meta.target_order; aa.n_order = (int32_t)p.n_target_order;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   aa.per_group = 1;

@@ -29,6 +29,10 @@ struct AttnArgs {
   const void* vd; int64_t ldvd;
   void* a; int64_t lda;          // output [query row][H*dh]; optional on the bf16 path (nullptr: not written)
   const int32_t* tiles; int32_t ntiles;
+  // bf16 path, optional work order (mask metadata): entry 8 k + x is the
+  // slice id 2 tile + half that XCD x takes k-th, -1 past its list; the grid is
+  // n_order (x G with per_group) workgroups.  nullptr: XCD-contiguous order.
+  const int32_t* order; int32_t n_order;
   const int32_t* p; const int32_t* n;  // per packed row
   const int32_t* lens;
   int32_t H, G, dh;

@@ -96,12 +96,23 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
   __shared__ __attribute__((aligned(1024))) char lds[AS * STAGE];
 
   // logical block: (query tile, 32-row half[, KV group]); with per_group the
-  // workgroup takes one group's heads (the grid has G times the blocks)
+  // workgroup takes one group's heads (the grid has G times the blocks).  With
+  // a work order, workgroup b runs on XCD b % 8 and takes the (b / 8)-th item
+  // of that XCD's list (the G groups of a slice one after another).
   const int ngrp = g.per_group ? g.G : 1;
-  const int nblocks = g.ntiles * 2 * ngrp;
-  const int lb = xcd_remap(blockIdx.x, nblocks);
-  const int gsel = lb % ngrp, sid = lb / ngrp;
+  int gsel, sid;
+  if (g.order) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    sid = g.order[8 * (k / ngrp) + x];
+    if (sid < 0) return;                       // past the end of this XCD's list (whole workgroup)
+    gsel = k % ngrp;
+  } else {
+    const int lb = xcd_remap(blockIdx.x, g.ntiles * 2 * ngrp);
+    gsel = lb % ngrp;
+    sid = lb / ngrp;
+  }
   const int slice = sid & 1, tile = sid >> 1;
+  MTFM_DCHECK_UNIFORM(tile < g.ntiles, "attention work-order entry");
   const int32_t* td = g.tiles + 8 * tile;
   const int u = td[TD_USER], row0 = td[TD_ROW0], tile_rows = td[TD_NROWS];
   const int qoff = slice * 32;
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs g) {
 
 template <int R, int GPP, int P>
 void launch_fused(const AttnArgs& a, hipStream_t s) {
-  const unsigned blocks = (unsigned)(a.ntiles * 2 * (a.per_group ? a.G : 1));
+  const unsigned blocks = (unsigned)((a.order ? (int64_t)a.n_order : 2 * (int64_t)a.ntiles) * (a.per_group ? a.G : 1));
   attn_bf16_kernel<R, GPP, P><<<blocks, 64 * R * GPP, 0, s>>>(a);
 }
 
@@ -498,6 +509,7 @@ mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
     // 32-bit buffer offsets: the whole V^T and one 64-row K tile
     if ((int64_t)a.G * 64 * a.ldvt * 2 >= (int64_t)1 << 32 || 64 * a.ldk * 2 >= (int64_t)1 << 31) return MTFM_E_UNSUPPORTED;
     if (a.per_group && a.y) return MTFM_E_UNSUPPORTED;   // the gated epilogue needs every head of a row
+    if (a.order && (a.n_order <= 0 || a.n_order % 8 != 0)) return MTFM_E_UNSUPPORTED;
     if (a.y && (!a.u || !a.ln_g || !a.ln_b || !a.type || a.ldy % 4 != 0 || a.ldu % 4 != 0 ||
                 ((uintptr_t)a.y & 7) || ((uintptr_t)a.u & 7)))
       return MTFM_E_UNSUPPORTED;

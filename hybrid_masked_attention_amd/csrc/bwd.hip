@@ -163,6 +163,7 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
       aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
       aa.a = a; aa.lda = hd;
       aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
+      aa.order = c.meta.full_order; aa.n_order = (int32_t)p.n_full_order;
       aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
       aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
       TRY(timed_attention(MTFM_K_ATTN_FULL, aa, MTFM_BF16, s));
@@ -316,6 +317,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
       aa.kd = zt + 2 * hd; aa.ldkd = zw; aa.vd = zt + 2 * hd + gd; aa.ldvd = zw;
       aa.a = a; aa.lda = hd;
       aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
+      aa.order = c.meta.target_order; aa.n_order = (int32_t)p.n_target_order;
       aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
       aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
       TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, MTFM_BF16, s));

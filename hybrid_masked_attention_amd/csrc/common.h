@@ -107,12 +107,57 @@ MTFM_DEV int upper_index(const int32_t* off, int n, int x) {
 }
 
 // ---------------------------------------------------------------------------
+// Attention work order.  The bf16 attention grids take their 32-row query
+// slices in an order that balances the 8 XCDs (each with its own L2; the
+// hardware deals consecutive workgroup ids to them round-robin): users ranked
+// by estimated work, largest first (ties: lower index first), dealt to the
+// XCDs in a boustrophedon 0..7, 7..0, 0..7 ..., each XCD taking its users in
+// rank order and a user's slices last first (the later rows see the most
+// keys).  A user's slices stay on one XCD, so its K / V tiles are fetched into
+// one L2.  The estimate depends on the lengths alone: the host sizes the grid
+// with the same integer arithmetic the device uses to write the order.
+#define MTFM_HD __host__ __device__ __forceinline__
+
+constexpr int kOrderMaxUsers = 2048;   // larger batches keep the plain XCD-contiguous order
+enum OrderLayer { OL_FULL = 0, OL_TARGET = 1 };
+
+// 32-row query slices of user u: every packed row (full layer) or its T rows.
+MTFM_HD int32_t order_slices(const int32_t* lens, int u, int split, int layer) {
+  const int32_t lt = split * lens[3 * u + 2];
+  const int32_t rows = layer == OL_FULL ? lens[3 * u] + lens[3 * u + 1] + lt : lt;
+  return (rows + 31) / 32;
+}
+
+// Work of slice k of user u: key tiles it can visit (a bound from the lengths:
+// an H row sees L_H keys, R row j L_H + j + 1, a T row at most L_H + L_R),
+// plus one for the slice's fixed cost.
+MTFM_HD int32_t order_slice_work(const int32_t* lens, int u, int split, int layer, int k) {
+  const int32_t lh = lens[3 * u], ctx = lh + lens[3 * u + 1];
+  if (layer == OL_TARGET) return (ctx + 63) / 64 + 1;
+  const int32_t rows = ctx + split * lens[3 * u + 2];
+  const int32_t last = (32 * k + 32 < rows ? 32 * k + 32 : rows) - 1;
+  const int32_t p = last < lh ? lh : (last < ctx ? last + 1 : ctx);
+  return (p + 63) / 64 + 1;
+}
+
+MTFM_HD int64_t order_user_work(const int32_t* lens, int u, int split, int layer) {
+  const int32_t ns = order_slices(lens, u, split, layer);
+  int64_t w = 0;
+  for (int k = 0; k < ns; ++k) w += order_slice_work(lens, u, split, layer, k);
+  return w;
+}
+
+// XCD of the user of rank r (boustrophedon over groups of 8 ranks).
+MTFM_HD int order_xcd(int r) { return ((r >> 3) & 1) ? 7 - (r & 7) : (r & 7); }
+
+// ---------------------------------------------------------------------------
 // Host-side plan of a batch: totals and device pointers into the metadata.
 struct MetaPlan {
   int32_t n_users = 0, split = 1;
   int64_t n_rows = 0, n_t_rows = 0, n_parents = 0, n_ctx_rows = 0;
   int64_t n_full_tiles = 0, n_target_tiles = 0, n_key_tiles = 0;
   int32_t max_user_rows = 0, max_t_rows = 0;
+  int64_t n_full_order = 0, n_target_order = 0;   // work-order entries (8 x longest XCD list; 0 = none)
   mtfm_meta_layout lay{};
 };
 
@@ -125,6 +170,8 @@ struct MetaPtrs {
   const int32_t* target_tiles;
   const int32_t* ctx_rows;
   const int32_t* parent_row;
+  const int32_t* full_order;     // nullptr when the batch has no work order
+  const int32_t* target_order;
 };
 
 mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan);

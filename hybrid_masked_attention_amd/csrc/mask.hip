@@ -180,6 +180,57 @@ __global__ __launch_bounds__(64) void target_tiles_kernel(const int32_t* __restr
   }
 }
 
+// One workgroup: the attention work order of both layers (ranking, dealing
+// to the XCDs and the per-XCD lists as described with order_xcd).  Users are
+// ranked by counting, O(n^2) over at most kOrderMaxUsers users in LDS.
+// Every entry of an order array is written once: a slice id or, past the end
+// of its XCD's list, -1.
+__global__ __launch_bounds__(kScanThreads) void work_order_kernel(const int32_t* __restrict__ lens, int n_users,
+                                                                  int split, const int32_t* __restrict__ table,
+                                                                  int32_t* __restrict__ order_full, int n_full,
+                                                                  int32_t* __restrict__ order_target, int n_target) {
+  __shared__ int64_t work[kOrderMaxUsers];
+  __shared__ int32_t rank[kOrderMaxUsers];
+  __shared__ int32_t nsl[kOrderMaxUsers];
+  __shared__ int32_t count[8];
+  const int t = threadIdx.x, n = n_users, stride = n_users + 1;
+  for (int layer = OL_FULL; layer <= OL_TARGET; ++layer) {
+    int32_t* order = layer == OL_FULL ? order_full : order_target;
+    const int len = layer == OL_FULL ? n_full : n_target;
+    if (len == 0) continue;
+    for (int u = t; u < n; u += kScanThreads) {
+      work[u] = order_user_work(lens, u, split, layer);
+      nsl[u] = order_slices(lens, u, split, layer);
+    }
+    if (t < 8) count[t] = 0;
+    __syncthreads();
+    for (int u = t; u < n; u += kScanThreads) {
+      const int64_t wu = work[u];
+      int r = 0;
+      for (int v = 0; v < n; ++v) r += (work[v] > wu) || (work[v] == wu && v < u);
+      rank[u] = r;
+    }
+    __syncthreads();
+    const int32_t* first_tile = table + (layer == OL_FULL ? UT_FTILE : UT_TTILE) * stride;
+    for (int u = t; u < n; u += kScanThreads) {
+      const int ru = rank[u], x = order_xcd(ru);
+      int off = 0;   // slices of the users dealt to XCD x ahead of u
+      for (int v = 0; v < n; ++v) off += (order_xcd(rank[v]) == x && rank[v] < ru) ? nsl[v] : 0;
+      const int ns = nsl[u], sid0 = 2 * first_tile[u];
+      for (int k = 0; k < ns; ++k) {
+        const int e = 8 * (off + k) + x;
+        MTFM_DCHECK_LANE(e < len, "work order entry within the planned length");
+        if (e < len) order[e] = sid0 + ns - 1 - k;
+      }
+      atomicAdd(&count[x], ns);
+    }
+    __syncthreads();
+    for (int e = t; e < len; e += kScanThreads)
+      if ((e >> 3) >= count[e & 7]) order[e] = -1;
+    __syncthreads();   // LDS is reused by the next layer
+  }
+}
+
 }  // namespace
 
 mtfm_status launch_mask_build(const mtfm_batch* b, const MetaPlan& plan, void* meta_d, hipStream_t s) {
@@ -199,6 +250,13 @@ mtfm_status launch_mask_build(const mtfm_batch* b, const MetaPlan& plan, void* m
     rows_full_tiles_kernel<<<(unsigned)plan.n_full_tiles, 64, 0, s>>>(b->lens_d, plan.n_users, plan.split, b->ts_r_d,
                                                                       b->ts_t_d, table, p, n, type, ft, ctx, par);
     MTFM_LAUNCH_CHECK("rows_full_tiles_kernel");
+  }
+  if (plan.n_full_order > 0 || plan.n_target_order > 0) {
+    work_order_kernel<<<1, kScanThreads, 0, s>>>(
+        b->lens_d, plan.n_users, plan.split, table, reinterpret_cast<int32_t*>(base + plan.lay.off_full_order),
+        (int)plan.n_full_order, reinterpret_cast<int32_t*>(base + plan.lay.off_target_order),
+        (int)plan.n_target_order);
+    MTFM_LAUNCH_CHECK("work_order_kernel");
   }
   if (plan.n_target_tiles > 0) {
     target_tiles_kernel<<<(unsigned)plan.n_target_tiles, 64, 0, s>>>(b->lens_d, plan.n_users, plan.split, table, p, tt);

@@ -152,6 +152,10 @@ typedef struct {
   int64_t off_target_tiles;  /* int32 [n_target_tiles][8] */
   int64_t off_ctx_rows;      /* int32 [n_ctx_rows] packed row of each H/R row, users in order */
   int64_t off_parent_row;    /* int32 [n_parents] packed row of each parent's first T row */
+  int64_t n_full_order;      /* work-order entries of the full / target layer's attention grid */
+  int64_t n_target_order;    /*   (0 for batches over 2048 users: plain order) */
+  int64_t off_full_order;    /* int32 [n_full_order]: entry 8 k + x = 2 tile + half of the k-th */
+  int64_t off_target_order;  /*   32-row query slice XCD x takes, -1 past the end of its list */
   int64_t total_bytes;
 } mtfm_meta_layout;
 /* Tile descriptor, int32 x 8:

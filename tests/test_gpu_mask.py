@@ -10,6 +10,7 @@ import pytest
 
 import synth
 from oracle import mask as omask
+from tests import _order
 from tests._parity import say
 
 pytestmark = pytest.mark.gpu
@@ -31,6 +32,9 @@ def _check(batch, users=None, fast=True):
     v = _device_meta(batch)
     off = batch.row_off
     sel = list(range(batch.n_users)) if users is None else list(users)
+    # attention work order: the rule rebuilt in Python (scheduling only; bit-exact)
+    np.testing.assert_array_equal(v["full_order"], _order.expected_order(batch.lens, batch.split, _order.FULL))
+    np.testing.assert_array_equal(v["target_order"], _order.expected_order(batch.lens, batch.split, _order.TARGET))
     for u in sel:
         ref = omask.batch_meta(batch.user(u), 64, 64, fast=fast)
         r0, r1 = off[u], off[u + 1]
