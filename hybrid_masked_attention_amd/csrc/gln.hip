@@ -1,4 +1,4 @@
-// Group LayerNorm kernels: one wave per row, the row held in registers
+// Group LayerNorm kernels: one wave per few rows, each row held in registers
 // (D / 64 contiguous values per lane, moved as 16-byte vectors), two-pass
 // mean and variance in fp32, type-indexed affine, optional multiplicative
 // gate, optional gathered input rows, and up to four outputs of the same
@@ -51,65 +51,94 @@ MTFM_DEV void store_row(T* p, const float* v) {
   }
 }
 
-template <typename T, int VPL, int NOUT>
+// One wave per RPW consecutive rows: every row's loads are issued before any
+// reduction, so a wave keeps RPW x 64 x 16 bytes in flight (the kernel streams
+// HBM; one row per wave left it latency-bound).
+template <typename T, int VPL, int NOUT, int RPW, bool GATE>
 __global__ __launch_bounds__(256) void gln_kernel(GlnArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
   const int lane = threadIdx.x & 63;
-  if (row >= a.rows) return;
-  const int64_t xrow = a.xlist ? (int64_t)a.xlist[row / a.xdiv] + row % a.xdiv : row;
-  float v[VPL];
-  load_row<T, VPL>((const T*)a.x + xrow * a.ldx + lane * VPL, v);
-  float s = 0.f;
+  if (row0 >= a.rows) return;
+  int64_t xrow[RPW];
+  bool ok[RPW];
+  float v[RPW][VPL], g[GATE ? RPW : 1][VPL];
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) s += v[j];
-  const float mean = wave_sum(s) / (float)a.D;
-  float q = 0.f;
+  for (int r = 0; r < RPW; ++r) {
+    const int row = row0 + r;
+    ok[r] = row < a.rows;
+    const int rr = ok[r] ? row : row0;   // a row past the end re-reads the first (never stored)
+    xrow[r] = a.xlist ? (int64_t)a.xlist[rr / a.xdiv] + rr % a.xdiv : rr;
+    load_row<T, VPL>((const T*)a.x + xrow[r] * a.ldx + lane * VPL, v[r]);
+    if constexpr (GATE) load_row<T, VPL>((const T*)a.gate + (int64_t)rr * a.ldg + lane * VPL, g[r]);
+  }
+  float mean[RPW], rstd[RPW];
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) { v[j] -= mean; q += v[j] * v[j]; }
-  const float rstd = rsqrtf(wave_sum(q) / (float)a.D + a.eps);
-  const int t = a.type ? a.type[xrow] : a.type_const;
-  const bool zero = a.zero_t && t == TT_T;
-  float g[VPL];
-  if (a.gate) load_row<T, VPL>((const T*)a.gate + (int64_t)row * a.ldg + lane * VPL, g);
+  for (int r = 0; r < RPW; ++r) {
+    float s = 0.f;
 #pragma unroll
-  for (int o = 0; o < NOUT; ++o) {
-    const float* gamma = o ? a.gamma_more[o - 1] : a.gamma;
-    const float* beta = o ? a.beta_more[o - 1] : a.beta;
-    T* y = (T*)(o ? a.y_more[o - 1] : a.y);
-    float gm[VPL], bt[VPL], w[VPL];
-    load_row<float, VPL>(gamma + t * a.D + lane * VPL, gm);
-    load_row<float, VPL>(beta + t * a.D + lane * VPL, bt);
+    for (int j = 0; j < VPL; ++j) s += v[r][j];
+    mean[r] = s;
+  }
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      w[j] = zero ? 0.f : v[j] * rstd * gm[j] + bt[j];
-      if (a.gate) w[j] *= g[j];
+  for (int r = 0; r < RPW; ++r) mean[r] = wave_sum(mean[r]) / (float)a.D;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) { v[r][j] -= mean[r]; q += v[r][j] * v[r][j]; }
+    rstd[r] = q;
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) rstd[r] = rsqrtf(wave_sum(rstd[r]) / (float)a.D + a.eps);
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    if (!ok[r]) continue;
+    const int t = a.type ? a.type[xrow[r]] : a.type_const;
+    const bool zero = a.zero_t && t == TT_T;
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) {
+      const float* gamma = o ? a.gamma_more[o - 1] : a.gamma;
+      const float* beta = o ? a.beta_more[o - 1] : a.beta;
+      T* y = (T*)(o ? a.y_more[o - 1] : a.y);
+      float gm[VPL], bt[VPL], w[VPL];
+      load_row<float, VPL>(gamma + t * a.D + lane * VPL, gm);
+      load_row<float, VPL>(beta + t * a.D + lane * VPL, bt);
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        w[j] = zero ? 0.f : v[r][j] * rstd[r] * gm[j] + bt[j];
+        if constexpr (GATE) w[j] *= g[r][j];
+      }
+      store_row<T, VPL>(y + (int64_t)(row0 + r) * a.ldy + lane * VPL, w);
     }
-    store_row<T, VPL>(y + (int64_t)row * a.ldy + lane * VPL, w);
   }
 }
 
-template <typename T, int NOUT>
+template <typename T, int NOUT, bool GATE>
 mtfm_status launch_n(const GlnArgs& a, hipStream_t s) {
-  const unsigned blocks = (unsigned)((a.rows + 3) / 4);
+  constexpr int RPW = 4;
+  const unsigned blocks = (unsigned)((a.rows + 4 * RPW - 1) / (4 * RPW));
   switch (a.D / 64) {
-    case 1: gln_kernel<T, 1, NOUT><<<blocks, 256, 0, s>>>(a); break;
-    case 2: gln_kernel<T, 2, NOUT><<<blocks, 256, 0, s>>>(a); break;
-    case 4: gln_kernel<T, 4, NOUT><<<blocks, 256, 0, s>>>(a); break;
-    case 8: gln_kernel<T, 8, NOUT><<<blocks, 256, 0, s>>>(a); break;
-    case 16: gln_kernel<T, 16, NOUT><<<blocks, 256, 0, s>>>(a); break;
+    case 1: gln_kernel<T, 1, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
+    case 2: gln_kernel<T, 2, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
+    case 4: gln_kernel<T, 4, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
+    case 8: gln_kernel<T, 8, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
+    case 16: gln_kernel<T, 16, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
     default: return MTFM_E_UNSUPPORTED;
   }
   MTFM_LAUNCH_CHECK("gln");
   return MTFM_OK;
 }
 
+// The gate goes with a single output (the gated LayerNorm after attention);
+// several outputs only for the ungated context normalisation.
 template <typename T>
 mtfm_status launch_t(const GlnArgs& a, hipStream_t s) {
+  if (a.gate) return a.n_more == 0 ? launch_n<T, 1, true>(a, s) : MTFM_E_UNSUPPORTED;
   switch (a.n_more) {
-    case 0: return launch_n<T, 1>(a, s);
-    case 1: return launch_n<T, 2>(a, s);
-    case 2: return launch_n<T, 3>(a, s);
-    case 3: return launch_n<T, 4>(a, s);
+    case 0: return launch_n<T, 1, false>(a, s);
+    case 1: return launch_n<T, 2, false>(a, s);
+    case 2: return launch_n<T, 3, false>(a, s);
+    case 3: return launch_n<T, 4, false>(a, s);
     default: return MTFM_E_UNSUPPORTED;
   }
 }

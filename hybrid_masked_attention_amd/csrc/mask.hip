@@ -182,7 +182,8 @@ __global__ __launch_bounds__(64) void target_tiles_kernel(const int32_t* __restr
 
 // One workgroup: the attention work order of both layers (ranking, dealing
 // to the XCDs and the per-XCD lists as described with order_xcd).  Users are
-// ranked by counting, O(n^2) over at most kOrderMaxUsers users in LDS.
+// ranked by counting, O(n^2) over at most kOrderMaxUsers users in LDS, with
+// the workgroup's threads split over (user, share of the other users) pairs.
 // Every entry of an order array is written once: a slice id or, past the end
 // of its XCD's list, -1.
 __global__ __launch_bounds__(kScanThreads) void work_order_kernel(const int32_t* __restrict__ lens, int n_users,
@@ -191,9 +192,11 @@ __global__ __launch_bounds__(kScanThreads) void work_order_kernel(const int32_t*
                                                                   int32_t* __restrict__ order_target, int n_target) {
   __shared__ int64_t work[kOrderMaxUsers];
   __shared__ int32_t rank[kOrderMaxUsers];
+  __shared__ int32_t off[kOrderMaxUsers];
   __shared__ int32_t nsl[kOrderMaxUsers];
   __shared__ int32_t count[8];
   const int t = threadIdx.x, n = n_users, stride = n_users + 1;
+  const int P = n > 0 && n < kScanThreads ? kScanThreads / n : 1;   // threads per user
   for (int layer = OL_FULL; layer <= OL_TARGET; ++layer) {
     int32_t* order = layer == OL_FULL ? order_full : order_target;
     const int len = layer == OL_FULL ? n_full : n_target;
@@ -201,30 +204,38 @@ __global__ __launch_bounds__(kScanThreads) void work_order_kernel(const int32_t*
     for (int u = t; u < n; u += kScanThreads) {
       work[u] = order_user_work(lens, u, split, layer);
       nsl[u] = order_slices(lens, u, split, layer);
+      rank[u] = 0;
+      off[u] = 0;
     }
     if (t < 8) count[t] = 0;
     __syncthreads();
-    for (int u = t; u < n; u += kScanThreads) {
+    for (int i = t; i < n * P; i += kScanThreads) {
+      const int u = i / P, j = i % P;
       const int64_t wu = work[u];
       int r = 0;
-      for (int v = 0; v < n; ++v) r += (work[v] > wu) || (work[v] == wu && v < u);
-      rank[u] = r;
+      for (int v = j; v < n; v += P) r += (work[v] > wu) || (work[v] == wu && v < u);
+      atomicAdd(&rank[u], r);
+    }
+    __syncthreads();
+    for (int i = t; i < n * P; i += kScanThreads) {
+      const int u = i / P, j = i % P;
+      const int ru = rank[u], x = order_xcd(ru);
+      int o = 0;   // slices of the users dealt to XCD x ahead of u
+      for (int v = j; v < n; v += P) o += (order_xcd(rank[v]) == x && rank[v] < ru) ? nsl[v] : 0;
+      atomicAdd(&off[u], o);
+      if (j == 0) atomicAdd(&count[x], nsl[u]);
     }
     __syncthreads();
     const int32_t* first_tile = table + (layer == OL_FULL ? UT_FTILE : UT_TTILE) * stride;
-    for (int u = t; u < n; u += kScanThreads) {
-      const int ru = rank[u], x = order_xcd(ru);
-      int off = 0;   // slices of the users dealt to XCD x ahead of u
-      for (int v = 0; v < n; ++v) off += (order_xcd(rank[v]) == x && rank[v] < ru) ? nsl[v] : 0;
-      const int ns = nsl[u], sid0 = 2 * first_tile[u];
-      for (int k = 0; k < ns; ++k) {
-        const int e = 8 * (off + k) + x;
+    for (int i = t; i < n * P; i += kScanThreads) {
+      const int u = i / P, j = i % P;
+      const int x = order_xcd(rank[u]), ns = nsl[u], o = off[u], sid0 = 2 * first_tile[u];
+      for (int k = j; k < ns; k += P) {
+        const int e = 8 * (o + k) + x;
         MTFM_DCHECK_LANE(e < len, "work order entry within the planned length");
         if (e < len) order[e] = sid0 + ns - 1 - k;
       }
-      atomicAdd(&count[x], ns);
     }
-    __syncthreads();
     for (int e = t; e < len; e += kScanThreads)
       if ((e >> 3) >= count[e & 7]) order[e] = -1;
     __syncthreads();   // LDS is reused by the next layer
