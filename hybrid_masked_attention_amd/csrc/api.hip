@@ -298,6 +298,14 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   gp.cend[3] = zw;
   if (dt == MTFM_BF16) { gp.vt = ws + L.vt; gp.ldvt = L.ldvt; gp.vt_col0 = 2 * hd + gd; gp.vt_cols = gd; }
   if (keep) { gp.pre = keep->hpre; gp.ldpre = zw; }
+  if (dt == MTFM_BF16 && !keep) {
+    // the attention reads K row-major for every key row but V row-major only
+    // for the T rows' own value (the keys' values come from V^T): the V
+    // segment is stored for T rows only (the backward keeps all of it)
+    gp.cend[2] = 2 * hd + gd;
+    gp.dst[3] = z + (2 * hd + gd) * es; gp.ld[3] = zw; gp.cend[3] = zw; gp.scale[3] = 1.f;
+    gp.seg3_type = c.meta.type;
+  }
   if (kv) {
     // K straight into the cache ([rows][gd]), V only transposed (bf16 path; no T rows, so
     // no query reads its own row-major K/V)

@@ -305,12 +305,14 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
       }
       part += __shfl_xor(part, 32, 64);
       const float ps = selfq ? (float)(bf16)silu_scaled(part) : 0.f;
+      // only a T row's own value is read (and may be stored): other rows' slots
+      // of the row-major V need not hold finite values
       const bf16* vrow = (const bf16*)g.vd + (int64_t)(qrow0 + qr) * g.ldvd + grp * DH + 4 * hi;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x4 vv = *(const bf16x4*)(vrow + mb * 32 + 8 * j);
+          const bf16x4 vv = selfq ? *(const bf16x4*)(vrow + mb * 32 + 8 * j) : bf16x4{};
 #pragma unroll
           for (int t = 0; t < 4; ++t) o[pp][mb][4 * j + t] = fmaf(ps, (float)vv[t], o[pp][mb][4 * j + t]);
         }

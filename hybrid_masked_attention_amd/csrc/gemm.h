@@ -41,6 +41,9 @@ struct GemmArgs {
   void* out; int64_t ldo;
   int32_t accumulate;
   void* pre; int64_t ldpre;       // EPI_SILU_SPLIT: if set, also store the pre-activation acc here
+  // EPI_SILU_SPLIT (bf16): if set, segment 3 is stored only for output rows r
+  // with seg3_type[r] == T (a layer's own V is read back only by its T rows)
+  const uint8_t* seg3_type;
   // EPI_SILU_SPLIT (bf16, identity row maps): if set, output columns
   // [vt_col0, vt_col0 + vt_cols) are also written transposed,
   //   vt[(n - vt_col0) * ldvt + perm16(m)]  for every m < ldvt,

@@ -445,11 +445,12 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
     int64_t ldseg = g.ld[0];
     float sc = g.scale[0];
     int c0 = 0;
+    const uint8_t* rtype = nullptr;   // segment 3 with a row filter: T rows only
     if (nw >= g.cend[0]) {
       c0 = g.cend[0]; dseg = g.dst[1]; ldseg = g.ld[1]; sc = g.scale[1];
       if (nw >= g.cend[1]) {
         c0 = g.cend[1]; dseg = g.dst[2]; ldseg = g.ld[2]; sc = g.scale[2];
-        if (nw >= g.cend[2]) { c0 = g.cend[2]; dseg = g.dst[3]; ldseg = g.ld[3]; sc = g.scale[3]; }
+        if (nw >= g.cend[2]) { c0 = g.cend[2]; dseg = g.dst[3]; ldseg = g.ld[3]; sc = g.scale[3]; rtype = g.seg3_type; }
       }
     }
     if (g.pre) {
@@ -471,7 +472,10 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
       for (int h = 0; h < G_WR / 64; ++h)
         staged_pass<false, 2>(ep, acc, 2 * h, l32, hi, lane, [&](int rl, int cl, const float (&v)[8]) {
           const int m = mw + rl;
-          if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)dseg + map_row(cmap, m) * ldseg + (nw - c0) + cl) = pack8(v);
+          if (m < g.M && nw + cl < g.N) {
+            const int64_t crow = map_row(cmap, m);
+            if (!rtype || rtype[crow] == TT_T) *(bf16x8*)((bf16*)dseg + crow * ldseg + (nw - c0) + cl) = pack8(v);
+          }
         });
     }
     if (g.vt && nw >= g.vt_col0 && nw < g.vt_col0 + g.vt_cols) {
