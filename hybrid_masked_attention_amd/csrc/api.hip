@@ -462,8 +462,13 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
 // full layer: one normalisation pass over all rows writes every layer's X~
 // (T rows as zeros: their K/V are never read as keys), then each layer's K
 // and V^T over all packed rows.
+//
+// With a side stream, the K|V projections of layers 1..k-1 go to it (after
+// the normalisation pass) and each marks event l when done, so that they
+// overlap the T-row work of the layers before them; the caller waits for mark
+// l before layer l's T rows and joins the side stream before returning.
 mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, int k, const void* x,
-                               char* ws, const BackboneWs& L, const KvOut* kv = nullptr) {
+                               char* ws, const BackboneWs& L, const KvOut* kv = nullptr, SideStream* side = nullptr) {
   const MetaPlan& p = c.plan;
   const int dt = d->dtype;
   const int64_t es = elem_size(dt);
@@ -476,7 +481,9 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
     g1.y_more[l - 1] = ws + L.xt[l]; g1.gamma_more[l - 1] = w[l].ln1_g; g1.beta_more[l - 1] = w[l].ln1_b;
   }
   TRY(timed_gln(g1, dt, c.s));
+  if (side && k > 1) TRY(side->fork(c.s));
   for (int l = 0; l < k; ++l) {
+    const hipStream_t st = (side && l > 0) ? side->side : c.s;
     GemmArgs gk{};
     gk.M = (int32_t)p.n_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
     gk.A = ws + L.xt[l]; gk.lda = D; gk.amap = identity_map();
@@ -487,7 +494,8 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
     gk.dst[0] = kv ? kv[l].k : ws + L.k[l]; gk.ld[0] = gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
     gk.dst[1] = nullptr; gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd; gk.scale[1] = 1.f;
     gk.vt = kv ? kv[l].vt : ws + L.vt[l]; gk.ldvt = kv ? kv[l].ldvt : L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
-    TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s));
+    TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, st));
+    if (side && l > 0) TRY(side->mark(l));
     (void)es;
   }
   return MTFM_OK;
@@ -995,14 +1003,26 @@ mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, in
   if (hoist) {
     const BackboneWs L = backbone_ws(c.plan, dims, k_target);
     char* w = (char*)ws;
-    for (int b = 0; b < n_blocks; ++b) {
-      TRY(run_full(c, dims, &full[b], x_inout, x_inout, w + L.full));
+    // the K|V projections of a block's later target layers overlap the T-row
+    // work of its earlier ones on a second stream (each layer waits for its own)
+    SideStream* side = nullptr;
+    if (k_target > 1) TRY(side_stream(&side));
+    mtfm_status st = MTFM_OK;
+    for (int b = 0; b < n_blocks && st == MTFM_OK; ++b) {
+      st = run_full(c, dims, &full[b], x_inout, x_inout, w + L.full);
       const mtfm_target_w* tw = &tgt[b * k_target];
-      if (c.plan.n_t_rows == 0) continue;   // target layers change T rows only
-      TRY(run_target_context(c, dims, tw, k_target, x_inout, w, L));
-      for (int t = 0; t < k_target; ++t) TRY(run_target_rows(c, dims, &tw[t], x_inout, w, L, t));
+      if (st != MTFM_OK || c.plan.n_t_rows == 0) continue;   // target layers change T rows only
+      st = run_target_context(c, dims, tw, k_target, x_inout, w, L, nullptr, side);
+      for (int t = 0; t < k_target && st == MTFM_OK; ++t) {
+        if (side && t > 0) st = side->wait_mark(c.s, t);
+        if (st == MTFM_OK) st = run_target_rows(c, dims, &tw[t], x_inout, w, L, t);
+      }
     }
-    return MTFM_OK;
+    if (side) {
+      const mtfm_status js = side->join(c.s);   // also after a failure: nothing of this call stays on the side
+      if (st == MTFM_OK) st = js;
+    }
+    return st;
   }
   for (int b = 0; b < n_blocks; ++b) {
     TRY(run_full(c, dims, &full[b], x_inout, x_inout, (char*)ws));
