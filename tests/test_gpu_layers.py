@@ -121,6 +121,17 @@ def test_edge_users_fp32(kind):
     _compare(wl, kind, _run_layer(wl, kind), TOL_F32)
 
 
+@pytest.mark.parametrize("n_users", [2048, 2049])
+def test_many_users_with_and_without_work_order(n_users):
+    """Up to 2048 users the attention grids take the XCD-balanced work order from the metadata;
+    past that the plain XCD-contiguous order.  Both on many small users, every row against the oracle."""
+    rng = np.random.default_rng(90)
+    lens = np.stack([rng.integers(0, 41, n_users), rng.integers(0, 21, n_users), rng.integers(0, 7, n_users)], 1)
+    wl = _small_workload(lens, 1, "bf16", 91)
+    _compare(wl, "full", _run_layer(wl, "full"), TOL_BF16)
+    _compare(wl, "target", _run_layer(wl, "target"), TOL_BF16)
+
+
 def test_fp32_head_dim_64_and_gqa_ratio_1():
     dims = synth.Dims(128, 2, 2, 64)
     wl = _small_workload([[20, 9, 4], [70, 3, 1]], 1, "f32", 51, dims=dims, w_std=0.1)
