@@ -89,7 +89,8 @@ class CMetaLayout(ctypes.Structure):
         "n_rows", "n_t_rows", "n_parents", "n_ctx_rows", "n_full_tiles", "n_target_tiles", "n_key_tiles",
         "off_user", "off_p",
         "off_n", "off_type", "off_full_tiles", "off_target_tiles", "off_ctx_rows", "off_parent_row",
-        "n_full_order", "n_target_order", "off_full_order", "off_target_order", "total_bytes")]
+        "n_full_order", "n_target_order", "off_full_order", "off_target_order",
+        "off_tsort_q", "off_tsort_g", "off_target_tiles_sorted", "total_bytes")]
 
 
 _lib = None
@@ -293,6 +294,10 @@ def meta_views(meta, layout: CMetaLayout, n_users: int) -> Dict[str, "object"]:
         "parent_row": view(L.off_parent_row, L.n_parents, torch.int32),
         "full_order": view(L.off_full_order, L.n_full_order, torch.int32),
         "target_order": view(L.off_target_order, L.n_target_order, torch.int32),
+        "tsort_q": view(L.off_tsort_q, L.n_t_rows, torch.int32),
+        "tsort_g": view(L.off_tsort_g, L.n_t_rows, torch.int32),
+        "target_tiles_sorted": view(L.off_target_tiles_sorted, L.n_target_tiles * 8, torch.int32,
+                                    (L.n_target_tiles, 8)),
     }
 
 

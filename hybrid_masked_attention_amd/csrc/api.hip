@@ -86,6 +86,9 @@ mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan) {
   l.n_full_order = p.n_full_order; l.n_target_order = p.n_target_order;
   l.off_full_order = take(p.n_full_order * 4);
   l.off_target_order = take(p.n_target_order * 4);
+  l.off_tsort_q = take(p.n_t_rows * 4);
+  l.off_tsort_g = take(p.n_t_rows * 4);
+  l.off_target_tiles_sorted = take(p.n_target_tiles * 32);
   l.total_bytes = off;
   *plan = p;
   return MTFM_OK;
@@ -104,6 +107,9 @@ MetaPtrs meta_ptrs(const MetaPlan& plan, const void* meta_d) {
   m.parent_row = reinterpret_cast<const int32_t*>(base + plan.lay.off_parent_row);
   m.full_order = plan.n_full_order ? reinterpret_cast<const int32_t*>(base + plan.lay.off_full_order) : nullptr;
   m.target_order = plan.n_target_order ? reinterpret_cast<const int32_t*>(base + plan.lay.off_target_order) : nullptr;
+  m.tsort_q = reinterpret_cast<const int32_t*>(base + plan.lay.off_tsort_q);
+  m.tsort_g = reinterpret_cast<const int32_t*>(base + plan.lay.off_tsort_g);
+  m.target_tiles_sorted = reinterpret_cast<const int32_t*>(base + plan.lay.off_target_tiles_sorted);
   return m;
 }
 
@@ -433,6 +439,10 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   aa.a = a; aa.lda = hd;
   aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
   aa.order = c.meta.target_order; aa.n_order = (int32_t)p.n_target_order;
+  if (dt == MTFM_BF16) {
+    // T rows ordered by visible prefix: slices of similar rows cut fewer key tiles
+    aa.tiles = c.meta.target_tiles_sorted; aa.qperm = c.meta.tsort_q; aa.gperm = c.meta.tsort_g;
+  }
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   aa.per_group = 1;
@@ -551,6 +561,10 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   aa.a = a; aa.lda = hd;
   aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
   aa.order = c.meta.target_order; aa.n_order = (int32_t)p.n_target_order;
+  if (dt == MTFM_BF16) {
+    // T rows ordered by visible prefix: slices of similar rows cut fewer key tiles
+    aa.tiles = c.meta.target_tiles_sorted; aa.qperm = c.meta.tsort_q; aa.gperm = c.meta.tsort_g;
+  }
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   aa.per_group = 1;
@@ -769,8 +783,9 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
-  aa.tiles = tiles; aa.ntiles = (int32_t)p.n_target_tiles;
+  aa.tiles = tiles; aa.ntiles = (int32_t)p.n_target_tiles;   // the sorted tiles, rebased on the cache
   aa.order = c.meta.target_order; aa.n_order = (int32_t)p.n_target_order;
+  aa.qperm = c.meta.tsort_q; aa.gperm = c.meta.tsort_g;
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   aa.per_group = 1;
@@ -834,7 +849,7 @@ mtfm_status serve_targets_run(const Ctx& c, const mtfm_dims* dims, int32_t n_blo
   int32_t* tiles = (int32_t*)(w + L.tiles);
   {
     const int n = (int)c.plan.n_target_tiles;
-    rebase_tiles_kernel<<<(n * 8 + 255) / 256, 256, 0, c.s>>>(c.meta.target_tiles, n,
+    rebase_tiles_kernel<<<(n * 8 + 255) / 256, 256, 0, c.s>>>(c.meta.target_tiles_sorted, n,
                                                                c.meta.user + UT_CTX * (c.plan.n_users + 1), tiles);
     MTFM_LAUNCH_CHECK("rebase_tiles");
   }

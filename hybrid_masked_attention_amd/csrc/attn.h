@@ -33,6 +33,10 @@ struct AttnArgs {
   // slice id 2 tile + half that XCD x takes k-th, -1 past its list; the grid is
   // n_order (x G with per_group) workgroups.  nullptr: XCD-contiguous order.
   const int32_t* order; int32_t n_order;
+  // bf16 path, optional query-row permutation: a tile's query-row field is
+  // then a position, and the row at position k is query row qperm[k] at
+  // packed row gperm[k] (both or neither)
+  const int32_t* qperm; const int32_t* gperm;
   const int32_t* p; const int32_t* n;  // per packed row
   const int32_t* lens;
   int32_t H, G, dh;

@@ -179,11 +179,14 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
     }
   };
 
-  // per query row: visible context prefix, self flag, output scale
+  // per query row: its query-space row qi and packed row gi (through the
+  // permutation if there is one), visible context prefix, self flag, output scale
   const bool ok = l32 < nrows;
   const int qr = ok ? l32 : 0;
-  const int plim = ok ? g.p[grow0 + qr] : 0;
-  const int nl = ok ? g.n[grow0 + qr] : 1;
+  const int qi = g.qperm ? g.qperm[qrow0 + qr] : qrow0 + qr;
+  const int gi = g.gperm ? g.gperm[qrow0 + qr] : grow0 + qr;
+  const int plim = ok ? g.p[gi] : 0;
+  const int nl = ok ? g.n[gi] : 1;
   const int selfq = ok ? nl - plim : 0;
   const float rq = ok ? g.out_scale / (float)nl : 0.f;
 
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
     // Q fragments (B operand of S^T = K Q^T): query l32, dims kk*16 + 8*hi + [0, 8)
     bf16x8 qf[4];
     {
-      const bf16* src = (const bf16*)g.q + (int64_t)(qrow0 + qr) * g.ldq + h * DH + 8 * hi;
+      const bf16* src = (const bf16*)g.q + (int64_t)qi * g.ldq + h * DH + 8 * hi;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) qf[kk] = ok ? *(const bf16x8*)(src + kk * 16) : bf16x8{};
     }
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
     // lane holds half of the query's dims (kk*16 + 8hi + [0, 8)); the other half
     // is in lane ^ 32.
     if (any_self) {
-      const bf16* krow = (const bf16*)g.kd + (int64_t)(qrow0 + qr) * g.ldkd + grp * DH + 8 * hi;
+      const bf16* krow = (const bf16*)g.kd + (int64_t)qi * g.ldkd + grp * DH + 8 * hi;
       float part = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
       const float ps = selfq ? (float)(bf16)silu_scaled(part) : 0.f;
       // only a T row's own value is read (and may be stored): other rows' slots
       // of the row-major V need not hold finite values
-      const bf16* vrow = (const bf16*)g.vd + (int64_t)(qrow0 + qr) * g.ldvd + grp * DH + 4 * hi;
+      const bf16* vrow = (const bf16*)g.vd + (int64_t)qi * g.ldvd + grp * DH + 4 * hi;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
   if (g.a && ok) {
 #pragma unroll
     for (int pp = 0; pp < P; ++pp) {
-      bf16* orow = (bf16*)g.a + (int64_t)(qrow0 + l32) * g.lda + ((gsel + pp) * W + wave) * DH + 4 * hi;
+      bf16* orow = (bf16*)g.a + (int64_t)qi * g.lda + ((gsel + pp) * W + wave) * DH + 4 * hi;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -384,12 +387,12 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
   for (int w = 0; w < W; ++w) var += red[(W + w) * 32 + l32];
   const float rstd = rsqrtf(var / (float)hd + g.eps);
   if (!ok) return;
-  const int t = g.type[grow0 + qr];
+  const int t = g.type[gi];
   const float* gam = g.ln_g + (int64_t)t * hd;
   const float* bet = g.ln_b + (int64_t)t * hd;
   const bool gb_vec = (((uintptr_t)g.ln_g | (uintptr_t)g.ln_b) & 15) == 0;   // 16-byte loads where aligned
-  const bf16* urow = (const bf16*)g.u + (int64_t)(qrow0 + l32) * g.ldu;
-  bf16* yrow = (bf16*)g.y + (int64_t)(qrow0 + l32) * g.ldy;
+  const bf16* urow = (const bf16*)g.u + (int64_t)qi * g.ldu;
+  bf16* yrow = (bf16*)g.y + (int64_t)qi * g.ldy;
 #pragma unroll
   for (int pp = 0; pp < P; ++pp)
 #pragma unroll
@@ -512,12 +515,14 @@ mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
     if ((int64_t)a.G * 64 * a.ldvt * 2 >= (int64_t)1 << 32 || 64 * a.ldk * 2 >= (int64_t)1 << 31) return MTFM_E_UNSUPPORTED;
     if (a.per_group && a.y) return MTFM_E_UNSUPPORTED;   // the gated epilogue needs every head of a row
     if (a.order && (a.n_order <= 0 || a.n_order % 8 != 0)) return MTFM_E_UNSUPPORTED;
+    if (!a.qperm != !a.gperm) return MTFM_E_UNSUPPORTED;
     if (a.y && (!a.u || !a.ln_g || !a.ln_b || !a.type || a.ldy % 4 != 0 || a.ldu % 4 != 0 ||
                 ((uintptr_t)a.y & 7) || ((uintptr_t)a.u & 7)))
       return MTFM_E_UNSUPPORTED;
     mtfm_status st = launch_bf16(a, r, s);
     if (st != MTFM_OK) return st;
   } else {
+    if (a.qperm) return MTFM_E_UNSUPPORTED;
     dim3 grid((unsigned)a.ntiles, (unsigned)a.H);
     if (a.dh == 32) attn_f32_kernel<32><<<grid, 64, 0, s>>>(a);
     else if (a.dh == 64) attn_f32_kernel<64><<<grid, 64, 0, s>>>(a);

@@ -119,6 +119,7 @@ MTFM_DEV int upper_index(const int32_t* off, int n, int x) {
 #define MTFM_HD __host__ __device__ __forceinline__
 
 constexpr int kOrderMaxUsers = 2048;   // larger batches keep the plain XCD-contiguous order
+constexpr int kTSortMaxRows = 4096;    // users with more T rows keep their own order
 enum OrderLayer { OL_FULL = 0, OL_TARGET = 1 };
 
 // 32-row query slices of user u: every packed row (full layer) or its T rows.
@@ -172,6 +173,12 @@ struct MetaPtrs {
   const int32_t* parent_row;
   const int32_t* full_order;     // nullptr when the batch has no work order
   const int32_t* target_order;
+  // T rows of each user in ascending order of their visible prefix (stable):
+  // position k holds T row tsort_q[k] (query space) at packed row tsort_g[k];
+  // target_tiles_sorted tiles those positions like target_tiles the T rows
+  const int32_t* tsort_q;
+  const int32_t* tsort_g;
+  const int32_t* target_tiles_sorted;
 };
 
 mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan);

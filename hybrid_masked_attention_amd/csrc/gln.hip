@@ -13,7 +13,9 @@ namespace {
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 // Load / store VPL contiguous elements through 16-byte vectors when they fill
-// whole vectors, element by element otherwise.
+// whole vectors, element by element otherwise.  Stores are non-temporal: the
+// rows stream out and are read back by another kernel, not from this one's
+// cache lines.
 template <typename T, int VPL>
 MTFM_DEV void load_row(const T* p, float* v) {
   constexpr int BYTES = VPL * (int)sizeof(T);
@@ -43,7 +45,7 @@ MTFM_DEV void store_row(T* p, const float* v) {
       T* e = reinterpret_cast<T*>(&w);
 #pragma unroll
       for (int j = 0; j < 16 / (int)sizeof(T); ++j) e[j] = from_f32<T>(v[c * (16 / sizeof(T)) + j]);
-      q[c] = w;
+      __builtin_nontemporal_store(w, &q[c]);
     }
   } else {
 #pragma unroll

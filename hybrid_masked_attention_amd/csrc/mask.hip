@@ -148,10 +148,43 @@ __global__ __launch_bounds__(64) void rows_full_tiles_kernel(const int32_t* __re
   }
 }
 
+// One workgroup per user: its T rows in ascending order of the visible prefix
+// p (ties by row; a parent's S sub-tokens share p and stay together), by
+// counting.  Only the order of the query rows changes, which no row's result
+// depends on; the target tiles over this order cut fewer key tiles (rows of
+// similar p share a slice).  Users with more than kTSortMaxRows T rows keep
+// their own order.
+__global__ __launch_bounds__(256) void tsort_kernel(const int32_t* __restrict__ lens, int n_users, int split,
+                                                     const int32_t* __restrict__ table,
+                                                     const int32_t* __restrict__ p_in, int32_t* __restrict__ tsq,
+                                                     int32_t* __restrict__ tsg) {
+  const int stride = n_users + 1;
+  const int u = blockIdx.x;
+  const int lc = lens[3 * u] + lens[3 * u + 1], nt = split * lens[3 * u + 2];
+  const int g0 = table[UT_ROW * stride + u] + lc, t0 = table[UT_TROW * stride + u];
+  const bool sort = nt <= kTSortMaxRows;
+  for (int i = threadIdx.x; i < nt; i += blockDim.x) {
+    int rank = i;
+    if (sort) {
+      const int pi = p_in[g0 + i];
+      rank = 0;
+      for (int j = 0; j < nt; ++j) {
+        const int pj = p_in[g0 + j];
+        rank += (pj < pi) || (pj == pi && j < i);
+      }
+    }
+    tsq[t0 + rank] = t0 + i;
+    tsg[t0 + rank] = g0 + i;
+  }
+}
+
 // One wave per target-layer query tile (T rows only); reads p written above.
+// With tsg, the tile's rows are the positions of the sorted order (tsg gives
+// their packed rows) and its query-row fields hold the position.
 __global__ __launch_bounds__(64) void target_tiles_kernel(const int32_t* __restrict__ lens, int n_users, int split,
                                                           const int32_t* __restrict__ table,
                                                           const int32_t* __restrict__ p_in,
+                                                          const int32_t* __restrict__ tsg,
                                                           int32_t* __restrict__ tiles) {
   const int stride = n_users + 1;
   const int b = blockIdx.x;
@@ -163,7 +196,7 @@ __global__ __launch_bounds__(64) void target_tiles_kernel(const int32_t* __restr
   const int rt = a * kTile + threadIdx.x;
   int pmin = INT32_MAX, pmax = 0;
   if (rt < nt) {
-    const int p = p_in[row0 + lc + rt];
+    const int p = p_in[tsg ? tsg[table[UT_TROW * stride + u] + rt] : row0 + lc + rt];
     pmin = p; pmax = p;
   }
   pmin = wave_min(pmin);
@@ -270,8 +303,17 @@ mtfm_status launch_mask_build(const mtfm_batch* b, const MetaPlan& plan, void* m
     MTFM_LAUNCH_CHECK("work_order_kernel");
   }
   if (plan.n_target_tiles > 0) {
-    target_tiles_kernel<<<(unsigned)plan.n_target_tiles, 64, 0, s>>>(b->lens_d, plan.n_users, plan.split, table, p, tt);
+    int32_t* tsq = reinterpret_cast<int32_t*>(base + plan.lay.off_tsort_q);
+    int32_t* tsg = reinterpret_cast<int32_t*>(base + plan.lay.off_tsort_g);
+    int32_t* tts = reinterpret_cast<int32_t*>(base + plan.lay.off_target_tiles_sorted);
+    target_tiles_kernel<<<(unsigned)plan.n_target_tiles, 64, 0, s>>>(b->lens_d, plan.n_users, plan.split, table, p,
+                                                                       nullptr, tt);
     MTFM_LAUNCH_CHECK("target_tiles_kernel");
+    tsort_kernel<<<(unsigned)plan.n_users, 256, 0, s>>>(b->lens_d, plan.n_users, plan.split, table, p, tsq, tsg);
+    MTFM_LAUNCH_CHECK("tsort_kernel");
+    target_tiles_kernel<<<(unsigned)plan.n_target_tiles, 64, 0, s>>>(b->lens_d, plan.n_users, plan.split, table, p,
+                                                                       tsg, tts);
+    MTFM_LAUNCH_CHECK("target_tiles_kernel (sorted)");
   }
   return MTFM_OK;
 }

@@ -156,6 +156,9 @@ typedef struct {
   int64_t n_target_order;    /*   (0 for batches over 2048 users: plain order) */
   int64_t off_full_order;    /* int32 [n_full_order]: entry 8 k + x = 2 tile + half of the k-th */
   int64_t off_target_order;  /*   32-row query slice XCD x takes, -1 past the end of its list */
+  int64_t off_tsort_q;       /* int32 [n_t_rows]: each user's T rows in ascending order of their */
+  int64_t off_tsort_g;       /*   prefix p (ties by row): T-row index / packed row at each position */
+  int64_t off_target_tiles_sorted;  /* int32 [n_target_tiles][8]: target tiles over those positions */
   int64_t total_bytes;
 } mtfm_meta_layout;
 /* Tile descriptor, int32 x 8:

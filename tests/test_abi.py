@@ -66,7 +66,8 @@ def test_meta_layout_counts_match_lengths(B):
         assert lay.n_target_tiles == int(np.sum((wl.batch.split * wl.batch.lens[:, 2] + 63) // 64))
         assert lay.n_ctx_rows == int(wl.batch.lens[:, :2].sum())
         offs = [lay.off_user, lay.off_p, lay.off_n, lay.off_type, lay.off_full_tiles, lay.off_target_tiles,
-                lay.off_ctx_rows, lay.off_parent_row, lay.off_full_order, lay.off_target_order, lay.total_bytes]
+                lay.off_ctx_rows, lay.off_parent_row, lay.off_full_order, lay.off_target_order, lay.off_tsort_q,
+                lay.off_tsort_g, lay.off_target_tiles_sorted, lay.total_bytes]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         assert B.meta_bytes(b) == lay.total_bytes
 

@@ -48,6 +48,27 @@ def _check(batch, users=None, fast=True):
             # packed-row fields
             np.testing.assert_array_equal(got[:, 5], r0 + got[:, 1])
             np.testing.assert_array_equal(got[:, 7], np.full(len(got), r0))
+    # T rows in ascending order of their prefix (stable; a parent's sub-tokens share it): the
+    # device permutation, and its tile descriptors against the oracle's tiles of the same user
+    # with the parents (targets) in that order
+    t_off = np.concatenate([[0], np.cumsum(batch.split * batch.lens[:, 2])])
+    for u in sel:
+        ref = omask.batch_meta(batch.user(u), 64, 64, fast=fast)
+        lc = int(batch.lens[u, 0] + batch.lens[u, 1])
+        nt = int(t_off[u + 1] - t_off[u])
+        if nt == 0:
+            continue
+        p_t = np.asarray(ref["p"][lc:])
+        want = np.argsort(p_t, kind="stable")
+        np.testing.assert_array_equal(v["tsort_q"][t_off[u]:t_off[u + 1]], t_off[u] + want)
+        np.testing.assert_array_equal(v["tsort_g"][t_off[u]:t_off[u + 1]], off[u] + lc + want)
+        uu = batch.user(u)
+        parents = want[::batch.split] // batch.split
+        perm_user = synth.Batch(uu.lens, uu.split, uu.ts_r, np.asarray(uu.ts_t)[parents])
+        ref_sorted = omask.batch_meta(perm_user, 64, 64, fast=fast)["target_tiles"]
+        got = v["target_tiles_sorted"][v["target_tiles_sorted"][:, 0] == u]
+        np.testing.assert_array_equal(got[:, 1:5], np.asarray(ref_sorted)[:, 1:5])
+        np.testing.assert_array_equal(got[:, 6], t_off[u] + np.asarray(ref_sorted)[:, 1] - lc)   # position base
     if users is None:
         for key in ("full_tiles", "target_tiles"):
             assert np.all(np.diff(v[key][:, 0]) >= 0)          # users in order

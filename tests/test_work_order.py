@@ -47,7 +47,7 @@ def test_layout_sizes_the_orders_by_the_rule(B, name, batch):
     assert lay.n_full_order == len(_order.expected_order(batch.lens, batch.split, _order.FULL))
     assert lay.n_target_order == len(_order.expected_order(batch.lens, batch.split, _order.TARGET))
     assert lay.off_full_order % 256 == 0 and lay.off_target_order % 256 == 0
-    assert lay.off_parent_row <= lay.off_full_order <= lay.off_target_order <= lay.total_bytes
+    assert lay.off_parent_row <= lay.off_full_order <= lay.off_target_order <= lay.off_tsort_q <= lay.total_bytes
 
 
 def test_no_order_past_the_user_limit(B):
