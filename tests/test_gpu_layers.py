@@ -239,3 +239,34 @@ def test_small_v2_backbone_against_oracle():
     r.close("X'", got, ref)
     r.branch("dX (8 roundings allowed)", got, ref, xr, "bf16", roundings=8)
     r.check()
+
+
+def test_backbone_forward_replays_from_a_hip_graph():
+    """The hoisted backbone forward, whose context stage runs on a second stream forked and joined
+    with events, captured into a HIP graph: every replay, with eager runs in between, equals the
+    eager result bit for bit."""
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    wl = _small_backbone(4, 80)
+    dw = DeviceWorkload(wl)
+    meta = B.mask_build(dw.batch)
+    ws = B.workspace(dw.batch, dw.dims, B.OP_BACKBONE, k_target=wl.k_target)
+
+    def eager():
+        x = dw.x.clone()
+        B.backbone_fwd(dw.batch, dw.dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, x, ws)
+        torch.cuda.synchronize()
+        return x
+
+    ref = eager()          # also creates the library's second stream before the capture
+    xg = dw.x.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.backbone_fwd(dw.batch, dw.dims, wl.n_blocks, wl.k_target, meta, dw.full, dw.target, xg, ws)
+    for i in range(3):
+        xg.copy_(dw.x)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xg, ref), f"replay {i}"
+        assert torch.equal(eager(), ref)

@@ -10,7 +10,9 @@ buffer the keys live in, and the cache packs context rows without the T rows
 in between, so keys are grouped differently inside the fp32 attention sums
 than in mtfm_backbone_fwd: the two agree to rounding, not bit for bit.  Bar:
 the residual branch within 1e-2 of max|branch| after allowing one bf16
-rounding of the stored X per layer (as the backbone tests).
+rounding of the stored X per layer against the oracle (as the backbone
+tests), and two per layer against mtfm_backbone_fwd (both sides are device
+results that round X at every layer, with differently grouped sums).
 """
 import numpy as np
 import pytest
@@ -85,9 +87,9 @@ def _serve_targets(wl, dw, B, torch, cache, x_t):
     return x_t
 
 
-def _compare(r, name, got, ref_dev, ref_or, x0):
-    r.branch(f"{name} vs oracle", got, ref_or, x0, "bf16", roundings=16)
-    r.branch(f"{name} vs backbone", got, ref_dev, x0, "bf16", roundings=16)
+def _compare(r, name, got, ref_dev, ref_or, x0, layers):
+    r.branch(f"{name} vs oracle", got, ref_or, x0, "bf16", roundings=layers)
+    r.branch(f"{name} vs backbone", got, ref_dev, x0, "bf16", roundings=2 * layers)
 
 
 @pytest.mark.parametrize("split", [1, 4])
@@ -107,8 +109,8 @@ def test_serving_matches_backbone_and_oracle(split):
     xr, full, tgt = rounded_inputs(wl)
     o = om.backbone(wl.batch, xr, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=om.bf16_round)
     r = Report(TOL_BF16)
-    _compare(r, "context rows", to_np(x_ctx), ref[ctx_rows], o[ctx_rows], xr[ctx_rows])
-    _compare(r, "T rows", to_np(x_t), ref[t_rows], o[t_rows], xr[t_rows])
+    _compare(r, "context rows", to_np(x_ctx), ref[ctx_rows], o[ctx_rows], xr[ctx_rows], wl.n_blocks * (1 + wl.k_target))
+    _compare(r, "T rows", to_np(x_t), ref[t_rows], o[t_rows], xr[t_rows], wl.n_blocks * (1 + wl.k_target))
     r.check()
 
 
@@ -142,8 +144,8 @@ def test_serving_reuses_one_cache_for_other_candidates():
         say(f"  candidates {trial}: {len(t_rows)} T rows")
         xr, full, tgt = rounded_inputs(wc)
         o = om.backbone(cand, xr, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=om.bf16_round)
-        _compare(r, f"candidates {trial} T rows", to_np(x_t), ref[t_rows], o[t_rows], xr[t_rows])
-        _compare(r, f"candidates {trial} context rows", x_ctx, ref[ctx_rows], o[ctx_rows], xr[ctx_rows])
+        _compare(r, f"candidates {trial} T rows", to_np(x_t), ref[t_rows], o[t_rows], xr[t_rows], wl.n_blocks * (1 + wl.k_target))
+        _compare(r, f"candidates {trial} context rows", x_ctx, ref[ctx_rows], o[ctx_rows], xr[ctx_rows], wl.n_blocks * (1 + wl.k_target))
     r.check()
 
 
