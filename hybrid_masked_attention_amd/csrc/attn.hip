@@ -85,12 +85,19 @@ template <int R, int GPP> struct FusedShape {
   static constexpr int STAGE = GPP * A_STAGE;
   static constexpr int AS = 2;                       // ring stages
   static constexpr int CPW = 16 * GPP / W;           // 1 KB DMA chunks per wave per stage
-  static constexpr int WG_PER_CU = (160 * 1024) / (AS * STAGE) >= 2 ? 2 : 1;
-  static constexpr int WAVES_PER_SIMD = W * WG_PER_CU / 4 < 1 ? 1 : (W * WG_PER_CU / 4 > 4 ? 4 : W * WG_PER_CU / 4);
+  static constexpr int WG_LDS = (160 * 1024) / (AS * STAGE) > 8 ? 8 : (160 * 1024) / (AS * STAGE);
+  // waves per SIMD the register budget is sized for: what LDS allows, at most
+  // 4 with one pass (one head's accumulators per wave), 3 with two, 2 beyond
+  template <int P>
+  static constexpr int occupancy() {
+    constexpr int lds = W * WG_LDS / 4 < 1 ? 1 : W * WG_LDS / 4;
+    constexpr int regs = P >= 4 ? 2 : (P == 2 ? 3 : 4);
+    return lds < regs ? lds : regs;
+  }
 };
 
 template <int R, int GPP, int P>
-__global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD)) void attn_bf16_kernel(AttnArgs g) {
+__global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupancy<P>())) void attn_bf16_kernel(AttnArgs g) {
   using SH = FusedShape<R, GPP>;
   constexpr int W = SH::W, AS = SH::AS, STAGE = SH::STAGE, CPW = SH::CPW;
   __shared__ __attribute__((aligned(1024))) char lds[AS * STAGE];
@@ -189,6 +196,9 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
   const int nl = ok ? g.n[gi] : 1;
   const int selfq = ok ? nl - plim : 0;
   const float rq = ok ? g.out_scale / (float)nl : 0.f;
+  // largest prefix over the slice's rows (the same rows in every wave, so
+  // workgroup-uniform): a 32-key block of a cut tile that no row sees is skipped
+  const int pmax_s = __builtin_amdgcn_readfirstlane(wave_max(plim));
 
   f32x16 o[P][2];   // O^T per pass: lane = query, registers = dims mb*32 + 8(i/4) + 4hi + i%4
 #pragma unroll
@@ -262,13 +272,24 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
     };
     // one 32-key block at a time (a wave gets no MFMA / VALU overlap within
     // itself, only with the other waves of its SIMD, so holding one block's
-    // scores keeps four waves per SIMD within their registers)
-    auto tile_body = [&](const char* st, auto mask_tag, int lo, int lim) {
+    // scores keeps four waves per SIMD within their registers).  On a cut tile
+    // the keys [lo, lim) of a row are visible (lo = 0 but on the user's first
+    // tile); lim_hi is the largest lim over the slice: a block no row sees is
+    // skipped (its products would all be zero).
+    auto tile_body = [&](const char* st, auto mask_tag, int lo, int lim, int lim_hi) {
+      constexpr int MK = decltype(mask_tag)::value;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 sc;
-        qk(st, kb, sc);
-        silu_pv(st, kb, sc, mask_tag, lo, lim);
+        if constexpr (MK == 0) {
+          qk(st, kb, sc);
+          silu_pv(st, kb, sc, mask_tag, lo, lim);
+        } else {
+          const int b0 = 32 * kb, b1 = b0 + 32;
+          if (lo >= b1 || lim_hi <= b0) continue;             // no row sees a key of the block
+          qk(st, kb, sc);
+          silu_pv(st, kb, sc, mask_tag, lo, lim);
+        }
       }
     };
 
@@ -277,11 +298,12 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::WAVES_PER_SIMD))
       const char* st = gl_lds + stage * STAGE;
       const int ts = T0 + it * 64;
       if (ts >= urow0 && ts + 64 <= kfull) {
-        tile_body(st, MaskNone{}, 0, 0);
+        tile_body(st, MaskNone{}, 0, 0, 0);
       } else {
         const int lim = urow0 + plim - ts;
-        if (ts >= urow0) tile_body(st, MaskUpper{}, 0, lim);   // only the prefix end cuts this tile
-        else tile_body(st, MaskRange{}, urow0 - ts, lim);      // the user's first tile
+        const int lim_hi = urow0 + pmax_s - ts;
+        if (ts >= urow0) tile_body(st, MaskUpper{}, 0, lim, lim_hi);   // only the prefix end cuts this tile
+        else tile_body(st, MaskRange{}, urow0 - ts, lim, lim_hi);      // the user's first tile
       }
       if (it + 1 < n_main) {
         // tile it + 1 has landed once at most AS - 2 newer tiles' DMA are in flight;
