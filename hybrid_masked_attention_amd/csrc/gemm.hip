@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "gemm.h"
 
@@ -123,13 +124,22 @@ typedef __attribute__((__vector_size__(2 * sizeof(int64_t)))) int64_t i64x2;
 // through this type may alias any store (no type-based reordering).
 typedef int64_t __attribute__((may_alias)) i64_any;
 
+struct NoPre {
+  MTFM_DEV void operator()() const {}
+};
+
 // One pass of the staged epilogue: the wave's fp32 accumulators of MFMA row
 // blocks [a0, a0 + NA) go through LDS as bf16 (OUTF32 = false; 136-byte rows)
 // or fp32 (272-byte rows), then each lane handles one row and 8 consecutive
-// columns, calling f(row_local, col_local, v[8]) with the values in fp32.
-template <bool OUTF32, int NA, int TM, typename F>
-MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][TM], int a0, int l32, int hi, int lane, F&& f) {
+// columns, calling f(row_local, col_local, v[8]) with the values in fp32
+// (or f(row_local, col_local, v[8], round) where f takes the read-back round
+// i, row_local = 32 a0 + 8 i + lane / 8).  pre() runs first: loads that the
+// pass consumes can be issued there, ahead of the LDS round trip.
+template <bool OUTF32, int NA, int TM, typename F, typename Pre = NoPre>
+MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][TM], int a0, int l32, int hi, int lane, F&& f,
+                          Pre&& pre = Pre{}) {
   constexpr int RS = OUTF32 ? G_WC * 4 + 16 : G_WC * 2 + 8;
+  pre();
   wave_lds_sync();   // the previous pass's reads of this buffer are done
 #pragma unroll
   for (int a = 0; a < NA; ++a)
@@ -168,7 +178,8 @@ MTFM_DEV void staged_pass(char* ep, const f32x16 (&acc)[G_TN][TM], int a0, int l
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = (float)x[q];
     }
-    f(a0 * 32 + r, c, v);
+    if constexpr (std::is_invocable_v<F&, int, int, const float (&)[8], int>) f(a0 * 32 + r, c, v, i);
+    else f(a0 * 32 + r, c, v);
   }
 }
 
@@ -536,6 +547,33 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
         const int m = mw + rl;
         if (m < g.M && nw + cl < g.N) *(bf16x8*)((bf16*)g.out + map_row(cmap, m) * g.ldo + nw + cl) = pack8(v);
       });
+  } else if constexpr (EPI == EPI_RESID) {
+    // fp32 staging in four passes of 32 rows; a pass's residual segments are
+    // loaded before its LDS round trip (their latency overlaps the staging)
+#pragma unroll
+    for (int h = 0; h < G_TM; ++h) {
+      bf16x8 res[4];
+      const int cl = (lane & 7) * 8;
+      staged_pass<true, 1>(
+          ep, acc, h, l32, hi, lane,
+          [&](int rl, int, const float (&v)[8], int i) {
+            const int m = mw + rl;
+            if (m >= g.M || nw + cl >= g.N) return;
+            float o[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[q] = v[q] + (float)res[i][q];
+            *(bf16x8*)((bf16*)g.out + map_row(cmap, m) * g.ldo + nw + cl) = pack8(o);
+          },
+          [&]() {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = mw + h * 32 + i * 8 + (lane >> 3);
+              res[i] = (m < g.M && nw + cl < g.N)
+                           ? *(const bf16x8*)((const bf16*)g.resid + map_row(cmap, m) * g.ldr + nw + cl)
+                           : bf16x8{};
+            }
+          });
+    }
   } else {
     // fp32 staging in four passes of 32 rows
 #pragma unroll
@@ -544,13 +582,7 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
         const int m = mw + rl;
         if (m >= g.M || nw + cl >= g.N) return;
         const int64_t crow = map_row(cmap, m);
-        if constexpr (EPI == EPI_RESID) {
-          const bf16x8 res = *(const bf16x8*)((const bf16*)g.resid + crow * g.ldr + nw + cl);
-          float o[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) o[q] = v[q] + (float)res[q];
-          *(bf16x8*)((bf16*)g.out + crow * g.ldo + nw + cl) = pack8(o);
-        } else {
+        {
           float* d = (float*)g.out + crow * g.ldo + nw + cl;
           f32x4 o0, o1;
           if (g.accumulate) { o0 = *(const f32x4*)d; o1 = *(const f32x4*)(d + 4); }
