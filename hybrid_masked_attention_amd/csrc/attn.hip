@@ -51,6 +51,7 @@ constexpr int A_STAGE = 2 * A_TILE;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+
 MTFM_DEV int a_swz(int r) { return (r >> 1) & 7; }
 
 MTFM_DEV void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
@@ -87,11 +88,13 @@ template <int R, int GPP> struct FusedShape {
   static constexpr int CPW = 16 * GPP / W;           // 1 KB DMA chunks per wave per stage
   static constexpr int WG_LDS = (160 * 1024) / (AS * STAGE) > 8 ? 8 : (160 * 1024) / (AS * STAGE);
   // waves per SIMD the register budget is sized for: what LDS allows, at most
-  // 4 with one pass (one head's accumulators per wave), 3 with two, 2 beyond
+  // 4 with one or two passes (128 registers: at two passes the accumulators of
+  // both heads stay live, and a few registers spill across the second pass
+  // only), 2 beyond
   template <int P>
   static constexpr int occupancy() {
     constexpr int lds = W * WG_LDS / 4 < 1 ? 1 : W * WG_LDS / 4;
-    constexpr int regs = P >= 4 ? 2 : (P == 2 ? 3 : 4);
+    constexpr int regs = P >= 4 ? 2 : 4;
     return lds < regs ? lds : regs;
   }
 };
@@ -139,15 +142,32 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
   const int l32 = lane & 31, hi = lane >> 5;
   const int hd = g.H * DH;
 
+  // per query row: its query-space row qi and packed row gi (through the
+  // permutation if there is one), visible context prefix, self flag, output scale
+  const bool ok = l32 < nrows;
+  const int qr = ok ? l32 : 0;
+  const int qi = g.qperm ? g.qperm[qrow0 + qr] : qrow0 + qr;
+  const int gi = g.gperm ? g.gperm[qrow0 + qr] : grow0 + qr;
+  const int plim = ok ? g.p[gi] : 0;
+  const int nl = ok ? g.n[gi] : 1;
+  const int selfq = ok ? nl - plim : 0;
+  const float rq = ok ? g.out_scale / (float)nl : 0.f;
+  // smallest and largest visible prefix over the slice's rows (the same rows in
+  // every wave, so workgroup-uniform)
+  const int pmax_s = __builtin_amdgcn_readfirstlane(wave_max(plim));
+  const int pmin_s = __builtin_amdgcn_readfirstlane(wave_min(ok ? plim : 0x7fffffff));
+
   // Key tiles are aligned to 64 packed rows: tile it covers rows ts = T0 + 64 it
-  // .. ts + 63.  The descriptor bounds the user's visible keys: rows below
-  // urow0 + 64 full_end (capped at the context) are visible to every query of
-  // the tile, none at or past urow0 + 64 end.
+  // .. ts + 63.  A row sees the user's keys [urow0, urow0 + p).  K rows below
+  // urow0 (an earlier user's) and at or past kz_end (no row of the slice sees
+  // them) reach LDS as zeros: their scores are 0 and SiLU(0) = 0, so they add
+  // exactly nothing.  Keys below kfull are seen by every row of the slice, so a
+  // tile needs per-row masks only where some row's prefix ends strictly inside
+  // the keys it loads (never in a slice whose rows share one prefix).
   const int T0 = urow0 & ~63;
-  const int key_end = td[TD_END];
-  const int kend = urow0 + min(64 * key_end, lctx);
-  const int n_main = key_end > 0 ? (kend - T0 + 63) >> 6 : 0;
-  const int kfull = urow0 + min(64 * td[TD_FULL_END], lctx);
+  const int kz_end = urow0 + pmax_s;
+  const int kfull = urow0 + pmin_s;
+  const int n_main = pmax_s > 0 ? (kz_end - T0 + 63) >> 6 : 0;
 
   // DMA: the stage's 16 GPP chunks of 1 KB (per group: 8 of K rows, 8 of V^T
   // rows, 8 rows of 128 B each); wave w issues chunks w + W i.  Lane -> row
@@ -173,32 +193,23 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
   auto issue = [&](int gbase, int it, int stage) {
     const bool real = it < n_main;
     const int ts = real ? T0 + it * 64 : T0;
-    const int valid = real ? min(64, g.n_key_rows - ts) : 0;
+    // K through one resource over the user's visible keys [urow0, kz_end): a row
+    // of the tile outside it has an offset (negative ones wrap) past the
+    // resource and reads as zero
     const __amdgpu_buffer_rsrc_t kr =
-        a_rsrc(kbase + (int64_t)ts * g.ldk + gbase * DH, (uint32_t)(max(valid, 0) * g.ldk * 2));
+        a_rsrc(kbase + (int64_t)urow0 * g.ldk + gbase * DH, real ? (uint32_t)(pmax_s * g.ldk * 2) : 0u);
+    const uint32_t kshift = (uint32_t)((ts - urow0) * g.ldk * 2);
     const int64_t vt0 = (int64_t)gbase * DH * g.ldvt + ts;
     const __amdgpu_buffer_rsrc_t vr = a_rsrc(vtbase + vt0, real ? (uint32_t)((vt_elems - vt0) * 2) : 0u);
     char* st = lds + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int c = wave + W * i;
-      lds_dma16(((c >> 3) & 1) ? vr : kr, (lds_void*)(st + dlds[i]), doff[i]);
+      const bool is_v = (c >> 3) & 1;
+      lds_dma16(is_v ? vr : kr, (lds_void*)(st + dlds[i]), doff[i] + (is_v ? 0u : kshift));
     }
   };
 
-  // per query row: its query-space row qi and packed row gi (through the
-  // permutation if there is one), visible context prefix, self flag, output scale
-  const bool ok = l32 < nrows;
-  const int qr = ok ? l32 : 0;
-  const int qi = g.qperm ? g.qperm[qrow0 + qr] : qrow0 + qr;
-  const int gi = g.gperm ? g.gperm[qrow0 + qr] : grow0 + qr;
-  const int plim = ok ? g.p[gi] : 0;
-  const int nl = ok ? g.n[gi] : 1;
-  const int selfq = ok ? nl - plim : 0;
-  const float rq = ok ? g.out_scale / (float)nl : 0.f;
-  // largest prefix over the slice's rows (the same rows in every wave, so
-  // workgroup-uniform): a 32-key block of a cut tile that no row sees is skipped
-  const int pmax_s = __builtin_amdgcn_readfirstlane(wave_max(plim));
 
   f32x16 o[P][2];   // O^T per pass: lane = query, registers = dims mb*32 + 8(i/4) + 4hi + i%4
 #pragma unroll
@@ -207,7 +218,6 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
   const int xk = hi ^ a_swz(l32);   // fragment slot = (even chunk) ^ xk for K and V^T rows
   using MaskNone = std::integral_constant<int, 0>;
   using MaskUpper = std::integral_constant<int, 1>;
-  using MaskRange = std::integral_constant<int, 2>;
 
 #pragma unroll
   for (int pp = 0; pp < P; ++pp) {
@@ -241,16 +251,16 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
     };
     // P chunk c of key block kb: keys kb*32 + 16c + {4hi + t, 8 + 4hi + t : t < 4}, the
     // order in which V^T holds them, so P^T is the B operand of O^T += V^T P^T as is.
-    // Masks (template MK): 0 none; 1 keys below lim visible; 2 keys in [lo, lim).
+    // Masks (template MK): 0 none; 1 keys below lim visible.
     // The invisible scores are set to 0 before SiLU (SiLU(0) = 0 exactly), so a
     // mask costs one compare and one select per element and P still converts to
     // bf16 in pairs.  Register i of this lane holds key kb*32 + kc(i) + 4*hi with
     // the compile-time kc(i) = 8*(i/4) + i%4: the bounds are shifted once.
-    auto silu_pv = [&](const char* st, int kb, const f32x16& sc, auto mask_tag, int lo, int lim) {
+    auto silu_pv = [&](const char* st, int kb, const f32x16& sc, auto mask_tag, int lim) {
       constexpr int MK = decltype(mask_tag)::value;
       bf16x8 pf[2];
       const int shift = kb * 32 + 4 * hi;
-      const int lo_l = lo - shift, lim_l = lim - shift;
+      const int lim_l = lim - shift;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -259,7 +269,6 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
           const int kc = 8 * (i >> 2) + (i & 3);
           float sv = sc[i];
           if constexpr (MK == 1) sv = kc < lim_l ? sv : 0.f;
-          if constexpr (MK == 2) sv = (kc >= lo_l && kc < lim_l) ? sv : 0.f;
           pf[c][e] = (bf16)silu_scaled(sv);
         }
 #pragma unroll
@@ -273,9 +282,10 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
     // one 32-key block at a time (a wave gets no MFMA / VALU overlap within
     // itself, only with the other waves of its SIMD, so holding one block's
     // scores keeps four waves per SIMD within their registers).  On a cut tile
-    // the keys [lo, lim) of a row are visible (lo = 0 but on the user's first
-    // tile); lim_hi is the largest lim over the slice: a block no row sees is
-    // skipped (its products would all be zero).
+    // the keys below lim of a row are visible (those below lo, an earlier
+    // user's, are zeros); lim_hi is the largest lim over the slice: a block
+    // entirely below lo or from lim_hi on is skipped (its products would all be
+    // zero).
     auto tile_body = [&](const char* st, auto mask_tag, int lo, int lim, int lim_hi) {
       constexpr int MK = decltype(mask_tag)::value;
 #pragma unroll
@@ -283,28 +293,18 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
         f32x16 sc;
         if constexpr (MK == 0) {
           qk(st, kb, sc);
-          silu_pv(st, kb, sc, mask_tag, lo, lim);
+          silu_pv(st, kb, sc, mask_tag, lim);
         } else {
           const int b0 = 32 * kb, b1 = b0 + 32;
           if (lo >= b1 || lim_hi <= b0) continue;             // no row sees a key of the block
           qk(st, kb, sc);
-          silu_pv(st, kb, sc, mask_tag, lo, lim);
+          silu_pv(st, kb, sc, mask_tag, lim);
         }
       }
     };
 
     int stage = 0;
-    for (int it = 0; it < n_main; ++it) {
-      const char* st = gl_lds + stage * STAGE;
-      const int ts = T0 + it * 64;
-      if (ts >= urow0 && ts + 64 <= kfull) {
-        tile_body(st, MaskNone{}, 0, 0, 0);
-      } else {
-        const int lim = urow0 + plim - ts;
-        const int lim_hi = urow0 + pmax_s - ts;
-        if (ts >= urow0) tile_body(st, MaskUpper{}, 0, lim, lim_hi);   // only the prefix end cuts this tile
-        else tile_body(st, MaskRange{}, urow0 - ts, lim, lim_hi);      // the user's first tile
-      }
+    auto next_tile = [&](int it) {
       if (it + 1 < n_main) {
         // tile it + 1 has landed once at most AS - 2 newer tiles' DMA are in flight;
         // after the barrier every wave is done with this stage and it is refilled
@@ -313,6 +313,21 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
         issue(gbase, it + AS, stage);
         stage = stage + 1 == AS ? 0 : stage + 1;
       }
+    };
+    // The leading tiles, whose nonzero keys every row sees (all of them when the
+    // slice's rows share one prefix), run without masks in a loop of their own
+    // (straight-line, so the compiler overlaps one block's SiLU with the next
+    // block's products); the few tiles in which some row's prefix ends follow.
+    const int n_unmasked = kfull >= kz_end ? n_main : min(n_main, max(kfull - T0, 0) >> 6);
+    int it = 0;
+    for (; it < n_unmasked; ++it) {
+      tile_body(gl_lds + stage * STAGE, MaskNone{}, 0, 0, 0);
+      next_tile(it);
+    }
+    for (; it < n_main; ++it) {
+      const int ts = T0 + it * 64;
+      tile_body(gl_lds + stage * STAGE, MaskUpper{}, max(urow0 - ts, 0), urow0 + plim - ts, kz_end - ts);
+      next_tile(it);
     }
 
     // A T row's only T key is itself ([explainer] §8.2 matrix; the user-to-item
