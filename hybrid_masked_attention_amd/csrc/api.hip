@@ -180,10 +180,14 @@ BackboneWs backbone_ws(const MetaPlan& p, const mtfm_dims* d, int k_target) {
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + std::max<int64_t>(bytes, 0), 256); return o; };
   w.full = take(layer_ws(p, d, MTFM_OP_FULL).total);
   w.ldvt = vt_ld(p.n_rows);
+  // each kind for the k layers back to back (one grouped projection writes them)
+  const int64_t xt0 = take(k_target * p.n_rows * d->d_model * es);
+  const int64_t k0 = take(k_target * p.n_rows * gd * es);
+  const int64_t vt0 = take(k_target * gd * w.ldvt * es);
   for (int l = 0; l < k_target; ++l) {
-    w.xt[l] = take(p.n_rows * d->d_model * es);
-    w.k[l] = take(p.n_rows * gd * es);
-    w.vt[l] = take(gd * w.ldvt * es);
+    w.xt[l] = xt0 + l * p.n_rows * d->d_model * es;
+    w.k[l] = k0 + l * p.n_rows * gd * es;
+    w.vt[l] = vt0 + l * gd * w.ldvt * es;
   }
   w.xtt = take(p.n_t_rows * d->d_model * es);
   w.zt = take(p.n_t_rows * zw * es);
@@ -471,12 +475,14 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
 // Context stage of the target layers l = 0..k-1 of one block, right after its
 // full layer: one normalisation pass over all rows writes every layer's X~
 // (T rows as zeros: their K/V are never read as keys), then each layer's K
-// and V^T over all packed rows.
+// and V^T over all packed rows: with dense weights one grouped launch for the
+// k layers (more workgroups than any one layer's, so a shorter tail).
 //
-// With a side stream, the K|V projections of layers 1..k-1 go to it (after
-// the normalisation pass) and each marks event l when done, so that they
-// overlap the T-row work of the layers before them; the caller waits for mark
-// l before layer l's T rows and joins the side stream before returning.
+// Packed (2:4) weights go layer by layer: with a side stream, the K|V
+// projections of layers 1..k-1 go to it (after the normalisation pass) and
+// each marks event l when done, so that they overlap the T-row work of the
+// layers before them; the caller waits for mark l before layer l's T rows and
+// joins the side stream before returning.
 mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, int k, const void* x,
                                char* ws, const BackboneWs& L, const KvOut* kv = nullptr, SideStream* side = nullptr) {
   const MetaPlan& p = c.plan;
@@ -491,6 +497,25 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
     g1.y_more[l - 1] = ws + L.xt[l]; g1.gamma_more[l - 1] = w[l].ln1_g; g1.beta_more[l - 1] = w[l].ln1_b;
   }
   TRY(timed_gln(g1, dt, c.s));
+  bool dense = !kv && dt == MTFM_BF16;
+  for (int l = 0; l < k; ++l) dense = dense && !w[l].w_kv_s24;
+  if (dense) {
+    // the k layers' projections as one grouped launch: group l reads X~_l and
+    // W_kv of layer l and writes K_l and V^T_l (the buffers lie back to back)
+    GemmArgs gk{};
+    gk.M = (int32_t)p.n_rows; gk.N = 2 * gd; gk.K = D; gk.groups = k;
+    gk.A = ws + L.xt[0]; gk.lda = D; gk.amap = identity_map(); gk.amap_zadd = (int32_t)p.n_rows;
+    gk.B[0] = w[0].w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
+    for (int l = 0; l < k; ++l) gk.bgroup[l] = w[l].w_kv;
+    gk.cmap = identity_map(); gk.cmap_zadd = (int32_t)p.n_rows;
+    gk.epi = EPI_SILU_SPLIT;
+    gk.dst[0] = ws + L.k[0]; gk.ld[0] = gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
+    gk.dst[1] = nullptr; gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd; gk.scale[1] = 1.f;
+    gk.vt = ws + L.vt[0]; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
+    gk.vt_zstride = (L.vt[k > 1 ? 1 : 0] - L.vt[0]) / es;
+    if (k == 1) gk.vt_zstride = 0;
+    return timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s);
+  }
   if (side && k > 1) TRY(side->fork(c.s));
   for (int l = 0; l < k; ++l) {
     const hipStream_t st = (side && l > 0) ? side->side : c.s;
@@ -1018,10 +1043,13 @@ mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, in
   if (hoist) {
     const BackboneWs L = backbone_ws(c.plan, dims, k_target);
     char* w = (char*)ws;
-    // the K|V projections of a block's later target layers overlap the T-row
-    // work of its earlier ones on a second stream (each layer waits for its own)
+    // packed K|V projections run layer by layer, a block's later ones on a
+    // second stream beside the T-row work of its earlier ones (each layer
+    // waits for its own); dense ones are one grouped launch per block
     SideStream* side = nullptr;
-    if (k_target > 1) TRY(side_stream(&side));
+    bool packed_kv = false;
+    for (int b = 0; b < n_blocks * k_target; ++b) packed_kv = packed_kv || tgt[b].w_kv_s24;
+    if (k_target > 1 && packed_kv) TRY(side_stream(&side));
     mtfm_status st = MTFM_OK;
     for (int b = 0; b < n_blocks && st == MTFM_OK; ++b) {
       st = run_full(c, dims, &full[b], x_inout, x_inout, w + L.full);

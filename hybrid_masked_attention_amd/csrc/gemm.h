@@ -50,6 +50,11 @@ struct GemmArgs {
   // rows past M as zeros; perm16 permutes rows within aligned groups of 16 as
   // {0-3, 8-11, 4-7, 12-15} (the key order of the attention's P V operand).
   void* vt; int64_t ldvt; int32_t vt_col0, vt_cols;
+  // with groups > 1: group z's transposed copy at vt + z * vt_zstride (elements)
+  int64_t vt_zstride;
+  // bf16, dense: if bgroup[0] is set, group z reads its weights (one segment of
+  // N rows, stride ldb) from bgroup[z] instead of B (up to 4 groups)
+  const void* bgroup[4];
   // bf16 only: if set, B is not read; the weights are 2:4-pruned and packed
   // (mtfm_s24_pack layout) as bs24_rows stacked rows, output column n of
   // group z taking packed row z * bs24_zrows + n; run on the sparse MFMA

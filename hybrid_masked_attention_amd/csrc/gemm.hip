@@ -285,6 +285,10 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
         nn -= g.bn[0]; bseg = g.B[1]; bz = g.bz[1];
         if (nn >= g.bn[1]) { nn -= g.bn[1]; bseg = g.B[2]; bz = g.bz[2]; }
       }
+      if (g.bgroup[0]) {   // per-group weight matrices
+        bseg = z == 0 ? g.bgroup[0] : z == 1 ? g.bgroup[1] : z == 2 ? g.bgroup[2] : g.bgroup[3];
+        bz = 0;
+      }
       const bf16* base = (const bf16*)bseg + (int64_t)z * bz + (int64_t)nn * g.ldb;
       rb[i] = make_rsrc(valid ? base : (const bf16*)g.B[0], valid ? (uint32_t)(((int64_t)(valid - 1) * g.ldb + g.K) * 2) : 0u);
       boff[i] = (uint32_t)(rin * g.ldb * 2 + (slot ^ g_swz(r)) * 16);
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
           i64x2 v; v[0] = *s0; v[1] = *s1;
           const int64_t slot0 = (int64_t)mw + pass * 64 + sc * 8;
           if (slot0 < g.ldvt && nw + col < g.N)
-            *(i64x2*)((bf16*)g.vt + (col0 + col) * g.ldvt + slot0) = v;
+            *(i64x2*)((bf16*)g.vt + (int64_t)z * g.vt_zstride + (col0 + col) * g.ldvt + slot0) = v;
         }
       }
     }
@@ -997,6 +1001,11 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
         return MTFM_E_UNSUPPORTED;
       }
     }
+    if (g.bgroup[0]) {
+      if (g.bs24 || g.groups > 4 || g.bn[0] != g.N) return MTFM_E_UNSUPPORTED;
+      for (int z = 0; z < g.groups; ++z)
+        if (!g.bgroup[z]) return MTFM_E_NULL;
+    }
     if (g.epi == EPI_SILU_SPLIT) {
       for (int r = 0; r < 4; ++r) {
         if (g.cend[r] % G_WC != 0 && g.cend[r] < g.N) return MTFM_E_UNSUPPORTED;
@@ -1005,7 +1014,10 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
       if (g.pre && (!aligned16(g.pre) || g.ldpre % 8 != 0)) return MTFM_E_UNSUPPORTED;
       if (g.vt) {
         // rows map to themselves; whole 64-column wave tiles; slots up to ldvt covered by the grid
-        if (g.amap.list || g.cmap.list || g.cmap.mul != 1 || g.cmap.add != 0 || g.groups != 1) return MTFM_E_UNSUPPORTED;
+        // (groups: each its own copy at vt_zstride, covering its rows)
+        if (g.amap.list || g.cmap.list || g.cmap.mul != 1 || g.cmap.add != 0) return MTFM_E_UNSUPPORTED;
+        if (g.groups != 1 && (g.vt_zstride < (int64_t)g.vt_cols * g.ldvt || g.vt_zstride % 8 != 0))
+          return MTFM_E_UNSUPPORTED;
         if (g.vt_col0 % G_WC != 0 || g.vt_cols % G_WC != 0 || !aligned16(g.vt) || g.ldvt % 64 != 0) return MTFM_E_UNSUPPORTED;
         if (g.ldvt < g.M) return MTFM_E_UNSUPPORTED;
       }
@@ -1048,7 +1060,7 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
       default: gemm_bf16_kernel<EPI_STORE, 128, false><<<grid, 256, 0, s>>>(g); break;
     }
   } else {
-    if (g.epi == EPI_SWIGLU || g.bs24) return MTFM_E_UNSUPPORTED;
+    if (g.epi == EPI_SWIGLU || g.bs24 || g.bgroup[0] || (g.vt && g.groups != 1)) return MTFM_E_UNSUPPORTED;
     const int64_t total = (int64_t)g.M * g.N;
     gemm_f32_kernel<<<dim3((unsigned)((total + 255) / 256), 1, g.groups), 256, 0, s>>>(g);
   }

@@ -241,15 +241,19 @@ def test_small_v2_backbone_against_oracle():
     r.check()
 
 
-def test_backbone_forward_replays_from_a_hip_graph():
-    """The hoisted backbone forward, whose context stage runs on a second stream forked and joined
-    with events, captured into a HIP graph: every replay, with eager runs in between, equals the
-    eager result bit for bit."""
+@pytest.mark.parametrize("packed", [False, True])
+def test_backbone_forward_replays_from_a_hip_graph(packed):
+    """The hoisted backbone forward captured into a HIP graph: every replay, with eager runs in
+    between, equals the eager result bit for bit.  With dense weights a block's context
+    projections are one grouped launch; with packed (2:4) ones they run layer by layer, the later
+    layers' on a second stream forked and joined with events."""
     import torch
     from hybrid_masked_attention_amd import binding as B
     from hybrid_masked_attention_amd.tensors import DeviceWorkload
     wl = _small_backbone(4, 80)
     dw = DeviceWorkload(wl)
+    if packed:
+        dw.pack_s24()
     meta = B.mask_build(dw.batch)
     ws = B.workspace(dw.batch, dw.dims, B.OP_BACKBONE, k_target=wl.k_target)
 
