@@ -335,7 +335,11 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
     // lane holds half of the query's dims (kk*16 + 8hi + [0, 8)); the other half
     // is in lane ^ 32.
     if (any_self) {
-      const bf16* krow = (const bf16*)g.kd + (int64_t)qi * g.ldkd + grp * DH + 8 * hi;
+      // (the row index passes through an empty asm so that the row addresses
+      // are formed here in each pass rather than kept live across the passes)
+      int qs = qi;
+      asm volatile("" : "+v"(qs));
+      const bf16* krow = (const bf16*)g.kd + (int64_t)qs * g.ldkd + grp * DH + 8 * hi;
       float part = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
       const float ps = selfq ? (float)(bf16)silu_scaled(part) : 0.f;
       // only a T row's own value is read (and may be stored): other rows' slots
       // of the row-major V need not hold finite values
-      const bf16* vrow = (const bf16*)g.vd + (int64_t)qi * g.ldvd + grp * DH + 4 * hi;
+      const bf16* vrow = (const bf16*)g.vd + (int64_t)qs * g.ldvd + grp * DH + 4 * hi;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
