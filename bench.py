@@ -400,9 +400,8 @@ def main():
         breakdown["full_layers_masked_TFLOPs"] = layers_full * (attn_full_flops + proj_full_flops) / (full_ms * 1e-3) / 1e12
         breakdown["full_layers_mfma_frac"] = breakdown["full_layers_masked_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
         breakdown["sum_ms_per_step"] = sum(v["ms_per_step"] for v in breakdown.values() if isinstance(v, dict))
-        breakdown["note"] = ("per-class times are HIP-event spans on each kernel's own stream; the K|V projections of "
-                             "a block's target layers 1..k-1 run on a second stream beside the T-row kernels of the "
-                             "layers before them, so those spans include the sharing and the sum exceeds ms_per_step")
+        breakdown["note"] = ("per-class times are HIP-event spans around each launch; the events themselves add a "
+                             "few microseconds between launches, so the sum slightly exceeds ms_per_step")
         log("breakdown: " + json.dumps(breakdown))
 
     train = None

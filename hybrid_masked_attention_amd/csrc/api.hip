@@ -475,16 +475,12 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
 // Context stage of the target layers l = 0..k-1 of one block, right after its
 // full layer: one normalisation pass over all rows writes every layer's X~
 // (T rows as zeros: their K/V are never read as keys), then each layer's K
-// and V^T over all packed rows: with dense weights one grouped launch for the
-// k layers (more workgroups than any one layer's, so a shorter tail).
-//
-// Packed (2:4) weights go layer by layer: with a side stream, the K|V
-// projections of layers 1..k-1 go to it (after the normalisation pass) and
-// each marks event l when done, so that they overlap the T-row work of the
-// layers before them; the caller waits for mark l before layer l's T rows and
-// joins the side stream before returning.
+// and V^T over all packed rows: when the k layers' K|V weights are all dense
+// or all packed (2:4), one grouped launch (more workgroups than any one
+// layer's, so a shorter tail), else one launch per layer; with a K/V cache
+// (serving), one launch per layer into its cache entry.
 mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w, int k, const void* x,
-                               char* ws, const BackboneWs& L, const KvOut* kv = nullptr, SideStream* side = nullptr) {
+                               char* ws, const BackboneWs& L, const KvOut* kv = nullptr) {
   const MetaPlan& p = c.plan;
   const int dt = d->dtype;
   const int64_t es = elem_size(dt);
@@ -497,28 +493,26 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
     g1.y_more[l - 1] = ws + L.xt[l]; g1.gamma_more[l - 1] = w[l].ln1_g; g1.beta_more[l - 1] = w[l].ln1_b;
   }
   TRY(timed_gln(g1, dt, c.s));
-  bool dense = !kv && dt == MTFM_BF16;
-  for (int l = 0; l < k; ++l) dense = dense && !w[l].w_kv_s24;
-  if (dense) {
-    // the k layers' projections as one grouped launch: group l reads X~_l and
-    // W_kv of layer l and writes K_l and V^T_l (the buffers lie back to back)
+  int n_packed = 0;
+  for (int l = 0; l < k; ++l) n_packed += w[l].w_kv_s24 ? 1 : 0;
+  if (!kv && dt == MTFM_BF16 && (n_packed == 0 || n_packed == k)) {
+    // group l reads X~_l and layer l's weights and writes K_l and V^T_l (the
+    // buffers of the k layers lie back to back)
     GemmArgs gk{};
     gk.M = (int32_t)p.n_rows; gk.N = 2 * gd; gk.K = D; gk.groups = k;
     gk.A = ws + L.xt[0]; gk.lda = D; gk.amap = identity_map(); gk.amap_zadd = (int32_t)p.n_rows;
     gk.B[0] = w[0].w_kv; gk.bn[0] = 2 * gd; gk.ldb = D;
-    for (int l = 0; l < k; ++l) gk.bgroup[l] = w[l].w_kv;
+    if (n_packed) { gk.bs24 = w[0].w_kv_s24; gk.bs24_rows = 2 * gd; gk.bs24_zrows = 0; }
+    for (int l = 0; l < k; ++l) gk.bgroup[l] = n_packed ? w[l].w_kv_s24 : w[l].w_kv;
     gk.cmap = identity_map(); gk.cmap_zadd = (int32_t)p.n_rows;
     gk.epi = EPI_SILU_SPLIT;
     gk.dst[0] = ws + L.k[0]; gk.ld[0] = gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
     gk.dst[1] = nullptr; gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd; gk.scale[1] = 1.f;
     gk.vt = ws + L.vt[0]; gk.ldvt = L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
-    gk.vt_zstride = (L.vt[k > 1 ? 1 : 0] - L.vt[0]) / es;
-    if (k == 1) gk.vt_zstride = 0;
+    gk.vt_zstride = k > 1 ? (L.vt[1] - L.vt[0]) / es : 0;
     return timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s);
   }
-  if (side && k > 1) TRY(side->fork(c.s));
   for (int l = 0; l < k; ++l) {
-    const hipStream_t st = (side && l > 0) ? side->side : c.s;
     GemmArgs gk{};
     gk.M = (int32_t)p.n_rows; gk.N = 2 * gd; gk.K = D; gk.groups = 1;
     gk.A = ws + L.xt[l]; gk.lda = D; gk.amap = identity_map();
@@ -529,9 +523,7 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
     gk.dst[0] = kv ? kv[l].k : ws + L.k[l]; gk.ld[0] = gd; gk.cend[0] = gd; gk.scale[0] = 1.f;
     gk.dst[1] = nullptr; gk.cend[1] = gk.cend[2] = gk.cend[3] = 2 * gd; gk.scale[1] = 1.f;
     gk.vt = kv ? kv[l].vt : ws + L.vt[l]; gk.ldvt = kv ? kv[l].ldvt : L.ldvt; gk.vt_col0 = gd; gk.vt_cols = gd;
-    TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, st));
-    if (side && l > 0) TRY(side->mark(l));
-    (void)es;
+    TRY(timed_gemm(MTFM_K_GEMM_KV, gk, dt, c.s));
   }
   return MTFM_OK;
 }
@@ -1043,29 +1035,14 @@ mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, in
   if (hoist) {
     const BackboneWs L = backbone_ws(c.plan, dims, k_target);
     char* w = (char*)ws;
-    // packed K|V projections run layer by layer, a block's later ones on a
-    // second stream beside the T-row work of its earlier ones (each layer
-    // waits for its own); dense ones are one grouped launch per block
-    SideStream* side = nullptr;
-    bool packed_kv = false;
-    for (int b = 0; b < n_blocks * k_target; ++b) packed_kv = packed_kv || tgt[b].w_kv_s24;
-    if (k_target > 1 && packed_kv) TRY(side_stream(&side));
-    mtfm_status st = MTFM_OK;
-    for (int b = 0; b < n_blocks && st == MTFM_OK; ++b) {
-      st = run_full(c, dims, &full[b], x_inout, x_inout, w + L.full);
+    for (int b = 0; b < n_blocks; ++b) {
+      TRY(run_full(c, dims, &full[b], x_inout, x_inout, w + L.full));
       const mtfm_target_w* tw = &tgt[b * k_target];
-      if (st != MTFM_OK || c.plan.n_t_rows == 0) continue;   // target layers change T rows only
-      st = run_target_context(c, dims, tw, k_target, x_inout, w, L, nullptr, side);
-      for (int t = 0; t < k_target && st == MTFM_OK; ++t) {
-        if (side && t > 0) st = side->wait_mark(c.s, t);
-        if (st == MTFM_OK) st = run_target_rows(c, dims, &tw[t], x_inout, w, L, t);
-      }
+      if (c.plan.n_t_rows == 0) continue;   // target layers change T rows only
+      TRY(run_target_context(c, dims, tw, k_target, x_inout, w, L));
+      for (int t = 0; t < k_target; ++t) TRY(run_target_rows(c, dims, &tw[t], x_inout, w, L, t));
     }
-    if (side) {
-      const mtfm_status js = side->join(c.s);   // also after a failure: nothing of this call stays on the side
-      if (st == MTFM_OK) st = js;
-    }
-    return st;
+    return MTFM_OK;
   }
   for (int b = 0; b < n_blocks; ++b) {
     TRY(run_full(c, dims, &full[b], x_inout, x_inout, (char*)ws));

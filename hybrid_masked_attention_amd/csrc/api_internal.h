@@ -113,22 +113,6 @@ mtfm_status serve_targets_run(const Ctx& c, const mtfm_dims* dims, int32_t n_blo
                               const mtfm_full_w* full, const mtfm_target_w* tgt, const void* kv_cache, void* x_t,
                               char* ws);
 
-// A second stream of the current device for work that may overlap the
-// caller's stream (default priority, non-blocking), with events to fork and
-// join; one per host thread and device, created on first use and kept until
-// the process ends.  fork(): the side stream waits for everything enqueued on
-// `main` so far.  mark(i) / wait_mark(i): event i recorded on the side stream,
-// `main` waits for it.  join(): `main` waits for all side work.
-struct SideStream {
-  hipStream_t side = nullptr;
-  hipEvent_t ev[5] = {};
-  mtfm_status fork(hipStream_t main);
-  mtfm_status mark(int i);
-  mtfm_status wait_mark(hipStream_t main, int i);
-  mtfm_status join(hipStream_t main);
-};
-mtfm_status side_stream(SideStream** out);
-
 // Launch helpers that time themselves under a kernel class.
 inline mtfm_status timed_gemm(int kclass, const GemmArgs& g, int dt, hipStream_t s) {
   TimedLaunch t(kclass, s);

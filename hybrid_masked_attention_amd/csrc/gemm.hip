@@ -381,13 +381,18 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
     // packed weights: slice (step, row, half) of this lane's output column in
     // each 32-column block; columns past N repeat row N - 1 (never stored)
     const char* wvals = (const char*)g.bs24;
+    int64_t zrows = g.bs24_zrows;
+    if (g.bgroup[0]) {   // per-group packed matrices
+      wvals = (const char*)(z == 0 ? g.bgroup[0] : z == 1 ? g.bgroup[1] : z == 2 ? g.bgroup[2] : g.bgroup[3]);
+      zrows = 0;
+    }
     const int64_t wrows = g.bs24_rows;
     const char* widx = wvals + wrows * g.K;
     int64_t wslice[G_TN];
 #pragma unroll
     for (int b = 0; b < G_TN; ++b) {
       const int n = min(n0 + wn * G_WC + b * 32 + l32, g.N - 1);
-      wslice[b] = ((int64_t)z * g.bs24_zrows + n) * 2 + hi;
+      wslice[b] = ((int64_t)z * zrows + n) * 2 + hi;
     }
     bf16x8 wv[S24_WS][G_TN];
     int wi[S24_WS][G_TN];
@@ -1002,9 +1007,12 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
       }
     }
     if (g.bgroup[0]) {
-      if (g.bs24 || g.groups > 4 || g.bn[0] != g.N) return MTFM_E_UNSUPPORTED;
-      for (int z = 0; z < g.groups; ++z)
+      // per-group weights: dense matrices of N rows, or packed ones of bs24_rows rows
+      if (g.groups > 4 || g.bn[0] != g.N || (g.bs24 && g.bs24_zrows != 0)) return MTFM_E_UNSUPPORTED;
+      for (int z = 0; z < g.groups; ++z) {
         if (!g.bgroup[z]) return MTFM_E_NULL;
+        if (g.bs24 && !aligned16(g.bgroup[z])) return MTFM_E_UNSUPPORTED;
+      }
     }
     if (g.epi == EPI_SILU_SPLIT) {
       for (int r = 0; r < 4; ++r) {

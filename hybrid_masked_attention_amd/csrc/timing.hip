@@ -90,52 +90,3 @@ extern "C" mtfm_status mtfm_timing_read(int32_t kernel_class, int64_t* launches,
   *total_ms = sum;
   return status;
 }
-
-// ---------------------------------------------------------------------------
-// Side streams (see api_internal.h).
-
-namespace {
-constexpr int kMaxDevices = 64;
-thread_local SideStream* g_side[kMaxDevices] = {};
-}  // namespace
-
-mtfm_status side_stream(SideStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return MTFM_E_UNSUPPORTED;
-  if (!g_side[dev]) {
-    SideStream* ss = new SideStream;
-    e = hipStreamCreateWithFlags(&ss->side, hipStreamNonBlocking);
-    for (int i = 0; e == hipSuccess && i < 5; ++i) e = hipEventCreateWithFlags(&ss->ev[i], hipEventDisableTiming);
-    if (e != hipSuccess) {
-      delete ss;   // the created handles stay with the runtime until the process ends
-      return hip_fail(e, "side stream");
-    }
-    g_side[dev] = ss;
-  }
-  *out = g_side[dev];
-  return MTFM_OK;
-}
-
-mtfm_status SideStream::fork(hipStream_t main) {
-  hipError_t e = hipEventRecord(ev[4], main);
-  if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[4], 0);
-  return e == hipSuccess ? MTFM_OK : hip_fail(e, "side stream fork");
-}
-
-mtfm_status SideStream::mark(int i) {
-  hipError_t e = hipEventRecord(ev[i], side);
-  return e == hipSuccess ? MTFM_OK : hip_fail(e, "side stream mark");
-}
-
-mtfm_status SideStream::wait_mark(hipStream_t main, int i) {
-  hipError_t e = hipStreamWaitEvent(main, ev[i], 0);
-  return e == hipSuccess ? MTFM_OK : hip_fail(e, "side stream wait");
-}
-
-mtfm_status SideStream::join(hipStream_t main) {
-  hipError_t e = hipEventRecord(ev[4], side);
-  if (e == hipSuccess) e = hipStreamWaitEvent(main, ev[4], 0);
-  return e == hipSuccess ? MTFM_OK : hip_fail(e, "side stream join");
-}

@@ -273,14 +273,8 @@ mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, in
  * changes H or R rows); each target layer then normalises only its T rows.
  * That needs this much workspace; with less (but at least
  * mtfm_workspace_bytes(batch, dims, MTFM_OP_BACKBONE)) the layers run one by
- * one.  Both orders compute the same values.  In the first order, with
- * packed (2:4) K/V weights, the K/V projections of a block's later target
- * layers run on a second stream that the library owns (one per host thread
- * and device, default priority; dense weights stay on `stream`): it
- * waits on `stream` with events before starting, and `stream` waits for each
- * projection before the layer that reads it and for all of them before the
- * call returns, so the call stays ordered on `stream` (also under HIP graph
- * capture, as event-joined work).  Returns 0 on invalid arguments.
+ * one.  Both orders compute the same values, and everything runs on
+ * `stream`.  Returns 0 on invalid arguments.
  * Host only. */
 size_t mtfm_backbone_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t k_target);
 

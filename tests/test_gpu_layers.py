@@ -244,9 +244,8 @@ def test_small_v2_backbone_against_oracle():
 @pytest.mark.parametrize("packed", [False, True])
 def test_backbone_forward_replays_from_a_hip_graph(packed):
     """The hoisted backbone forward captured into a HIP graph: every replay, with eager runs in
-    between, equals the eager result bit for bit.  With dense weights a block's context
-    projections are one grouped launch; with packed (2:4) ones they run layer by layer, the later
-    layers' on a second stream forked and joined with events."""
+    between, equals the eager result bit for bit, with dense and with packed (2:4) weights (each
+    block's context projections one grouped launch over per-layer weight matrices)."""
     import torch
     from hybrid_masked_attention_amd import binding as B
     from hybrid_masked_attention_amd.tensors import DeviceWorkload
@@ -263,7 +262,7 @@ def test_backbone_forward_replays_from_a_hip_graph(packed):
         torch.cuda.synchronize()
         return x
 
-    ref = eager()          # also creates the library's second stream before the capture
+    ref = eager()
     xg = dw.x.clone()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
