@@ -217,11 +217,12 @@ def _small_backbone(split, seed, n_blocks=2, k_target=3):
                           n_blocks=n_blocks, k_target=k_target)
 
 
-@pytest.mark.parametrize("split", [1, 4])
-def test_backbone_context_stage_matches_layer_by_layer(split):
+@pytest.mark.parametrize("split,k_target", [(1, 3), (4, 3), (1, 1), (1, 2), (4, 4)])
+def test_backbone_context_stage_matches_layer_by_layer(split, k_target):
     """The block-level context stage (one normalisation pass and the K/V of all target layers
-    right after the full layer) computes bit-identical outputs to running the layers one by one."""
-    wl = _small_backbone(split, 60 + split)
+    right after the full layer, one grouped projection launch) computes bit-identical outputs to
+    running the layers one by one, for 1 to 4 target layers per block."""
+    wl = _small_backbone(split, 60 + split + 10 * k_target, k_target=k_target)
     _, a = _backbone_gpu(wl, hoist=True)
     _, b = _backbone_gpu(wl, hoist=False)
     assert np.all(np.isfinite(a))
