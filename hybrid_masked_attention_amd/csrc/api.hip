@@ -329,7 +329,7 @@ mtfm_status run_full(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w, con
   aa.q = z + hd * es; aa.ldq = zw;
   aa.k = z + 2 * hd * es; aa.ldk = zw;
   aa.v = z + (2 * hd + gd) * es; aa.ldv = zw;
-  aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows;
+  aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows; aa.max_user_rows = p.max_user_rows;
   aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
   if (kv) {
     aa.k = kv->k; aa.ldk = gd; aa.v = nullptr; aa.ldv = 0;
@@ -437,7 +437,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   aa.q = zt + hd * es; aa.ldq = zw;
   aa.k = kv; aa.ldk = 2 * gd;
   aa.v = kv + gd * es; aa.ldv = 2 * gd;
-  aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows;
+  aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows; aa.max_user_rows = p.max_user_rows;
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
@@ -572,7 +572,7 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   aa.q = zt + hd * es; aa.ldq = zw;
   aa.k = ws + L.k[l]; aa.ldk = gd;
   aa.v = nullptr; aa.ldv = 0;
-  aa.vt = ws + L.vt[l]; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows;
+  aa.vt = ws + L.vt[l]; aa.ldvt = L.ldvt; aa.n_key_rows = (int32_t)p.n_rows; aa.max_user_rows = p.max_user_rows;
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;
@@ -796,7 +796,7 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   aa.q = zt + hd * es; aa.ldq = zw;
   aa.k = kv.k; aa.ldk = gd;
   aa.v = nullptr; aa.ldv = 0;
-  aa.vt = kv.vt; aa.ldvt = kv.ldvt; aa.n_key_rows = (int32_t)p.n_ctx_rows;
+  aa.vt = kv.vt; aa.ldvt = kv.ldvt; aa.n_key_rows = (int32_t)p.n_ctx_rows; aa.max_user_rows = p.max_user_rows;
   aa.kd = zt + 2 * hd * es; aa.ldkd = zw;
   aa.vd = zt + (2 * hd + gd) * es; aa.ldvd = zw;
   aa.a = a; aa.lda = hd;

@@ -25,6 +25,7 @@ struct AttnArgs {
   // ldvt a multiple of 64 covering every packed row, slots past the last row zero
   const void* vt; int64_t ldvt;
   int32_t n_key_rows;            // packed rows in k (rows past it read as zero)
+  int32_t max_user_rows;         // bf16 path: most packed rows of one user (bounds one user's K resource)
   const void* kd; int64_t ldkd;  // the query rows' own keys / values (query space)
   const void* vd; int64_t ldvd;
   void* a; int64_t lda;          // output [query row][H*dh]; optional on the bf16 path (nullptr: not written)

@@ -552,8 +552,12 @@ mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
     if (((uintptr_t)a.k | (uintptr_t)a.vt | (uintptr_t)a.kd | (uintptr_t)a.vd) & 15) return MTFM_E_UNSUPPORTED;
     if (a.ldk % 8 != 0 || a.ldkd % 8 != 0 || a.ldvd % 8 != 0 || a.ldq % 8 != 0 || a.lda % 4 != 0 || ((uintptr_t)a.a & 7))
       return MTFM_E_UNSUPPORTED;
-    // 32-bit buffer offsets: the whole V^T and one 64-row K tile
-    if ((int64_t)a.G * 64 * a.ldvt * 2 >= (int64_t)1 << 32 || 64 * a.ldk * 2 >= (int64_t)1 << 31) return MTFM_E_UNSUPPORTED;
+    // 32-bit buffer offsets: the whole V^T and one user's K rows (with a tile's
+    // reach below the user's first row)
+    if ((int64_t)a.G * 64 * a.ldvt * 2 >= (int64_t)1 << 32 ||
+        ((int64_t)max(a.max_user_rows, 0) + 64) * a.ldk * 2 >= (int64_t)1 << 31)
+      return MTFM_E_UNSUPPORTED;
+    if (a.max_user_rows <= 0) return MTFM_E_UNSUPPORTED;
     if (a.per_group && a.y) return MTFM_E_UNSUPPORTED;   // the gated epilogue needs every head of a row
     if (a.order && (a.n_order <= 0 || a.n_order % 8 != 0)) return MTFM_E_UNSUPPORTED;
     if (!a.qperm != !a.gperm) return MTFM_E_UNSUPPORTED;

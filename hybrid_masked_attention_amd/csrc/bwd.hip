@@ -159,7 +159,7 @@ mtfm_status run_full_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* w,
     {
       AttnArgs aa{};
       aa.q = z + hd; aa.ldq = zw; aa.k = z + 2 * hd; aa.ldk = zw; aa.v = z + 2 * hd + gd; aa.ldv = zw;
-      aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
+      aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R; aa.max_user_rows = p.max_user_rows;
       aa.kd = aa.k; aa.ldkd = zw; aa.vd = aa.v; aa.ldvd = zw;
       aa.a = a; aa.lda = hd;
       aa.tiles = c.meta.full_tiles; aa.ntiles = (int32_t)p.n_full_tiles;
@@ -313,7 +313,7 @@ mtfm_status run_target_bwd(const Ctx& c, const mtfm_dims* d, const mtfm_target_w
     {
       AttnArgs aa{};
       aa.q = zt + hd; aa.ldq = zw; aa.k = kv; aa.ldk = 2 * gd; aa.v = kv + gd; aa.ldv = 2 * gd;
-      aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R;
+      aa.vt = ws + L.vt; aa.ldvt = L.ldvt; aa.n_key_rows = R; aa.max_user_rows = p.max_user_rows;
       aa.kd = zt + 2 * hd; aa.ldkd = zw; aa.vd = zt + 2 * hd + gd; aa.ldvd = zw;
       aa.a = a; aa.lda = hd;
       aa.tiles = c.meta.target_tiles; aa.ntiles = (int32_t)p.n_target_tiles;
