@@ -96,6 +96,27 @@ def dense_mask_fast(l_h, l_r, l_t, split, ts_r, ts_t):
 
 
 
+def mask_row(i: int, l_h: int, l_r: int, l_t: int, split: int, ts_r, ts_t) -> np.ndarray:
+    """Row i of the user's mask (the keys query token i sees), 0/1 of length N.
+
+    The rules of `visible` for one query against every key at once, for users
+    too long to hold the N x N matrix.
+    """
+    n = l_h + l_r + split * l_t
+    lc = l_h + l_r
+    row = np.zeros(n, bool)
+    kind = _kind(i, l_h, l_r)
+    row[:l_h] = True                            # every query sees every H key
+    if kind == R_TYPE:
+        row[l_h:i + 1] = True                   # R keys up to and including itself
+    elif kind == T_TYPE:
+        e_t = int(ts_t[(i - lc) // split])      # the parent target's exposure time
+        if l_r:
+            row[l_h:lc] = np.asarray(ts_r, np.int64) < e_t
+        row[i] = True                           # itself, the only T key it sees
+    return row.astype(np.uint8)
+
+
 def row_types(l_h: int, l_r: int, l_t: int, split: int) -> np.ndarray:
     n = l_h + l_r + split * l_t
     return np.array([_kind(i, l_h, l_r) for i in range(n)], dtype=np.uint8)

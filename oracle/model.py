@@ -91,6 +91,30 @@ def full_layer_user(x, m, types, w: Dict[str, np.ndarray], dims, return_parts=Fa
     return out
 
 
+def full_layer_rows(x, l_h, l_r, l_t, split, ts_r, ts_t, w: Dict[str, np.ndarray], dims, rows):
+    """Selected rows of one user's full-attention layer ([explainer] §4.1).
+
+    The equations of `full_layer_user` for the query rows `rows` only, each
+    row's mask from `mask.mask_row`: for users too long for an N x N mask.
+    K and V are projected for every row of the user (any of them may be a
+    key); U and Q for the selected rows.
+    """
+    x = np.asarray(x, np.float64)
+    rows = np.asarray(rows, np.int64)
+    hd, gd = dims.n_q_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
+    types = _mask.row_types(l_h, l_r, l_t, split)
+    xt = gln(x, w["ln1_g"], w["ln1_b"], types, dims.ln_eps)
+    w1 = np.asarray(w["w_uqkv"], np.float64)
+    kv = silu(xt @ w1[2 * hd:2 * hd + 2 * gd].T)
+    k, v = kv[:, :gd], kv[:, gd:]
+    uq = silu(xt[rows] @ w1[:2 * hd].T)
+    u, q = uq[:, :hd], uq[:, hd:]
+    m = np.stack([_mask.mask_row(int(i), l_h, l_r, l_t, split, ts_r, ts_t) for i in rows])
+    a = masked_attention(q, k, v, m, dims.n_q_heads, dims.n_kv_heads, dims.head_dim)
+    y = gln(a, w["ln2_g"], w["ln2_b"], types[rows], dims.ln_eps) * u
+    return y @ np.asarray(w["w_o"], np.float64).T + x[rows]
+
+
 def target_layer_user(x, m, types, l_ctx, split, w: Dict[str, np.ndarray], dims, return_parts=False):
     """One user's target-attention layer ([explainer] §4.2; V2 per-sub-token Q, [blog] §3.3.2)."""
     x = np.asarray(x, np.float64)

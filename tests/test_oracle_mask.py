@@ -207,3 +207,22 @@ def test_batch_meta_tile_tables_hand_derived():
         [0, 0, 2, 1, 2], [0, 2, 2, 1, 2], [0, 4, 2, 3, 3], [0, 6, 1, 3, 3],
         [1, 0, 2, 1, 1], [1, 2, 2, 1, 2], [1, 4, 2, 2, 3], [1, 6, 1, 1, 1]])
     np.testing.assert_array_equal(meta["target_tiles"], [[0, 5, 2, 3, 3], [1, 5, 2, 1, 2]])
+
+
+def test_mask_row_equals_enumerated_mask():
+    """mask_row restates the rules one query at a time: row for row it equals the
+    pure-Python enumeration (timestamp ties, empty parts, V2 split 3)."""
+    rng = np.random.default_rng(11)
+    checked = 0
+    for trial in range(80):
+        split = (1, 3)[trial % 2]
+        l_h, l_r, l_t = (int(v) for v in rng.integers(0, 6, size=3))
+        if l_h + l_r + l_t == 0:
+            continue
+        ts_r = np.sort(rng.integers(0, 5, size=l_r))
+        ts_t = rng.integers(0, 5, size=l_t)
+        m = om.dense_mask(l_h, l_r, l_t, split, ts_r, ts_t)
+        for i in range(m.shape[0]):
+            np.testing.assert_array_equal(om.mask_row(i, l_h, l_r, l_t, split, ts_r, ts_t), m[i])
+            checked += 1
+    assert checked > 300

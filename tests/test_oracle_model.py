@@ -251,3 +251,16 @@ def test_backbone_keeps_context_rows_through_target_layers():
     np.testing.assert_array_equal(out[:9], after_full[:9])
     t1 = om_model.target_layer_user(after_full, m, types, 9, 1, wt, dims)
     np.testing.assert_allclose(out, om_model.target_layer_user(t1, m, types, 9, 1, wt, dims), rtol=1e-13)
+
+
+@pytest.mark.parametrize("lens,split", [((9, 7, 4), 1), ((5, 0, 3), 3), ((12, 6, 0), 1), ((1, 1, 1), 1), ((0, 4, 2), 2)])
+def test_full_layer_rows_equals_dense_full_layer(lens, split):
+    """full_layer_rows (per-row masks, selected query rows) gives the rows of the dense full layer."""
+    rng = np.random.default_rng(12)
+    b, dims, x, wf, _ = small_workload(rng, [lens], split)
+    l_h, l_r, l_t = lens
+    m = om.dense_mask(l_h, l_r, l_t, split, b.ts_r, b.ts_t)
+    ref = om_model.full_layer_user(x, m, om.row_types(l_h, l_r, l_t, split), wf, dims)
+    rows = rng.permutation(x.shape[0])[:max(1, x.shape[0] // 2)]
+    got = om_model.full_layer_rows(x, l_h, l_r, l_t, split, b.ts_r, b.ts_t, wf, dims, rows)
+    np.testing.assert_allclose(got, ref[rows], rtol=1e-12, atol=1e-12)
