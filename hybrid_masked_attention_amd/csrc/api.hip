@@ -31,7 +31,10 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // Entries of a layer's attention work order: 8 x the longest XCD list, from
 // the same ranking and dealing the device performs (users by estimated work,
-// descending, ties by index; rank r goes to XCD order_xcd(r)).
+// descending, ties by index; rank r goes to XCD order_xcd(r)).  0 (no order:
+// the kernels keep the XCD-contiguous one, which splits a long user over
+// several XCDs) when the dealing would load some XCD with more than 1.25 x
+// the mean work, as with a few users or one user far longer than the rest.
 static int64_t order_entries(const int32_t* lens, int n_users, int split, int layer) {
   if (n_users <= 0 || n_users > kOrderMaxUsers) return 0;
   std::vector<int64_t> work(n_users);
@@ -41,8 +44,13 @@ static int64_t order_entries(const int32_t* lens, int n_users, int split, int la
     idx[u] = u;
   }
   std::sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return work[a] != work[b] ? work[a] > work[b] : a < b; });
-  int64_t count[8] = {};
-  for (int r = 0; r < n_users; ++r) count[order_xcd(r)] += order_slices(lens, idx[r], split, layer);
+  int64_t count[8] = {}, load[8] = {}, total = 0;
+  for (int r = 0; r < n_users; ++r) {
+    count[order_xcd(r)] += order_slices(lens, idx[r], split, layer);
+    load[order_xcd(r)] += work[idx[r]];
+    total += work[idx[r]];
+  }
+  if (4 * 8 * *std::max_element(load, load + 8) > 5 * total) return 0;
   return 8 * *std::max_element(count, count + 8);
 }
 mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan) {

@@ -118,7 +118,8 @@ MTFM_DEV int upper_index(const int32_t* off, int n, int x) {
 // with the same integer arithmetic the device uses to write the order.
 #define MTFM_HD __host__ __device__ __forceinline__
 
-constexpr int kOrderMaxUsers = 2048;   // larger batches keep the plain XCD-contiguous order
+constexpr int kOrderMaxUsers = 2048;   // larger batches keep the plain XCD-contiguous order (as do
+                                        // batches the dealing would leave unbalanced)
 constexpr int kTSortMaxRows = 4096;    // users with more T rows keep their own order
 enum OrderLayer { OL_FULL = 0, OL_TARGET = 1 };
 

@@ -6,7 +6,9 @@ index), dealt to the XCDs in a boustrophedon 0..7, 7..0, ..., every XCD's
 users in rank order and each user's slices last first.  Entry 8 k + x of the
 order is the slice id (2 tile + half) that XCD x takes k-th, -1 past the end
 of its list; the array holds 8 x the longest list.  Batches of more than 2048
-users have no order (the kernels keep the XCD-contiguous one).
+users have no order (the kernels keep the XCD-contiguous one), nor have those
+whose dealing would give some XCD more than 1.25 x the mean work (a few users,
+or one far longer than the rest: that user's slices would all sit on one XCD).
 
 This is scheduling, not the method's arithmetic: any order that lists every
 non-empty slice once gives the same attention output, which the parity tests
@@ -46,10 +48,25 @@ def xcd_of_rank(r):
     return 7 - r % 8 if (r // 8) % 2 else r % 8
 
 
+def xcd_loads(lens, split, layer):
+    """Work the dealing gives each XCD."""
+    lens = np.asarray(lens, np.int64).reshape(-1, 3)
+    work = user_work(lens, split, layer)
+    loads = np.zeros(8, np.int64)
+    for r, u in enumerate(sorted(range(len(lens)), key=lambda u: (-work[u], u))):
+        loads[xcd_of_rank(r)] += work[u]
+    return loads
+
+
+def balanced(lens, split, layer):
+    loads = xcd_loads(lens, split, layer)
+    return 4 * 8 * int(loads.max()) <= 5 * int(loads.sum())
+
+
 def expected_order(lens, split, layer):
     lens = np.asarray(lens, np.int64).reshape(-1, 3)
     n = len(lens)
-    if n == 0 or n > MAX_USERS:
+    if n == 0 or n > MAX_USERS or not balanced(lens, split, layer):
         return np.zeros(0, np.int32)
     work = user_work(lens, split, layer)
     ns = slices(lens, split, layer)

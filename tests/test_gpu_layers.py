@@ -132,6 +132,52 @@ def test_many_users_with_and_without_work_order(n_users):
     _compare(wl, "target", _run_layer(wl, "target"), TOL_BF16)
 
 
+
+def test_longest_user_within_the_key_offset_bound():
+    """The longest user the bf16 attention takes at d 1024 with 16 query and 16 KV heads (8 KB
+    of U|Q|K|V per packed row): 262,000 rows, whose keys span 2.15e9 bytes of the K buffer the
+    kernel addresses through 32-bit offsets from the user's first row.  Behind a 60-row user (so
+    the long user starts mid-tile), its sampled rows against the oracle; one row more than the
+    bound allows (262,100) is refused with MTFM_E_UNSUPPORTED before the attention launch."""
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    rng = np.random.default_rng(93)
+    dims = synth.Dims(1024, 16, 16, 64)
+    l_h, l_r, l_t = 200_000, 61_992, 8
+    batch = synth.make_batch(rng, np.array([[37, 20, 3], [l_h, l_r, l_t]], np.int32), 1)
+    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
+    wl = synth.Workload("longest_user", batch, dims, "bf16", x, full=[synth.full_weights(rng, dims, 0.02, 0.02)])
+    x_dev, out_dev, _, _ = _run_layer(wl, "full")
+    xr, full, _ = rounded_inputs(wl)
+    np.testing.assert_array_equal(x_dev, xr)
+    off = batch.row_off
+    r = Report(TOL_BF16)
+    r.close("X' (60-row user)", out_dev[off[0]:off[1]], om.full_layer(batch.subset([0]), xr[off[0]:off[1]], full[0], dims))
+    # first and last rows of each part and of 64-row tiles, and the T rows
+    sel = np.array([0, 1, 63, 64, 131_071, l_h - 1, l_h, l_h + 1, l_h + 31_000, l_h + l_r - 1] +
+                   list(range(l_h + l_r, l_h + l_r + l_t)))
+    say(f"  oracle on {len(sel)} rows of the {l_h + l_r + l_t}-row user")
+    ts_r = batch.ts_r[batch.r_off[1]:batch.r_off[2]]
+    ts_t = batch.ts_t[batch.t_off[1]:batch.t_off[2]]
+    ref = om.full_layer_rows(xr[off[1]:off[2]], l_h, l_r, l_t, 1, ts_r, ts_t, full[0], dims, sel)
+    r.close("X' (262,000-row user, sampled rows)", out_dev[off[1] + sel], ref)
+    r.branch("dX (262,000-row user, sampled rows)", out_dev[off[1] + sel], ref, xr[off[1] + sel], "bf16")
+    r.check()
+    del x_dev, out_dev, xr, x
+    torch.cuda.empty_cache()
+
+    over = synth.make_batch(rng, np.array([[262_100, 0, 0]], np.int32), 1)
+    wl2 = synth.Workload("over_the_bound", over, dims, "bf16", np.zeros((over.total_rows, dims.d_model), np.float32),
+                         full=[wl.full[0]])
+    dw = DeviceWorkload(wl2)
+    meta = B.mask_build(dw.batch)
+    ws = B.workspace(dw.batch, dw.dims, B.OP_FULL)
+    with pytest.raises(B.MtfmError) as e:
+        B.attn_full(dw.batch, dw.dims, meta, dw.full[0], dw.x, torch.empty_like(dw.x), ws)
+    assert e.value.status == B.E_UNSUPPORTED
+
+
 def test_fp32_head_dim_64_and_gqa_ratio_1():
     dims = synth.Dims(128, 2, 2, 64)
     wl = _small_workload([[20, 9, 4], [70, 3, 1]], 1, "f32", 51, dims=dims, w_std=0.1)

@@ -65,7 +65,7 @@ def test_rule_properties(name, batch, layer):
     lens = batch.lens.astype(np.int64)
     order = _order.expected_order(lens, batch.split, layer)
     if len(order) == 0:
-        assert batch.n_users == 0
+        assert batch.n_users == 0 or not _order.balanced(lens, batch.split, layer)
         return
     ns = _order.slices(lens, batch.split, layer)
     tiles = (ns + 1) // 2
@@ -93,3 +93,21 @@ def test_rule_properties(name, batch, layer):
         loads.append(int(sum(work[u] for u in seq)))
     if len(lens) >= 8:
         assert max(loads) - min(loads) <= int(work.max())
+
+
+def test_unbalanced_dealing_keeps_the_plain_order(B):
+    """A few users, or one user far longer than the rest, would put most of the work on one or
+    two XCDs: such batches get no order (the kernels' XCD-contiguous order spreads the long user's
+    slices over all of them); the benchmarked configurations keep theirs."""
+    rng = np.random.default_rng(5)
+    lopsided = np.array([[37, 20, 3], [200000, 61992, 8]], np.int32)
+    few = np.array([[1000, 200, 20]] * 4, np.int32)
+    one_long = np.concatenate([np.array([[3000, 500, 40]], np.int32), np.tile([[40, 10, 2]], (60, 1)).astype(np.int32)])
+    for lens in (lopsided, few, one_long):
+        batch = synth.make_batch(rng, lens, 1)
+        lay = _layout(B, batch)
+        assert lay.n_full_order == 0 and lay.n_target_order == 0, lens[:3]
+        assert not _order.balanced(lens, 1, _order.FULL)
+    for batch in (synth.config1().batch, synth.config3(weights=False).batch, synth.config4(arrays=False).batch):
+        lay = _layout(B, batch)
+        assert lay.n_full_order > 0 and lay.n_target_order > 0
