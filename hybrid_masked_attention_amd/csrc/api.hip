@@ -74,6 +74,7 @@ mtfm_status plan_meta(const mtfm_batch* b, MetaPlan* plan) {
     p.n_key_tiles += (lh + lr + kTile - 1) / kTile;
     p.max_user_rows = (int32_t)std::min<int64_t>(std::max<int64_t>(p.max_user_rows, rows), INT32_MAX);
     p.max_t_rows = (int32_t)std::min<int64_t>(std::max<int64_t>(p.max_t_rows, b->split * lt), INT32_MAX);
+    p.max_ctx_rows = (int32_t)std::min<int64_t>(std::max<int64_t>(p.max_ctx_rows, lh + lr), INT32_MAX);
     if (p.n_rows > INT32_MAX - 4096) return MTFM_E_DIMS;
   }
   p.n_full_order = order_entries(b->lens_h, b->n_users, b->split, OL_FULL);
@@ -168,14 +169,31 @@ LayerWs layer_ws(const MetaPlan& p, const mtfm_dims* d, int op) {
   return w;
 }
 
+// Key splits of the per-group target attention on the inference paths.  Its
+// grid is (32-row T slice, KV group): with few T rows against long contexts
+// (a request of one user with a long history) it fills few of the ~1,024
+// workgroup slots (256 CUs x 4) while each workgroup walks a whole context.
+// A is a plain sum over keys divided by n, so a slice's key tiles can be
+// split over ks workgroups whose fp32 partials the gated LayerNorm adds.  ks
+// fills the slots, leaves each run at least 8 key tiles of the longest
+// context, and stays at most 16 with the partials within 16 MiB (1: none).
+static int target_key_splits(const MetaPlan& p, const mtfm_dims* d) {
+  if (d->dtype != MTFM_BF16 || p.n_t_rows == 0) return 1;
+  const int64_t wgs = std::max<int64_t>(2 * p.n_target_tiles * d->n_kv_heads, 1);
+  const int64_t part = std::max<int64_t>(p.n_t_rows * (int64_t)d->n_q_heads * d->head_dim * 4, 1);
+  const int64_t ks = std::min<int64_t>({1024 / wgs, ((int64_t)p.max_ctx_rows + 63) / 64 / 8, 16, ((int64_t)16 << 20) / part});
+  return ks >= 2 ? (int)ks : 1;
+}
+
 // Workspace of the backbone with the target layers' context stage hoisted
 // (bf16): the full layer's workspace, then per target layer of a block its
 // normalised rows X~ [R][d], K [R][G*dh] and V^T [G*dh][ldvt], then the T-row
-// buffers shared by the target layers.
+// buffers shared by the target layers (with key splits, the fp32 partials of A).
 struct BackboneWs {
   int64_t full = 0;
   int64_t xt[4] = {}, k[4] = {}, vt[4] = {};
-  int64_t xtt = 0, zt = 0, a = 0, y = 0;
+  int64_t xtt = 0, zt = 0, a = 0, y = 0, apart = 0;
+  int32_t ksplit = 1;
   int64_t ldvt = 0, total = 0;
 };
 
@@ -201,6 +219,8 @@ BackboneWs backbone_ws(const MetaPlan& p, const mtfm_dims* d, int k_target) {
   w.zt = take(p.n_t_rows * zw * es);
   w.a = take(p.n_t_rows * hd * es);
   w.y = take(p.n_t_rows * hd * es);
+  w.ksplit = target_key_splits(p, d);
+  w.apart = take(w.ksplit > 1 ? w.ksplit * p.n_t_rows * hd * 4 : 0);
   w.total = off;
   return w;
 }
@@ -271,10 +291,12 @@ static void fuse_gated_gln(AttnArgs& aa, const Ctx& c, const mtfm_dims* d, const
 // workgroup per KV group and the normalisation, which needs every head of a
 // row, follows as a pass over the T rows alone.
 static mtfm_status target_gated_gln(const Ctx& c, const mtfm_dims* d, const float* g2, const float* b2,
-                                    const void* a, const void* u, int64_t ldu, void* y, int dt) {
+                                    const void* a, const void* u, int64_t ldu, void* y, int dt,
+                                    const float* parts = nullptr, int n_parts = 0) {
   const int hd = d->n_q_heads * d->head_dim;
   GlnArgs g{};
   g.rows = (int32_t)c.plan.n_t_rows; g.D = hd; g.x = a; g.ldx = hd; g.y = y; g.ldy = hd;
+  g.x_parts = parts; g.n_parts = n_parts; g.part_stride = c.plan.n_t_rows * hd;
   g.gate = u; g.ldg = ldu;
   g.gamma = g2; g.beta = b2; g.type = nullptr; g.type_const = TT_T; g.eps = d->ln_eps;
   return timed_gln(g, dt, c.s);
@@ -593,9 +615,11 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   aa.per_group = 1;
+  float* parts = L.ksplit > 1 ? (float*)(ws + L.apart) : nullptr;
+  if (parts) { aa.ksplit = L.ksplit; aa.a_part = parts; aa.part_stride = p.n_t_rows * hd; }
   TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
 
-  TRY(target_gated_gln(c, d, w->ln2_g, w->ln2_b, a, zt, zw, y, dt));
+  TRY(target_gated_gln(c, d, w->ln2_g, w->ln2_b, a, zt, zw, y, dt, parts, L.ksplit));
 
   GemmArgs go{};
   go.M = (int32_t)p.n_parents; go.N = D; go.K = hd; go.groups = S;
@@ -736,7 +760,8 @@ __global__ void rebase_tiles_kernel(const int32_t* in, int n, const int32_t* ctx
 }
 
 struct ServeWs {
-  int64_t tiles = 0, xtt = 0, zt = 0, a = 0, y = 0, total = 0;
+  int64_t tiles = 0, xtt = 0, zt = 0, a = 0, y = 0, apart = 0, total = 0;
+  int32_t ksplit = 1;   // key splits of the target attention (fp32 partials of A at apart)
 };
 
 ServeWs serve_ws(const MetaPlan& p, const mtfm_dims* d) {
@@ -750,6 +775,8 @@ ServeWs serve_ws(const MetaPlan& p, const mtfm_dims* d) {
   w.zt = take(T * zw * 2);
   w.a = take(T * hd * 2);
   w.y = take(T * hd * 2);
+  w.ksplit = target_key_splits(p, d);
+  w.apart = take(w.ksplit > 1 ? w.ksplit * T * hd * 4 : 0);
   w.total = off;
   return w;
 }
@@ -814,9 +841,12 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   aa.p = c.meta.p; aa.n = c.meta.n; aa.lens = c.b->lens_d;
   aa.H = H; aa.G = G; aa.dh = dh; aa.out_scale = kLn2;
   aa.per_group = 1;
+  float* parts = L.ksplit > 1 ? (float*)(ws + L.apart) : nullptr;
+  if (parts) { aa.ksplit = L.ksplit; aa.a_part = parts; aa.part_stride = p.n_t_rows * hd; }
   TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
 
-  TRY(target_gated_gln(c, d, fw ? fw->ln2_g : tw->ln2_g, fw ? fw->ln2_b : tw->ln2_b, a, zt, zw, y, dt));
+  TRY(target_gated_gln(c, d, fw ? fw->ln2_g : tw->ln2_g, fw ? fw->ln2_b : tw->ln2_b, a, zt, zw, y, dt, parts,
+                       L.ksplit));
 
   GemmArgs go{};
   go.M = (int32_t)p.n_t_rows; go.N = D; go.K = hd; go.groups = 1;

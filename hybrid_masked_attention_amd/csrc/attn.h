@@ -53,6 +53,14 @@ struct AttnArgs {
   // bf16 path: one workgroup per KV group of a query half instead of one per
   // query half (G times the workgroups; A only, no fused epilogue)
   int32_t per_group;
+  // bf16 path with per_group, optional key splits (ksplit > 1): each slice's
+  // key tiles are divided into ksplit contiguous runs, one workgroup each
+  // (ksplit times the workgroups); run s writes its fp32 partial of A (the
+  // 1/n scale applied; the T row's own key in run 0) to
+  // a_part + s * part_stride with row stride lda, and A itself is not written.
+  // The partials of every run are written, zeros for an empty run.
+  int32_t ksplit;
+  float* a_part; int64_t part_stride;
 };
 
 mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s);

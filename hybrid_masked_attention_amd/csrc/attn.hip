@@ -109,7 +109,12 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
   // workgroup takes one group's heads (the grid has G times the blocks).  With
   // a work order, workgroup b runs on XCD b % 8 and takes the (b / 8)-th item
   // of that XCD's list (the G groups of a slice one after another).
-  const int ngrp = g.per_group ? g.G : 1;
+  // (with key splits, the ksplit runs of a (slice, group) are further
+  // consecutive logical blocks, the group varying fastest; splits come with
+  // per_group, whose instances make one pass)
+  const int ng = g.per_group ? g.G : 1;
+  const int nks = P == 1 && g.ksplit > 1 ? g.ksplit : 1;
+  const int ngrp = ng * nks;
   int gsel, sid;
   if (g.order) {
     const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
@@ -121,6 +126,8 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
     gsel = lb % ngrp;
     sid = lb / ngrp;
   }
+  const int ks = gsel / ng;
+  gsel %= ng;
   const int slice = sid & 1, tile = sid >> 1;
   MTFM_DCHECK_UNIFORM(tile < g.ntiles, "attention work-order entry");
   const int32_t* td = g.tiles + 8 * tile;
@@ -168,6 +175,8 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
   const int kz_end = urow0 + pmax_s;
   const int kfull = urow0 + pmin_s;
   const int n_main = pmax_s > 0 ? (kz_end - T0 + 63) >> 6 : 0;
+  // this workgroup's run of key tiles [it0, it1) (all of them without splits)
+  const int it0 = (int)((int64_t)n_main * ks / nks), it1 = (int)((int64_t)n_main * (ks + 1) / nks);
 
   // DMA: the stage's 16 GPP chunks of 1 KB (per group: 8 of K rows, 8 of V^T
   // rows, 8 rows of 128 B each); wave w issues chunks w + W i.  Lane -> row
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
   // Tiles past the last one are issued as empty loads (zero-size resources), so
   // that the number of DMA instructions in flight is a constant at every wait.
   auto issue = [&](int gbase, int it, int stage) {
-    const bool real = it < n_main;
+    const bool real = it < it1;
     const int ts = real ? T0 + it * 64 : T0;
     // K through one resource over the user's visible keys [urow0, kz_end): a row
     // of the tile outside it has an offset (negative ones wrap) past the
@@ -229,7 +238,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
       a_barrier();                             // every wave is done with the previous pass's ring
     }
 #pragma unroll
-    for (int s = 0; s < AS; ++s) issue(gbase, s, s);
+    for (int s = 0; s < AS; ++s) issue(gbase, it0 + s, s);
     // Q fragments (B operand of S^T = K Q^T): query l32, dims kk*16 + 8*hi + [0, 8)
     bf16x8 qf[4];
     {
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
 
     int stage = 0;
     auto next_tile = [&](int it) {
-      if (it + 1 < n_main) {
+      if (it + 1 < it1) {
         // tile it + 1 has landed once at most AS - 2 newer tiles' DMA are in flight;
         // after the barrier every wave is done with this stage and it is refilled
         a_wait_vm_lgkm<(AS - 2) * CPW>();
@@ -319,12 +328,12 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
     // (straight-line, so the compiler overlaps one block's SiLU with the next
     // block's products); the few tiles in which some row's prefix ends follow.
     const int n_unmasked = kfull >= kz_end ? n_main : min(n_main, max(kfull - T0, 0) >> 6);
-    int it = 0;
-    for (; it < n_unmasked; ++it) {
+    int it = it0;
+    for (; it < min(n_unmasked, it1); ++it) {
       tile_body(gl_lds + stage * STAGE, MaskNone{}, 0, 0, 0);
       next_tile(it);
     }
-    for (; it < n_main; ++it) {
+    for (; it < it1; ++it) {
       const int ts = T0 + it * 64;
       tile_body(gl_lds + stage * STAGE, MaskUpper{}, max(urow0 - ts, 0), urow0 + plim - ts, kz_end - ts);
       next_tile(it);
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
     // direction is never tiled): its score and value term in registers.  The
     // lane holds half of the query's dims (kk*16 + 8hi + [0, 8)); the other half
     // is in lane ^ 32.
-    if (any_self) {
+    if (any_self && ks == 0) {
       // (the row index passes through an empty asm so that the row addresses
       // are formed here in each pass rather than kept live across the passes)
       int qs = qi;
@@ -370,6 +379,22 @@ __global__ __launch_bounds__(64 * R * GPP, (FusedShape<R, GPP>::template occupan
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[pp][mb][i] *= rq;
+  if (nks > 1) {
+    // key splits: this run's fp32 partial (per_group: one pass, one head per wave)
+    if (ok) {
+      float* prow = g.a_part + ks * g.part_stride + (int64_t)qi * g.lda + (gsel * W + wave) * DH + 4 * hi;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = o[0][mb][4 * j + t];
+          *(f32x4*)(prow + mb * 32 + 8 * j) = v;
+        }
+    }
+    return;
+  }
   if (g.a && ok) {
 #pragma unroll
     for (int pp = 0; pp < P; ++pp) {
@@ -492,7 +517,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs g) {
 
 template <int R, int GPP, int P>
 void launch_fused(const AttnArgs& a, hipStream_t s) {
-  const unsigned blocks = (unsigned)((a.order ? (int64_t)a.n_order : 2 * (int64_t)a.ntiles) * (a.per_group ? a.G : 1));
+  const unsigned blocks = (unsigned)((a.order ? (int64_t)a.n_order : 2 * (int64_t)a.ntiles) * (a.per_group ? a.G : 1) *
+                                     (a.ksplit > 1 ? a.ksplit : 1));
   attn_bf16_kernel<R, GPP, P><<<blocks, 64 * R * GPP, 0, s>>>(a);
 }
 
@@ -559,6 +585,9 @@ mtfm_status launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
       return MTFM_E_UNSUPPORTED;
     if (a.max_user_rows <= 0) return MTFM_E_UNSUPPORTED;
     if (a.per_group && a.y) return MTFM_E_UNSUPPORTED;   // the gated epilogue needs every head of a row
+    if (a.ksplit > 1 && (!a.per_group || !a.a_part || ((uintptr_t)a.a_part & 15) || a.part_stride % 4 != 0 ||
+                         a.ksplit > 64))
+      return MTFM_E_UNSUPPORTED;
     if (a.order && (a.n_order <= 0 || a.n_order % 8 != 0)) return MTFM_E_UNSUPPORTED;
     if (!a.qperm != !a.gperm) return MTFM_E_UNSUPPORTED;
     if (a.y && (!a.u || !a.ln_g || !a.ln_b || !a.type || a.ldy % 4 != 0 || a.ldu % 4 != 0 ||

@@ -158,7 +158,7 @@ struct MetaPlan {
   int32_t n_users = 0, split = 1;
   int64_t n_rows = 0, n_t_rows = 0, n_parents = 0, n_ctx_rows = 0;
   int64_t n_full_tiles = 0, n_target_tiles = 0, n_key_tiles = 0;
-  int32_t max_user_rows = 0, max_t_rows = 0;
+  int32_t max_user_rows = 0, max_t_rows = 0, max_ctx_rows = 0;
   int64_t n_full_order = 0, n_target_order = 0;   // work-order entries (8 x longest XCD list; 0 = none)
   mtfm_meta_layout lay{};
 };

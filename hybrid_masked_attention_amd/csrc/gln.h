@@ -26,6 +26,10 @@ struct GlnArgs {
   void* y_more[3];
   const float* gamma_more[3]; const float* beta_more[3];
   int32_t zero_t;
+  // optional (gated form only): the input row is the sum of n_parts fp32
+  // rows x_parts + k * part_stride + row * ldx, k = 0, 1, ... in that order
+  // (the attention's key-split partials); x is then not read
+  const float* x_parts; int32_t n_parts; int64_t part_stride;
 };
 
 mtfm_status launch_gln(const GlnArgs& a, int dtype, hipStream_t s);

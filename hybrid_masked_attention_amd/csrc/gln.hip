@@ -70,7 +70,17 @@ __global__ __launch_bounds__(256) void gln_kernel(GlnArgs a) {
     ok[r] = row < a.rows;
     const int rr = ok[r] ? row : row0;   // a row past the end re-reads the first (never stored)
     xrow[r] = a.xlist ? (int64_t)a.xlist[rr / a.xdiv] + rr % a.xdiv : rr;
-    load_row<T, VPL>((const T*)a.x + xrow[r] * a.ldx + lane * VPL, v[r]);
+    if (GATE && a.x_parts) {
+      load_row<float, VPL>(a.x_parts + xrow[r] * a.ldx + lane * VPL, v[r]);
+      for (int k = 1; k < a.n_parts; ++k) {
+        float w[VPL];
+        load_row<float, VPL>(a.x_parts + k * a.part_stride + xrow[r] * a.ldx + lane * VPL, w);
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) v[r][j] += w[j];
+      }
+    } else {
+      load_row<T, VPL>((const T*)a.x + xrow[r] * a.ldx + lane * VPL, v[r]);
+    }
     if constexpr (GATE) load_row<T, VPL>((const T*)a.gate + (int64_t)rr * a.ldg + lane * VPL, g[r]);
   }
   float mean[RPW], rstd[RPW];
@@ -152,5 +162,8 @@ mtfm_status launch_gln(const GlnArgs& a, int dtype, hipStream_t s) {
   if (a.D % 64 != 0 || a.n_more < 0 || a.n_more > 3 || (a.xlist && a.xdiv < 1)) return MTFM_E_UNSUPPORTED;
   for (int o = 0; o < a.n_more; ++o)
     if (!a.y_more[o] || !a.gamma_more[o] || !a.beta_more[o]) return MTFM_E_NULL;
+  if (a.x_parts && (!a.gate || a.n_parts < 1 || ((uintptr_t)a.x_parts & 15) || a.ldx % 4 != 0 ||
+                    a.part_stride % 4 != 0))
+    return MTFM_E_UNSUPPORTED;
   return dtype == MTFM_BF16 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
 }

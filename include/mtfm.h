@@ -273,8 +273,12 @@ mtfm_status mtfm_backbone_fwd(const mtfm_batch* batch, const mtfm_dims* dims, in
  * changes H or R rows); each target layer then normalises only its T rows.
  * That needs this much workspace; with less (but at least
  * mtfm_workspace_bytes(batch, dims, MTFM_OP_BACKBONE)) the layers run one by
- * one.  Both orders compute the same values, and everything runs on
- * `stream`.  Returns 0 on invalid arguments.
+ * one.  Both orders compute the same values bit for bit, except with few T
+ * rows against long contexts: there the hoisted order splits each T slice's
+ * keys in the target attention over several workgroups (fp32 partials added
+ * in a fixed order by the following normalisation), which agrees with the
+ * one-by-one order to rounding.  Everything runs on `stream`.  Returns 0 on
+ * invalid arguments.
  * Host only. */
 size_t mtfm_backbone_workspace_bytes(const mtfm_batch* batch, const mtfm_dims* dims, int32_t k_target);
 
@@ -392,8 +396,13 @@ mtfm_status mtfm_backbone_v2_fwd(const mtfm_batch* batch, const mtfm_dims* dims,
  *     attending to the cached context K/V of its user (visible prefix from
  *     the mask) and to itself.
  *
- * The T rows come out exactly as mtfm_backbone_fwd would leave them for the
- * batch holding context and candidates together.  Cache layout, per layer l
+ * The T rows come out as mtfm_backbone_fwd would leave them for the batch
+ * holding context and candidates together, to rounding (the cache packs the
+ * context rows without the T rows between users, so the attention groups its
+ * keys differently).  With few candidates against long contexts the target
+ * attention splits each 32-row slice's keys over several workgroups (fp32
+ * partials added in a fixed order by the following normalisation; up to 16
+ * MiB of the workspace).  Cache layout, per layer l
  * in stack order (block b's full layer, then its target layers): K
  * [n_ctx_rows][G*dh], then V^T [G*dh][ldvt] with ldvt = n_ctx_rows rounded up
  * to 64 (bf16, 256-byte aligned pieces); context rows of all users back to

@@ -100,3 +100,19 @@ def ws_tensor(ws, off, rows, width, dtype):
     es = 2 if dtype == "bf16" else 4
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     return ws[off:off + rows * width * es].view(tdt).view(rows, width)
+
+
+def target_key_splits(batch, dims):
+    """Key splits the library gives the target attention on its inference paths (the host rule:
+    fill ~1,024 workgroup slots, at least 8 key tiles of the longest context per run, at most 16
+    runs, fp32 partials within 16 MiB; 1 = none)."""
+    lens = np.asarray(batch.lens, np.int64)
+    t_rows = int((batch.split * lens[:, 2]).sum()) if len(lens) else 0
+    if t_rows == 0:
+        return 1
+    tiles = int(((batch.split * lens[:, 2] + 63) // 64).sum())
+    wgs = max(2 * tiles * dims.n_kv_heads, 1)
+    part = max(t_rows * dims.n_q_heads * dims.head_dim * 4, 1)
+    ctx = int((lens[:, 0] + lens[:, 1]).max())
+    ks = min(1024 // wgs, (ctx + 63) // 64 // 8, 16, (16 << 20) // part)
+    return ks if ks >= 2 else 1

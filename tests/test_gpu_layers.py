@@ -13,7 +13,7 @@ import pytest
 
 import synth
 from oracle import model as om
-from tests._parity import TOL_BF16, TOL_F32, Report, rounded_inputs, say, to_np, ws_tensor
+from tests._parity import TOL_BF16, TOL_F32, Report, rounded_inputs, say, target_key_splits, to_np, ws_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -273,6 +273,41 @@ def test_backbone_context_stage_matches_layer_by_layer(split, k_target):
     _, b = _backbone_gpu(wl, hoist=False)
     assert np.all(np.isfinite(a))
     np.testing.assert_array_equal(a, b)
+
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_backbone_with_key_split_target_attention(split):
+    """Few T rows against long contexts (two users, 64 candidates): the target attention splits
+    each slice's key tiles over several workgroups and the gated LayerNorm adds their fp32
+    partials.  The hoisted backbone (which splits) against the oracle, and against the
+    layer-by-layer entry points (which keep one workgroup per slice) to rounding.
+
+    Branch bar against the oracle: two half-ulps per layer.  Both sides round X' to bf16 at every
+    layer boundary, so after a layer they can sit one ulp apart whichever path runs: on this
+    workload the unsplit path's T rows, after three layers, reach exactly one half-ulp past a
+    one-half-ulp-per-layer allowance, as the split path's do."""
+    rng = np.random.default_rng(96 + split)
+    lens = np.array([[6000, 2000, 40 // split], [3000, 500, 24 // split]], np.int32)
+    batch = synth.make_batch(rng, lens, split)
+    dims = synth.Dims(512, 8, 2, 64)
+    ks = target_key_splits(batch, dims)
+    say(f"key splits: {ks}")
+    assert ks >= 8
+    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
+    full = [synth.full_weights(rng, dims, 0.02, 0.02)]
+    tgt = [synth.target_weights(rng, dims, split, 0.02, 0.02) for _ in range(2)]
+    wl = synth.Workload(f"key_split_s{split}", batch, dims, "bf16", x, full=full, target=tgt, n_blocks=1, k_target=2)
+    x0, got = _backbone_gpu(wl, hoist=True)
+    _, lbl = _backbone_gpu(wl, hoist=False)
+    xr, fw, tw = rounded_inputs(wl)
+    np.testing.assert_array_equal(x0, xr)
+    ref = om.backbone(batch, xr, fw, tw, dims, 1, 2, boundary=om.bf16_round)
+    r = Report(TOL_BF16)
+    r.close("X'", got, ref)
+    r.branch("dX vs oracle (6 roundings allowed)", got, ref, xr, "bf16", roundings=6)
+    r.branch("dX vs layer by layer (6 roundings allowed)", got, lbl, xr, "bf16", roundings=6)
+    r.check()
 
 
 def test_small_v2_backbone_against_oracle():

@@ -177,3 +177,32 @@ def test_config3_serving():
     r.branch(f"context rows of user {u} vs oracle", got_c[mc], o[np.searchsorted(urows, ctx_rows[mc])],
              xr[ctx_rows[mc]], "bf16", roundings=16)
     r.check()
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_serving_long_contexts_with_key_splits(split):
+    """Candidates of two users with long histories: the serving target attention splits the
+    cached keys of each slice over several workgroups.  Against the oracle and the backbone,
+    two bf16 half-ulps of X' allowed per layer on both (both sides round X' at every layer
+    boundary, so they can sit one ulp apart after each)."""
+    import torch
+    from hybrid_masked_attention_amd import binding as B
+    from hybrid_masked_attention_amd.tensors import DeviceWorkload
+    from tests._parity import target_key_splits
+    wl = _small(split, 140 + split, n_blocks=1, k_target=2,
+                lens=[[6000, 2000, 40 // split], [3000, 500, 24 // split]])
+    assert target_key_splits(wl.batch, wl.dims) >= 8
+    dw = DeviceWorkload(wl)
+    ref = to_np(_backbone(wl, dw, B, torch))
+    ctx_rows, t_rows = _rows(wl.batch)
+    x_ctx, cache = _serve_context(wl, dw, B, torch)
+    x_t = dw.x[torch.as_tensor(t_rows, device="cuda")].contiguous()
+    _serve_targets(wl, dw, B, torch, cache, x_t)
+    torch.cuda.synchronize()
+    xr, full, tgt = rounded_inputs(wl)
+    o = om.backbone(wl.batch, xr, full, tgt, wl.dims, wl.n_blocks, wl.k_target, boundary=om.bf16_round)
+    r = Report(TOL_BF16)
+    layers = wl.n_blocks * (1 + wl.k_target)
+    r.branch("T rows vs oracle", to_np(x_t), o[t_rows], xr[t_rows], "bf16", roundings=2 * layers)
+    r.branch("T rows vs backbone", to_np(x_t), ref[t_rows], xr[t_rows], "bf16", roundings=2 * layers)
+    r.check()
