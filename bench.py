@@ -510,6 +510,43 @@ def main():
             f"({serve['candidates_per_s']:.0f} candidates/s, {serve['vs_full_forward'] or 0:.1f}x the full forward)")
         del cache, ws_c, ws_t, x_c, x_t, x_c0, x_t0
 
+        # one request: a single user's long history cached, a list of candidates against it (the
+        # target attention then splits each slice's keys over several workgroups)
+        b1 = synth.make_batch(np.random.default_rng(31), np.array([[6000, 2000, 512]], np.int32), 1)
+        db1 = B.DeviceBatch(b1.lens, 1, b1.ts_r, b1.ts_t)
+        lens1c = b1.lens.copy()
+        lens1c[:, 2] = 0
+        cb1 = B.DeviceBatch(lens1c, 1, b1.ts_r, np.zeros(0, np.int32))
+        meta1c, meta1 = B.mask_build(cb1), B.mask_build(db1)
+        cache1 = torch.empty(B.kv_cache_bytes(cb1, dims, wl.n_blocks, wl.k_target), dtype=torch.uint8, device="cuda")
+        ws1c = torch.empty(B.serve_workspace_bytes(cb1, dims, wl.k_target, B.SERVE_CONTEXT), dtype=torch.uint8,
+                           device="cuda")
+        ws1t = torch.empty(B.serve_workspace_bytes(db1, dims, wl.k_target, B.SERVE_TARGETS), dtype=torch.uint8,
+                           device="cuda")
+        gen = torch.Generator().manual_seed(32)
+        xc1 = torch.randn(8000, dims.d_model, generator=gen).to(device="cuda", dtype=torch.bfloat16)
+        xt1_0 = torch.randn(512, dims.d_model, generator=gen).to(device="cuda", dtype=torch.bfloat16)
+        xt1 = xt1_0.clone()
+        B.serve_context(cb1, dims, wl.n_blocks, wl.k_target, meta1c, dw.full, dw.target, xc1, cache1, ws1c)
+
+        def one_pass():
+            xt1.copy_(xt1_0)
+            B.mask_build(db1, meta1)
+            B.serve_targets(db1, dims, wl.n_blocks, wl.k_target, meta1, dw.full, dw.target, cache1, xt1, ws1t)
+
+        one_pass()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.serve_steps):
+            one_pass()
+        torch.cuda.synchronize()
+        one_ms = 1000.0 * (time.perf_counter() - t0) / args.serve_steps
+        serve["one_user"] = {"what": "one user's 6000 H + 2000 R rows cached (16 layers), 512 candidates through "
+                                     "the 16 layers against it; metadata build included",
+                             "candidate_pass_ms": one_ms, "candidates_per_s": 512 / (one_ms * 1e-3)}
+        log(f"serving one user (8000 context rows, 512 candidates): {one_ms:.3f} ms/pass")
+        del cache1, ws1c, ws1t, xc1, xt1, xt1_0
+
     v2 = None
     if args.v2_steps > 0:
         from hybrid_masked_attention_amd.tensors import to_device, weights_to_device
