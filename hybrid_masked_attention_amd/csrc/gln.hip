@@ -56,7 +56,7 @@ MTFM_DEV void store_row(T* p, const float* v) {
 // One wave per RPW consecutive rows: every row's loads are issued before any
 // reduction, so a wave keeps RPW x 64 x 16 bytes in flight (the kernel streams
 // HBM; one row per wave left it latency-bound).
-template <typename T, int VPL, int NOUT, int RPW, bool GATE>
+template <typename T, int VPL, int NOUT, int RPW, bool GATE, bool PARTS = false>
 __global__ __launch_bounds__(256) void gln_kernel(GlnArgs a) {
   const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
   const int lane = threadIdx.x & 63;
@@ -70,18 +70,29 @@ __global__ __launch_bounds__(256) void gln_kernel(GlnArgs a) {
     ok[r] = row < a.rows;
     const int rr = ok[r] ? row : row0;   // a row past the end re-reads the first (never stored)
     xrow[r] = a.xlist ? (int64_t)a.xlist[rr / a.xdiv] + rr % a.xdiv : rr;
-    if (GATE && a.x_parts) {
-      load_row<float, VPL>(a.x_parts + xrow[r] * a.ldx + lane * VPL, v[r]);
-      for (int k = 1; k < a.n_parts; ++k) {
-        float w[VPL];
-        load_row<float, VPL>(a.x_parts + k * a.part_stride + xrow[r] * a.ldx + lane * VPL, w);
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) v[r][j] += w[j];
-      }
-    } else {
-      load_row<T, VPL>((const T*)a.x + xrow[r] * a.ldx + lane * VPL, v[r]);
-    }
+    if constexpr (PARTS) load_row<float, VPL>(a.x_parts + xrow[r] * a.ldx + lane * VPL, v[r]);
+    else load_row<T, VPL>((const T*)a.x + xrow[r] * a.ldx + lane * VPL, v[r]);
     if constexpr (GATE) load_row<T, VPL>((const T*)a.gate + (int64_t)rr * a.ldg + lane * VPL, g[r]);
+  }
+  if constexpr (PARTS) {
+    // the other partials, added in order; two parts of every row in flight at once
+    for (int k = 1; k < a.n_parts; k += 2) {
+      const bool two = k + 1 < a.n_parts;
+      float w[2][RPW][VPL];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float* base = a.x_parts + xrow[r] * a.ldx + lane * VPL;
+        load_row<float, VPL>(base + k * a.part_stride, w[0][r]);
+        load_row<float, VPL>(base + (two ? k + 1 : k) * a.part_stride, w[1][r]);
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          v[r][j] += w[0][r][j];
+          if (two) v[r][j] += w[1][r][j];
+        }
+    }
   }
   float mean[RPW], rstd[RPW];
 #pragma unroll
@@ -125,16 +136,16 @@ __global__ __launch_bounds__(256) void gln_kernel(GlnArgs a) {
   }
 }
 
-template <typename T, int NOUT, bool GATE>
+template <typename T, int NOUT, bool GATE, bool PARTS = false>
 mtfm_status launch_n(const GlnArgs& a, hipStream_t s) {
   constexpr int RPW = 4;
   const unsigned blocks = (unsigned)((a.rows + 4 * RPW - 1) / (4 * RPW));
   switch (a.D / 64) {
-    case 1: gln_kernel<T, 1, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
-    case 2: gln_kernel<T, 2, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
-    case 4: gln_kernel<T, 4, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
-    case 8: gln_kernel<T, 8, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
-    case 16: gln_kernel<T, 16, NOUT, RPW, GATE><<<blocks, 256, 0, s>>>(a); break;
+    case 1: gln_kernel<T, 1, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
+    case 2: gln_kernel<T, 2, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
+    case 4: gln_kernel<T, 4, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
+    case 8: gln_kernel<T, 8, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
+    case 16: gln_kernel<T, 16, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
     default: return MTFM_E_UNSUPPORTED;
   }
   MTFM_LAUNCH_CHECK("gln");
@@ -145,7 +156,10 @@ mtfm_status launch_n(const GlnArgs& a, hipStream_t s) {
 // several outputs only for the ungated context normalisation.
 template <typename T>
 mtfm_status launch_t(const GlnArgs& a, hipStream_t s) {
-  if (a.gate) return a.n_more == 0 ? launch_n<T, 1, true>(a, s) : MTFM_E_UNSUPPORTED;
+  if (a.gate) {
+    if (a.n_more != 0) return MTFM_E_UNSUPPORTED;
+    return a.x_parts ? launch_n<T, 1, true, true>(a, s) : launch_n<T, 1, true>(a, s);
+  }
   switch (a.n_more) {
     case 0: return launch_n<T, 1, false>(a, s);
     case 1: return launch_n<T, 2, false>(a, s);

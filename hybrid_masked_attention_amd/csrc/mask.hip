@@ -158,18 +158,23 @@ __global__ __launch_bounds__(256) void tsort_kernel(const int32_t* __restrict__ 
                                                      const int32_t* __restrict__ table,
                                                      const int32_t* __restrict__ p_in, int32_t* __restrict__ tsq,
                                                      int32_t* __restrict__ tsg) {
+  __shared__ int32_t ps[kTSortMaxRows];   // the user's prefixes, read from LDS by every comparison
   const int stride = n_users + 1;
   const int u = blockIdx.x;
   const int lc = lens[3 * u] + lens[3 * u + 1], nt = split * lens[3 * u + 2];
   const int g0 = table[UT_ROW * stride + u] + lc, t0 = table[UT_TROW * stride + u];
-  const bool sort = nt <= kTSortMaxRows;
+  const bool sort = nt <= kTSortMaxRows;   // the same for the whole workgroup
+  if (sort) {
+    for (int i = threadIdx.x; i < nt; i += blockDim.x) ps[i] = p_in[g0 + i];
+    __syncthreads();
+  }
   for (int i = threadIdx.x; i < nt; i += blockDim.x) {
     int rank = i;
     if (sort) {
-      const int pi = p_in[g0 + i];
+      const int pi = ps[i];
       rank = 0;
       for (int j = 0; j < nt; ++j) {
-        const int pj = p_in[g0 + j];
+        const int pj = ps[j];
         rank += (pj < pi) || (pj == pi && j < i);
       }
     }
