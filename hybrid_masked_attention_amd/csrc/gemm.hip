@@ -80,14 +80,16 @@ constexpr int G_EP_BYTES = 9216;                  // per-wave epilogue staging: 
 
 // Tile rows: 256 (wave tile 128 x 64, three workgroups per CU) for large M,
 // 128 (wave tile 64 x 64, four per CU) when 256-row tiles would leave CUs idle.
-template <int BM> struct GShape {
+// NS ring stages: GS, or four for grids smaller than the CU count (a lone
+// workgroup per CU waits on each K step's loads; LDS is no constraint there).
+template <int BM, int NS = GS> struct GShape {
   static constexpr int LA = BM / G_RPC / GNW;     // DMA instructions per wave per K step: A
   static constexpr int TM = BM / 64;              // MFMA row blocks per wave
   static constexpr int WR = BM / 2;               // wave tile rows
   static constexpr int STAGE = (BM + GBN) * GBK * 2;
-  static constexpr int VMC0 = (GS - 1) * (LA + G_LB);
-  static constexpr int WG_PER_CU = BM == 256 ? 3 : 4;
-  static constexpr int LDS = GS * STAGE > GNW * G_EP_BYTES ? GS * STAGE : GNW * G_EP_BYTES;  // ring, then staging
+  static constexpr int VMC0 = (NS - 1) * (LA + G_LB);
+  static constexpr int WG_PER_CU = NS != GS ? 2 : (BM == 256 ? 3 : 4);
+  static constexpr int LDS = NS * STAGE > GNW * G_EP_BYTES ? NS * STAGE : GNW * G_EP_BYTES;  // ring, then staging
 };
 constexpr uint32_t kOobOffset = 0x80000000u;      // voffset of a row past the end (reads zero)
 
@@ -221,11 +223,11 @@ template <int BM> struct S24Shape {
 
 typedef __attribute__((__vector_size__(16 * sizeof(__bf16)))) __bf16 bf16x16;
 
-template <int EPI, int GBM, bool SP>
-__global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::WG_PER_CU) void gemm_bf16_kernel(GemmArgs g) {
-  using SH = GShape<GBM>;
+template <int EPI, int GBM, bool SP, int NS = GS>
+__global__ __launch_bounds__(256, (SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM, NS>::WG_PER_CU)) void gemm_bf16_kernel(GemmArgs g) {
+  using SH = GShape<GBM, NS>;
   constexpr int G_LA = SH::LA, G_TM = SH::TM, G_WR = SH::WR, G_STAGE = SH::STAGE, G_VMC0 = SH::VMC0;
-  constexpr int G_VMC = (GS - 2) * (G_LA + G_LB);
+  constexpr int G_VMC = (NS - 2) * (G_LA + G_LB);
   __shared__ __attribute__((aligned(1024))) char lds[SP ? S24Shape<GBM>::LDS : SH::LDS];
 
   const int n_mt = (g.M + GBM - 1) / GBM, n_nt = (g.N + GBN - 1) / GBN;
@@ -333,9 +335,9 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
 
     const int nk = g.K / GBK;
 #pragma unroll
-    for (int s = 0; s < GS; ++s)
+    for (int s = 0; s < NS; ++s)
       if (s < nk) issue(s, s);
-    if (GS - 1 < nk) wait_vm<G_VMC0>();
+    if (NS - 1 < nk) wait_vm<G_VMC0>();
     else wait_vm<0>();
     barrier_only();
     read(0, 0, 0);
@@ -349,12 +351,12 @@ __global__ __launch_bounds__(256, SP ? S24Shape<GBM>::WG_PER_CU : GShape<GBM>::W
         } else {
           // step s + 1 has landed once at most G_VMC newer DMA instructions are
           // outstanding; the barrier also tells every wave that this stage has
-          // been read (lgkmcnt(0)) so it can be refilled with step s + GS
-          if (s + GS - 1 < nk) wait_vm_lgkm<G_VMC>();
+          // been read (lgkmcnt(0)) so it can be refilled with step s + NS
+          if (s + NS - 1 < nk) wait_vm_lgkm<G_VMC>();
           else wait_vm_lgkm<0>();
           barrier_only();
-          if (s + GS < nk) issue(s + GS, stage);
-          stage = (stage + 1 == GS) ? 0 : stage + 1;
+          if (s + NS < nk) issue(s + NS, stage);
+          stage = (stage + 1 == NS) ? 0 : stage + 1;
           read(stage, 0, cur ^ 1);
         }
         mma(cur);
@@ -1053,6 +1055,13 @@ mtfm_status launch_gemm(const GemmArgs& g, int dtype, hipStream_t s) {
         default: return MTFM_E_UNSUPPORTED;   // the forward projections use these two epilogues
       }
       MTFM_LAUNCH_CHECK("gemm_s24");
+      return MTFM_OK;
+    }
+    if (tiles < device_cu_count() && (g.epi == EPI_SILU_SPLIT || g.epi == EPI_RESID)) {
+      // fewer workgroups than CUs (a few hundred rows): the four-stage ring
+      if (g.epi == EPI_SILU_SPLIT) gemm_bf16_kernel<EPI_SILU_SPLIT, 128, false, 4><<<grid, 256, 0, s>>>(g);
+      else gemm_bf16_kernel<EPI_RESID, 128, false, 4><<<grid, 256, 0, s>>>(g);
+      MTFM_LAUNCH_CHECK("gemm");
       return MTFM_OK;
     }
     switch (g.epi * 2 + (small ? 1 : 0)) {
