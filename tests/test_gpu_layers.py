@@ -276,8 +276,24 @@ def test_backbone_context_stage_matches_layer_by_layer(split, k_target):
 
 
 
-@pytest.mark.parametrize("split", [1, 4])
-def test_backbone_with_key_split_target_attention(split):
+def _long_context_backbone(split, seed, lens):
+    rng = np.random.default_rng(seed)
+    batch = synth.make_batch(rng, np.asarray(lens, np.int32), split)
+    dims = synth.Dims(512, 8, 2, 64)
+    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
+    full = [synth.full_weights(rng, dims, 0.02, 0.02)]
+    tgt = [synth.target_weights(rng, dims, split, 0.02, 0.02) for _ in range(2)]
+    return synth.Workload(f"long_context_s{split}", batch, dims, "bf16", x, full=full, target=tgt, n_blocks=1,
+                          k_target=2)
+
+
+@pytest.mark.parametrize("split,lens", [
+    (1, [[6000, 2000, 40], [3000, 500, 24]]),
+    (4, [[6000, 2000, 10], [3000, 500, 6]]),
+    # degenerate users beside a long one: no context at all, no R rows, one T row
+    (1, [[6000, 2000, 30], [0, 0, 3], [5, 0, 2], [0, 12, 1], [700, 0, 9]]),
+], ids=["s1", "s4", "degenerate_users"])
+def test_backbone_with_key_split_target_attention(split, lens):
     """Few T rows against long contexts (two users, 64 candidates): the target attention splits
     each slice's key tiles over several workgroups and the gated LayerNorm adds their fp32
     partials.  The hoisted backbone (which splits) against the oracle, and against the
@@ -287,17 +303,11 @@ def test_backbone_with_key_split_target_attention(split):
     layer boundary, so after a layer they can sit one ulp apart whichever path runs: on this
     workload the unsplit path's T rows, after three layers, reach exactly one half-ulp past a
     one-half-ulp-per-layer allowance, as the split path's do."""
-    rng = np.random.default_rng(96 + split)
-    lens = np.array([[6000, 2000, 40 // split], [3000, 500, 24 // split]], np.int32)
-    batch = synth.make_batch(rng, lens, split)
-    dims = synth.Dims(512, 8, 2, 64)
+    wl = _long_context_backbone(split, 96 + split + len(lens), lens)
+    batch, dims = wl.batch, wl.dims
     ks = target_key_splits(batch, dims)
     say(f"key splits: {ks}")
     assert ks >= 8
-    x = rng.standard_normal((batch.total_rows, dims.d_model)).astype(np.float32)
-    full = [synth.full_weights(rng, dims, 0.02, 0.02)]
-    tgt = [synth.target_weights(rng, dims, split, 0.02, 0.02) for _ in range(2)]
-    wl = synth.Workload(f"key_split_s{split}", batch, dims, "bf16", x, full=full, target=tgt, n_blocks=1, k_target=2)
     x0, got = _backbone_gpu(wl, hoist=True)
     _, lbl = _backbone_gpu(wl, hoist=False)
     xr, fw, tw = rounded_inputs(wl)
@@ -323,15 +333,20 @@ def test_small_v2_backbone_against_oracle():
     r.check()
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_backbone_forward_replays_from_a_hip_graph(packed):
+@pytest.mark.parametrize("packed,kind", [(False, "small"), (True, "small"), (False, "key_split")])
+def test_backbone_forward_replays_from_a_hip_graph(packed, kind):
     """The hoisted backbone forward captured into a HIP graph: every replay, with eager runs in
     between, equals the eager result bit for bit, with dense and with packed (2:4) weights (each
-    block's context projections one grouped launch over per-layer weight matrices)."""
+    block's context projections one grouped launch over per-layer weight matrices), and on long
+    contexts with few T rows (the target attention's key splits and their summed partials)."""
     import torch
     from hybrid_masked_attention_amd import binding as B
     from hybrid_masked_attention_amd.tensors import DeviceWorkload
-    wl = _small_backbone(4, 80)
+    if kind == "small":
+        wl = _small_backbone(4, 80)
+    else:
+        wl = _long_context_backbone(1, 81, [[6000, 2000, 40], [0, 0, 3], [3000, 500, 24]])
+        assert target_key_splits(wl.batch, wl.dims) >= 8
     dw = DeviceWorkload(wl)
     if packed:
         dw.pack_s24()
