@@ -44,6 +44,42 @@ def visible_pairs(n_rows_meta, lens, split):
     return int(n.sum()), t_sum
 
 
+def computed_pairs(tiles, p, n, gperm=None):
+    """(query, key) pairs per head that the bf16 attention kernel computes over one layer's tile
+    list, and the visible pairs sum(n_i) of the same rows.
+
+    Follows the kernel's own walk: per 32-row slice of a tile, the key tiles of 64 from the user's
+    aligned first row up to the slice's largest visible prefix; tiles below its smallest prefix run
+    both 32-key blocks, the others skip a block no row of the slice sees; every block computes 32
+    rows x 32 keys (rows past the tile's end included); a T row's own key is one more pair.
+    """
+    import numpy as np
+    comp = vis = 0
+    for u, row0, nr, _fe, _end, grow0, qrow0, urow0 in tiles.tolist():
+        for s in (0, 1):
+            m = min(32, nr - 32 * s)
+            if m <= 0:
+                continue
+            q0 = qrow0 + 32 * s
+            gi = gperm[q0:q0 + m] if gperm is not None else np.arange(grow0 + 32 * s, grow0 + 32 * s + m)
+            pl, nl = p[gi], n[gi]
+            vis += int(nl.sum())
+            comp += int((nl - pl).sum())
+            pmax, pmin = int(pl.max()), int(pl.min())
+            if pmax <= 0:
+                continue
+            t0, kz, kf = urow0 & ~63, urow0 + pmax, urow0 + pmin
+            n_main = (kz - t0 + 63) >> 6
+            n_un = n_main if kf >= kz else min(n_main, max(kf - t0, 0) >> 6)
+            blocks = 2 * n_un
+            for it in range(n_un, n_main):
+                ts = t0 + 64 * it
+                lo, lim_hi = max(urow0 - ts, 0), kz - ts
+                blocks += sum(1 for b0 in (0, 32) if not (lo >= b0 + 32 or lim_hi <= b0))
+            comp += 32 * 32 * blocks
+    return comp, vis
+
+
 def recorded_traffic():
     """HBM bytes per launch of the full-layer attention kernel from the committed PMC summary.
 
@@ -337,6 +373,17 @@ def main():
     views = B.meta_views(meta, lay, wl.batch.n_users)
     n_host = views["n"].cpu().numpy().astype(np.int64)
     pairs_full, pairs_t = visible_pairs(n_host, wl.batch.lens.astype(np.int64), wl.batch.split)
+    # tile-padding waste: pairs the kernel computes per head over visible pairs
+    p_host = views["p"].cpu().numpy().astype(np.int64)
+    comp_f, vis_f = computed_pairs(views["full_tiles"].cpu().numpy(), p_host, n_host)
+    comp_t, vis_t = computed_pairs(views["target_tiles_sorted"].cpu().numpy(), p_host, n_host,
+                                   gperm=views["tsort_g"].cpu().numpy().astype(np.int64))
+    assert vis_f == pairs_full and vis_t == pairs_t, "tile walk and row metadata disagree on the visible pairs"
+    tile_padding = {"what": "(query, key) pairs the attention kernel computes per head (32 x 32 MFMA blocks "
+                            "it runs plus each T row's self term) over the visible pairs sum(n_i)",
+                    "full_layer": comp_f / vis_f if vis_f else None,
+                    "target_layer": comp_t / vis_t if vis_t else None}
+    log("tile padding: " + json.dumps(tile_padding))
     d = wl.dims
     H, G, dh, D = d.n_q_heads, d.n_kv_heads, d.head_dim, d.d_model
     hd, gd = H * dh, G * dh
@@ -375,9 +422,13 @@ def main():
 
     breakdown = None
     if not args.no_breakdown and args.steps > 0:
-        classes = [B.K_MASK, B.K_GLN, B.K_GEMM_UQKV, B.K_ATTN_FULL, B.K_GEMM_OUT, B.K_GEMM_KV, B.K_GEMM_T,
-                   B.K_ATTN_TARGET]
-        names = ["mask", "gln", "gemm_uqkv", "attn_full", "gemm_out", "gemm_kv", "gemm_t", "attn_target"]
+        # full layers: pre-norm, U|Q|K|V projection, attention (gated GLN fused), output projection;
+        # target layers: context and T-row normalisations, K|V and T-row projections, attention,
+        # T-row output projection
+        classes = [B.K_MASK, B.K_GLN, B.K_GEMM_UQKV, B.K_ATTN_FULL, B.K_GEMM_OUT, B.K_GLN_T, B.K_GEMM_KV,
+                   B.K_GEMM_T, B.K_ATTN_TARGET, B.K_GEMM_OUT_T]
+        names = ["mask", "gln_full", "gemm_uqkv", "attn_full", "gemm_out_full", "gln_target", "gemm_kv",
+                 "gemm_t", "attn_target", "gemm_out_t"]
         B.timing_enable(classes)
         for k in classes:
             B.timing_read(k)
@@ -395,8 +446,8 @@ def main():
         breakdown["attn_target"]["achieved_GBs"] = attn_t_bytes / (tat * 1e-3) / 1e9 if tat > 0 else None
         breakdown["attn_target"]["hbm_frac"] = (breakdown["attn_target"]["achieved_GBs"] or 0) / HBM_PEAK_GBS
         breakdown["attn_target"]["achieved_TFLOPs"] = attn_t_flops / (tat * 1e-3) / 1e12 if tat > 0 else None
-        full_ms = (breakdown["attn_full"]["ms_per_step"] + breakdown["gemm_uqkv"]["ms_per_step"]
-                   + breakdown["gemm_out"]["ms_per_step"])
+        full_ms = sum(breakdown[k]["ms_per_step"] for k in ("gln_full", "gemm_uqkv", "attn_full", "gemm_out_full"))
+        breakdown["full_layers_ms_per_step"] = full_ms
         breakdown["full_layers_masked_TFLOPs"] = layers_full * (attn_full_flops + proj_full_flops) / (full_ms * 1e-3) / 1e12
         breakdown["full_layers_mfma_frac"] = breakdown["full_layers_masked_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
         breakdown["sum_ms_per_step"] = sum(v["ms_per_step"] for v in breakdown.values() if isinstance(v, dict))
@@ -617,7 +668,7 @@ def main():
             sparse_step()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        proj = [B.K_GEMM_UQKV, B.K_GEMM_OUT, B.K_GEMM_KV, B.K_GEMM_T]
+        proj = [B.K_GEMM_UQKV, B.K_GEMM_OUT, B.K_GEMM_KV, B.K_GEMM_T, B.K_GEMM_OUT_T]
         B.timing_enable(proj)
         for k in proj:
             B.timing_read(k)
@@ -635,7 +686,8 @@ def main():
                   "projection_ms_per_step": proj_ms,
                   "projection_dense_equiv_TFLOPs": proj_flops / (proj_ms * 1e-3) / 1e12 if proj_ms > 0 else None}
         if breakdown:
-            dense_proj = sum(breakdown[k]["ms_per_step"] for k in ("gemm_uqkv", "gemm_out", "gemm_kv", "gemm_t"))
+            dense_proj = sum(breakdown[k]["ms_per_step"]
+                             for k in ("gemm_uqkv", "gemm_out_full", "gemm_kv", "gemm_t", "gemm_out_t"))
             sparse["projection_dense_ms_per_step"] = dense_proj
             sparse["projection_speedup"] = dense_proj / proj_ms if proj_ms > 0 else None
         if ms_step:
@@ -676,6 +728,7 @@ def main():
                      "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS if attn_tflops else None,
                      "traffic": recorded_traffic(), "flops_per_launch": attn_full_flops,
                      "ms_per_launch": attn_ms} if args.steps > 0 else None,
+        "tile_padding": tile_padding,
         "breakdown": breakdown,
         "train": train,
         "serve": serve,

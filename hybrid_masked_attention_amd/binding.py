@@ -41,7 +41,8 @@ ENTRY_POINTS = [
 ]
 BAD_ACTION_ORDER, BAD_LENGTHS = 1, 2
 SERVE_CONTEXT, SERVE_TARGETS = 0, 1
-K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD, K_V2 = range(10)
+(K_MASK, K_GLN, K_GEMM_UQKV, K_ATTN_FULL, K_GEMM_OUT, K_GEMM_KV, K_GEMM_T, K_ATTN_TARGET, K_BWD, K_V2,
+ K_GLN_T, K_GEMM_OUT_T) = range(12)
 
 
 class MtfmError(RuntimeError):

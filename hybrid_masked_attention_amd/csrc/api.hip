@@ -299,7 +299,7 @@ static mtfm_status target_gated_gln(const Ctx& c, const mtfm_dims* d, const floa
   g.x_parts = parts; g.n_parts = n_parts; g.part_stride = c.plan.n_t_rows * hd;
   g.gate = u; g.ldg = ldu;
   g.gamma = g2; g.beta = b2; g.type = nullptr; g.type_const = TT_T; g.eps = d->ln_eps;
-  return timed_gln(g, dt, c.s);
+  return timed_gln(g, dt, c.s, MTFM_K_GLN_T);
 }
 
 // ---------------------------------------------------------------------------
@@ -422,7 +422,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   GlnArgs g1{};
   g1.rows = (int32_t)p.n_rows; g1.D = D; g1.x = x_in; g1.ldx = D; g1.y = xt; g1.ldy = D;
   g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
-  TRY(timed_gln(g1, dt, c.s));
+  TRY(timed_gln(g1, dt, c.s, MTFM_K_GLN_T));
 
   if (p.n_ctx_rows > 0) {
     // K (row-major) and V of every packed row (the T rows' are unused): the
@@ -487,7 +487,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
     g2.rows = (int32_t)p.n_t_rows; g2.D = hd; g2.x = a; g2.ldx = hd; g2.y = y; g2.ldy = hd;
     g2.gate = zt; g2.ldg = zw;
     g2.gamma = w->ln2_g; g2.beta = w->ln2_b; g2.type = nullptr; g2.type_const = TT_T; g2.eps = d->ln_eps;
-    TRY(timed_gln(g2, dt, c.s));
+    TRY(timed_gln(g2, dt, c.s, MTFM_K_GLN_T));
   }
 
   GemmArgs go{};
@@ -497,7 +497,7 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
   go.bs24 = w->w_o_s24; go.bs24_rows = D;
   go.cmap = RowMap{c.meta.parent_row, 0, 0}; go.cmap_zadd = 1;
   go.epi = EPI_RESID; go.resid = x_in; go.ldr = D; go.out = x_out; go.ldo = D;
-  TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
+  TRY(timed_gemm(MTFM_K_GEMM_OUT_T, go, dt, c.s));
   return MTFM_OK;
 }
 
@@ -522,7 +522,7 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
   for (int l = 1; l < k; ++l) {
     g1.y_more[l - 1] = ws + L.xt[l]; g1.gamma_more[l - 1] = w[l].ln1_g; g1.beta_more[l - 1] = w[l].ln1_b;
   }
-  TRY(timed_gln(g1, dt, c.s));
+  TRY(timed_gln(g1, dt, c.s, MTFM_K_GLN_T));
   int n_packed = 0;
   for (int l = 0; l < k; ++l) n_packed += w[l].w_kv_s24 ? 1 : 0;
   if (!kv && dt == MTFM_BF16 && (n_packed == 0 || n_packed == k)) {
@@ -580,7 +580,7 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   g1.rows = (int32_t)p.n_t_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = xtt; g1.ldy = D;
   g1.xlist = c.meta.parent_row; g1.xdiv = S;
   g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = nullptr; g1.type_const = TT_T; g1.eps = d->ln_eps;
-  TRY(timed_gln(g1, dt, c.s));
+  TRY(timed_gln(g1, dt, c.s, MTFM_K_GLN_T));
 
   GemmArgs gt{};
   gt.M = (int32_t)p.n_parents; gt.N = zw; gt.K = D; gt.groups = S;
@@ -628,7 +628,7 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   go.bs24 = w->w_o_s24; go.bs24_rows = D;
   go.cmap = RowMap{c.meta.parent_row, 0, 0}; go.cmap_zadd = 1;
   go.epi = EPI_RESID; go.resid = x; go.ldr = D; go.out = x; go.ldo = D;
-  TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
+  TRY(timed_gemm(MTFM_K_GEMM_OUT_T, go, dt, c.s));
   return MTFM_OK;
 }
 
@@ -801,7 +801,7 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   g1.rows = (int32_t)p.n_t_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = xtt; g1.ldy = D;
   g1.gamma = fw ? fw->ln1_g : tw->ln1_g; g1.beta = fw ? fw->ln1_b : tw->ln1_b;
   g1.type = nullptr; g1.type_const = TT_T; g1.eps = d->ln_eps;
-  TRY(timed_gln(g1, dt, c.s));
+  TRY(timed_gln(g1, dt, c.s, MTFM_K_GLN_T));
 
   GemmArgs gt{};
   gt.K = D; gt.A = xtt; gt.lda = D; gt.ldb = D;
@@ -855,7 +855,7 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   go.bs24 = fw ? fw->w_o_s24 : tw->w_o_s24; go.bs24_rows = D;
   go.cmap = identity_map();
   go.epi = EPI_RESID; go.resid = x; go.ldr = D; go.out = x; go.ldo = D;
-  TRY(timed_gemm(MTFM_K_GEMM_OUT, go, dt, c.s));
+  TRY(timed_gemm(MTFM_K_GEMM_OUT_T, go, dt, c.s));
   return MTFM_OK;
 }
 

@@ -122,7 +122,7 @@ inline mtfm_status timed_attention(int kclass, const AttnArgs& a, int dt, hipStr
   TimedLaunch t(kclass, s);
   return launch_attention(a, dt, s);
 }
-inline mtfm_status timed_gln(const GlnArgs& a, int dt, hipStream_t s) {
-  TimedLaunch t(MTFM_K_GLN, s);
+inline mtfm_status timed_gln(const GlnArgs& a, int dt, hipStream_t s, int kclass = MTFM_K_GLN) {
+  TimedLaunch t(kclass, s);
   return launch_gln(a, dt, s);
 }

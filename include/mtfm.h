@@ -451,16 +451,20 @@ mtfm_status mtfm_serve_targets_noalloc(const mtfm_batch* batch, const mtfm_dims*
  */
 typedef enum {
   MTFM_K_MASK = 0,         /* mask-metadata builder */
-  MTFM_K_GLN = 1,          /* group LayerNorm (pre-norm and gated post-norm) */
+  MTFM_K_GLN = 1,          /* group LayerNorm over all rows: the full layer's pre-norm (and its
+                              gated post-norm on the fp32 path), the backward's and V2's */
   MTFM_K_GEMM_UQKV = 2,    /* full layer: U|Q|K|V projection */
   MTFM_K_ATTN_FULL = 3,    /* full layer: masked attention */
-  MTFM_K_GEMM_OUT = 4,     /* output projection + residual (both layer types) */
+  MTFM_K_GEMM_OUT = 4,     /* full layer: output projection + residual (all rows) */
   MTFM_K_GEMM_KV = 5,      /* target layer: K|V projection of the H/R rows */
   MTFM_K_GEMM_T = 6,       /* target layer: U|Q|K|V projection of the T rows */
   MTFM_K_ATTN_TARGET = 7,  /* target layer: masked attention */
   MTFM_K_BWD = 8,          /* backward kernels */
   MTFM_K_V2 = 9,           /* V2 target side: AutoSplit, token FFN, mixing, pooling */
-  MTFM_K_COUNT = 10
+  MTFM_K_GLN_T = 10,       /* target layers: context pre-norm of a block's target layers, T-row
+                              pre-norm and gated post-norm (also serving's T-row passes) */
+  MTFM_K_GEMM_OUT_T = 11,  /* output projection + residual of the T rows (target layers, serving) */
+  MTFM_K_COUNT = 12
 } mtfm_kernel_class;
 
 mtfm_status mtfm_timing_enable(uint32_t class_mask);  /* bit k enables class k; 0 disables all */

@@ -48,6 +48,20 @@ def test_status_strings(B):
     assert B.status_str(-4) == "MTFM_E_WORKSPACE"
 
 
+def test_timing_classes_match_the_header(B):
+    """The binding's kernel-class numbers are the header's, and the library refuses a class past the
+    last one (host bookkeeping only: nothing is recorded while no class is enabled)."""
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "mtfm.h")).read()
+    enum = dict((k, int(v)) for k, v in re.findall(r"MTFM_K_(\w+) = (\d+)", text))
+    assert enum.pop("COUNT") == 12
+    for name, value in enum.items():
+        assert getattr(B, "K_" + name) == value, name
+    B.timing_enable([])
+    assert B.timing_read(B.K_GEMM_OUT_T) == (0, 0.0)
+    with pytest.raises(B.MtfmError):
+        B.timing_read(12)
+
+
 def _host_batch(B, lens, split=1, ts_r=None, ts_t=None):
     lens = np.asarray(lens, np.int32).reshape(-1, 3)
     ts_r = np.zeros(max(0, int(lens[:, 1].sum())), np.int32) if ts_r is None else ts_r
