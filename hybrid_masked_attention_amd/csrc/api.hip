@@ -504,7 +504,9 @@ mtfm_status run_target(const Ctx& c, const mtfm_dims* d, const mtfm_target_w* w,
 // ---------------------------------------------------------------------------
 // Context stage of the target layers l = 0..k-1 of one block, right after its
 // full layer: one normalisation pass over all rows writes every layer's X~
-// (T rows as zeros: their K/V are never read as keys), then each layer's K
+// (T rows as zeros in layers 1..k-1: their K/V are never read as keys; layer
+// 0's T rows are its T-row pre-norm, which run_target_rows reads from there,
+// since the T rows have not changed since the full layer), then each layer's K
 // and V^T over all packed rows: when the k layers' K|V weights are all dense
 // or all packed (2:4), one grouped launch (more workgroups than any one
 // layer's, so a shorter tail), else one launch per layer; with a K/V cache
@@ -518,7 +520,7 @@ mtfm_status run_target_context(const Ctx& c, const mtfm_dims* d, const mtfm_targ
   GlnArgs g1{};
   g1.rows = (int32_t)p.n_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = ws + L.xt[0]; g1.ldy = D;
   g1.gamma = w[0].ln1_g; g1.beta = w[0].ln1_b; g1.type = c.meta.type; g1.eps = d->ln_eps;
-  g1.n_more = k - 1; g1.zero_t = 1;
+  g1.n_more = k - 1; g1.zero_t = ((1 << k) - 1) & ~1;
   for (int l = 1; l < k; ++l) {
     g1.y_more[l - 1] = ws + L.xt[l]; g1.gamma_more[l - 1] = w[l].ln1_g; g1.beta_more[l - 1] = w[l].ln1_b;
   }
@@ -576,15 +578,22 @@ mtfm_status run_target_rows(const Ctx& c, const mtfm_dims* d, const mtfm_target_
   if (p.n_t_rows == 0) return MTFM_OK;
 
   // T row t = parent m * S + sub-token z sits at packed row parent_row[m] + z
-  GlnArgs g1{};
-  g1.rows = (int32_t)p.n_t_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = xtt; g1.ldy = D;
-  g1.xlist = c.meta.parent_row; g1.xdiv = S;
-  g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = nullptr; g1.type_const = TT_T; g1.eps = d->ln_eps;
-  TRY(timed_gln(g1, dt, c.s, MTFM_K_GLN_T));
-
   GemmArgs gt{};
   gt.M = (int32_t)p.n_parents; gt.N = zw; gt.K = D; gt.groups = S;
-  gt.A = xtt; gt.lda = D; gt.amap = RowMap{nullptr, S, 0}; gt.amap_zadd = 1;
+  // gathered GEMM rows are addressed through one 31-bit offset range
+  if (l == 0 && (int64_t)p.n_rows * D * 2 + (int64_t)D * 2 < ((int64_t)1 << 31)) {
+    // the context stage's normalisation of layer 0 already holds the T rows' X~
+    // (same rows, same parameters): gather them from there
+    gt.A = ws + L.xt[0]; gt.lda = D; gt.amap = RowMap{c.meta.parent_row, 0, 0}; gt.amap_zadd = 1;
+    gt.a_rows = p.n_rows;
+  } else {
+    GlnArgs g1{};
+    g1.rows = (int32_t)p.n_t_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = xtt; g1.ldy = D;
+    g1.xlist = c.meta.parent_row; g1.xdiv = S;
+    g1.gamma = w->ln1_g; g1.beta = w->ln1_b; g1.type = nullptr; g1.type_const = TT_T; g1.eps = d->ln_eps;
+    TRY(timed_gln(g1, dt, c.s, MTFM_K_GLN_T));
+    gt.A = xtt; gt.lda = D; gt.amap = RowMap{nullptr, S, 0}; gt.amap_zadd = 1;
+  }
   gt.B[0] = w->w_u; gt.bn[0] = hd;
   gt.B[1] = w->w_q; gt.bn[1] = hd; gt.bz[1] = (int64_t)hd * D;
   gt.B[2] = w->w_kv; gt.bn[2] = 2 * gd;

@@ -20,8 +20,9 @@ struct GlnArgs {
   // optional: input row of output row i is xlist[i / xdiv] + i % xdiv (type from that row)
   const int32_t* xlist; int32_t xdiv;
   // optional: up to three more outputs of the same statistics with their own
-  // parameters (same stride ldy); rows of type T written as zeros in every
-  // output when zero_t is set (context-only normalisation)
+  // parameters (same stride ldy); rows of type T written as zeros in output o
+  // (0 = y, o = y_more[o - 1]) when bit o of zero_t is set (context-only
+  // normalisation)
   int32_t n_more;
   void* y_more[3];
   const float* gamma_more[3]; const float* beta_more[3];

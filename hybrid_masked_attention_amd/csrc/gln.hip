@@ -117,9 +117,9 @@ __global__ __launch_bounds__(256) void gln_kernel(GlnArgs a) {
   for (int r = 0; r < RPW; ++r) {
     if (!ok[r]) continue;
     const int t = a.type ? a.type[xrow[r]] : a.type_const;
-    const bool zero = a.zero_t && t == TT_T;
 #pragma unroll
     for (int o = 0; o < NOUT; ++o) {
+      const bool zero = ((a.zero_t >> o) & 1) && t == TT_T;
       const float* gamma = o ? a.gamma_more[o - 1] : a.gamma;
       const float* beta = o ? a.beta_more[o - 1] : a.beta;
       T* y = (T*)(o ? a.y_more[o - 1] : a.y);
