@@ -292,13 +292,14 @@ static void fuse_gated_gln(AttnArgs& aa, const Ctx& c, const mtfm_dims* d, const
 // row, follows as a pass over the T rows alone.
 static mtfm_status target_gated_gln(const Ctx& c, const mtfm_dims* d, const float* g2, const float* b2,
                                     const void* a, const void* u, int64_t ldu, void* y, int dt,
-                                    const float* parts = nullptr, int n_parts = 0) {
+                                    const float* parts = nullptr, int n_parts = 0, bool temporal = false) {
   const int hd = d->n_q_heads * d->head_dim;
   GlnArgs g{};
   g.rows = (int32_t)c.plan.n_t_rows; g.D = hd; g.x = a; g.ldx = hd; g.y = y; g.ldy = hd;
   g.x_parts = parts; g.n_parts = n_parts; g.part_stride = c.plan.n_t_rows * hd;
   g.gate = u; g.ldg = ldu;
   g.gamma = g2; g.beta = b2; g.type = nullptr; g.type_const = TT_T; g.eps = d->ln_eps;
+  g.temporal = temporal ? 1 : 0;
   return timed_gln(g, dt, c.s, MTFM_K_GLN_T);
 }
 
@@ -810,6 +811,10 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   g1.rows = (int32_t)p.n_t_rows; g1.D = D; g1.x = x; g1.ldx = D; g1.y = xtt; g1.ldy = D;
   g1.gamma = fw ? fw->ln1_g : tw->ln1_g; g1.beta = fw ? fw->ln1_b : tw->ln1_b;
   g1.type = nullptr; g1.type_const = TT_T; g1.eps = d->ln_eps;
+  // a candidate pass is T-row work alone: its small normalised outputs stay in
+  // L2 for the projection that reads them next (cached stores; the backbone's
+  // T-row passes measured slower with them, beside its all-row streams)
+  g1.temporal = 1;
   TRY(timed_gln(g1, dt, c.s, MTFM_K_GLN_T));
 
   GemmArgs gt{};
@@ -855,7 +860,7 @@ mtfm_status serve_rows(const Ctx& c, const mtfm_dims* d, const mtfm_full_w* fw, 
   TRY(timed_attention(MTFM_K_ATTN_TARGET, aa, dt, c.s));
 
   TRY(target_gated_gln(c, d, fw ? fw->ln2_g : tw->ln2_g, fw ? fw->ln2_b : tw->ln2_b, a, zt, zw, y, dt, parts,
-                       L.ksplit));
+                       L.ksplit, true));
 
   GemmArgs go{};
   go.M = (int32_t)p.n_t_rows; go.N = D; go.K = hd; go.groups = 1;

@@ -19,6 +19,10 @@ struct GlnArgs {
   float eps;
   // optional: input row of output row i is xlist[i / xdiv] + i % xdiv (type from that row)
   const int32_t* xlist; int32_t xdiv;
+  // ordinary (cached) stores instead of non-temporal ones, single-output forms
+  // only: for small T-row outputs that the next GEMM reads at once (the all-row
+  // outputs stream past L2)
+  int32_t temporal;
   // optional: up to three more outputs of the same statistics with their own
   // parameters (same stride ldy); rows of type T written as zeros in output o
   // (0 = y, o = y_more[o - 1]) when bit o of zero_t is set (context-only

@@ -34,7 +34,7 @@ MTFM_DEV void load_row(const T* p, float* v) {
   }
 }
 
-template <typename T, int VPL>
+template <typename T, int VPL, bool NT>
 MTFM_DEV void store_row(T* p, const float* v) {
   constexpr int BYTES = VPL * (int)sizeof(T);
   if constexpr (BYTES % 16 == 0) {
@@ -45,7 +45,8 @@ MTFM_DEV void store_row(T* p, const float* v) {
       T* e = reinterpret_cast<T*>(&w);
 #pragma unroll
       for (int j = 0; j < 16 / (int)sizeof(T); ++j) e[j] = from_f32<T>(v[c * (16 / sizeof(T)) + j]);
-      __builtin_nontemporal_store(w, &q[c]);
+      if constexpr (NT) __builtin_nontemporal_store(w, &q[c]);
+      else q[c] = w;
     }
   } else {
 #pragma unroll
@@ -56,7 +57,7 @@ MTFM_DEV void store_row(T* p, const float* v) {
 // One wave per RPW consecutive rows: every row's loads are issued before any
 // reduction, so a wave keeps RPW x 64 x 16 bytes in flight (the kernel streams
 // HBM; one row per wave left it latency-bound).
-template <typename T, int VPL, int NOUT, int RPW, bool GATE, bool PARTS = false>
+template <typename T, int VPL, int NOUT, int RPW, bool GATE, bool PARTS = false, bool NT = true>
 __global__ __launch_bounds__(256) void gln_kernel(GlnArgs a) {
   const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
   const int lane = threadIdx.x & 63;
@@ -131,25 +132,35 @@ __global__ __launch_bounds__(256) void gln_kernel(GlnArgs a) {
         w[j] = zero ? 0.f : v[r][j] * rstd[r] * gm[j] + bt[j];
         if constexpr (GATE) w[j] *= g[r][j];
       }
-      store_row<T, VPL>(y + (int64_t)(row0 + r) * a.ldy + lane * VPL, w);
+      store_row<T, VPL, NT>(y + (int64_t)(row0 + r) * a.ldy + lane * VPL, w);
     }
   }
 }
 
-template <typename T, int NOUT, bool GATE, bool PARTS = false>
-mtfm_status launch_n(const GlnArgs& a, hipStream_t s) {
+template <typename T, int NOUT, bool GATE, bool PARTS, bool NT>
+mtfm_status launch_nt(const GlnArgs& a, hipStream_t s) {
   constexpr int RPW = 4;
   const unsigned blocks = (unsigned)((a.rows + 4 * RPW - 1) / (4 * RPW));
   switch (a.D / 64) {
-    case 1: gln_kernel<T, 1, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
-    case 2: gln_kernel<T, 2, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
-    case 4: gln_kernel<T, 4, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
-    case 8: gln_kernel<T, 8, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
-    case 16: gln_kernel<T, 16, NOUT, RPW, GATE, PARTS><<<blocks, 256, 0, s>>>(a); break;
+    case 1: gln_kernel<T, 1, NOUT, RPW, GATE, PARTS, NT><<<blocks, 256, 0, s>>>(a); break;
+    case 2: gln_kernel<T, 2, NOUT, RPW, GATE, PARTS, NT><<<blocks, 256, 0, s>>>(a); break;
+    case 4: gln_kernel<T, 4, NOUT, RPW, GATE, PARTS, NT><<<blocks, 256, 0, s>>>(a); break;
+    case 8: gln_kernel<T, 8, NOUT, RPW, GATE, PARTS, NT><<<blocks, 256, 0, s>>>(a); break;
+    case 16: gln_kernel<T, 16, NOUT, RPW, GATE, PARTS, NT><<<blocks, 256, 0, s>>>(a); break;
     default: return MTFM_E_UNSUPPORTED;
   }
   MTFM_LAUNCH_CHECK("gln");
   return MTFM_OK;
+}
+
+// Cached stores only for single-output forms asked for them (small T-row
+// outputs read at once); every other form stores non-temporally.
+template <typename T, int NOUT, bool GATE, bool PARTS = false>
+mtfm_status launch_n(const GlnArgs& a, hipStream_t s) {
+  if constexpr (NOUT == 1) {
+    if (a.temporal) return launch_nt<T, NOUT, GATE, PARTS, false>(a, s);
+  }
+  return launch_nt<T, NOUT, GATE, PARTS, true>(a, s);
 }
 
 // The gate goes with a single output (the gated LayerNorm after attention);
